@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of CPR Gated DeltaNet on one MI355X.
+
+Step = one gdn_prefill over the rollout-prefill workload: 5 sequences x 2048 tokens, 32 value
+heads over 16 key heads, d_k = d_v = 128, chunk 64, bf16 q/k/v/o, fp32 a/b/state (both passes
+plus the position update).  value = tokens per second of that step.  Alongside: the rollout
+decode workload (256 slots seeded by prefilling ragged prompts of 1..2048 tokens, then 128 timed
+decode steps of one token each), reported as microseconds per step.
+
+Timing: W untimed warm-up steps, then K steps bracketed by torch.cuda.synchronize(); per-kernel
+durations come from HIP events the library records on the launch stream around each pass.
+Inputs are seeded synthetic tensors already resident in HBM.  The fp64 oracle is timed on the
+host over the same prefill workload (a process pool started before the GPU is touched).
+Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "CPR-GDN prefill tok/s (5×2048) + decode µs/step (256×1), % HBM peak"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 FLOP/clk/CU)
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle) worker
+def _oracle_item(item):
+    """Run the oracle on one (sequence, value head); inputs are bf16 bit patterns (uint16)."""
+    import numpy as np
+    from oracle import bf16_bits_to_f64, recurrence
+    q, k, v, a, b = item
+    w = lambda x: bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    t = time.perf_counter()
+    o, S, _ = recurrence(w(q), w(k), w(v), w(a), w(b), chunk=64)
+    return o, S, time.perf_counter() - t
+
+
+def _start_pool(workers):
+    import multiprocessing as mp
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    os.environ["MKL_NUM_THREADS"] = "1"
+    return mp.get_context("spawn").Pool(workers)
+
+
+# ------------------------------------------------------------------ HIP events via the runtime
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev
+
+    def record(self, ev, stream_ptr):
+        rc = self.lib.hipEventRecord(ev, ctypes.c_void_p(stream_ptr))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, e0, e1) -> float:
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), e0, e1)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+
+def prefill_flops(lengths, h_v, dk, dv, chunk):
+    """Algorithmic FLOPs of the two passes.  Per token-head: pass 1 (state only) 5*dk*dv
+    (u = S^T k: 2 dk dv; a*S: dk dv; k c^T added: 2 dk dv); pass 2 adds o = S^T q: 7*dk*dv."""
+    p1_tokens = sum(max(0, ((L - 1) // chunk) * chunk) for L in lengths if L > 0)
+    p2_tokens = sum(lengths)
+    return p1_tokens * h_v * 5 * dk * dv, p2_tokens * h_v * 7 * dk * dv, p1_tokens
+
+
+def decode_bytes(batch, h_k, h_v, dk, dv, io_bytes=2):
+    """Algorithmic HBM bytes of one decode step: the state read and written once, the token's
+    q, k (per key head), v, a, b read and o written."""
+    state = 2 * batch * h_v * dk * dv * 4
+    tokens = batch * (2 * h_k * dk * io_bytes + 2 * h_v * dv * io_bytes + 2 * h_v * 4)
+    return state + tokens
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the CPR kernels are "
+              "benchmarked on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("--steps must be >= 1 and --warmup >= 0")
+
+    pool = None if args.no_cpu_baseline else _start_pool(args.cpu_workers)
+
+    import numpy as np
+    import torch
+
+    import bitwise_aligned_gated_amd as cpr
+    import gdn_inputs as gi
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # ---------------------------------------------------------------- prefill (the timed step)
+    x = gi.config1(device=dev)
+    P = cpr.Policy(x.h_k, x.h_v, x.dk, x.dv, x.chunk, x.io)
+    N, B = x.total_tokens, x.num_seqs
+    spool = cpr.StatePool(P, B, device=dev)
+    rows = cpr.gdn_chunk_rows_bound(N, B, P.chunk)
+    cs = torch.empty((rows, P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)
+    o = torch.empty((N, P.h_v, P.dv), dtype=torch.bfloat16, device=dev)
+    cu = torch.from_numpy(x.cu_seqlens).to(dev)
+    ids = torch.arange(B, dtype=torch.int32, device=dev)
+
+    def step(events=None):
+        cpr.gdn_prefill(spool, cu, x.q, x.k, x.v, x.a, x.b, slot_ids=ids, o=o, chunk_states=cs, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    p1_ms = statistics.mean(hip.ms(e[0], e[1]) for e in evs)
+    p2_ms = statistics.mean(hip.ms(e[1], e[2]) for e in evs)
+    f1, f2, p1_tokens = prefill_flops(list(x.lengths), P.h_v, P.dk, P.dv, P.chunk)
+    kernels = {
+        "boundary_pass": {"avg_ms": p1_ms, "tflops": f1 / (p1_ms * 1e-3) / 1e12, "flop": f1},
+        "output_pass": {"avg_ms": p2_ms, "tflops": f2 / (p2_ms * 1e-3) / 1e12, "flop": f2},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    roofline = {"bound": "alu", "kernel": dom, "achieved": round(kernels[dom]["tflops"], 3),
+                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kernels[dom]["tflops"] / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None}
+    # prefill HBM fraction (the metric's "% HBM peak"): algorithmic bytes of the whole CPR step
+    io = 2
+    in_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4)
+    pass1_reread = p1_tokens * (P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4)
+    n_rows = int(cpr.gdn_chunk_rows(x.cu_seqlens, P.chunk)[-1])
+    bstate = n_rows * P.h_v * P.dk * P.dv * 4
+    cpr_bytes = in_bytes + pass1_reread + 2 * bstate + N * P.h_v * P.dv * io + B * P.h_v * P.dk * P.dv * 4
+    prefill_gbs = cpr_bytes / (ms_step * 1e-3) / 1e9
+
+    # parity of the timed prefill output against the oracle (computed in the CPU leg below)
+    o_host = o.float().cpu().numpy()
+    S_host = spool.state.cpu().numpy()
+
+    # ---------------------------------------------------------------- decode workload
+    decode = None
+    if not args.no_decode:
+        prompts = gi.config2_prompts(device=dev)
+        nb = prompts.num_seqs
+        dpool = cpr.StatePool(P, nb, device=dev)
+        cpr.gdn_prefill(dpool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
+        del prompts
+        toks = [gi.config2_decode_tokens(s, nb, device=dev) for s in range(args.decode_steps)]
+        od = torch.empty((nb, P.h_v, P.dv), dtype=torch.bfloat16, device=dev)
+        dids = torch.arange(nb, dtype=torch.int32, device=dev)
+        wpool = cpr.StatePool(P, nb, device=dev)          # warm-up on a copy; the real states stay put
+        wpool.state.copy_(dpool.state)
+        wpool.pos.copy_(dpool.pos)
+        for s in range(args.warmup):
+            t = toks[s % len(toks)]
+            cpr.gdn_decode_step(wpool, t.q, t.k, t.v, t.a, t.b, slot_ids=dids, o=od)
+        del wpool
+        torch.cuda.synchronize()
+        devs = [[hip.event() for _ in range(3)] for _ in range(args.decode_steps)]
+        t0 = time.perf_counter()
+        for s in range(args.decode_steps):
+            t = toks[s]
+            cpr.gdn_decode_step(dpool, t.q, t.k, t.v, t.a, t.b, slot_ids=dids, o=od, events=devs[s][:2])
+            hip.record(devs[s][2], stream)
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        k_us = sorted(hip.ms(e[0], e[1]) * 1e3 for e in devs)
+        call_us = sorted(hip.ms(e[0], e[2]) * 1e3 for e in devs)
+        med = statistics.median(k_us)
+        dbytes = decode_bytes(nb, P.h_k, P.h_v, P.dk, P.dv)
+        k_avg_us = statistics.mean(k_us)
+        decode = {
+            "workload": "decode 256x1, 128 steps, slots seeded by ragged prompts 1..2048",
+            "us_per_step_median": round(statistics.median(call_us), 2),
+            "us_per_step_p90": round(call_us[int(0.9 * (len(call_us) - 1))], 2),
+            "kernel_us_median": round(med, 2),
+            "wall_us_per_step": round(dwall * 1e6 / args.decode_steps, 2),
+            "hbm_frac": round(dbytes / (statistics.median(call_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dbytes / (k_avg_us * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dbytes / (k_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None, "bytes_per_step": dbytes},
+        }
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if pool is not None:
+        xh = x.to("cpu")
+        u16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+        qh, kh, vh = u16(xh.q), u16(xh.k), u16(xh.v)
+        ah, bh = xh.a.numpy(), xh.b.numpy()
+        items, keys = [], []
+        grp = P.h_v // P.h_k
+        for i in range(B):
+            s0, s1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+            for h in range(P.h_v):
+                g = h // grp
+                items.append((qh[s0:s1, g], kh[s0:s1, g], vh[s0:s1, h], ah[s0:s1, h], bh[s0:s1, h]))
+                keys.append((i, h, s0, s1))
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_item, items, chunksize=1)
+        cpu_wall = time.perf_counter() - t0
+        pool.close()
+        pool.join()
+        worst_o = worst_S = 0.0
+        for (i, h, s0, s1), (ro, rS, _) in zip(keys, res):
+            d = np.linalg.norm(ro)
+            worst_o = max(worst_o, float(np.linalg.norm(o_host[s0:s1, h] - ro) / (d if d else 1.0)))
+            dS = np.linalg.norm(rS)
+            worst_S = max(worst_S, float(np.linalg.norm(S_host[i, h].T - rS) / (dS if dS else 1.0)))
+        cpu = {"value": round(N / cpu_wall, 1), "unit": "tok/s", "cores": args.cpu_workers, "kind": "oracle",
+               "sample": f"the whole prefill workload ({B}x{x.lengths[0]} tokens, {P.h_v} value heads): "
+                         f"{len(items)} (sequence, head) recurrences over a {args.cpu_workers}-process pool, "
+                         f"{cpu_wall:.1f} s wall",
+               "parity_vs_gpu": {"max_normwise_o": worst_o, "max_normwise_S": worst_S, "tolerance": 3e-3}}
+
+    out = {
+        "metric": METRIC, "value": round(N / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill 5x2048 (config 1): H_k=16, H_v=32, dk=dv=128, chunk=64, "
+                               "bf16 q/k/v/o, fp32 a/b/state",
+                   "global_batch": B, "seq_len": int(x.lengths[0]), "parallelism": "single-gpu"},
+        "prefill": {"boundary_pass_ms": round(p1_ms, 4), "output_pass_ms": round(p2_ms, 4),
+                    "cpr_bytes": int(cpr_bytes), "hbm_frac": round(prefill_gbs / HBM_PEAK_GBS, 4),
+                    "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                                for k, v in kernels.items()}},
+        "roofline": roofline,
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "decode_256x1_cpr": 0.0846},
+                    "note": "pages' H100 figures; head layout not stated there"},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,298 @@
+"""Python binding of libcpr_gdn: CPR Gated DeltaNet on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the library's HIP kernels;
+PyTorch supplies device memory and the current HIP stream.  Importing this package loads the
+built ``libcpr_gdn.so`` and raises ImportError when it is missing -- there is no fallback path.
+The function names mirror the C entry points declared in ``include/cpr_gdn.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "GdnError", "Policy", "StatePool", "gdn_policy_digest", "gdn_policy_check",
+    "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
+    "gdn_decode_step", "gdn_state_resync", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpr_gdn.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libcpr_gdn.so is not built at {LIB_PATH}; run "
+                      "`python -m bitwise_aligned_gated_amd.build` (or __graft_entry__.build())")
+_lib = ctypes.CDLL(LIB_PATH)
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP, GDN_EPOLICY = 0, 1, 2, 3, 4
+GDN_F32, GDN_BF16 = 0, 1
+_CODES = {1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED", 3: "GDN_EHIP", 4: "GDN_EPOLICY"}
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _CPolicy(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("h_k", "h_v", "dk", "dv", "chunk", "io_dtype", "state_dtype", "schedule")]
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_SIGS = {
+    "gdn_last_error": (ctypes.c_char_p, []),
+    "gdn_policy_digest": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _u8p]),
+    "gdn_sha256": (ctypes.c_int, [_P, _sz, _u8p]),
+    "gdn_policy_check": (ctypes.c_int, [_u8p, _u8p]),
+    "gdn_policy_validate": (ctypes.c_int, [ctypes.POINTER(_CPolicy)]),
+    "gdn_state_bytes": (_sz, [ctypes.POINTER(_CPolicy), _i32]),
+    "gdn_state_alloc": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _i32, _P, _P, _sz, _P, _P,
+                                       ctypes.POINTER(_P)]),
+    "gdn_state_free": (ctypes.c_int, [_P]),
+    "gdn_state_data": (_P, [_P]),
+    "gdn_state_positions": (_P, [_P]),
+    "gdn_check_cu_seqlens": (ctypes.c_int, [_P, _i32, _i64]),
+    "gdn_chunk_rows_bound": (_i64, [_i64, _i32, _i32]),
+    "gdn_chunk_rows": (ctypes.c_int, [_P, _P, _i32, _i32, _P]),
+    "gdn_prefill": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
+    "gdn_decode_step": (ctypes.c_int, [_P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_state_resync": (ctypes.c_int, [_P, _P, _i32, _P]),
+}
+EXPORTS = tuple(_SIGS)
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(rc: int):
+    if rc != GDN_OK:
+        raise GdnError(rc, _lib.gdn_last_error().decode())
+
+
+@dataclass(frozen=True)
+class Policy:
+    """Numerical policy (C struct gdn_policy)."""
+    h_k: int
+    h_v: int
+    dk: int
+    dv: int
+    chunk: int = 64
+    io: str = "bf16"            # "f32" or "bf16"
+    schedule: int = 1
+
+    @property
+    def io_dtype(self) -> int:
+        return {"f32": GDN_F32, "bf16": GDN_BF16}[self.io]
+
+    @property
+    def torch_io(self) -> torch.dtype:
+        return {"f32": torch.float32, "bf16": torch.bfloat16}[self.io]
+
+    def c(self) -> _CPolicy:
+        return _CPolicy(self.h_k, self.h_v, self.dk, self.dv, self.chunk, self.io_dtype, GDN_F32,
+                        self.schedule)
+
+    def validate(self):
+        _check(_lib.gdn_policy_validate(ctypes.byref(self.c())))
+
+
+def gdn_policy_digest(policy: Policy) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.gdn_policy_digest(ctypes.byref(policy.c()), out))
+    return bytes(out)
+
+
+def gdn_policy_check(mine: bytes, theirs: bytes):
+    a = (ctypes.c_uint8 * 32).from_buffer_copy(mine)
+    b = (ctypes.c_uint8 * 32).from_buffer_copy(theirs)
+    _check(_lib.gdn_policy_check(a, b))
+
+
+def gdn_sha256(data) -> bytes:
+    buf = bytes(data)
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.gdn_sha256(buf, len(buf), out))
+    return bytes(out)
+
+
+def _host_i32(x) -> torch.Tensor:
+    t = torch.as_tensor(x, dtype=torch.int32, device="cpu").contiguous()
+    return t
+
+
+def gdn_check_cu_seqlens(cu_seqlens, total_tokens: int):
+    cu = _host_i32(cu_seqlens)
+    _check(_lib.gdn_check_cu_seqlens(cu.data_ptr(), cu.numel() - 1, total_tokens))
+
+
+def gdn_chunk_rows_bound(total_tokens: int, num_seqs: int, chunk: int) -> int:
+    r = _lib.gdn_chunk_rows_bound(total_tokens, num_seqs, chunk)
+    if r < 0:
+        _check(GDN_EINVAL)
+    return int(r)
+
+
+def gdn_chunk_rows(cu_seqlens, chunk: int, pos0=None) -> torch.Tensor:
+    """Row offsets [num_seqs + 1] of each sequence's chunk states (host computation)."""
+    cu = _host_i32(cu_seqlens)
+    n = cu.numel() - 1
+    p = None if pos0 is None else torch.as_tensor(pos0, dtype=torch.int64).contiguous()
+    out = torch.zeros(n + 1, dtype=torch.int64)
+    _check(_lib.gdn_chunk_rows(cu.data_ptr(), None if p is None else p.data_ptr(), n, chunk,
+                               out.data_ptr()))
+    return out
+
+
+def _events(events, n: int):
+    """None, or a ctypes array of n hipEvent_t handles (ints / c_void_p)."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"expected {n} events")
+    arr = (ctypes.c_void_p * n)()
+    for i, e in enumerate(events):
+        arr[i] = e.value if isinstance(e, ctypes.c_void_p) else e
+    return arr
+
+
+def _stream_ptr(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape, device) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() and t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+    return t
+
+
+class StatePool:
+    """A pool of recurrent states (slots) in torch device memory, bound to a C handle.
+
+    state [num_slots, H_v, dv, dk] fp32 (S transposed), pos [num_slots] int64, and optionally a
+    boundary record of the same shapes that resynchronisation commits chunk-start states to."""
+
+    def __init__(self, policy: Policy, num_slots: int, device="cuda", boundary: bool = False):
+        policy.validate()
+        self.policy = policy
+        self.num_slots = num_slots
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        shape = (num_slots, policy.h_v, policy.dv, policy.dk)
+        self.state = torch.zeros(shape, dtype=torch.float32, device=self.device)
+        self.pos = torch.zeros(num_slots, dtype=torch.int64, device=self.device)
+        self.boundary = torch.zeros(shape, dtype=torch.float32, device=self.device) if boundary else None
+        self.boundary_pos = (torch.full((num_slots,), -1, dtype=torch.int64, device=self.device)
+                             if boundary else None)
+        h = _P()
+        nbytes = self.state.numel() * 4
+        _check(_lib.gdn_state_alloc(ctypes.byref(policy.c()), num_slots, self.state.data_ptr(),
+                                    self.pos.data_ptr(), nbytes,
+                                    self.boundary.data_ptr() if boundary else None,
+                                    self.boundary_pos.data_ptr() if boundary else None,
+                                    ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.gdn_state_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ids(ids, n: int, device) -> torch.Tensor:
+    if ids is None:
+        return torch.arange(n, dtype=torch.int32, device=device)
+    t = torch.as_tensor(ids, dtype=torch.int32)
+    return t.to(device).contiguous()
+
+
+def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                o=None, chunk_states=None, stream=None, events=None):
+    """Prefill / trainer forward over a packed batch (C gdn_prefill).
+
+    cu_seqlens: host sequence (checked on the host, then copied) or a device int32 tensor.
+    Returns (o, chunk_states); chunk_states is allocated with the bound's row count when None."""
+    P, dev = pool.policy, pool.device
+    N = q.shape[0]
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+        cu_d = _dev(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev)
+    else:
+        cu_h = _host_i32(cu_seqlens)
+        gdn_check_cu_seqlens(cu_h, N)
+        cu_d = cu_h.to(dev)
+    B = cu_d.numel() - 1
+    ids = _ids(slot_ids, B, dev)
+    _dev(ids, "slot_ids", torch.int32, (B,), dev)
+    io = P.torch_io
+    _dev(q, "q", io, (N, P.h_k, P.dk), dev)
+    _dev(k, "k", io, (N, P.h_k, P.dk), dev)
+    _dev(v, "v", io, (N, P.h_v, P.dv), dev)
+    _dev(a, "a", torch.float32, (N, P.h_v), dev)
+    _dev(b, "b", torch.float32, (N, P.h_v), dev)
+    if o is None:
+        o = torch.empty((N, P.h_v, P.dv), dtype=io, device=dev)
+    _dev(o, "o", io, (N, P.h_v, P.dv), dev)
+    bound = gdn_chunk_rows_bound(N, B, P.chunk)
+    if chunk_states is None:
+        chunk_states = torch.empty((max(bound, 1), P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)
+    _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    _check(_lib.gdn_prefill(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
+                            q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
+                            o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0],
+                            _stream_ptr(stream), _events(events, 3)))
+    return o, chunk_states
+
+
+def gdn_decode_step(pool: StatePool, q, k, v, a, b, slot_ids=None, o=None, stream=None, events=None):
+    """One token for each listed slot (C gdn_decode_step).  Returns o [batch, H_v, dv]."""
+    P, dev = pool.policy, pool.device
+    n = q.shape[0]
+    ids = _ids(slot_ids, n, dev)
+    _dev(ids, "slot_ids", torch.int32, (n,), dev)
+    io = P.torch_io
+    _dev(q, "q", io, (n, P.h_k, P.dk), dev)
+    _dev(k, "k", io, (n, P.h_k, P.dk), dev)
+    _dev(v, "v", io, (n, P.h_v, P.dv), dev)
+    _dev(a, "a", torch.float32, (n, P.h_v), dev)
+    _dev(b, "b", torch.float32, (n, P.h_v), dev)
+    if o is None:
+        o = torch.empty((n, P.h_v, P.dv), dtype=io, device=dev)
+    _dev(o, "o", io, (n, P.h_v, P.dv), dev)
+    _check(_lib.gdn_decode_step(pool.handle, ids.data_ptr(), n, q.data_ptr(), k.data_ptr(),
+                                v.data_ptr(), a.data_ptr(), b.data_ptr(), o.data_ptr(),
+                                _stream_ptr(stream), _events(events, 2)))
+    return o
+
+
+def gdn_state_resync(pool: StatePool, slot_ids, stream=None):
+    """Resynchronise listed slots at chunk starts (C gdn_state_resync)."""
+    dev = pool.device
+    ids = _ids(slot_ids, 0, dev)
+    _check(_lib.gdn_state_resync(pool.handle, ids.data_ptr(), ids.numel(), _stream_ptr(stream)))

@@ -1,0 +1,366 @@
+// cpr_host.cpp -- the C ABI of libcpr_gdn (declared in include/cpr_gdn.h): argument validation,
+// error reporting, the numerical-policy digest and the kernel launches.  No call here synchronises
+// the host or allocates device memory, except gdn_state_alloc's self-allocating mode.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/cpr_gdn.h"
+#include "cpr_args.hpp"
+#include "cpr_schedule.hpp"
+#include "cpr_launch.hpp"
+
+struct gdn_state {
+  gdn_policy policy;
+  int32_t num_slots;
+  float* state;
+  int64_t* pos;
+  float* boundary;
+  int64_t* boundary_pos;
+  bool owns;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return GDN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_dims(int dk, int dv) {
+  return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+int validate_policy(const gdn_policy* p) {
+  if (p == nullptr) return fail(GDN_EINVAL, "policy is NULL");
+  if (p->h_k <= 0 || p->h_v <= 0) return fail(GDN_EINVAL, "head counts must be positive (h_k=%d h_v=%d)", p->h_k, p->h_v);
+  if (p->h_v % p->h_k != 0) return fail(GDN_EINVAL, "h_v (%d) must be a multiple of h_k (%d)", p->h_v, p->h_k);
+  if (p->h_v > 65535) return fail(GDN_EUNSUPPORTED, "h_v (%d) above 65535", p->h_v);
+  if (p->dk <= 0 || p->dv <= 0) return fail(GDN_EINVAL, "head dims must be positive (dk=%d dv=%d)", p->dk, p->dv);
+  if (p->chunk <= 0) return fail(GDN_EINVAL, "chunk must be positive (got %d)", p->chunk);
+  if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16) return fail(GDN_EINVAL, "io_dtype %d unknown", p->io_dtype);
+  if (p->state_dtype != GDN_F32) return fail(GDN_EUNSUPPORTED, "only the fp32 state/boundary dtype is built");
+  if (p->schedule != cpr::kSchedule)
+    return fail(GDN_EUNSUPPORTED, "schedule %d not built (only %d)", p->schedule, cpr::kSchedule);
+  if (!supported_dims(p->dk, p->dv))
+    return fail(GDN_EUNSUPPORTED, "head dims dk=%d dv=%d not built (dk = dv in {16, 32, 64, 128})", p->dk, p->dv);
+  return GDN_OK;
+}
+
+// ---- SHA-256, FIPS 180-4 --------------------------------------------------------------------
+struct Sha256 {
+  uint32_t h[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au,
+                   0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u};
+  uint8_t buf[64];
+  size_t nbuf = 0;
+  uint64_t nbits = 0;
+
+  static uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+
+  void block(const uint8_t* p) {
+    static const uint32_t K[64] = {
+        0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u, 0xab1c5ed5u,
+        0xd807aa98u, 0x12835b01u, 0x243185beu, 0x550c7dc3u, 0x72be5d74u, 0x80deb1feu, 0x9bdc06a7u, 0xc19bf174u,
+        0xe49b69c1u, 0xefbe4786u, 0x0fc19dc6u, 0x240ca1ccu, 0x2de92c6fu, 0x4a7484aau, 0x5cb0a9dcu, 0x76f988dau,
+        0x983e5152u, 0xa831c66du, 0xb00327c8u, 0xbf597fc7u, 0xc6e00bf3u, 0xd5a79147u, 0x06ca6351u, 0x14292967u,
+        0x27b70a85u, 0x2e1b2138u, 0x4d2c6dfcu, 0x53380d13u, 0x650a7354u, 0x766a0abbu, 0x81c2c92eu, 0x92722c85u,
+        0xa2bfe8a1u, 0xa81a664bu, 0xc24b8b70u, 0xc76c51a3u, 0xd192e819u, 0xd6990624u, 0xf40e3585u, 0x106aa070u,
+        0x19a4c116u, 0x1e376c08u, 0x2748774cu, 0x34b0bcb5u, 0x391c0cb3u, 0x4ed8aa4au, 0x5b9cca4fu, 0x682e6ff3u,
+        0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau, 0xa4506cebu, 0xbef9a3f7u, 0xc67178f2u};
+    uint32_t w[64];
+    for (int i = 0; i < 16; ++i)
+      w[i] = (uint32_t(p[4 * i]) << 24) | (uint32_t(p[4 * i + 1]) << 16) | (uint32_t(p[4 * i + 2]) << 8) | p[4 * i + 3];
+    for (int i = 16; i < 64; ++i) {
+      const uint32_t s0 = rotr(w[i - 15], 7) ^ rotr(w[i - 15], 18) ^ (w[i - 15] >> 3);
+      const uint32_t s1 = rotr(w[i - 2], 17) ^ rotr(w[i - 2], 19) ^ (w[i - 2] >> 10);
+      w[i] = w[i - 16] + s0 + w[i - 7] + s1;
+    }
+    uint32_t a = h[0], b = h[1], c = h[2], d = h[3], e = h[4], f = h[5], g = h[6], hh = h[7];
+    for (int i = 0; i < 64; ++i) {
+      const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+      const uint32_t ch = (e & f) ^ (~e & g);
+      const uint32_t t1 = hh + S1 + ch + K[i] + w[i];
+      const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+      const uint32_t mj = (a & b) ^ (a & c) ^ (b & c);
+      const uint32_t t2 = S0 + mj;
+      hh = g; g = f; f = e; e = d + t1; d = c; c = b; b = a; a = t1 + t2;
+    }
+    h[0] += a; h[1] += b; h[2] += c; h[3] += d; h[4] += e; h[5] += f; h[6] += g; h[7] += hh;
+  }
+
+  void update(const uint8_t* p, size_t n) {
+    nbits += uint64_t(n) * 8;
+    while (n > 0) {
+      const size_t take = (64 - nbuf) < n ? (64 - nbuf) : n;
+      std::memcpy(buf + nbuf, p, take);
+      nbuf += take; p += take; n -= take;
+      if (nbuf == 64) { block(buf); nbuf = 0; }
+    }
+  }
+
+  void final(uint8_t out[32]) {
+    const uint64_t bits = nbits;
+    const uint8_t one = 0x80, zero = 0;
+    update(&one, 1);
+    while (nbuf != 56) update(&zero, 1);
+    uint8_t len[8];
+    for (int i = 0; i < 8; ++i) len[i] = uint8_t(bits >> (56 - 8 * i));
+    update(len, 8);
+    for (int i = 0; i < 8; ++i) {
+      out[4 * i] = uint8_t(h[i] >> 24); out[4 * i + 1] = uint8_t(h[i] >> 16);
+      out[4 * i + 2] = uint8_t(h[i] >> 8); out[4 * i + 3] = uint8_t(h[i]);
+    }
+  }
+};
+
+void put_le32(std::string& s, int32_t v) {
+  for (int i = 0; i < 4; ++i) s.push_back(char((uint32_t(v) >> (8 * i)) & 0xFF));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err.c_str(); }
+
+// Exposed for tests of the digest primitive against a reference implementation.
+int gdn_sha256(const void* data, size_t n, uint8_t out[32]) {
+  if ((data == nullptr && n != 0) || out == nullptr) return fail(GDN_EINVAL, "gdn_sha256: NULL pointer");
+  Sha256 s;
+  s.update(static_cast<const uint8_t*>(data), n);
+  s.final(out);
+  return ok();
+}
+
+int gdn_policy_validate(const gdn_policy* policy) {
+  const int rc = validate_policy(policy);
+  return rc == GDN_OK ? ok() : rc;
+}
+
+int gdn_policy_digest(const gdn_policy* p, uint8_t out[32]) {
+  if (p == nullptr || out == nullptr) return fail(GDN_EINVAL, "gdn_policy_digest: NULL pointer");
+  std::string bytes = "cpr-gdn-policy-v1";
+  put_le32(bytes, p->h_k);
+  put_le32(bytes, p->h_v);
+  put_le32(bytes, p->dk);
+  put_le32(bytes, p->dv);
+  put_le32(bytes, p->io_dtype);
+  put_le32(bytes, p->state_dtype);
+  put_le32(bytes, p->schedule);
+  put_le32(bytes, cpr::kLeaf);
+  put_le32(bytes, 0);  // GQA rule: value head h reads key head h / (h_v / h_k)
+  Sha256 s;
+  s.update(reinterpret_cast<const uint8_t*>(bytes.data()), bytes.size());
+  s.final(out);
+  return ok();
+}
+
+int gdn_policy_check(const uint8_t mine[32], const uint8_t theirs[32]) {
+  if (mine == nullptr || theirs == nullptr) return fail(GDN_EINVAL, "gdn_policy_check: NULL digest");
+  if (std::memcmp(mine, theirs, 32) != 0)
+    return fail(GDN_EPOLICY, "numerical policy digests differ: refusing to run mismatched kernels");
+  return ok();
+}
+
+size_t gdn_state_bytes(const gdn_policy* p, int32_t num_slots) {
+  if (validate_policy(p) != GDN_OK || num_slots < 0) return 0;
+  return size_t(num_slots) * size_t(p->h_v) * size_t(p->dv) * size_t(p->dk) * sizeof(float);
+}
+
+int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, int64_t* pos, size_t state_bytes,
+                    float* boundary, int64_t* boundary_pos, gdn_state** out) {
+  if (out == nullptr) return fail(GDN_EINVAL, "gdn_state_alloc: out is NULL");
+  *out = nullptr;
+  int rc = validate_policy(policy);
+  if (rc != GDN_OK) return rc;
+  if (num_slots <= 0) return fail(GDN_EINVAL, "num_slots must be positive (got %d)", num_slots);
+  if ((boundary == nullptr) != (boundary_pos == nullptr))
+    return fail(GDN_EINVAL, "boundary and boundary_pos must both be NULL or both be set");
+  const size_t need = gdn_state_bytes(policy, num_slots);
+  const bool self = state == nullptr && pos == nullptr;
+  if (!self) {
+    if (state == nullptr || pos == nullptr) return fail(GDN_EINVAL, "state and pos must both be set (or both NULL)");
+    if (state_bytes != need) return fail(GDN_EINVAL, "state_bytes %zu != %zu required", state_bytes, need);
+  }
+  if (self) {
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&state), need);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(state)");
+    e = hipMalloc(reinterpret_cast<void**>(&pos), sizeof(int64_t) * size_t(num_slots));
+    if (e != hipSuccess) {
+      (void)hipFree(state);
+      return hip_fail(e, "hipMalloc(pos)");
+    }
+    e = hipMemset(state, 0, need);
+    if (e == hipSuccess) e = hipMemset(pos, 0, sizeof(int64_t) * size_t(num_slots));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(state);
+      (void)hipFree(pos);
+      return hip_fail(e, "zero-filling the state pool");
+    }
+  }
+  gdn_state* st = new (std::nothrow) gdn_state;
+  if (st == nullptr) return fail(GDN_EINVAL, "out of host memory");
+  st->policy = *policy;
+  st->num_slots = num_slots;
+  st->state = state;
+  st->pos = pos;
+  st->boundary = boundary;
+  st->boundary_pos = boundary_pos;
+  st->owns = self;
+  *out = st;
+  return ok();
+}
+
+int gdn_state_free(gdn_state* st) {
+  if (st == nullptr) return ok();
+  if (st->owns) {
+    (void)hipFree(st->state);
+    (void)hipFree(st->pos);
+  }
+  delete st;
+  return ok();
+}
+
+float* gdn_state_data(gdn_state* st) { return st ? st->state : nullptr; }
+int64_t* gdn_state_positions(gdn_state* st) { return st ? st->pos : nullptr; }
+
+int gdn_check_cu_seqlens(const int32_t* cu, int32_t num_seqs, int64_t total_tokens) {
+  if (num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0");
+  if (cu == nullptr) return fail(GDN_EINVAL, "cu_seqlens is NULL");
+  if (cu[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  for (int32_t i = 0; i < num_seqs; ++i)
+    if (cu[i + 1] < cu[i]) return fail(GDN_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", i, cu[i], cu[i + 1]);
+  if (int64_t(cu[num_seqs]) != total_tokens)
+    return fail(GDN_EINVAL, "cu_seqlens[%d] = %d but total_tokens = %lld", num_seqs, cu[num_seqs], (long long)total_tokens);
+  return ok();
+}
+
+int64_t gdn_chunk_rows_bound(int64_t total_tokens, int32_t num_seqs, int32_t chunk) {
+  if (total_tokens < 0 || num_seqs < 0 || chunk <= 0) {
+    fail(GDN_EINVAL, "gdn_chunk_rows_bound: bad arguments");
+    return -1;
+  }
+  ok();
+  return total_tokens / chunk + 2 * int64_t(num_seqs);
+}
+
+int gdn_chunk_rows(const int32_t* cu, const int64_t* pos0, int32_t num_seqs, int32_t chunk, int64_t* row_offsets) {
+  if (cu == nullptr || row_offsets == nullptr) return fail(GDN_EINVAL, "gdn_chunk_rows: NULL pointer");
+  if (num_seqs < 0 || chunk <= 0) return fail(GDN_EINVAL, "gdn_chunk_rows: bad sizes");
+  int64_t acc = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    row_offsets[i] = acc;
+    const int64_t L = int64_t(cu[i + 1]) - cu[i];
+    const int64_t p = pos0 ? pos0[i] : 0;
+    if (L < 0 || p < 0) return fail(GDN_EINVAL, "gdn_chunk_rows: negative length or position at %d", i);
+    if (L > 0) acc += 1 + (p + L - 1) / chunk - p / chunk;
+  }
+  row_offsets[num_seqs] = acc;
+  return ok();
+}
+
+int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                void* stream, void* const* events) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_prefill: state handle is NULL");
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill: negative sizes");
+  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "gdn_prefill: total_tokens must fit int32 cu_seqlens");
+  if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill: cu_seqlens/slot_ids NULL");
+  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "gdn_prefill: from_state must be 0 or 1");
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr || o == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill: token tensor NULL");
+  const gdn_policy& P = st->policy;
+  const int64_t bound = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
+  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "gdn_prefill: chunk_states is NULL");
+  if (chunk_state_rows < bound)
+    return fail(GDN_EINVAL, "gdn_prefill: chunk_state_rows %lld < bound %lld", (long long)chunk_state_rows,
+                (long long)bound);
+  if (bound > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_prefill: too many chunks for one launch");
+  cpr::PrefillArgs A;
+  A.cu = cu_seqlens;
+  A.slot_ids = slot_ids;
+  A.pos = st->pos;
+  A.pos_out = st->pos;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  A.state = st->state;
+  A.chunk_states = chunk_states;
+  A.total_tokens = total_tokens;
+  A.rows_cap = bound < chunk_state_rows ? bound : chunk_state_rows;   // rows any plan can use
+  A.num_seqs = num_seqs;
+  A.num_slots = st->num_slots;
+  A.from_state = from_state;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.events = events;
+  const hipError_t e = cpr::launch_prefill(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_prefill launch");
+  return ok();
+}
+
+int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const void* q, const void* k,
+                    const void* v, const float* a, const float* b, void* o, void* stream,
+                    void* const* events) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_decode_step: state handle is NULL");
+  if (batch < 0) return fail(GDN_EINVAL, "gdn_decode_step: negative batch");
+  if (batch > 0 && (slot_ids == nullptr || q == nullptr || k == nullptr || v == nullptr || a == nullptr ||
+                    b == nullptr || o == nullptr))
+    return fail(GDN_EINVAL, "gdn_decode_step: NULL pointer");
+  const gdn_policy& P = st->policy;
+  cpr::DecodeArgs A;
+  A.slot_ids = slot_ids;
+  A.pos = st->pos;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  A.state = st->state;
+  A.boundary = st->boundary;
+  A.boundary_pos = st->boundary_pos;
+  A.batch = batch;
+  A.num_slots = st->num_slots;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.events = events;
+  const hipError_t e = cpr::launch_decode(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
+  return ok();
+}
+
+int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* stream) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_state_resync: state handle is NULL");
+  if (n < 0) return fail(GDN_EINVAL, "gdn_state_resync: negative count");
+  if (n > 0 && slot_ids == nullptr) return fail(GDN_EINVAL, "gdn_state_resync: slot_ids is NULL");
+  const gdn_policy& P = st->policy;
+  cpr::DecodeArgs A;
+  std::memset(&A, 0, sizeof A);
+  A.slot_ids = slot_ids;
+  A.pos = st->pos;
+  A.state = st->state;
+  A.boundary = st->boundary;
+  A.boundary_pos = st->boundary_pos;
+  A.batch = n;
+  A.num_slots = st->num_slots;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  const hipError_t e = cpr::launch_resync(P.dk, P.dv, A, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_state_resync launch");
+  return ok();
+}
+
+}  // extern "C"

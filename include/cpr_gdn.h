@@ -1,0 +1,206 @@
+/*
+ * cpr_gdn.h -- C ABI of libcpr_gdn: chunkwise-parallel recurrent (CPR) evaluation of the
+ * Gated DeltaNet gated delta rule on AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the IsoExec articles (alphasignal.ai, "NovaSky's IsoExec Fixes the Hidden
+ * Math Bug Corrupting AI Training Runs"), section "Solving the linear-attention headache": CPR
+ * keeps the recurrence as the primary algorithm; a first pass computes the recurrent state at
+ * chunk boundaries, a parallel pass fills in each chunk's outputs from its boundary state, and
+ * decode runs the recurrent form, re-synchronising the hidden state every chunk-size tokens so
+ * that its rounding matches prefill and training.  Section "The execution contract" fixes what an
+ * implementation must pin (accumulation and boundary dtypes, reduction decomposition) and the use
+ * of SHA-256 digests to refuse mismatched numerical policies.  Section "Making kernels
+ * parallelism-invariant" requires identical bits however the work is split.
+ *
+ * The recurrence, per (sequence, value head h), key head g = h / (H_v / H_k), fp32 state S
+ * (d_k x d_v):
+ *     u_t = S_{t-1}^T k_t,   S_t = a_t S_{t-1} + b_t k_t (v_t - a_t u_t)^T,   o_t = S_t^T q_t.
+ *
+ * Every entry point evaluates each token with the same pinned fp32 arithmetic schedule
+ * (schedule 1, described at gdn_policy.schedule), so prefill, trainer forward and decode give
+ * bitwise-identical o and S for any batch composition, packing, chunk size or launch shape.
+ *
+ * Conventions shared by every call
+ *   Return value   GDN_OK (0) or one of the GDN_E* codes; gdn_last_error() gives a message
+ *                  (per host thread).  No C++ exception crosses this interface.
+ *   Memory         all tensor pointers are DEVICE pointers owned by the caller and must stay
+ *                  valid until the stream work completes.  Except in gdn_state_alloc's
+ *                  self-allocating mode, the library allocates no device memory and never frees
+ *                  caller memory; calls never synchronise the host.
+ *   Streams        `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *                  asynchronous; device-side faults surface at the caller's next synchronisation.
+ *   Layouts        contiguous, row-major:
+ *                    q, k  [N][H_k][d_k]     v, o  [N][H_v][d_v]     a, b  [N][H_v] (fp32)
+ *                    state [num_slots][H_v][d_v][d_k] fp32  (S transposed: each d_v column of S
+ *                          is d_k contiguous floats)
+ *                    pos   [num_slots] int64  (tokens absorbed by each slot so far)
+ *                  N is the total number of tokens of the call; sequences are packed back to
+ *                  back as described by cu_seqlens (int32, [num_seqs + 1], cu[0] = 0,
+ *                  non-decreasing, cu[num_seqs] = N).
+ *   Dtypes         q, k, v and o share the policy's io dtype (fp32 or bf16); a, b, the state and
+ *                  chunk states are always fp32.  bf16 outputs are rounded to nearest even.
+ *   Chunks         chunk c of a sequence covers absolute positions [cC, (c+1)C), positions being
+ *                  counted from the sequence's first token across prefill and decode calls.
+ *   Device-side    kernels never read or write outside the sizes given; a sequence whose
+ *   robustness     cu_seqlens entries are out of order or out of range, or whose slot id is out
+ *                  of range, is skipped (its outputs are left unwritten).  Use
+ *                  gdn_check_cu_seqlens on a host copy to reject such input up front.
+ */
+#ifndef CPR_GDN_H
+#define CPR_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------------------------- */
+#define GDN_OK 0
+#define GDN_EINVAL 1       /* malformed argument (null pointer, bad size, inconsistent shapes) */
+#define GDN_EUNSUPPORTED 2 /* valid but not built: head dims, dtypes or schedule not compiled in */
+#define GDN_EHIP 3         /* a HIP runtime call or kernel launch failed */
+#define GDN_EPOLICY 4      /* numerical-policy digests differ (see gdn_policy_check) */
+
+/* ---- dtypes -------------------------------------------------------------------------------- */
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/* The numerical policy of a state pool ("The execution contract": the constants an
+ * implementation pins).  h_k, h_v: key and value heads (h_v a multiple of h_k; value head h reads
+ * key head h / (h_v / h_k)).  dk, dv: head dims; builds support dk = dv in {16, 32, 64, 128}.
+ * chunk: boundary spacing C >= 1.  io_dtype: GDN_F32 or GDN_BF16.  state_dtype: GDN_F32 (the only
+ * boundary dtype; with it, resynchronisation is exact).  schedule: 1, the pinned per-token schedule:
+ *   for every value column j independently, in fp32 with IEEE denormals and round-to-nearest-even,
+ *   (1) leaf partials over consecutive 8-row leaves of the d_k rows: p = S[r0][j]*k[r0], then
+ *       p = fma(S[r][j], k[r], p) for r = r0+1 .. r0+7;
+ *   (2) u_j = balanced pairwise sum of the d_k/8 leaf partials (leaf 2m with 2m+1, then pairs of
+ *       those, ...);
+ *   (3) w_j = fma(-a, u_j, v_j);  c_j = b * w_j;
+ *   (4) S[r][j] = fma(k[r], c_j, a * S[r][j]) for every row r;
+ *   (5) o_j = steps (1)-(2) applied to the updated S and q.
+ * chunk is a deployment setting: it decides which states are materialised, never a value, so it
+ * is left out of the policy digest. */
+typedef struct gdn_policy {
+  int32_t h_k;
+  int32_t h_v;
+  int32_t dk;
+  int32_t dv;
+  int32_t chunk;
+  int32_t io_dtype;
+  int32_t state_dtype;
+  int32_t schedule;
+} gdn_policy;
+
+/* Opaque host handle describing a pool of recurrent states ("slots") on one device. */
+typedef struct gdn_state gdn_state;
+
+/* Message for the last failing call on this host thread ("" if none).  Never NULL; the buffer is
+ * owned by the library and valid until the next call on this thread. */
+const char* gdn_last_error(void);
+
+/* SHA-256 (FIPS 180-4) of the policy's canonical bytes: the ASCII tag "cpr-gdn-policy-v1"
+ * followed by h_k, h_v, dk, dv, io_dtype, state_dtype, schedule, the leaf size (8) and the GQA
+ * rule (0 = repeat-interleave) as little-endian int32.  chunk is excluded.  Writes 32 bytes.
+ * ("The execution contract": digests exchanged at start-up.)  Host-only; needs no GPU. */
+int gdn_policy_digest(const gdn_policy* policy, uint8_t out[32]);
+
+/* SHA-256 (FIPS 180-4) of n host bytes into out[32]; the primitive behind the policy digest and
+ * the identity digests of outputs ("The execution contract": SHA-256 identity digests).
+ * Host-only. */
+int gdn_sha256(const void* data, size_t n, uint8_t out[32]);
+
+/* Compare two 32-byte policy digests: GDN_OK when equal, GDN_EPOLICY otherwise (the caller must
+ * then refuse to run, as the execution contract prescribes).  Host-only. */
+int gdn_policy_check(const uint8_t mine[32], const uint8_t theirs[32]);
+
+/* Validate a policy against this build: GDN_OK, GDN_EINVAL or GDN_EUNSUPPORTED.  Host-only. */
+int gdn_policy_validate(const gdn_policy* policy);
+
+/* Bytes of a state array for num_slots slots: num_slots * h_v * dv * dk * 4 (0 on bad input). */
+size_t gdn_state_bytes(const gdn_policy* policy, int32_t num_slots);
+
+/* Create a state pool handle for num_slots slots.
+ *   state, pos:     caller-owned device arrays (layouts above; state_bytes must equal
+ *                   gdn_state_bytes).  The caller initialises them (normally to zero).  If both
+ *                   are NULL the library allocates and zero-fills them itself (hipMalloc,
+ *                   synchronous) and frees them in gdn_state_free.
+ *   boundary, boundary_pos:  optional (both NULL or both set) caller-owned device arrays with the
+ *                   layouts of state and pos.  When present, every resynchronisation records the
+ *                   slot's chunk-start state and its position there.
+ * The handle itself is host memory; free it with gdn_state_free.  On error *out is set to NULL. */
+int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, int64_t* pos,
+                    size_t state_bytes, float* boundary, int64_t* boundary_pos,
+                    gdn_state** out);
+
+/* Release a handle (and the device arrays if the library allocated them).  NULL is a no-op. */
+int gdn_state_free(gdn_state* st);
+
+/* Device pointers of a pool (for callers that let the library allocate).  Host-only. */
+float* gdn_state_data(gdn_state* st);
+int64_t* gdn_state_positions(gdn_state* st);
+
+/* Host-side check of a cu_seqlens array (host copy): GDN_OK if cu[0] == 0, non-decreasing and
+ * cu[num_seqs] == total_tokens; GDN_EINVAL otherwise. */
+int gdn_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens);
+
+/* Upper bound on the chunk-state rows any prefill over total_tokens tokens in num_seqs sequences
+ * can need: floor(total_tokens / chunk) + 2 * num_seqs.  Returns -1 on bad input. */
+int64_t gdn_chunk_rows_bound(int64_t total_tokens, int32_t num_seqs, int32_t chunk);
+
+/* Exact chunk-state row layout of a prefill, from host copies.  For sequence i of length L_i
+ * starting at absolute position p_i (0, or the slot's pos when continuing), the rows are the
+ * states entering position p_i and every chunk start strictly inside [p_i, p_i + L_i); there are
+ * R_i = 1 + floor((p_i + L_i - 1)/C) - floor(p_i/C) of them (0 if L_i = 0), stored consecutively
+ * from row_offsets[i]; row_offsets has num_seqs + 1 entries, the last being the total.
+ * pos0_host may be NULL (all zero). */
+int gdn_chunk_rows(const int32_t* cu_seqlens_host, const int64_t* pos0_host, int32_t num_seqs,
+                   int32_t chunk, int64_t* row_offsets);
+
+/* Prefill / trainer forward over a packed batch ("Solving the linear-attention headache": first
+ * pass to the chunk boundaries, then the chunk-parallel output pass).
+ *   cu_seqlens   device int32 [num_seqs + 1]; total_tokens = N.
+ *   slot_ids     device int32 [num_seqs]: sequence i starts from and ends in slot slot_ids[i]
+ *                (distinct slots; num_seqs may be 0).
+ *   from_state   0: start from the zero state at position 0 (slot contents ignored);
+ *                1: continue from the slot's state at position pos[slot].
+ *   q, k, v, o   io dtype; a, b fp32 (layouts above).  o receives every token's output.
+ *   chunk_states device fp32 [chunk_state_rows][H_v][d_v][d_k]: the chunk-boundary states, in the
+ *                layout gdn_chunk_rows describes (row 0 of a sequence is its initial state).
+ *                For engine prefill this is scratch; for the trainer forward it is the stash the
+ *                caller keeps.  chunk_state_rows must be >= gdn_chunk_rows_bound(N, num_seqs, C).
+ * On return (stream order) each slot holds its sequence's final state and pos[slot] = p_i + L_i.
+ * Launches the boundary pass, the output pass and a position update on `stream`.
+ * events: NULL, or 3 hipEvent_t (as void*) recorded on `stream` before the boundary pass, between
+ * the two passes and after the output pass, so a caller can time each pass. */
+int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                const int32_t* slot_ids, int32_t from_state,
+                const void* q, const void* k, const void* v, const float* a, const float* b,
+                void* o, float* chunk_states, int64_t chunk_state_rows, void* stream,
+                void* const* events);
+
+/* One decode step: one token for each of `batch` slots ("For decode, the recurrent form runs").
+ *   slot_ids device int32 [batch] (distinct); q, k [batch][H_k][d_k]; v, o [batch][H_v][d_v];
+ *   a, b [batch][H_v].
+ * For a slot whose position is a multiple of C the incoming state is a chunk-start state: it is
+ * resynchronised first (see gdn_state_resync) and then the token is applied with the same pinned
+ * step as prefill.  Afterwards pos[slot] += 1.  batch may be 0.
+ * events: NULL, or 2 hipEvent_t (as void*) recorded on `stream` before and after the step kernel
+ * (the position update follows the second). */
+int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
+                    const void* q, const void* k, const void* v, const float* a, const float* b,
+                    void* o, void* stream, void* const* events);
+
+/* Resynchronise listed slots ("re-synchronizes the hidden state every chunk-size tokens").  For a
+ * slot at a chunk start (pos % C == 0) the state is re-based on the boundary state in the
+ * policy's boundary dtype; with the fp32 boundary dtype that state is already exact, so values are
+ * unchanged and the state is committed: copied, with pos, into the pool's boundary record if it
+ * has one.  Slots that are not at a chunk start are left alone.  slot_ids device int32 [n]. */
+int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPR_GDN_H */

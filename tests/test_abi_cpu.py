@@ -1,0 +1,158 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and its host-only
+logic (SHA-256, policy digest and check, validation, chunk-row planning, argument errors that are
+raised before any launch) is correct."""
+import ctypes
+import hashlib
+import os
+import re
+import struct
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import num_boundary_rows
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpr_gdn.h")
+
+
+def _lib_module():
+    from bitwise_aligned_gated_amd import build
+    if not os.path.exists(build.LIB):
+        build.build_library()
+    import bitwise_aligned_gated_amd as cpr
+    return cpr
+
+
+cpr = _lib_module()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", cpr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (gdn_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(cpr.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n) is not None
+    assert set(cpr.EXPORTS) == set(names)
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 55, 56, 57, 63, 64, 65, 119, 120, 1000, 4097])
+def test_sha256_matches_hashlib(n):
+    data = np.random.default_rng(n).integers(0, 256, n, dtype=np.uint8).tobytes()
+    assert cpr.gdn_sha256(data) == hashlib.sha256(data).digest()
+
+
+def test_policy_digest_is_sha256_of_canonical_bytes():
+    p = cpr.Policy(16, 32, 128, 128, chunk=64, io="bf16")
+    canon = b"cpr-gdn-policy-v1" + struct.pack("<9i", 16, 32, 128, 128, 1, 0, 1, 8, 0)
+    assert cpr.gdn_policy_digest(p) == hashlib.sha256(canon).digest()
+    # chunk is a deployment setting and does not enter the digest; dtypes and shapes do
+    assert cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128, chunk=16)) == cpr.gdn_policy_digest(p)
+    assert cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128, io="f32")) != cpr.gdn_policy_digest(p)
+    assert cpr.gdn_policy_digest(cpr.Policy(8, 32, 128, 128)) != cpr.gdn_policy_digest(p)
+
+
+def test_policy_check_refuses_mismatch():
+    d1 = cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128))
+    d2 = cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128, io="f32"))
+    cpr.gdn_policy_check(d1, d1)
+    with pytest.raises(cpr.GdnError) as e:
+        cpr.gdn_policy_check(d1, d2)
+    assert e.value.code == 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((16, 32, 96, 96), 2), ((16, 32, 128, 64), 2), ((16, 30, 128, 128), 1), ((0, 32, 128, 128), 1),
+    ((16, 32, 128, 128, 0), 1), ((16, 32, 128, 128, 64, "bf16", 2), 2),
+])
+def test_policy_validation(args, code):
+    with pytest.raises(cpr.GdnError) as e:
+        cpr.Policy(*args).validate()
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("dims", [16, 32, 64, 128])
+def test_supported_policies(dims):
+    cpr.Policy(2, 4, dims, dims, io="f32").validate()
+    cpr.Policy(2, 4, dims, dims, io="bf16").validate()
+
+
+def test_check_cu_seqlens():
+    cpr.gdn_check_cu_seqlens([0, 3, 3, 10], 10)
+    for bad, n in (([1, 3], 3), ([0, 5, 4], 4), ([0, 5], 6)):
+        with pytest.raises(cpr.GdnError):
+            cpr.gdn_check_cu_seqlens(bad, n)
+
+
+def test_chunk_rows_match_oracle_and_bound():
+    rng = np.random.default_rng(0)
+    for chunk in (1, 7, 16, 64):
+        for _ in range(20):
+            B = int(rng.integers(1, 12))
+            lens = rng.integers(0, 300, B)
+            pos0 = rng.integers(0, 500, B)
+            cu = np.concatenate([[0], np.cumsum(lens)])
+            off = cpr.gdn_chunk_rows(cu, chunk, pos0).numpy()
+            expect = np.concatenate([[0], np.cumsum([num_boundary_rows(int(p), int(L), chunk)
+                                                     for p, L in zip(pos0, lens)])])
+            assert np.array_equal(off, expect)
+            assert off[-1] <= cpr.gdn_chunk_rows_bound(int(cu[-1]), B, chunk)
+
+
+def test_chunk_rows_bound_errors():
+    with pytest.raises(cpr.GdnError):
+        cpr.gdn_chunk_rows_bound(10, 1, 0)
+
+
+def test_prefill_argument_errors_before_launch():
+    """Errors the host detects return GDN_EINVAL before any kernel is launched (no GPU needed).
+    The state handle binds fake device addresses that are never dereferenced."""
+    lib = cpr._lib
+    pol = cpr.Policy(2, 4, 16, 16, io="f32").c()
+    h = ctypes.c_void_p()
+    nbytes = lib.gdn_state_bytes(ctypes.byref(pol), 3)
+    assert nbytes == 3 * 4 * 16 * 16 * 4
+    fake = 0x10000
+    assert lib.gdn_state_alloc(ctypes.byref(pol), 3, fake, fake, nbytes, None, None, ctypes.byref(h)) == 0
+    try:
+        # wrong state size
+        h2 = ctypes.c_void_p()
+        assert lib.gdn_state_alloc(ctypes.byref(pol), 3, fake, fake, nbytes + 4, None, None, ctypes.byref(h2)) == 1
+        assert h2.value is None
+        # boundary without boundary_pos
+        assert lib.gdn_state_alloc(ctypes.byref(pol), 3, fake, fake, nbytes, fake, None, ctypes.byref(h2)) == 1
+        # too few chunk-state rows: bound(100 tokens, 2 seqs, C=64) = 1 + 4 = 5
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 4, None, None)
+        assert rc == 1 and b"chunk_state_rows" in lib.gdn_last_error()
+        rc = lib.gdn_prefill(h, fake, -1, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+        assert rc == 1
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 2, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+        assert rc == 1
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, None, fake, fake, fake, fake, fake, fake, 99, None, None)
+        assert rc == 1
+        rc = lib.gdn_prefill(None, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+        assert rc == 1
+        rc = lib.gdn_decode_step(h, fake, -1, fake, fake, fake, fake, fake, fake, None, None)
+        assert rc == 1
+        rc = lib.gdn_decode_step(h, None, 3, fake, fake, fake, fake, fake, fake, None, None)
+        assert rc == 1
+        rc = lib.gdn_state_resync(h, None, 2, None)
+        assert rc == 1
+        # empty work launches nothing and succeeds
+        assert lib.gdn_decode_step(h, None, 0, None, None, None, None, None, None, None, None) == 0
+        assert lib.gdn_state_resync(h, None, 0, None) == 0
+        assert lib.gdn_last_error() == b""
+    finally:
+        assert lib.gdn_state_free(h) == 0
+    assert lib.gdn_state_free(None) == 0

@@ -1,0 +1,187 @@
+"""GPU parity and bitwise identity on small and medium inputs (through the C ABI binding).
+
+Parity: the HIP path against the fp64 oracle on the same bytes (fp32 inputs: max-abs 1e-4;
+bf16 inputs: normwise 3e-3 per (sequence, value head)).  Identity: SHA-256 of output bytes equal
+across prefill, trainer forward (stash), decode, packing, order and chunk size -- the property
+"Solving the linear-attention headache" (IsoExec articles) asks of CPR.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from tests.gpu_util import (check_close, decode_all, gpu_state_math, lib, oracle_all, oracle_seq_head,
+                            policy_of, prefill, say, sha)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_config0_prefill_matches_oracle():
+    x = gi.config0()
+    say("config0 prefill vs oracle")
+    o, pool, cs = prefill(x)
+    ref_o, ref_S, ref_R = oracle_all(x)
+    check_close("f32", o.cpu().double().numpy(), ref_o, "o")
+    for h in range(x.h_v):
+        check_close("f32", gpu_state_math(pool, 0, h), ref_S[0, h], f"S head {h}")
+        for r in range(len(ref_R)):
+            check_close("f32", cs[r, h].cpu().double().numpy().T, ref_R[r, h], f"chunk state {r} head {h}")
+    assert int(pool.pos[0]) == 256
+
+
+def test_config0_decode_bitwise_equals_prefill():
+    cpr = lib()
+    x = gi.config0()
+    say("config0 prefill vs 256 decode steps")
+    o_p, pool_p, cs = prefill(x)
+    pool_d = cpr.StatePool(policy_of(x), 1, boundary=True)
+    o_d = decode_all(x, pool_d)
+    assert sha(o_d) == sha(o_p)
+    assert sha(pool_d.state) == sha(pool_p.state)
+    assert int(pool_d.pos[0]) == 256
+    # the last resynchronisation happened at position 192: the chunk-3 boundary state
+    assert int(pool_d.boundary_pos[0]) == 192
+    assert sha(pool_d.boundary[0]) == sha(cs[3])
+    ref_o, _, _ = oracle_all(x)
+    check_close("f32", o_d.cpu().double().numpy(), ref_o, "decode o")
+
+
+def _exact_inputs(T=150, dk=16, hv=2, seed=3):
+    """a = b = 1, one-hot keys, small integer values and queries: every fp32 operation of the
+    step is exact, so any correct evaluation order gives the same bits as the oracle."""
+    r = np.random.default_rng(seed)
+    perm = r.integers(0, dk, (T, 1))
+    k = np.eye(dk, dtype=np.float32)[perm]                     # [T, 1, dk]
+    q = r.integers(-4, 5, (T, 1, dk)).astype(np.float32)
+    v = r.integers(-8, 9, (T, hv, dk)).astype(np.float32)
+    ones = np.ones((T, hv), np.float32)
+    t = lambda z: torch.from_numpy(np.ascontiguousarray(z))
+    return gi.GdnInputs("exact", 1, hv, dk, dk, 64, "f32", gi.cu_from_lengths([T]),
+                        t(q), t(k), t(v), t(ones), t(ones.copy()))
+
+
+@pytest.mark.parametrize("dk", [16, 128])
+def test_exact_vector_is_bitwise_equal_to_oracle(dk):
+    x = _exact_inputs(dk=dk)
+    say(f"exact vector dk={dk}")
+    o, pool, _ = prefill(x)
+    ref_o, ref_S, _ = oracle_all(x)
+    assert np.array_equal(o.cpu().double().numpy(), ref_o)
+    for h in range(x.h_v):
+        assert np.array_equal(gpu_state_math(pool, 0, h), ref_S[0, h])
+    pool_d = lib().StatePool(policy_of(x), 1)
+    o_d = decode_all(x, pool_d)
+    assert np.array_equal(o_d.cpu().double().numpy(), ref_o)
+
+
+LENS = [1, 5, 64, 65, 130, 33, 0, 97]
+
+
+@pytest.mark.parametrize("dim", [16, 32, 64, 128])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_varlen_gqa_matches_oracle(dim, io):
+    """Ragged lengths (one token, a chunk and a token, several tiles, an empty sequence) with
+    GQA 2:1; o, final S and every chunk-start state against the oracle."""
+    cpr = lib()
+    x = gi.make_inputs(11, LENS, h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io=io)
+    say(f"varlen dim={dim} io={io}")
+    o, pool, cs = prefill(x)
+    rows = cpr.gdn_chunk_rows(x.cu_seqlens, 32).numpy()
+    o_np = o.cpu().double().numpy()
+    for i, L in enumerate(LENS):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        for h in range(x.h_v):
+            ref_o, ref_S, ref_R = oracle_seq_head(x, i, h)
+            if L:
+                check_close(io, o_np[t0:t1, h], ref_o, f"o seq {i} head {h}")
+            check_close(io, gpu_state_math(pool, i, h), ref_S, f"S seq {i} head {h}")
+            for r in range(len(ref_R)):
+                got = cs[rows[i] + r, h].cpu().double().numpy().T
+                check_close(io, got, ref_R[r], f"chunk state seq {i} row {r} head {h}")
+        assert int(pool.pos[i]) == L
+
+
+def test_packing_and_order_invariance():
+    x = gi.make_inputs(12, [70, 200, 1, 129, 64], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    say("packing / order invariance")
+    o_all, pool_all, _ = prefill(x)
+    for i in range(x.num_seqs):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        o_i, pool_i, _ = prefill(x.select([i]))
+        assert sha(o_i) == sha(o_all[t0:t1]), f"seq {i}"
+        assert sha(pool_i.state[0]) == sha(pool_all.state[i])
+    order = [4, 2, 0, 3, 1]
+    y = x.select(order)
+    o_y, pool_y, _ = prefill(y)
+    for j, i in enumerate(order):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        s0, s1 = int(y.cu_seqlens[j]), int(y.cu_seqlens[j + 1])
+        assert sha(o_y[s0:s1]) == sha(o_all[t0:t1])
+        assert sha(pool_y.state[j]) == sha(pool_all.state[i])
+
+
+def test_slot_mapping_is_respected():
+    """Sequences land in the slots slot_ids names; untouched slots keep their contents."""
+    cpr = lib()
+    x = gi.make_inputs(13, [40, 90], h_k=1, h_v=2, dk=64, dv=64, chunk=16, io="bf16")
+    say("slot mapping")
+    o_ref, pool_ref, _ = prefill(x)
+    pool = cpr.StatePool(policy_of(x), 5)
+    pool.state[2].fill_(7.0)
+    o, _ = cpr.gdn_prefill(pool, x.cu_seqlens, *[t.cuda() for t in (x.q, x.k, x.v, x.a, x.b)],
+                           slot_ids=[4, 0])
+    torch.cuda.synchronize()
+    assert sha(o) == sha(o_ref)
+    assert sha(pool.state[4]) == sha(pool_ref.state[0]) and sha(pool.state[0]) == sha(pool_ref.state[1])
+    assert bool((pool.state[2] == 7.0).all()) and bool((pool.state[1] == 0).all())
+    assert pool.pos.tolist() == [90, 0, 0, 0, 40]
+
+
+@pytest.mark.parametrize("chunk", [1, 8, 16, 100, 1000])
+def test_chunk_size_changes_no_bit(chunk):
+    x = gi.make_inputs(14, [300, 77], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    say(f"chunk invariance C={chunk}")
+    o64, pool64, _ = prefill(x)
+    oc, poolc, _ = prefill(x, chunk=chunk)
+    assert sha(oc) == sha(o64)
+    assert sha(poolc.state) == sha(pool64.state)
+
+
+def test_continue_from_state_then_decode_equals_one_prefill():
+    cpr = lib()
+    x = gi.make_inputs(15, [300], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    say("split prefill + decode vs one prefill")
+    o_full, pool_full, cs_full = prefill(x)
+    pool = cpr.StatePool(policy_of(x), 1, boundary=True)
+    o1, _, _ = prefill(x.token_slice(0, 100), pool=pool)
+    o2, _, cs2 = prefill(x.token_slice(100, 250), pool=pool, from_state=True)
+    o3 = decode_all(x.token_slice(250, 300), pool)
+    assert sha(torch.cat([o1, o2, o3])) == sha(o_full)
+    assert sha(pool.state) == sha(pool_full.state)
+    assert int(pool.pos[0]) == 300
+    # continuation rows: the state entering 100, then the chunk starts 128 and 192
+    assert sha(cs2[1]) == sha(cs_full[2]) and sha(cs2[2]) == sha(cs_full[3])
+    ref = oracle_seq_head(x, 0, 3)[0]
+    check_close("bf16", torch.cat([o1, o2, o3])[:, 3].cpu().double().numpy(), ref, "o head 3")
+    # decode resynchronised at 256: its boundary record is chunk 4's entering state
+    assert int(pool.boundary_pos[0]) == 256 and sha(pool.boundary[0]) == sha(cs_full[4])
+
+
+def test_explicit_resync_commits_only_at_chunk_starts():
+    cpr = lib()
+    x = gi.make_inputs(16, [128, 100], h_k=1, h_v=2, dk=32, dv=32, chunk=64, io="f32")
+    say("explicit resync")
+    o, pool, cs = prefill(x, boundary=True)
+    cpr.gdn_state_resync(pool, [0, 1])
+    torch.cuda.synchronize()
+    assert pool.boundary_pos.tolist() == [128, -1]         # 100 is not a chunk start
+    assert sha(pool.boundary[0]) == sha(pool.state[0])
+    assert bool((pool.boundary[1] == 0).all())
+
+
+def test_repeat_runs_are_identical():
+    x = gi.make_inputs(17, [333, 1000], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    say("repeat runs")
+    first = [sha(t) for t in (prefill(x)[0],)]
+    for _ in range(3):
+        assert [sha(prefill(x)[0])] == first

@@ -20,7 +20,7 @@ def test_generator_is_deterministic_and_streams_differ():
     a = gi.config0()
     b = gi.config0()
     assert a.digest() == b.digest()
-    assert not np.array_equal(a.q, a.k)
+    assert not torch.equal(a.q, a.k)
     c = gi.make_inputs(0, [256], 2, 2, 16, 16, io="f32", sub=1)
     assert c.digest() != a.digest()
 
@@ -28,20 +28,30 @@ def test_generator_is_deterministic_and_streams_differ():
 def test_config0_shapes_and_distributions():
     x = gi.config0()
     assert x.q.shape == (256, 2, 16) and x.v.shape == (256, 2, 16) and x.a.shape == (256, 2)
-    assert x.q.dtype == np.float32 and x.a.dtype == np.float32
-    assert (x.a > 0).all() and (x.a < 1).all() and (x.b > 0).all() and (x.b < 1).all()
+    assert x.q.dtype == torch.float32 and x.a.dtype == torch.float32
+    assert bool((x.a > 0).all() and (x.a < 1).all() and (x.b > 0).all() and (x.b < 1).all())
     nrm = np.linalg.norm(x.widen("k"), axis=-1)
     assert np.allclose(nrm, 1.0, atol=1e-6)
     assert list(x.cu_seqlens) == [0, 256]
+    assert abs(float(x.a.double().mean()) - 0.5) < 0.05      # E[sigmoid(-x)] = 1/2
 
 
-def test_small_bf16_batch_and_select_concat():
+def test_bf16_batch_is_rounded_fp32_sample():
     x = gi.make_inputs(5, [3, 70, 1], h_k=2, h_v=4, dk=16, dv=16, io="bf16")
-    assert x.q.dtype == np.uint16 and x.total_tokens == 74
+    y = gi.make_inputs(5, [3, 70, 1], h_k=2, h_v=4, dk=16, dv=16, io="f32")
+    assert x.q.dtype == torch.bfloat16 and x.total_tokens == 74
+    assert torch.equal(x.q, y.q.to(torch.bfloat16)) and torch.equal(x.v, y.v.to(torch.bfloat16))
+    assert torch.equal(x.a, y.a)
     assert np.allclose(np.linalg.norm(x.widen("k"), axis=-1), 1.0, atol=2 ** -7)
+
+
+def test_select_and_concat():
+    x = gi.make_inputs(5, [3, 70, 1], h_k=2, h_v=4, dk=16, dv=16, io="bf16")
     y = gi.GdnInputs.concat([x.select([2]), x.select([0, 1])])
     assert list(y.lengths) == [1, 3, 70]
-    assert np.array_equal(y.v[0], x.v[73]) and np.array_equal(y.v[1:], x.v[:73])
+    assert torch.equal(y.v[0], x.v[73]) and torch.equal(y.v[1:], x.v[:73])
+    z = x.token_slice(3, 73)
+    assert torch.equal(z.q, x.q[3:73]) and list(z.cu_seqlens) == [0, 70]
 
 
 def test_config3_lengths():
@@ -61,4 +71,4 @@ def test_config4_embedding_keeps_x(batch):
     assert y.num_seqs == batch
     t0 = int(y.cu_seqlens[pos])
     assert y.lengths[pos] == 300
-    assert np.array_equal(y.q[t0:t0 + 300], x.q) and np.array_equal(y.a[t0:t0 + 300], x.a)
+    assert torch.equal(y.q[t0:t0 + 300], x.q) and torch.equal(y.a[t0:t0 + 300], x.a)
