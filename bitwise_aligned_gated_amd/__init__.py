@@ -166,7 +166,8 @@ def _stream_ptr(stream) -> int:
     return s.cuda_stream
 
 
-def _dev(t: torch.Tensor, name: str, dtype, shape, device) -> torch.Tensor:
+def _dev(t: torch.Tensor, name: str, dtype, shape, device, align: int = 16) -> torch.Tensor:
+    """Check a device tensor argument; vector-loaded tensors need 16-byte alignment, scalars 4."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype != dtype:
@@ -177,8 +178,8 @@ def _dev(t: torch.Tensor, name: str, dtype, shape, device) -> torch.Tensor:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.numel() and t.data_ptr() % 16:
-        raise ValueError(f"{name} must be 16-byte aligned")
+    if t.numel() and t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
     return t
 
 
@@ -242,20 +243,20 @@ def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_
     P, dev = pool.policy, pool.device
     N = q.shape[0]
     if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
-        cu_d = _dev(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev)
+        cu_d = _dev(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev, align=4)
     else:
         cu_h = _host_i32(cu_seqlens)
         gdn_check_cu_seqlens(cu_h, N)
         cu_d = cu_h.to(dev)
     B = cu_d.numel() - 1
     ids = _ids(slot_ids, B, dev)
-    _dev(ids, "slot_ids", torch.int32, (B,), dev)
+    _dev(ids, "slot_ids", torch.int32, (B,), dev, align=4)
     io = P.torch_io
     _dev(q, "q", io, (N, P.h_k, P.dk), dev)
     _dev(k, "k", io, (N, P.h_k, P.dk), dev)
     _dev(v, "v", io, (N, P.h_v, P.dv), dev)
-    _dev(a, "a", torch.float32, (N, P.h_v), dev)
-    _dev(b, "b", torch.float32, (N, P.h_v), dev)
+    _dev(a, "a", torch.float32, (N, P.h_v), dev, align=4)
+    _dev(b, "b", torch.float32, (N, P.h_v), dev, align=4)
     if o is None:
         o = torch.empty((N, P.h_v, P.dv), dtype=io, device=dev)
     _dev(o, "o", io, (N, P.h_v, P.dv), dev)
@@ -275,13 +276,13 @@ def gdn_decode_step(pool: StatePool, q, k, v, a, b, slot_ids=None, o=None, strea
     P, dev = pool.policy, pool.device
     n = q.shape[0]
     ids = _ids(slot_ids, n, dev)
-    _dev(ids, "slot_ids", torch.int32, (n,), dev)
+    _dev(ids, "slot_ids", torch.int32, (n,), dev, align=4)
     io = P.torch_io
     _dev(q, "q", io, (n, P.h_k, P.dk), dev)
     _dev(k, "k", io, (n, P.h_k, P.dk), dev)
     _dev(v, "v", io, (n, P.h_v, P.dv), dev)
-    _dev(a, "a", torch.float32, (n, P.h_v), dev)
-    _dev(b, "b", torch.float32, (n, P.h_v), dev)
+    _dev(a, "a", torch.float32, (n, P.h_v), dev, align=4)
+    _dev(b, "b", torch.float32, (n, P.h_v), dev, align=4)
     if o is None:
         o = torch.empty((n, P.h_v, P.dv), dtype=io, device=dev)
     _dev(o, "o", io, (n, P.h_v, P.dv), dev)
