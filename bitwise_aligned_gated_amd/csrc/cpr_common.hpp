@@ -90,6 +90,17 @@ __device__ __forceinline__ void store1(void* base, int64_t elem, float x) {
     static_cast<unsigned short*>(base)[elem] = f32_to_bf16_rne(x);
 }
 
+// Store two consecutive outputs with one 4-byte (bf16) or 8-byte (fp32) write.
+template <int IO>
+__device__ __forceinline__ void store2(void* base, int64_t elem, float x0, float x1) {
+  if constexpr (IO == IO_F32) {
+    *reinterpret_cast<float2*>(static_cast<float*>(base) + elem) = make_float2(x0, x1);
+  } else {
+    *reinterpret_cast<unsigned int*>(static_cast<unsigned short*>(base) + elem) =
+        static_cast<unsigned int>(f32_to_bf16_rne(x0)) | (static_cast<unsigned int>(f32_to_bf16_rne(x1)) << 16);
+  }
+}
+
 template <int IO>
 __device__ __forceinline__ float load1(const void* base, int64_t elem) {
   if constexpr (IO == IO_F32)

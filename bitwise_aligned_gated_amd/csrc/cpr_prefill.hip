@@ -5,17 +5,22 @@
 // from that chunk's boundary state.  Both passes here apply the shared pinned step (cpr_step.hpp)
 // to every token, so the states pass 1 stores are exactly the states pass 2 and decode reach.
 //
-// Work mapping (both passes): one workgroup owns WG_COLS value columns of one value head; a
-// column's d_k rows are spread over G = d_k/8 consecutive lanes, one 8-row leaf per lane, so the
-// state lives in registers (8 floats per lane).  Token tiles of TT tokens (k, q as fp32, the
-// workgroup's v columns, a and b) are staged through LDS; the next tile is fetched into registers
-// while the current one is computed.
-//   pass 1 (boundary_pass)  grid (sequence, value head, column group); runs each sequence up to
-//                           its last chunk start and stores the state entering every chunk.
-//   pass 2 (output_pass)    grid (boundary row, value head, column group); a row is one chunk:
-//                           load its entering state, run its tokens with output, store o; the
-//                           last chunk of a sequence also stores the final state in the slot.
+// Work mapping.  A column's d_k rows are split over G consecutive lanes, each holding NL leaves
+// of 8 rows (R = 8*NL rows), and a lane owns NC columns; the state lives in registers.  Token
+// tiles (k, q widened to fp32, the workgroup's v columns, a and b) are staged through LDS and
+// the next tile is fetched into registers while the current one is computed.
+//   pass 1 (boundary_pass)  parallel only over (sequence, value head, column): G = d_k/8 so a
+//                           sequence's chain is spread over as many lanes as possible.  Grid
+//                           (sequence, value head, column group); runs each sequence up to its
+//                           last chunk start and stores the state entering every chunk.
+//   pass 2 (output_pass)    parallel over chunks too, so lanes take more rows (G <= 4) and two
+//                           columns each, which cuts the tree and per-column overhead per
+//                           element.  Grid (boundary row, value head, column group); a row is
+//                           one chunk: load its entering state, run its tokens with output,
+//                           store o; the last chunk of a sequence also stores the final state.
 //   finish                  pos[slot] = p0 + length, after both passes have read pos.
+// The schedule fixes the leaves and the tree, not the lane mapping, so both mappings (and the
+// decode kernel's) produce identical bits.
 #include <hip/hip_runtime.h>
 
 #include "cpr_common.hpp"
@@ -23,55 +28,57 @@
 
 namespace cpr {
 
-template <int DK, int DV, int IO>
-struct PrefillCfg {
-  static constexpr int G = DK / kLeaf;                       // lanes per column
-  static constexpr int WG_COLS = (256 / G < DV) ? 256 / G : DV;
-  static constexpr int THREADS = WG_COLS * G;
-  static constexpr int TT = 32;                              // tokens per LDS tile
-  static constexpr int K_UNITS = TT * DK / 8;                // 8-element units per k (or q) tile
+template <int DK, int DV, bool OUT>
+struct PassCfg {
+  static constexpr int G = OUT ? (DK / kLeaf < 4 ? DK / kLeaf : 4) : DK / kLeaf;  // lanes per column
+  static constexpr int NL = DK / (kLeaf * G);                                  // leaves per lane
+  static constexpr int R = NL * kLeaf;                                         // rows per lane
+  static constexpr int NC = OUT ? 2 : 1;                                       // columns per lane
+  static constexpr int WG_MAX_COLS = 256 / G * NC;                             // 4 waves
+  static constexpr int WG_COLS = WG_MAX_COLS < DV ? WG_MAX_COLS : DV;
+  static constexpr int THREADS = WG_COLS / NC * G;
+  static constexpr int TT = OUT ? 16 : 32;                                     // tokens per tile
+  static constexpr int K_UNITS = TT * DK / 8;          // 8-element units of a k (or q) tile
   static constexpr int V_UNITS = TT * WG_COLS / 8;
   static constexpr int K_PER_T = (K_UNITS + THREADS - 1) / THREADS;
   static constexpr int V_PER_T = (V_UNITS + THREADS - 1) / THREADS;
   static constexpr int AB_PER_T = (2 * TT + THREADS - 1) / THREADS;
-  static_assert(DK % 8 == 0 && DV % WG_COLS == 0 && WG_COLS % 8 == 0, "shape");
+  static_assert(DK % (kLeaf * G) == 0 && DV % WG_COLS == 0 && WG_COLS % 8 == 0, "shape");
   static_assert(THREADS % 64 == 0 || (THREADS & (THREADS - 1)) == 0, "block size");
 };
 
-// Registers holding one tile in flight (global -> registers -> LDS).
+// One tile in flight (global -> registers -> LDS).
 template <int DK, int DV, int IO, bool OUT>
 struct TileRegs {
-  using Cfg = PrefillCfg<DK, DV, IO>;
+  using Cfg = PassCfg<DK, DV, OUT>;
   Raw8<IO> k[Cfg::K_PER_T];
   Raw8<IO> q[OUT ? Cfg::K_PER_T : 1];
   Raw8<IO> v[Cfg::V_PER_T];
   float ab[Cfg::AB_PER_T];
 };
 
-template <int DK, int DV, int IO, bool OUT>
+template <int DK, int DV, bool OUT>
 struct TileLds {
-  using Cfg = PrefillCfg<DK, DV, IO>;
+  using Cfg = PassCfg<DK, DV, OUT>;
   float k[Cfg::TT][DK];
   float q[OUT ? Cfg::TT : 1][DK];
   float v[Cfg::TT][Cfg::WG_COLS];
-  float o[OUT ? Cfg::TT : 1][Cfg::WG_COLS];
-  float a[Cfg::TT];
-  float b[Cfg::TT];
+  float2 ab[Cfg::TT];   // (a, b) of each token
 };
 
-// Fetch tokens [t0, t0 + n) (packed indices, n <= TT) of key head g / value head h into registers.
-// Tokens past n are zero-filled and never read from memory.
+// Fetch packed tokens [t0, t0 + n) (n <= TT) of key head kh / value head h into registers.
+// Units past n are zero-filled and never read from memory.
 template <int DK, int DV, int IO, bool OUT>
-__device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV, IO, OUT>& R, int64_t t0,
-                                           int n, int kh, int h, int col0) {
-  using Cfg = PrefillCfg<DK, DV, IO>;
+__device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV, IO, OUT>& R, int t0, int n,
+                                           int kh, int h, int col0) {
+  using Cfg = PassCfg<DK, DV, OUT>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < Cfg::K_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
     const int tt = u / (DK / 8), c8 = u % (DK / 8);
     const bool ok = u < Cfg::K_UNITS && tt < n;
-    const int64_t e = ((t0 + tt) * A.h_k + kh) * DK + c8 * 8;
+    const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_k + kh) * DK + c8 * 8;
     R.k[i] = ok ? load_raw8<IO>(A.k, e) : zero_raw8<IO>();
     if constexpr (OUT) R.q[i] = ok ? load_raw8<IO>(A.q, e) : zero_raw8<IO>();
   }
@@ -80,7 +87,7 @@ __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV
     const int u = tid + i * Cfg::THREADS;
     const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
     const bool ok = u < Cfg::V_UNITS && tt < n;
-    const int64_t e = ((t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
+    const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
     R.v[i] = ok ? load_raw8<IO>(A.v, e) : zero_raw8<IO>();
   }
 #pragma unroll
@@ -89,13 +96,13 @@ __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV
     const int tt = u % Cfg::TT;
     const bool ok = u < 2 * Cfg::TT && tt < n;
     const float* src = u < Cfg::TT ? A.a : A.b;
-    R.ab[i] = ok ? src[(t0 + tt) * A.h_v + h] : 0.0f;
+    R.ab[i] = ok ? src[static_cast<int64_t>(t0 + tt) * A.h_v + h] : 0.0f;
   }
 }
 
 template <int DK, int DV, int IO, bool OUT>
-__device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, OUT>& R, TileLds<DK, DV, IO, OUT>& L) {
-  using Cfg = PrefillCfg<DK, DV, IO>;
+__device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, OUT>& R, TileLds<DK, DV, OUT>& L) {
+  using Cfg = PassCfg<DK, DV, OUT>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < Cfg::K_PER_T; ++i) {
@@ -125,109 +132,128 @@ __device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, OUT>& R, 
   for (int i = 0; i < Cfg::AB_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
     if (u < Cfg::TT)
-      L.a[u] = R.ab[i];
+      L.ab[u].x = R.ab[i];
     else if (u < 2 * Cfg::TT)
-      L.b[u - Cfg::TT] = R.ab[i];
+      L.ab[u - Cfg::TT].y = R.ab[i];
   }
 }
 
-// Run tokens [tb, te) (offsets from the sequence start) of one sequence through this lane's column
-// slice.  OUT: write o for every token.  !OUT: store the state entering every chunk start reached
-// inside (tb, te] into chunk_states.
+template <int N>
+__device__ __forceinline__ void lds_read(const float* p, float (&x)[N]) {
+  static_assert(N % 4 == 0, "vector reads");
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    const float4 f = reinterpret_cast<const float4*>(p)[i];
+    x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+  }
+}
+
+// Run tokens [tb, te) (offsets from the sequence start; tb < te) of one sequence through this
+// lane's columns.  OUT: write o for every token.  !OUT: store the state entering every chunk
+// start in (tb, te] into chunk_states (rows row0 + 1, row0 + 2, ...; the first one is `first_nb`
+// tokens after tb).
 template <int DK, int DV, int IO, bool OUT>
-__device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV, IO, OUT>& L, float (&s)[8],
-                                           const SeqMeta& m, int64_t row0, int64_t tb, int64_t te, int h,
-                                           int cg) {
-  using Cfg = PrefillCfg<DK, DV, IO>;
-  constexpr int G = Cfg::G;
+__device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV, OUT>& L,
+                                           float (&s)[PassCfg<DK, DV, OUT>::NC][PassCfg<DK, DV, OUT>::R],
+                                           int tok0, int tb, int te, int h, int cg, int64_t row0, int first_nb) {
+  using Cfg = PassCfg<DK, DV, OUT>;
+  constexpr int G = Cfg::G, NL = Cfg::NL, R = Cfg::R, NC = Cfg::NC;
   const int tid = threadIdx.x;
-  const int lc = tid / G, g = tid % G;
+  const int cp = tid / G, g = tid % G;
   const int col0 = cg * Cfg::WG_COLS;
   const int kh = h / (A.h_v / A.h_k);
-  const int64_t C = A.chunk;
-  const int64_t plane = static_cast<int64_t>(DV) * DK;      // one head's state
+  const int64_t plane = static_cast<int64_t>(DV) * DK;
+  int nb = first_nb;        // tokens until the next chunk start (pass 1)
+  int64_t row = row0 + 1;   // row the next chunk-start state goes to (pass 1)
 
-  TileRegs<DK, DV, IO, OUT> R;
-  if (tb < te) {
-    fetch_tile<DK, DV, IO, OUT>(A, R, m.tok0 + tb, static_cast<int>(te - tb < Cfg::TT ? te - tb : Cfg::TT), kh, h,
-                                col0);
-    commit_tile<DK, DV, IO, OUT>(R, L);
-  }
+  TileRegs<DK, DV, IO, OUT> Rg;
+  fetch_tile<DK, DV, IO, OUT>(A, Rg, tok0 + tb, te - tb < Cfg::TT ? te - tb : Cfg::TT, kh, h, col0);
+  commit_tile<DK, DV, IO, OUT>(Rg, L);
   __syncthreads();
-  for (int64_t t0 = tb; t0 < te; t0 += Cfg::TT) {
-    const int n = static_cast<int>(te - t0 < Cfg::TT ? te - t0 : Cfg::TT);
-    const int64_t t1 = t0 + Cfg::TT;
+  for (int t0 = tb; t0 < te; t0 += Cfg::TT) {
+    const int n = te - t0 < Cfg::TT ? te - t0 : Cfg::TT;
+    const int t1 = t0 + Cfg::TT;
     const bool more = t1 < te;
-    if (more)
-      fetch_tile<DK, DV, IO, OUT>(A, R, m.tok0 + t1, static_cast<int>(te - t1 < Cfg::TT ? te - t1 : Cfg::TT), kh, h,
-                                  col0);
+    if (more) fetch_tile<DK, DV, IO, OUT>(A, Rg, tok0 + t1, te - t1 < Cfg::TT ? te - t1 : Cfg::TT, kh, h, col0);
     for (int tt = 0; tt < n; ++tt) {
-      float kr[8], qr[8];
-      load_f32x8(&L.k[tt][g * 8], kr);
-      if constexpr (OUT) load_f32x8(&L.q[tt][g * 8], qr);
-      const float o = cpr_step<1, G, OUT>(s, kr, qr, L.v[tt][lc], L.a[tt], L.b[tt]);
+      float kr[R], qr[R];
+      lds_read<R>(&L.k[tt][g * R], kr);
+      if constexpr (OUT) lds_read<R>(&L.q[tt][g * R], qr);
+      const float2 ab = L.ab[tt];
+      float vv[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vv[c] = L.v[tt][cp * NC + c];
+      float o[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c] = cpr_step<NL, G, OUT>(s[c], kr, qr, vv[c], ab.x, ab.y);
       if constexpr (OUT) {
-        if (g == 0) L.o[tt][lc] = o;
+        if (g == 0) {
+          const int64_t oe = (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + cp * NC;
+          if constexpr (NC == 2) {
+            store2<IO>(A.o, oe, o[0], o[1]);
+          } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) store1<IO>(A.o, oe + c, o[c]);
+          }
+        }
       } else {
-        const int64_t p = m.p0 + t0 + tt + 1;               // position the new state enters
-        if (p % C == 0 && t0 + tt + 1 <= te) {
-          const int64_t row = row0 + (p / C - m.p0 / C);
-          if (row < A.rows_cap)
-            store_f32x8(A.chunk_states + (row * A.h_v + h) * plane + static_cast<int64_t>(col0 + lc) * DK + g * 8, s);
+        if (--nb == 0) {                                   // the new state enters a chunk start
+          nb = A.chunk;
+          if (row < A.rows_cap) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              store_f32x8(A.chunk_states + (row * A.h_v + h) * plane +
+                              static_cast<int64_t>(col0 + cp * NC + c) * DK + g * R,
+                          *reinterpret_cast<float(*)[8]>(&s[c][0]));
+          }
+          ++row;
         }
       }
     }
     __syncthreads();
-    if constexpr (OUT) {
-      // the tile's outputs, 8 columns per unit
-      for (int u = tid; u < n * (Cfg::WG_COLS / 8); u += Cfg::THREADS) {
-        const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = L.o[tt][c8 * 8 + i];
-        store8<IO>(A.o, ((m.tok0 + t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8, x);
-      }
-    }
-    if (more) commit_tile<DK, DV, IO, OUT>(R, L);
+    if (more) commit_tile<DK, DV, IO, OUT>(Rg, L);
     __syncthreads();
   }
 }
 
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PrefillCfg<DK, DV, IO>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
-  using Cfg = PrefillCfg<DK, DV, IO>;
-  __shared__ TileLds<DK, DV, IO, false> L;
+__global__ void __launch_bounds__((PassCfg<DK, DV, false>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, false>;
+  static_assert(Cfg::R == kLeaf && Cfg::NC == 1, "pass 1 holds one leaf of one column per lane");
+  __shared__ TileLds<DK, DV, false> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
   const SeqMeta m = seq_meta(A, i);
   const int64_t row0 = plan_row_offset(A, i, red);
   const int tid = threadIdx.x, lc = tid / Cfg::G, g = tid % Cfg::G;
   const int64_t plane = static_cast<int64_t>(DV) * DK;
-  const int64_t col_off = static_cast<int64_t>(cg * Cfg::WG_COLS + lc) * DK + g * 8;
-  float s[8];
+  const int64_t col_off = static_cast<int64_t>(cg * Cfg::WG_COLS + lc) * DK + g * Cfg::R;
+  float s[1][Cfg::R];
   if (m.slot >= 0 && m.len == 0 && !A.from_state) {          // an empty sequence from zero: zero slot
 #pragma unroll
-    for (int r = 0; r < 8; ++r) s[r] = 0.0f;
-    store_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s);
+    for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
+    store_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s[0]);
   }
   if (m.nrows == 0 || row0 >= A.rows_cap) return;            // uniform across the block
   if (A.from_state) {
-    load_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s);
+    load_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s[0]);
   } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) s[r] = 0.0f;
+    for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
   }
-  store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s);
-  // tokens up to the last recorded chunk start
+  store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s[0]);
+  if (m.nrows < 2) return;
+  // tokens up to the last recorded chunk start; the first chunk start is C - p0 % C tokens in
   const int64_t C = A.chunk;
-  const int64_t last = m.nrows > 1 ? (m.p0 / C + m.nrows - 1) * C - m.p0 : 0;
-  run_tokens<DK, DV, IO, false>(A, L, s, m, row0, 0, last, h, cg);
+  const int first_nb = static_cast<int>(C - m.p0 % C);
+  const int last = static_cast<int>((m.p0 / C + m.nrows - 1) * C - m.p0);
+  run_tokens<DK, DV, IO, false>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, first_nb);
 }
 
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PrefillCfg<DK, DV, IO>::THREADS)) output_pass_kernel(PrefillArgs A) {
-  using Cfg = PrefillCfg<DK, DV, IO>;
-  __shared__ TileLds<DK, DV, IO, true> L;
+__global__ void __launch_bounds__((PassCfg<DK, DV, true>::THREADS)) output_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, true>;
+  __shared__ TileLds<DK, DV, true> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int64_t w = blockIdx.x;
   const int h = blockIdx.y, cg = blockIdx.z;
@@ -240,13 +266,27 @@ __global__ void __launch_bounds__((PrefillCfg<DK, DV, IO>::THREADS)) output_pass
   const int64_t tb = c == 0 ? 0 : (m.p0 / C + c) * C - m.p0;
   const int64_t next = (m.p0 / C + c + 1) * C - m.p0;
   const int64_t te = next < m.len ? next : m.len;
-  const int tid = threadIdx.x, lc = tid / Cfg::G, g = tid % Cfg::G;
+  const int tid = threadIdx.x, cp = tid / Cfg::G, g = tid % Cfg::G;
   const int64_t plane = static_cast<int64_t>(DV) * DK;
-  const int64_t col_off = static_cast<int64_t>(cg * Cfg::WG_COLS + lc) * DK + g * 8;
-  float s[8];
-  load_f32x8(A.chunk_states + (w * A.h_v + h) * plane + col_off, s);
-  run_tokens<DK, DV, IO, true>(A, L, s, m, w - c, tb, te, h, cg);
-  if (c == m.nrows - 1) store_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s);
+  float s[Cfg::NC][Cfg::R];
+  const float* src = A.chunk_states + (w * A.h_v + h) * plane;
+#pragma unroll
+  for (int cc = 0; cc < Cfg::NC; ++cc) {
+    const int64_t off = static_cast<int64_t>(cg * Cfg::WG_COLS + cp * Cfg::NC + cc) * DK + g * Cfg::R;
+#pragma unroll
+    for (int r = 0; r < Cfg::R; r += 8) load_f32x8(src + off + r, *reinterpret_cast<float(*)[8]>(&s[cc][r]));
+  }
+  run_tokens<DK, DV, IO, true>(A, L, s, static_cast<int>(m.tok0), static_cast<int>(tb), static_cast<int>(te), h, cg,
+                               0, 0);
+  if (c == m.nrows - 1) {
+    float* dst = A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane;
+#pragma unroll
+    for (int cc = 0; cc < Cfg::NC; ++cc) {
+      const int64_t off = static_cast<int64_t>(cg * Cfg::WG_COLS + cp * Cfg::NC + cc) * DK + g * Cfg::R;
+#pragma unroll
+      for (int r = 0; r < Cfg::R; r += 8) store_f32x8(dst + off + r, *reinterpret_cast<float(*)[8]>(&s[cc][r]));
+    }
+  }
 }
 
 __global__ void prefill_finish_kernel(PrefillArgs A) {
@@ -259,19 +299,19 @@ __global__ void prefill_finish_kernel(PrefillArgs A) {
 
 template <int DK, int DV, int IO>
 static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
-  using Cfg = PrefillCfg<DK, DV, IO>;
-  const dim3 block(Cfg::THREADS);
-  const unsigned ncg = DV / Cfg::WG_COLS;
+  using C1 = PassCfg<DK, DV, false>;
+  using C2 = PassCfg<DK, DV, true>;
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.num_seqs > 0) {
-    hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO>), dim3(A.num_seqs, A.h_v, ncg), block, 0, stream, A);
+    hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO>), dim3(A.num_seqs, A.h_v, DV / C1::WG_COLS),
+                       dim3(C1::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0 && A.rows_cap > 0) {
-    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(A.rows_cap), A.h_v, ncg), block, 0,
-                       stream, A);
+    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(A.rows_cap), A.h_v, DV / C2::WG_COLS),
+                       dim3(C2::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
