@@ -4,9 +4,9 @@
 // IsoExec articles).
 //
 // A slot's state is read from HBM, advanced by one token in registers and written back; the
-// kernel is bound by those 2 x d_k x d_v x 4 bytes per (slot, value head).  Work mapping is the
-// prefill one (G = d_k/8 lanes per column, one 8-row leaf per lane), so a wave reads and writes
-// 64/G whole columns = contiguous 512-byte runs at d_k = 128.
+// kernel is bound by those 2 x d_k x d_v x 4 bytes per (slot, value head).  Work mapping: G =
+// d_k/8 lanes per column with one 8-row leaf each (the boundary pass's mapping), one workgroup
+// per (slot, value head), several columns per lane so that each lane has many loads in flight.
 //
 // Resynchronisation: a slot whose position is a multiple of C holds a chunk-start state.  The
 // boundary dtype is fp32, so re-basing it on the boundary state is exact and leaves the values
@@ -20,42 +20,62 @@ namespace cpr {
 
 template <int DK, int DV>
 struct DecodeCfg {
-  static constexpr int G = DK / kLeaf;
-  static constexpr int WG_COLS = (256 / G < DV) ? 256 / G : DV;
-  static constexpr int THREADS = WG_COLS * G;
+  static constexpr int G = DK / kLeaf;                         // lanes per column, one leaf each
+  static constexpr int SLOTS = (256 / G < DV) ? 256 / G : DV;  // column slots per workgroup
+  static constexpr int NC = DV / SLOTS;                        // columns per lane
+  static constexpr int THREADS = SLOTS * G;
+  static_assert(DV % SLOTS == 0, "shape");
 };
 
+// One workgroup per (entry, value head): every lane first issues the loads of all its NC columns
+// (NC x 32 bytes of state), then runs the step on each column; lane (slot, g) owns columns
+// slot + SLOTS * c, so each load instruction of a wave covers whole 512-byte columns.
 template <int DK, int DV, int IO>
 __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kernel(DecodeArgs A) {
   using Cfg = DecodeCfg<DK, DV>;
-  constexpr int G = Cfg::G;
-  const int e = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+  constexpr int G = Cfg::G, NC = Cfg::NC, SLOTS = Cfg::SLOTS;
+  __shared__ float o_lds[DV];
+  const int e = blockIdx.x, h = blockIdx.y;
   const int32_t slot = A.slot_ids[e];
-  if (slot < 0 || slot >= A.num_slots) return;
+  if (slot < 0 || slot >= A.num_slots) return;                  // uniform across the block
   const int64_t p = A.pos[slot];
-  const int tid = threadIdx.x, lc = tid / G, g = tid % G;
-  const int col = cg * Cfg::WG_COLS + lc;
-  const int64_t plane = static_cast<int64_t>(DV) * DK;
-  const int64_t soff = (static_cast<int64_t>(slot) * A.h_v + h) * plane + static_cast<int64_t>(col) * DK + g * 8;
+  const int tid = threadIdx.x, cs = tid / G, g = tid % G;
+  const int64_t head = (static_cast<int64_t>(slot) * A.h_v + h) * DV * DK;
   const int kh = h / (A.h_v / A.h_k);
-  const int64_t kq = (static_cast<int64_t>(e) * A.h_k + kh) * DK + g * 8;
+  const int64_t kq = (static_cast<int64_t>(e) * A.h_k + kh) * DK + g * kLeaf;
+  const int64_t vo = (static_cast<int64_t>(e) * A.h_v + h) * DV;
 
-  float s[8], kr[8], qr[8];
-  load_f32x8(A.state + soff, s);
+  float s[NC][kLeaf];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) load_f32x8(A.state + head + static_cast<int64_t>(cs + SLOTS * c) * DK + g * kLeaf, s[c]);
+  float kr[kLeaf], qr[kLeaf], v[NC];
   widen8<IO>(load_raw8<IO>(A.k, kq), kr);
   widen8<IO>(load_raw8<IO>(A.q, kq), qr);
-  const int64_t vo = (static_cast<int64_t>(e) * A.h_v + h) * DV + col;
-  const float v = load1<IO>(A.v, vo);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) v[c] = load1<IO>(A.v, vo + cs + SLOTS * c);
   const float a = A.a[static_cast<int64_t>(e) * A.h_v + h];
   const float b = A.b[static_cast<int64_t>(e) * A.h_v + h];
 
-  if (A.boundary != nullptr && p >= 0 && p % A.chunk == 0) {
-    store_f32x8(A.boundary + soff, s);
-    if (h == 0 && cg == 0 && tid == 0) A.boundary_pos[slot] = p;
+  if (A.boundary != nullptr && p >= 0 && p % A.chunk == 0) {    // resynchronise: commit the state
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      store_f32x8(A.boundary + head + static_cast<int64_t>(cs + SLOTS * c) * DK + g * kLeaf, s[c]);
+    if (h == 0 && tid == 0) A.boundary_pos[slot] = p;
   }
-  const float o = cpr_step<1, G, true>(s, kr, qr, v, a, b);
-  store_f32x8(A.state + soff, s);
-  if (g == 0) store1<IO>(A.o, vo, o);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float o = cpr_step<1, G, true>(s[c], kr, qr, v[c], a, b);
+    if (g == 0) o_lds[cs + SLOTS * c] = o;
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) store_f32x8(A.state + head + static_cast<int64_t>(cs + SLOTS * c) * DK + g * kLeaf, s[c]);
+  __syncthreads();
+  if (tid < DV / 8) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = o_lds[tid * 8 + i];
+    store8<IO>(A.o, vo + tid * 8, x);
+  }
 }
 
 __global__ void decode_advance_kernel(DecodeArgs A) {
@@ -69,19 +89,21 @@ __global__ void decode_advance_kernel(DecodeArgs A) {
 template <int DK, int DV>
 __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) resync_kernel(DecodeArgs A) {
   using Cfg = DecodeCfg<DK, DV>;
-  const int e = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+  const int e = blockIdx.x, h = blockIdx.y;
   const int32_t slot = A.slot_ids[e];
   if (slot < 0 || slot >= A.num_slots || A.boundary == nullptr) return;
   const int64_t p = A.pos[slot];
   if (p < 0 || p % A.chunk != 0) return;
-  const int tid = threadIdx.x, lc = tid / Cfg::G, g = tid % Cfg::G;
-  const int64_t plane = static_cast<int64_t>(DV) * DK;
-  const int64_t soff = (static_cast<int64_t>(slot) * A.h_v + h) * plane +
-                       static_cast<int64_t>(cg * Cfg::WG_COLS + lc) * DK + g * 8;
-  float s[8];
-  load_f32x8(A.state + soff, s);
-  store_f32x8(A.boundary + soff, s);
-  if (h == 0 && cg == 0 && tid == 0) A.boundary_pos[slot] = p;
+  const int tid = threadIdx.x, cs = tid / Cfg::G, g = tid % Cfg::G;
+  const int64_t head = (static_cast<int64_t>(slot) * A.h_v + h) * DV * DK;
+#pragma unroll
+  for (int c = 0; c < Cfg::NC; ++c) {
+    const int64_t off = head + static_cast<int64_t>(cs + Cfg::SLOTS * c) * DK + g * kLeaf;
+    float s[kLeaf];
+    load_f32x8(A.state + off, s);
+    store_f32x8(A.boundary + off, s);
+  }
+  if (h == 0 && tid == 0) A.boundary_pos[slot] = p;
 }
 
 template <int DK, int DV, int IO>
@@ -90,8 +112,7 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.batch > 0) {
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS),
-                       0, stream, A);
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO>), dim3(A.batch, A.h_v), dim3(Cfg::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
@@ -106,8 +127,7 @@ template <int DK, int DV>
 static hipError_t launch_resync_t(const DecodeArgs& A, hipStream_t stream) {
   using Cfg = DecodeCfg<DK, DV>;
   if (A.batch == 0 || A.boundary == nullptr) return hipSuccess;
-  hipLaunchKernelGGL((resync_kernel<DK, DV>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS), 0, stream,
-                     A);
+  hipLaunchKernelGGL((resync_kernel<DK, DV>), dim3(A.batch, A.h_v), dim3(Cfg::THREADS), 0, stream, A);
   return hipGetLastError();
 }
 
