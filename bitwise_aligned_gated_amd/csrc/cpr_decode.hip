@@ -1,7 +1,7 @@
 // cpr_decode.hip -- CPR decode: one token per slot with the shared pinned step, and the
-// chunk-cadence resynchronisation ("For decode, the recurrent form runs but resynchronizes the
-// hidden state every chunk-size tokens", section "Solving the linear-attention headache" of the
-// IsoExec articles).
+// once-per-chunk resynchronisation (section "Solving the linear-attention headache" of the
+// IsoExec articles: decode advances the state a token at a time and re-bases it at every chunk
+// start so that its rounding agrees with prefill and training).
 //
 // A slot's state is read from HBM, advanced by one token in registers and written back; the
 // kernel is bound by those 2 x d_k x d_v x 4 bytes per (slot, value head).  Work mapping: G =

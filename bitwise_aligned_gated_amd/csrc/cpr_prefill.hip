@@ -1,8 +1,8 @@
 // cpr_prefill.hip -- the two CPR passes over a packed varlen batch.
 //
-// "Solving the linear-attention headache" (IsoExec articles): a first pass computes the
-// recurrent state at chunk boundaries, then the outputs inside each chunk are filled in parallel
-// from that chunk's boundary state.  Both passes here apply the shared pinned step (cpr_step.hpp)
+// "Solving the linear-attention headache" (IsoExec articles): one pass finds the state at the
+// start of every chunk; a second pass, parallel over chunks, produces each chunk's outputs
+// starting from that state.  Both passes here apply the shared pinned step (cpr_step.hpp)
 // to every token, so the states pass 1 stores are exactly the states pass 2 and decode reach.
 //
 // Work mapping.  A column's d_k rows are split over G consecutive lanes, each holding NL leaves
@@ -163,7 +163,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
   const int col0 = cg * Cfg::WG_COLS;
   const int kh = h / (A.h_v / A.h_k);
   const int64_t plane = static_cast<int64_t>(DV) * DK;
-  int nb = first_nb;        // tokens until the next chunk start (pass 1)
+  int nb = __builtin_amdgcn_readfirstlane(first_nb);   // tokens until the next chunk start (pass 1)
   int64_t row = row0 + 1;   // row the next chunk-start state goes to (pass 1)
 
   TileRegs<DK, DV, IO, OUT> Rg;
@@ -175,7 +175,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
     const int t1 = t0 + Cfg::TT;
     const bool more = t1 < te;
     if (more) fetch_tile<DK, DV, IO, OUT>(A, Rg, tok0 + t1, te - t1 < Cfg::TT ? te - t1 : Cfg::TT, kh, h, col0);
-    for (int tt = 0; tt < n; ++tt) {
+    auto token = [&](int tt) {
       float kr[R], qr[R];
       lds_read<R>(&L.k[tt][g * R], kr);
       if constexpr (OUT) lds_read<R>(&L.q[tt][g * R], qr);
@@ -209,6 +209,12 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
           ++row;
         }
       }
+    };
+    if (!OUT && n == Cfg::TT) {              // pass 1, full tile: unrolled, immediate LDS offsets
+#pragma unroll 4
+      for (int tt = 0; tt < Cfg::TT; ++tt) token(tt);
+    } else {
+      for (int tt = 0; tt < n; ++tt) token(tt);
     }
     __syncthreads();
     if (more) commit_tile<DK, DV, IO, OUT>(Rg, L);

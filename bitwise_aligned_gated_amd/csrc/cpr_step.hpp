@@ -1,8 +1,8 @@
 // cpr_step.hpp -- the one per-token step of the gated delta rule shared by every kernel.
 //
-// CPR ("Solving the linear-attention headache", IsoExec articles) keeps the recurrence as the
-// primary algorithm and gets bitwise agreement between prefill, training and decode by making
-// every path apply the same per-token rounding schedule.  This header is that schedule; the
+// CPR ("Solving the linear-attention headache", IsoExec articles) makes the per-token recurrence
+// the reference computation and obtains bitwise agreement between prefill, training and decode by
+// having every path apply the same per-token rounding schedule.  This header is that schedule; the
 // boundary pass, the output pass and the decode step all call cpr_step() below and nothing else
 // touches the state's arithmetic.
 //

@@ -4,10 +4,10 @@
  *
  * Source of the method: the IsoExec articles (alphasignal.ai, "NovaSky's IsoExec Fixes the Hidden
  * Math Bug Corrupting AI Training Runs"), section "Solving the linear-attention headache": CPR
- * keeps the recurrence as the primary algorithm; a first pass computes the recurrent state at
- * chunk boundaries, a parallel pass fills in each chunk's outputs from its boundary state, and
- * decode runs the recurrent form, re-synchronising the hidden state every chunk-size tokens so
- * that its rounding matches prefill and training.  Section "The execution contract" fixes what an
+ * makes the per-token recurrence the reference computation; one pass finds the state at the
+ * start of every chunk, a second pass (parallel over chunks) computes each chunk's outputs from
+ * that state, and decode advances one token at a time, re-basing its state at every chunk start
+ * so that its rounding agrees with prefill and training.  Section "The execution contract" fixes what an
  * implementation must pin (accumulation and boundary dtypes, reduction decomposition) and the use
  * of SHA-256 digests to refuse mismatched numerical policies.  Section "Making kernels
  * parallelism-invariant" requires identical bits however the work is split.
@@ -180,7 +180,8 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
                 void* o, float* chunk_states, int64_t chunk_state_rows, void* stream,
                 void* const* events);
 
-/* One decode step: one token for each of `batch` slots ("For decode, the recurrent form runs").
+/* One decode step: one token for each of `batch` slots (section "Solving the linear-attention
+ * headache": decode applies the recurrence one token at a time).
  *   slot_ids device int32 [batch] (distinct); q, k [batch][H_k][d_k]; v, o [batch][H_v][d_v];
  *   a, b [batch][H_v].
  * For a slot whose position is a multiple of C the incoming state is a chunk-start state: it is
@@ -192,7 +193,7 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
                     const void* q, const void* k, const void* v, const float* a, const float* b,
                     void* o, void* stream, void* const* events);
 
-/* Resynchronise listed slots ("re-synchronizes the hidden state every chunk-size tokens").  For a
+/* Resynchronise listed slots (same section: decode re-bases its state once per chunk).  For a
  * slot at a chunk start (pos % C == 0) the state is re-based on the boundary state in the
  * policy's boundary dtype; with the fp32 boundary dtype that state is already exact, so values are
  * unchanged and the state is committed: copied, with pos, into the pool's boundary record if it

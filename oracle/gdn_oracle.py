@@ -7,11 +7,12 @@ or their host library and imports nothing from them.
 
 What it computes
 ----------------
-"Solving the linear-attention headache" (alphasignal.ai page on IsoExec) says CPR keeps the
-recurrence as the primary algorithm: a first pass produces the recurrent state at chunk
-boundaries, a second pass fills in each chunk's outputs from its boundary state, and decode runs
-the recurrent form, re-synchronising every chunk-size tokens.  All three evaluate the same
-recurrence, so the plain definition of the result is that recurrence run token by token.  The
+Per section "Solving the linear-attention headache" of the alphasignal.ai article on IsoExec,
+CPR treats the token-by-token recurrence as the definition of the result: one pass finds the
+state where each chunk begins, a second pass computes every chunk's outputs from that starting
+state, and decode applies the recurrence one token at a time, re-basing its state once per chunk.
+All three evaluate the same recurrence, so the plain definition of the result is that recurrence
+run token by token.  The
 pages print no formula; the gated delta rule used here is
 
     u_t = S_{t-1}^T k_t

@@ -1,0 +1,216 @@
+"""GPU parity and identity at the workloads' full sizes, in the launch configuration the
+benchmark times.  The oracle checks sampled (sequence, value head) pairs one by one; identity is
+checked on every output byte with SHA-256.
+
+  prefill   5 x 2048 tokens, 32 value heads over 16 key heads, d = 128, chunk 64, bf16
+  decode    256 slots seeded by ragged prompts (1..2048 tokens), 128 steps, resync every 64
+  trainer   10240 tokens packed varlen (lengths 64..4096), boundary states stashed
+  long      one 65536-token sequence alone, among neighbours, at other chunk sizes, and decoded
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from tests.gpu_util import (check_close, gpu_state_math, lib, oracle_seq_head, policy_of, prefill, say, sha)
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_seq(pool, x, slot=0, on_step=None):
+    """Decode the single sequence x token by token into `slot`; returns o [T, H_v, dv]."""
+    cpr = lib()
+    xd = x.to("cuda")
+    ids = torch.tensor([slot], dtype=torch.int32, device="cuda")
+    out = torch.empty((x.total_tokens, x.h_v, x.dv), dtype=xd.v.dtype, device="cuda")
+    for t in range(x.total_tokens):
+        cpr.gdn_decode_step(pool, xd.q[t:t + 1], xd.k[t:t + 1], xd.v[t:t + 1], xd.a[t:t + 1], xd.b[t:t + 1],
+                            slot_ids=ids, o=out[t:t + 1])
+        if on_step is not None:
+            on_step(t)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_prefill_5x2048():
+    cpr = lib()
+    x = gi.config1(device="cuda")
+    say("prefill 5x2048: packed run")
+    o, pool, cs = prefill(x)
+    rows = cpr.gdn_chunk_rows(x.cu_seqlens, 64).numpy()
+    o_np = o.float().cpu().numpy()
+    for (i, h) in [(0, 0), (1, 7), (2, 16), (3, 25), (4, 31)]:
+        say(f"prefill 5x2048: oracle seq {i} head {h}")
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        ref_o, ref_S, ref_R = oracle_seq_head(x, i, h)
+        check_close("bf16", o_np[t0:t1, h], ref_o, f"o seq {i} head {h}")
+        check_close("bf16", gpu_state_math(pool, i, h), ref_S, f"S seq {i} head {h}")
+        for r in (0, 1, 17, len(ref_R) - 1):
+            check_close("bf16", cs[rows[i] + r, h].cpu().double().numpy().T, ref_R[r], f"row {r}")
+    say("prefill 5x2048: sequence 2 alone")
+    o2, pool2, _ = prefill(x.select([2]))
+    assert sha(o2) == sha(o[int(x.cu_seqlens[2]):int(x.cu_seqlens[3])])
+    assert sha(pool2.state[0]) == sha(pool.state[2])
+    say("prefill 5x2048: sequence 4 decoded token by token")
+    dpool = cpr.StatePool(policy_of(x), 1, boundary=True)
+    seen = []
+
+    def check_boundary(t):
+        if t % 64 == 0:                      # the step at a chunk start committed its state
+            seen.append(sha(dpool.boundary[0]) == sha(cs[rows[4] + t // 64]))
+
+    od = _decode_seq(dpool, x.select([4]), on_step=check_boundary)
+    assert sha(od) == sha(o[int(x.cu_seqlens[4]):])
+    assert sha(dpool.state[0]) == sha(pool.state[4])
+    assert len(seen) == 32 and all(seen)
+
+
+def _with_generated(prompts: gi.GdnInputs, steps):
+    """Pack each sequence's prompt followed by its generated tokens (one per decode step)."""
+    n = prompts.num_seqs
+    L = prompts.lengths
+    T = len(steps)
+    dec = {name: torch.stack([getattr(s, name) for s in steps]) for name in ("q", "k", "v", "a", "b")}
+    idx_p, idx_d = [], []
+    out_len = L + T
+    cu = gi.cu_from_lengths(out_len)
+    total = int(cu[-1])
+    src_prompt = torch.full((total,), -1, dtype=torch.int64)
+    src_step = torch.full((total,), -1, dtype=torch.int64)
+    for i in range(n):
+        o0 = int(cu[i])
+        p0 = int(prompts.cu_seqlens[i])
+        src_prompt[o0:o0 + L[i]] = torch.arange(p0, p0 + L[i])
+        src_step[o0 + L[i]:o0 + L[i] + T] = torch.arange(T) * n + i
+    dev = prompts.device
+    src_prompt, src_step = src_prompt.to(dev), src_step.to(dev)
+    is_p = src_prompt >= 0
+
+    def gather(name):
+        p = getattr(prompts, name)
+        d = dec[name].reshape((T * n,) + tuple(p.shape[1:]))
+        out = torch.empty((total,) + tuple(p.shape[1:]), dtype=p.dtype, device=dev)
+        out[is_p] = p[src_prompt[is_p]]
+        out[~is_p] = d[src_step[~is_p]]
+        return out
+
+    return gi.GdnInputs("prompt+generated", prompts.h_k, prompts.h_v, prompts.dk, prompts.dv, prompts.chunk,
+                        prompts.io, cu, gather("q"), gather("k"), gather("v"), gather("a"), gather("b"))
+
+
+def test_decode_256x1_128_steps_equals_one_prefill():
+    cpr = lib()
+    prompts = gi.config2_prompts(device="cuda")
+    n = prompts.num_seqs
+    say(f"decode: prefill {n} prompts ({prompts.total_tokens} tokens)")
+    P = policy_of(prompts)
+    pool = cpr.StatePool(P, n, boundary=True)
+    cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
+    steps = [gi.config2_decode_tokens(s, n, device="cuda") for s in range(128)]
+    say("decode: 128 steps")
+    outs = []
+    for s in steps:
+        outs.append(cpr.gdn_decode_step(pool, s.q, s.k, s.v, s.a, s.b))
+    torch.cuda.synchronize()
+    L = prompts.lengths
+    assert pool.pos.cpu().numpy().tolist() == (L + 128).tolist()
+    # every slot resynchronised at its last chunk start inside the decoded range, if any
+    bp = pool.boundary_pos.cpu().numpy()
+    for i in range(n):
+        starts = [p for p in range(int(L[i]), int(L[i]) + 128) if p % 64 == 0]
+        assert bp[i] == (starts[-1] if starts else -1)
+    say("decode: one packed prefill over prompt + generated tokens")
+    full = _with_generated(prompts, steps)
+    o_full, pool_full, cs_full = prefill(full)
+    dec_o = torch.stack(outs, dim=1)                    # [n, 128, H_v, dv]
+    for i in range(n):
+        t1 = int(full.cu_seqlens[i + 1])
+        assert sha(dec_o[i]) == sha(o_full[t1 - 128:t1]), f"slot {i}"
+    assert sha(pool.state) == sha(pool_full.state)
+    rows = cpr.gdn_chunk_rows(full.cu_seqlens, 64).numpy()
+    for i in range(n):
+        if bp[i] >= 0:
+            assert sha(pool.boundary[i]) == sha(cs_full[rows[i] + bp[i] // 64]), f"boundary {i}"
+    for (i, h) in [(int(np.argmin(L)), 3), (int(np.argmax(L)), 30)]:
+        say(f"decode: oracle slot {i} head {h}")
+        ref_o, ref_S, _ = oracle_seq_head(full, i, h)
+        check_close("bf16", dec_o[i, :, h].float().cpu().numpy(), ref_o[-128:], f"decode o slot {i}")
+        check_close("bf16", gpu_state_math(pool, i, h), ref_S, f"decode S slot {i}")
+
+
+def test_trainer_forward_10240_varlen_with_stash():
+    cpr = lib()
+    x = gi.config3(device="cuda")
+    say(f"trainer: lengths {list(x.lengths)}")
+    rows = cpr.gdn_chunk_rows(x.cu_seqlens, 64).numpy()
+    stash = torch.empty((int(rows[-1]) + 2 * x.num_seqs + x.total_tokens // 64, x.h_v, x.dv, x.dk),
+                        dtype=torch.float32, device="cuda")
+    o, pool, cs = prefill(x, chunk_states=stash)
+    assert cs is stash
+    for (i, h) in [(0, 1), (int(np.argmax(x.lengths)), 22)]:
+        say(f"trainer: oracle seq {i} head {h}")
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        ref_o, ref_S, ref_R = oracle_seq_head(x, i, h)
+        check_close("bf16", o[t0:t1, h].float().cpu().numpy(), ref_o, f"o seq {i}")
+        check_close("bf16", gpu_state_math(pool, i, h), ref_S, f"S seq {i}")
+        assert len(ref_R) == rows[i + 1] - rows[i]
+        for r in range(0, len(ref_R), 7):
+            check_close("bf16", stash[rows[i] + r, h].cpu().double().numpy().T, ref_R[r], f"stash row {r}")
+    for i in range(x.num_seqs):
+        say(f"trainer: sequence {i} alone")
+        oi, pi, ci = prefill(x.select([i]))
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        assert sha(oi) == sha(o[t0:t1])
+        assert sha(ci[:rows[i + 1] - rows[i]]) == sha(stash[rows[i]:rows[i + 1]])
+    i = int(np.argmin(x.lengths))
+    say(f"trainer: sequence {i} replayed by decode")
+    dpool = cpr.StatePool(policy_of(x), 1, boundary=True)
+    ok = []
+    _decode_seq(dpool, x.select([i]),
+                on_step=lambda t: ok.append(sha(dpool.boundary[0]) == sha(stash[rows[i] + t // 64]))
+                if t % 64 == 0 else None)
+    assert ok and all(ok)
+    assert sha(dpool.state[0]) == sha(pool.state[i])
+
+
+@pytest.fixture(scope="module")
+def long_x():
+    x = gi.config4_x(device="cuda")
+    say("long: X alone")
+    o, pool, _ = prefill(x)
+    return x, sha(o), sha(pool.state), o
+
+
+def test_long_sequence_matches_oracle(long_x):
+    x, _, _, o = long_x
+    for h in (0, 19):
+        say(f"long: oracle head {h}")
+        ref_o, _, _ = oracle_seq_head(x, 0, h)
+        check_close("bf16", o[:, h].float().cpu().numpy(), ref_o, f"o head {h}")
+
+
+@pytest.mark.parametrize("batch", [2, 8, 64])
+def test_long_sequence_invariant_to_neighbours(long_x, batch):
+    x, so, sS, _ = long_x
+    y, pos = gi.config4_batch(x, batch, sub=batch)
+    say(f"long: X among {batch - 1} neighbours at position {pos} ({y.total_tokens} tokens)")
+    o, pool, _ = prefill(y)
+    t0 = int(y.cu_seqlens[pos])
+    assert sha(o[t0:t0 + x.total_tokens]) == so
+    assert sha(pool.state[pos:pos + 1]) == sS
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 128, 1024])
+def test_long_sequence_invariant_to_chunk(long_x, chunk):
+    x, so, sS, _ = long_x
+    say(f"long: chunk {chunk}")
+    o, pool, _ = prefill(x, chunk=chunk)
+    assert sha(o) == so and sha(pool.state) == sS
+
+
+def test_long_sequence_decoded_65536_steps(long_x):
+    x, so, sS, _ = long_x
+    say("long: 65536 decode steps")
+    pool = lib().StatePool(policy_of(x), 1)
+    od = _decode_seq(pool, x)
+    assert sha(od) == so and sha(pool.state) == sS
