@@ -79,6 +79,33 @@ class Hip:
         return float(out.value)
 
 
+def kernel_source_digest() -> str:
+    """SHA-256 over the HIP sources (name + bytes, sorted), to tie stored counters to a build."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "bitwise_aligned_gated_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE counters, or {} when the
+    kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            tr = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    if tr.get("fingerprint") != kernel_source_digest():
+        return {}
+    return {k: v["bytes"] for k, v in tr.get("kernels", {}).items()}
+
+
 def prefill_flops(lengths, h_v, dk, dv, chunk):
     """Algorithmic FLOPs of the two passes.  Per token-head: pass 1 (state only) 5*dk*dv
     (u = S^T k: 2 dk dv; a*S: dk dv; k c^T added: 2 dk dv); pass 2 adds o = S^T q: 7*dk*dv."""
@@ -169,9 +196,11 @@ def main():
         "output_pass": {"avg_ms": p2_ms, "tflops": f2 / (p2_ms * 1e-3) / 1e12, "flop": f2},
     }
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    traffic = measured_traffic()
     roofline = {"bound": "alu", "kernel": dom, "achieved": round(kernels[dom]["tflops"], 3),
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kernels[dom]["tflops"] / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(kernels[dom]["tflops"] / FP32_VECTOR_PEAK_TFLOPS, 4),
+                "traffic": traffic.get(dom)}
     # prefill HBM fraction (the metric's "% HBM peak"): algorithmic bytes of the whole CPR step
     io = 2
     in_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4)
@@ -227,7 +256,7 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(dbytes / (k_avg_us * 1e-6) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dbytes / (k_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None, "bytes_per_step": dbytes},
+                         "traffic": traffic.get("decode_step"), "bytes_per_step": dbytes},
         }
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
