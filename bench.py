@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = "CPR-GDN prefill tok/s (5×2048) + decode µs/step (256×1), % HBM peak"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 FLOP/clk/CU)
+FP32_UNPACKED_PEAK_TFLOPS = 78.6  # the same without packed fp32 (disabled in this build)
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle) worker
@@ -200,7 +201,9 @@ def main():
     roofline = {"bound": "alu", "kernel": dom, "achieved": round(kernels[dom]["tflops"], 3),
                 "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kernels[dom]["tflops"] / FP32_VECTOR_PEAK_TFLOPS, 4),
-                "traffic": traffic.get(dom)}
+                "traffic": traffic.get(dom),
+                "peak_unpacked": FP32_UNPACKED_PEAK_TFLOPS,
+                "frac_unpacked": round(kernels[dom]["tflops"] / FP32_UNPACKED_PEAK_TFLOPS, 4)}
     # prefill HBM fraction (the metric's "% HBM peak"): algorithmic bytes of the whole CPR step
     io = 2
     in_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4)

@@ -22,7 +22,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpr_gdn.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libcpr_gdn.so is not built at {LIB_PATH}; run "
-                      "`python -m bitwise_aligned_gated_amd.build` (or __graft_entry__.build())")
+                      "`python bitwise_aligned_gated_amd/build.py` (or __graft_entry__.build())")
 _lib = ctypes.CDLL(LIB_PATH)
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP, GDN_EPOLICY = 0, 1, 2, 3, 4

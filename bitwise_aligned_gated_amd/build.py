@@ -1,6 +1,7 @@
 """Build libcpr_gdn.so in place (hipcc, gfx950).
 
-Usage: python -m bitwise_aligned_gated_amd.build   (or call build_library()).
+Usage: python bitwise_aligned_gated_amd/build.py   (run by path: importing the package needs the
+library to exist already).
 Every HIP translation unit is compiled with the flags that pin the arithmetic: no FMA
 contraction beyond the explicit fmaf calls, no fast-math, IEEE fp32 denormals, and packed fp32
 instructions disabled.
@@ -16,9 +17,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libcpr_gdn.so")
-BUILD_DIR = os.path.join(ROOT, "_build")
+BUILD_DIR = os.environ.get("CPR_BUILD_DIR", os.path.join(ROOT, "_build"))
 
 SOURCES = ["cpr_prefill.hip", "cpr_decode.hip", "cpr_host.cpp"]
+EXTRA_FLAGS = os.environ.get("CPR_EXTRA_HIPCC_FLAGS", "").split()
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -32,7 +34,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -116,6 +116,24 @@ __device__ __forceinline__ void load_f32x8(const float* p, float (&x)[8]) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// Streaming (non-temporal) variants for data touched once per launch, such as a decode step's
+// state: they keep the stream from displacing reusable lines in L2.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_f32x8_nt(const float* p, float (&x)[8]) {
+  const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p) + 1);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store_f32x8_nt(float* p, const float (&x)[8]) {
+  const f32x4_t a = {x[0], x[1], x[2], x[3]};
+  const f32x4_t b = {x[4], x[5], x[6], x[7]};
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(p));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(p) + 1);
+}
+
 __device__ __forceinline__ void store_f32x8(float* p, const float (&x)[8]) {
   reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);

@@ -18,36 +18,59 @@
 
 namespace cpr {
 
+constexpr int kPosBits = 48;                               // positions below 2^48
+constexpr int64_t kPosMask = (int64_t(1) << kPosBits) - 1;
+
+#ifndef CPR_DECODE_MAX_NC
+#define CPR_DECODE_MAX_NC 8   // columns per lane: 8 -> one workgroup per (slot, value head) at d = 128
+#endif
+#ifndef CPR_DECODE_NT
+#define CPR_DECODE_NT 0       // 1: streaming (non-temporal) state loads and stores
+#endif
+
+__device__ __forceinline__ void state_load(const float* p, float (&x)[8]) {
+  if constexpr (CPR_DECODE_NT) load_f32x8_nt(p, x); else load_f32x8(p, x);
+}
+__device__ __forceinline__ void state_store(float* p, const float (&x)[8]) {
+  if constexpr (CPR_DECODE_NT) store_f32x8_nt(p, x); else store_f32x8(p, x);
+}
+
 template <int DK, int DV>
 struct DecodeCfg {
   static constexpr int G = DK / kLeaf;                         // lanes per column, one leaf each
   static constexpr int SLOTS = (256 / G < DV) ? 256 / G : DV;  // column slots per workgroup
-  static constexpr int NC = DV / SLOTS;                        // columns per lane
+  static constexpr int NC_ALL = DV / SLOTS;
+  static constexpr int NC = NC_ALL < CPR_DECODE_MAX_NC ? NC_ALL : CPR_DECODE_MAX_NC;  // columns per lane
+  static constexpr int WG_COLS = SLOTS * NC;                   // columns per workgroup
   static constexpr int THREADS = SLOTS * G;
-  static_assert(DV % SLOTS == 0, "shape");
+  static_assert(DV % SLOTS == 0 && NC_ALL % NC == 0, "shape");
 };
 
-// One workgroup per (entry, value head): every lane first issues the loads of all its NC columns
-// (NC x 32 bytes of state), then runs the step on each column; lane (slot, g) owns columns
-// slot + SLOTS * c, so each load instruction of a wave covers whole 512-byte columns.
+// One workgroup per (entry, value head, column group): every lane first issues the streaming
+// loads of all its NC columns (NC x 32 bytes of state), then runs the step on each column; lane
+// (slot, g) owns columns col0 + slot + SLOTS * c, so each load instruction of a wave covers whole
+// 512-byte columns.
 template <int DK, int DV, int IO>
 __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kernel(DecodeArgs A) {
   using Cfg = DecodeCfg<DK, DV>;
   constexpr int G = Cfg::G, NC = Cfg::NC, SLOTS = Cfg::SLOTS;
-  __shared__ float o_lds[DV];
+  __shared__ float o_lds[Cfg::WG_COLS];
   const int e = blockIdx.x, h = blockIdx.y;
+  const int col0 = blockIdx.z * Cfg::WG_COLS;
   const int32_t slot = A.slot_ids[e];
   if (slot < 0 || slot >= A.num_slots) return;                  // uniform across the block
-  const int64_t p = A.pos[slot];
+  // the low 48 bits are the position; the high bits count this step's finished workgroups
+  const int64_t p = A.pos[slot] & kPosMask;
   const int tid = threadIdx.x, cs = tid / G, g = tid % G;
   const int64_t head = (static_cast<int64_t>(slot) * A.h_v + h) * DV * DK;
   const int kh = h / (A.h_v / A.h_k);
   const int64_t kq = (static_cast<int64_t>(e) * A.h_k + kh) * DK + g * kLeaf;
-  const int64_t vo = (static_cast<int64_t>(e) * A.h_v + h) * DV;
+  const int64_t vo = (static_cast<int64_t>(e) * A.h_v + h) * DV + col0;
+  const float* src = A.state + head + static_cast<int64_t>(col0) * DK + g * kLeaf;
 
   float s[NC][kLeaf];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) load_f32x8(A.state + head + static_cast<int64_t>(cs + SLOTS * c) * DK + g * kLeaf, s[c]);
+  for (int c = 0; c < NC; ++c) state_load(src + static_cast<int64_t>(cs + SLOTS * c) * DK, s[c]);
   float kr[kLeaf], qr[kLeaf], v[NC];
   widen8<IO>(load_raw8<IO>(A.k, kq), kr);
   widen8<IO>(load_raw8<IO>(A.q, kq), qr);
@@ -59,8 +82,8 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kern
   if (A.boundary != nullptr && p >= 0 && p % A.chunk == 0) {    // resynchronise: commit the state
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      store_f32x8(A.boundary + head + static_cast<int64_t>(cs + SLOTS * c) * DK + g * kLeaf, s[c]);
-    if (h == 0 && tid == 0) A.boundary_pos[slot] = p;
+      state_store(A.boundary + head + static_cast<int64_t>(col0 + cs + SLOTS * c) * DK + g * kLeaf, s[c]);
+    if (h == 0 && blockIdx.z == 0 && tid == 0) A.boundary_pos[slot] = p;
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -68,22 +91,23 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kern
     if (g == 0) o_lds[cs + SLOTS * c] = o;
   }
 #pragma unroll
-  for (int c = 0; c < NC; ++c) store_f32x8(A.state + head + static_cast<int64_t>(cs + SLOTS * c) * DK + g * kLeaf, s[c]);
+  for (int c = 0; c < NC; ++c)
+    state_store(A.state + head + static_cast<int64_t>(col0 + cs + SLOTS * c) * DK + g * kLeaf, s[c]);
   __syncthreads();
-  if (tid < DV / 8) {
+  if (tid < Cfg::WG_COLS / 8) {
     float x[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = o_lds[tid * 8 + i];
     store8<IO>(A.o, vo + tid * 8, x);
   }
-}
-
-__global__ void decode_advance_kernel(DecodeArgs A) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= A.batch) return;
-  const int32_t slot = A.slot_ids[e];
-  if (slot < 0 || slot >= A.num_slots) return;
-  A.pos[slot] += 1;
+  if (tid == 0) {
+    // Every workgroup of this slot read pos above, before its own increment here, so the last
+    // one to finish can advance the position and clear the counter without racing a reader.
+    const unsigned long long done = static_cast<unsigned long long>(gridDim.y) * gridDim.z;
+    const unsigned long long old =
+        atomicAdd(reinterpret_cast<unsigned long long*>(A.pos + slot), 1ull << kPosBits);
+    if ((old >> kPosBits) == done - 1) A.pos[slot] = static_cast<int64_t>(old & kPosMask) + 1;
+  }
 }
 
 template <int DK, int DV>
@@ -95,15 +119,16 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) resync_kernel(De
   const int64_t p = A.pos[slot];
   if (p < 0 || p % A.chunk != 0) return;
   const int tid = threadIdx.x, cs = tid / Cfg::G, g = tid % Cfg::G;
+  const int col0 = blockIdx.z * Cfg::WG_COLS;
   const int64_t head = (static_cast<int64_t>(slot) * A.h_v + h) * DV * DK;
 #pragma unroll
   for (int c = 0; c < Cfg::NC; ++c) {
-    const int64_t off = head + static_cast<int64_t>(cs + Cfg::SLOTS * c) * DK + g * kLeaf;
+    const int64_t off = head + static_cast<int64_t>(col0 + cs + Cfg::SLOTS * c) * DK + g * kLeaf;
     float s[kLeaf];
     load_f32x8(A.state + off, s);
     store_f32x8(A.boundary + off, s);
   }
-  if (h == 0 && tid == 0) A.boundary_pos[slot] = p;
+  if (h == 0 && blockIdx.z == 0 && tid == 0) A.boundary_pos[slot] = p;
 }
 
 template <int DK, int DV, int IO>
@@ -112,22 +137,18 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.batch > 0) {
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO>), dim3(A.batch, A.h_v), dim3(Cfg::THREADS), 0, stream, A);
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS), 0,
+                       stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
-  if (A.batch > 0) {
-    hipLaunchKernelGGL(decode_advance_kernel, dim3((A.batch + 255) / 256), dim3(256), 0, stream, A);
-    e = hipGetLastError();
-  }
-  return e;
+  return record_event(A.events, 1, stream);
 }
 
 template <int DK, int DV>
 static hipError_t launch_resync_t(const DecodeArgs& A, hipStream_t stream) {
   using Cfg = DecodeCfg<DK, DV>;
   if (A.batch == 0 || A.boundary == nullptr) return hipSuccess;
-  hipLaunchKernelGGL((resync_kernel<DK, DV>), dim3(A.batch, A.h_v), dim3(Cfg::THREADS), 0, stream, A);
+  hipLaunchKernelGGL((resync_kernel<DK, DV>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS), 0, stream, A);
   return hipGetLastError();
 }
 

@@ -18,9 +18,11 @@ HEADER = os.path.join(ROOT, "include", "cpr_gdn.h")
 
 
 def _lib_module():
-    from bitwise_aligned_gated_amd import build
-    if not os.path.exists(build.LIB):
-        build.build_library()
+    """Load the binding, building the library first only if nothing is built."""
+    lib = os.path.join(ROOT, "bitwise_aligned_gated_amd", "libcpr_gdn.so")
+    if not os.path.exists(lib):
+        import runpy
+        runpy.run_path(os.path.join(ROOT, "bitwise_aligned_gated_amd", "build.py"))["build_library"]()
     import bitwise_aligned_gated_amd as cpr
     return cpr
 
