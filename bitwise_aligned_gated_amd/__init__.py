@@ -60,6 +60,7 @@ _SIGS = {
     "gdn_chunk_rows_bound": (_i64, [_i64, _i32, _i32]),
     "gdn_chunk_rows": (ctypes.c_int, [_P, _P, _i32, _i32, _P]),
     "gdn_prefill": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
+    "gdn_prefill_fused": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
     "gdn_decode_step": (ctypes.c_int, [_P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_state_resync": (ctypes.c_int, [_P, _P, _i32, _P]),
 }
@@ -234,12 +235,7 @@ def _ids(ids, n: int, device) -> torch.Tensor:
     return t.to(device).contiguous()
 
 
-def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
-                o=None, chunk_states=None, stream=None, events=None):
-    """Prefill / trainer forward over a packed batch (C gdn_prefill).
-
-    cu_seqlens: host sequence (checked on the host, then copied) or a device int32 tensor.
-    Returns (o, chunk_states); chunk_states is allocated with the bound's row count when None."""
+def _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o):
     P, dev = pool.policy, pool.device
     N = q.shape[0]
     if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
@@ -260,6 +256,34 @@ def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_
     if o is None:
         o = torch.empty((N, P.h_v, P.dv), dtype=io, device=dev)
     _dev(o, "o", io, (N, P.h_v, P.dv), dev)
+    return N, B, cu_d, ids, o
+
+
+def gdn_prefill_fused(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                      o=None, chunk_states=None, stream=None, events=None):
+    """One-pass prefill (C gdn_prefill_fused); bitwise equal to gdn_prefill.  chunk_states None:
+    no stash.  Returns (o, chunk_states)."""
+    P, dev = pool.policy, pool.device
+    N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
+    rows = 0
+    if chunk_states is not None:
+        _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+        rows = chunk_states.shape[0]
+    _check(_lib.gdn_prefill_fused(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
+                                  q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                  o.data_ptr(), None if chunk_states is None else chunk_states.data_ptr(), rows,
+                                  _stream_ptr(stream), _events(events, 2)))
+    return o, chunk_states
+
+
+def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                o=None, chunk_states=None, stream=None, events=None):
+    """Prefill / trainer forward over a packed batch (C gdn_prefill).
+
+    cu_seqlens: host sequence (checked on the host, then copied) or a device int32 tensor.
+    Returns (o, chunk_states); chunk_states is allocated with the bound's row count when None."""
+    P, dev = pool.policy, pool.device
+    N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
     bound = gdn_chunk_rows_bound(N, B, P.chunk)
     if chunk_states is None:
         chunk_states = torch.empty((max(bound, 1), P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)

@@ -318,6 +318,44 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
   return ok();
 }
 
+int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                      const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                      void* stream, void* const* events) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_prefill_fused: state handle is NULL");
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill_fused: negative sizes");
+  if (total_tokens >= (int64_t(1) << 31))
+    return fail(GDN_EINVAL, "gdn_prefill_fused: total_tokens must fit int32 cu_seqlens");
+  if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill_fused: cu_seqlens/slot_ids NULL");
+  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "gdn_prefill_fused: from_state must be 0 or 1");
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr || o == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill_fused: token tensor NULL");
+  const gdn_policy& P = st->policy;
+  const int64_t bound = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
+  if (chunk_states != nullptr && chunk_state_rows < bound)
+    return fail(GDN_EINVAL, "gdn_prefill_fused: chunk_state_rows %lld < bound %lld", (long long)chunk_state_rows,
+                (long long)bound);
+  cpr::PrefillArgs A;
+  A.cu = cu_seqlens;
+  A.slot_ids = slot_ids;
+  A.pos = st->pos;
+  A.pos_out = st->pos;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  A.state = st->state;
+  A.chunk_states = chunk_states;
+  A.total_tokens = total_tokens;
+  A.rows_cap = chunk_states != nullptr ? (bound < chunk_state_rows ? bound : chunk_state_rows) : 0;
+  A.num_seqs = num_seqs;
+  A.num_slots = st->num_slots;
+  A.from_state = from_state;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.events = events;
+  const hipError_t e = cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_prefill_fused launch");
+  return ok();
+}
+
 int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const void* q, const void* k,
                     const void* v, const float* a, const float* b, void* o, void* stream,
                     void* const* events) {

@@ -10,6 +10,7 @@ struct DecodeArgs;
 
 // Each returns hipErrorInvalidValue for a (dk, dv, io) combination that is not compiled in.
 hipError_t launch_prefill(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream);
 

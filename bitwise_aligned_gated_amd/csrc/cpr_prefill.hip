@@ -18,7 +18,9 @@
 //                           element.  Grid (boundary row, value head, column group); a row is
 //                           one chunk: load its entering state, run its tokens with output,
 //                           store o; the last chunk of a sequence also stores the final state.
-//   finish                  pos[slot] = p0 + length, after both passes have read pos.
+//   fused (fused_pass)      the one-pass variant: pass 1's mapping and grid, every token with
+//                           output, chunk-start rows only when a stash is given.
+//   finish                  pos[slot] = p0 + length, after the passes have read pos.
 // The schedule fixes the leaves and the tree, not the lane mapping, so both mappings (and the
 // decode kernel's) produce identical bits.
 #include <hip/hip_runtime.h>
@@ -28,16 +30,23 @@
 
 namespace cpr {
 
-template <int DK, int DV, bool OUT>
+// What a token loop does: pass 1 stores chunk-start states, pass 2 writes outputs, the fused
+// one-pass variant does both (it runs a whole sequence like pass 1, with outputs like pass 2).
+enum : int { kBoundary = 0, kOutput = 1, kFused = 2 };
+constexpr bool has_out(int mode) { return mode != kBoundary; }
+constexpr bool has_rows(int mode) { return mode != kOutput; }
+
+template <int DK, int DV, int MODE>
 struct PassCfg {
-  static constexpr int G = OUT ? (DK / kLeaf < 4 ? DK / kLeaf : 4) : DK / kLeaf;  // lanes per column
+  static constexpr bool WIDE = MODE == kOutput;   // parallel over chunks: fewer, longer lanes
+  static constexpr int G = WIDE ? (DK / kLeaf < 4 ? DK / kLeaf : 4) : DK / kLeaf;  // lanes per column
   static constexpr int NL = DK / (kLeaf * G);                                  // leaves per lane
   static constexpr int R = NL * kLeaf;                                         // rows per lane
-  static constexpr int NC = OUT ? 2 : 1;                                       // columns per lane
+  static constexpr int NC = WIDE ? 2 : 1;                                      // columns per lane
   static constexpr int WG_MAX_COLS = 256 / G * NC;                             // 4 waves
   static constexpr int WG_COLS = WG_MAX_COLS < DV ? WG_MAX_COLS : DV;
   static constexpr int THREADS = WG_COLS / NC * G;
-  static constexpr int TT = OUT ? 16 : 32;                                     // tokens per tile
+  static constexpr int TT = MODE == kBoundary ? 32 : 16;     // tokens per tile (LDS: all resident)
   static constexpr int K_UNITS = TT * DK / 8;          // 8-element units of a k (or q) tile
   static constexpr int V_UNITS = TT * WG_COLS / 8;
   static constexpr int K_PER_T = (K_UNITS + THREADS - 1) / THREADS;
@@ -48,30 +57,31 @@ struct PassCfg {
 };
 
 // One tile in flight (global -> registers -> LDS).
-template <int DK, int DV, int IO, bool OUT>
+template <int DK, int DV, int IO, int MODE>
 struct TileRegs {
-  using Cfg = PassCfg<DK, DV, OUT>;
+  using Cfg = PassCfg<DK, DV, MODE>;
   Raw8<IO> k[Cfg::K_PER_T];
-  Raw8<IO> q[OUT ? Cfg::K_PER_T : 1];
+  Raw8<IO> q[has_out(MODE) ? Cfg::K_PER_T : 1];
   Raw8<IO> v[Cfg::V_PER_T];
   float ab[Cfg::AB_PER_T];
 };
 
-template <int DK, int DV, bool OUT>
+template <int DK, int DV, int MODE>
 struct TileLds {
-  using Cfg = PassCfg<DK, DV, OUT>;
+  using Cfg = PassCfg<DK, DV, MODE>;
   float k[Cfg::TT][DK];
-  float q[OUT ? Cfg::TT : 1][DK];
+  float q[has_out(MODE) ? Cfg::TT : 1][DK];
   float v[Cfg::TT][Cfg::WG_COLS];
+  float o[MODE == kFused ? Cfg::TT : 1][Cfg::WG_COLS];  // fused: outputs gathered for row stores
   float2 ab[Cfg::TT];   // (a, b) of each token
 };
 
 // Fetch packed tokens [t0, t0 + n) (n <= TT) of key head kh / value head h into registers.
 // Units past n are zero-filled and never read from memory.
-template <int DK, int DV, int IO, bool OUT>
-__device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV, IO, OUT>& R, int t0, int n,
+template <int DK, int DV, int IO, int MODE>
+__device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV, IO, MODE>& R, int t0, int n,
                                            int kh, int h, int col0) {
-  using Cfg = PassCfg<DK, DV, OUT>;
+  using Cfg = PassCfg<DK, DV, MODE>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < Cfg::K_PER_T; ++i) {
@@ -80,7 +90,7 @@ __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV
     const bool ok = u < Cfg::K_UNITS && tt < n;
     const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_k + kh) * DK + c8 * 8;
     R.k[i] = ok ? load_raw8<IO>(A.k, e) : zero_raw8<IO>();
-    if constexpr (OUT) R.q[i] = ok ? load_raw8<IO>(A.q, e) : zero_raw8<IO>();
+    if constexpr (has_out(MODE)) R.q[i] = ok ? load_raw8<IO>(A.q, e) : zero_raw8<IO>();
   }
 #pragma unroll
   for (int i = 0; i < Cfg::V_PER_T; ++i) {
@@ -100,9 +110,9 @@ __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV
   }
 }
 
-template <int DK, int DV, int IO, bool OUT>
-__device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, OUT>& R, TileLds<DK, DV, OUT>& L) {
-  using Cfg = PassCfg<DK, DV, OUT>;
+template <int DK, int DV, int IO, int MODE>
+__device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, MODE>& R, TileLds<DK, DV, MODE>& L) {
+  using Cfg = PassCfg<DK, DV, MODE>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < Cfg::K_PER_T; ++i) {
@@ -112,7 +122,7 @@ __device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, OUT>& R, 
       float x[8];
       widen8<IO>(R.k[i], x);
       store_f32x8(&L.k[tt][c8 * 8], x);
-      if constexpr (OUT) {
+      if constexpr (has_out(MODE)) {
         widen8<IO>(R.q[i], x);
         store_f32x8(&L.q[tt][c8 * 8], x);
       }
@@ -149,32 +159,35 @@ __device__ __forceinline__ void lds_read(const float* p, float (&x)[N]) {
 }
 
 // Run tokens [tb, te) (offsets from the sequence start; tb < te) of one sequence through this
-// lane's columns.  OUT: write o for every token.  !OUT: store the state entering every chunk
-// start in (tb, te] into chunk_states (rows row0 + 1, row0 + 2, ...; the first one is `first_nb`
-// tokens after tb).
-template <int DK, int DV, int IO, bool OUT>
-__device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV, OUT>& L,
-                                           float (&s)[PassCfg<DK, DV, OUT>::NC][PassCfg<DK, DV, OUT>::R],
-                                           int tok0, int tb, int te, int h, int cg, int64_t row0, int first_nb) {
-  using Cfg = PassCfg<DK, DV, OUT>;
+// lane's columns.  Modes with output write o for every token; modes with rows store the state
+// entering every chunk start reached after a token, as rows row0 + 1, row0 + 2, ... below
+// row_end (the first one `first_nb` tokens after tb).
+template <int DK, int DV, int IO, int MODE>
+__device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV, MODE>& L,
+                                           float (&s)[PassCfg<DK, DV, MODE>::NC][PassCfg<DK, DV, MODE>::R],
+                                           int tok0, int tb, int te, int h, int cg, int64_t row0, int64_t row_end,
+                                           int first_nb) {
+  using Cfg = PassCfg<DK, DV, MODE>;
   constexpr int G = Cfg::G, NL = Cfg::NL, R = Cfg::R, NC = Cfg::NC;
+  constexpr bool OUT = has_out(MODE);
   const int tid = threadIdx.x;
   const int cp = tid / G, g = tid % G;
   const int col0 = cg * Cfg::WG_COLS;
   const int kh = h / (A.h_v / A.h_k);
   const int64_t plane = static_cast<int64_t>(DV) * DK;
-  int nb = __builtin_amdgcn_readfirstlane(first_nb);   // tokens until the next chunk start (pass 1)
-  int64_t row = row0 + 1;   // row the next chunk-start state goes to (pass 1)
+  int nb = __builtin_amdgcn_readfirstlane(first_nb);   // tokens until the next chunk start
+  int64_t row = row0 + 1;                              // row the next chunk-start state goes to
+  const bool rows_on = has_rows(MODE) && A.chunk_states != nullptr;
 
-  TileRegs<DK, DV, IO, OUT> Rg;
-  fetch_tile<DK, DV, IO, OUT>(A, Rg, tok0 + tb, te - tb < Cfg::TT ? te - tb : Cfg::TT, kh, h, col0);
-  commit_tile<DK, DV, IO, OUT>(Rg, L);
+  TileRegs<DK, DV, IO, MODE> Rg;
+  fetch_tile<DK, DV, IO, MODE>(A, Rg, tok0 + tb, te - tb < Cfg::TT ? te - tb : Cfg::TT, kh, h, col0);
+  commit_tile<DK, DV, IO, MODE>(Rg, L);
   __syncthreads();
   for (int t0 = tb; t0 < te; t0 += Cfg::TT) {
     const int n = te - t0 < Cfg::TT ? te - t0 : Cfg::TT;
     const int t1 = t0 + Cfg::TT;
     const bool more = t1 < te;
-    if (more) fetch_tile<DK, DV, IO, OUT>(A, Rg, tok0 + t1, te - t1 < Cfg::TT ? te - t1 : Cfg::TT, kh, h, col0);
+    if (more) fetch_tile<DK, DV, IO, MODE>(A, Rg, tok0 + t1, te - t1 < Cfg::TT ? te - t1 : Cfg::TT, kh, h, col0);
     auto token = [&](int tt) {
       float kr[R], qr[R];
       lds_read<R>(&L.k[tt][g * R], kr);
@@ -186,7 +199,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
       float o[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) o[c] = cpr_step<NL, G, OUT>(s[c], kr, qr, vv[c], ab.x, ab.y);
-      if constexpr (OUT) {
+      if constexpr (MODE == kOutput) {
         if (g == 0) {
           const int64_t oe = (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + cp * NC;
           if constexpr (NC == 2) {
@@ -196,10 +209,13 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
             for (int c = 0; c < NC; ++c) store1<IO>(A.o, oe + c, o[c]);
           }
         }
-      } else {
+      } else if constexpr (MODE == kFused) {
+        if (g == 0) L.o[tt][cp] = o[0];
+      }
+      if constexpr (has_rows(MODE)) {
         if (--nb == 0) {                                   // the new state enters a chunk start
           nb = A.chunk;
-          if (row < A.rows_cap) {
+          if (rows_on && row < row_end && row < A.rows_cap) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
               store_f32x8(A.chunk_states + (row * A.h_v + h) * plane +
@@ -210,23 +226,32 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
         }
       }
     };
-    if (!OUT && n == Cfg::TT) {              // pass 1, full tile: unrolled, immediate LDS offsets
+    if (MODE != kOutput && n == Cfg::TT) {    // one-leaf lanes, full tile: unrolled, immediate offsets
 #pragma unroll 4
       for (int tt = 0; tt < Cfg::TT; ++tt) token(tt);
     } else {
       for (int tt = 0; tt < n; ++tt) token(tt);
     }
     __syncthreads();
-    if (more) commit_tile<DK, DV, IO, OUT>(Rg, L);
+    if constexpr (MODE == kFused) {                    // the tile's outputs, 8 columns per unit
+      for (int u = tid; u < n * (Cfg::WG_COLS / 8); u += Cfg::THREADS) {
+        const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = L.o[tt][c8 * 8 + i];
+        store8<IO>(A.o, (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8, x);
+      }
+    }
+    if (more) commit_tile<DK, DV, IO, MODE>(Rg, L);
     __syncthreads();
   }
 }
 
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PassCfg<DK, DV, false>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
-  using Cfg = PassCfg<DK, DV, false>;
+__global__ void __launch_bounds__((PassCfg<DK, DV, kBoundary>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, kBoundary>;
   static_assert(Cfg::R == kLeaf && Cfg::NC == 1, "pass 1 holds one leaf of one column per lane");
-  __shared__ TileLds<DK, DV, false> L;
+  __shared__ TileLds<DK, DV, kBoundary> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
   const SeqMeta m = seq_meta(A, i);
@@ -253,13 +278,14 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, false>::THREADS)) boundary_pa
   const int64_t C = A.chunk;
   const int first_nb = static_cast<int>(C - m.p0 % C);
   const int last = static_cast<int>((m.p0 / C + m.nrows - 1) * C - m.p0);
-  run_tokens<DK, DV, IO, false>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, first_nb);
+  run_tokens<DK, DV, IO, kBoundary>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, row0 + m.nrows,
+                                    first_nb);
 }
 
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PassCfg<DK, DV, true>::THREADS)) output_pass_kernel(PrefillArgs A) {
-  using Cfg = PassCfg<DK, DV, true>;
-  __shared__ TileLds<DK, DV, true> L;
+__global__ void __launch_bounds__((PassCfg<DK, DV, kOutput>::THREADS)) output_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, kOutput>;
+  __shared__ TileLds<DK, DV, kOutput> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int64_t w = blockIdx.x;
   const int h = blockIdx.y, cg = blockIdx.z;
@@ -282,8 +308,8 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, true>::THREADS)) output_pass_
 #pragma unroll
     for (int r = 0; r < Cfg::R; r += 8) load_f32x8(src + off + r, *reinterpret_cast<float(*)[8]>(&s[cc][r]));
   }
-  run_tokens<DK, DV, IO, true>(A, L, s, static_cast<int>(m.tok0), static_cast<int>(tb), static_cast<int>(te), h, cg,
-                               0, 0);
+  run_tokens<DK, DV, IO, kOutput>(A, L, s, static_cast<int>(m.tok0), static_cast<int>(tb), static_cast<int>(te), h,
+                                  cg, 0, 0, 0);
   if (c == m.nrows - 1) {
     float* dst = A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane;
 #pragma unroll
@@ -293,6 +319,39 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, true>::THREADS)) output_pass_
       for (int r = 0; r < Cfg::R; r += 8) store_f32x8(dst + off + r, *reinterpret_cast<float(*)[8]>(&s[cc][r]));
     }
   }
+}
+
+// The one-pass variant: every token of a sequence in one launch, with outputs, and (when a stash
+// is given) the same chunk-start rows as pass 1.  Same step, same bits as the two passes.
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, kFused>;
+  __shared__ TileLds<DK, DV, kFused> L;
+  __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
+  const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+  const SeqMeta m = seq_meta(A, i);
+  const int64_t row0 = A.chunk_states != nullptr ? plan_row_offset(A, i, red) : 0;
+  if (m.slot < 0) return;                                    // uniform across the block
+  const int tid = threadIdx.x, lc = tid / Cfg::G, g = tid % Cfg::G;
+  const int64_t plane = static_cast<int64_t>(DV) * DK;
+  const int64_t col_off = static_cast<int64_t>(cg * Cfg::WG_COLS + lc) * DK + g * Cfg::R;
+  float* slot_state = A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off;
+  float s[1][Cfg::R];
+  if (A.from_state) {
+    load_f32x8(slot_state, s[0]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
+  }
+  if (m.len > 0) {
+    if (A.chunk_states != nullptr && row0 < A.rows_cap)
+      store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s[0]);
+    const int64_t C = A.chunk;
+    const int first_nb = static_cast<int>(C - m.p0 % C);
+    run_tokens<DK, DV, IO, kFused>(A, L, s, static_cast<int>(m.tok0), 0, m.len, h, cg, row0, row0 + m.nrows,
+                                   first_nb);
+  }
+  store_f32x8(slot_state, s[0]);
 }
 
 __global__ void prefill_finish_kernel(PrefillArgs A) {
@@ -305,8 +364,8 @@ __global__ void prefill_finish_kernel(PrefillArgs A) {
 
 template <int DK, int DV, int IO>
 static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
-  using C1 = PassCfg<DK, DV, false>;
-  using C2 = PassCfg<DK, DV, true>;
+  using C1 = PassCfg<DK, DV, kBoundary>;
+  using C2 = PassCfg<DK, DV, kOutput>;
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.num_seqs > 0) {
@@ -326,6 +385,35 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
     e = hipGetLastError();
   }
   return e;
+}
+
+template <int DK, int DV, int IO>
+static hipError_t launch_fused_t(const PrefillArgs& A, hipStream_t stream) {
+  using CF = PassCfg<DK, DV, kFused>;
+  hipError_t e = record_event(A.events, 0, stream);
+  if (e != hipSuccess) return e;
+  if (A.num_seqs > 0) {
+    hipLaunchKernelGGL((fused_pass_kernel<DK, DV, IO>), dim3(A.num_seqs, A.h_v, DV / CF::WG_COLS), dim3(CF::THREADS), 0,
+                       stream, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
+  if (A.num_seqs > 0) {
+    hipLaunchKernelGGL(prefill_finish_kernel, dim3((A.num_seqs + 255) / 256), dim3(256), 0, stream, A);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
+#define CPR_CASE(D, IOV) \
+  if (dk == D && dv == D && io == IOV) return launch_fused_t<D, D, IOV>(A, stream);
+  CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
+  CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
+  CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)
+  CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
+#undef CPR_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {

@@ -180,6 +180,20 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
                 void* o, float* chunk_states, int64_t chunk_state_rows, void* stream,
                 void* const* events);
 
+/* One-pass prefill: the same recurrence and the same outputs, final states and chunk-start rows
+ * as gdn_prefill, bit for bit, evaluated by a single kernel that runs every token of a sequence
+ * in order (the per-layer table of section "Solving the linear-attention headache" calls this
+ * evaluation "recurrent everywhere").  It does no second pass, so it suits batches whose
+ * (sequence, value head, column) chains already fill the GPU; gdn_prefill's chunk-parallel
+ * pass suits few long sequences.  Arguments as gdn_prefill, except that chunk_states may be NULL
+ * (no stash is written; chunk_state_rows is then ignored).
+ * events: NULL, or 2 hipEvent_t recorded before and after the kernel. */
+int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      const int32_t* slot_ids, int32_t from_state,
+                      const void* q, const void* k, const void* v, const float* a, const float* b,
+                      void* o, float* chunk_states, int64_t chunk_state_rows, void* stream,
+                      void* const* events);
+
 /* One decode step: one token for each of `batch` slots (section "Solving the linear-attention
  * headache": decode applies the recurrence one token at a time).
  *   slot_ids device int32 [batch] (distinct); q, k [batch][H_k][d_k]; v, o [batch][H_v][d_v];
