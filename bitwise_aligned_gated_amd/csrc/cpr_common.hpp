@@ -145,6 +145,31 @@ inline hipError_t record_event(void* const* events, int i, hipStream_t stream) {
   return hipEventRecord(static_cast<hipEvent_t>(events[i]), stream);
 }
 
+// ---- XCD-aware workgroup order ---------------------------------------------------------------
+// MI355X hands linear workgroup ids to its 8 XCDs round-robin, and each XCD has its own L2.
+// Workgroups that read the same inputs (a key head's k and q, shared by its value heads and
+// column groups) form a group; a group's members get ids with one residue mod 8, consecutive in
+// that XCD's order, so the shared lines are fetched into one L2 once.  Launch
+// xcd_grid(n_groups, group_size) workgroups; ids past the last group have no work.
+constexpr int kXcds = 8;
+
+inline int64_t xcd_grid(int64_t n_groups, int group_size) {
+  return (n_groups + kXcds - 1) / kXcds * kXcds * group_size;
+}
+
+struct GroupSlot {
+  int64_t group;
+  int member;
+};
+
+__device__ __forceinline__ GroupSlot xcd_group(int64_t b, int group_size) {
+  const int64_t x = b % kXcds, u = b / kXcds;
+  GroupSlot r;
+  r.group = (u / group_size) * kXcds + x;
+  r.member = static_cast<int>(u % group_size);
+  return r;
+}
+
 // ---- varlen plan ------------------------------------------------------------------------------
 // Metadata of packed sequence j.  A sequence with malformed cu_seqlens entries, an out-of-range
 // slot or a negative start position is treated as empty (no rows, no tokens) so no kernel ever

@@ -10,14 +10,17 @@
 // tiles (k, q widened to fp32, the workgroup's v columns, a and b) are staged through LDS and
 // the next tile is fetched into registers while the current one is computed.
 //   pass 1 (boundary_pass)  parallel only over (sequence, value head, column): G = d_k/8 so a
-//                           sequence's chain is spread over as many lanes as possible.  Grid
-//                           (sequence, value head, column group); runs each sequence up to its
-//                           last chunk start and stores the state entering every chunk.
+//                           sequence's chain is spread over as many lanes as possible.  One
+//                           workgroup per (sequence, value head, column group); runs each
+//                           sequence up to its last chunk start and stores the state entering
+//                           every chunk.
 //   pass 2 (output_pass)    parallel over chunks too, so lanes take more rows (G <= 4) and two
 //                           columns each, which cuts the tree and per-column overhead per
-//                           element.  Grid (boundary row, value head, column group); a row is
-//                           one chunk: load its entering state, run its tokens with output,
-//                           store o; the last chunk of a sequence also stores the final state.
+//                           element.  One workgroup per (boundary row, value head, column
+//                           group); a row is one chunk: load its entering state, run its tokens
+//                           with output, store o; the last chunk also stores the final state.
+// Workgroups are ordered XCD-aware (cpr_common.hpp): those reading one key head's tokens share
+// an XCD and its L2.
 //   fused (fused_pass)      the one-pass variant: pass 1's mapping and grid, every token with
 //                           output, chunk-start rows only when a stash is given.
 //   finish                  pos[slot] = p0 + length, after the passes have read pos.
@@ -253,7 +256,12 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kBoundary>::THREADS)) boundar
   static_assert(Cfg::R == kLeaf && Cfg::NC == 1, "pass 1 holds one leaf of one column per lane");
   __shared__ TileLds<DK, DV, kBoundary> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
-  const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+  // group = (sequence, key head); members = its value heads x column groups
+  const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio * ncg);
+  if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
+  const int i = static_cast<int>(gs.group / A.h_k);
+  const int h = static_cast<int>(gs.group % A.h_k) * ratio + gs.member / ncg, cg = gs.member % ncg;
   const SeqMeta m = seq_meta(A, i);
   const int64_t row0 = plan_row_offset(A, i, red);
   const int tid = threadIdx.x, lc = tid / Cfg::G, g = tid % Cfg::G;
@@ -287,9 +295,12 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kOutput>::THREADS)) output_pa
   using Cfg = PassCfg<DK, DV, kOutput>;
   __shared__ TileLds<DK, DV, kOutput> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
-  const int64_t w = blockIdx.x;
-  const int h = blockIdx.y, cg = blockIdx.z;
-  if (w >= A.rows_cap) return;
+  // group = (boundary row, key head); members = its value heads x column groups
+  const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio * ncg);
+  const int64_t w = gs.group / A.h_k;
+  const int h = static_cast<int>(gs.group % A.h_k) * ratio + gs.member / ncg, cg = gs.member % ncg;
+  if (w >= A.rows_cap) return;                               // uniform across the block
   int i;
   int64_t c;
   if (!plan_find_row(A, w, &i, &c, red)) return;             // uniform across the block
@@ -328,7 +339,11 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass
   using Cfg = PassCfg<DK, DV, kFused>;
   __shared__ TileLds<DK, DV, kFused> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
-  const int i = blockIdx.x, h = blockIdx.y, cg = blockIdx.z;
+  const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio * ncg);
+  if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
+  const int i = static_cast<int>(gs.group / A.h_k);
+  const int h = static_cast<int>(gs.group % A.h_k) * ratio + gs.member / ncg, cg = gs.member % ncg;
   const SeqMeta m = seq_meta(A, i);
   const int64_t row0 = A.chunk_states != nullptr ? plan_row_offset(A, i, red) : 0;
   if (m.slot < 0) return;                                    // uniform across the block
@@ -369,14 +384,18 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.num_seqs > 0) {
-    hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO>), dim3(A.num_seqs, A.h_v, DV / C1::WG_COLS),
-                       dim3(C1::THREADS), 0, stream, A);
+    const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
+    if (g1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g1)), dim3(C1::THREADS), 0, stream,
+                       A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0 && A.rows_cap > 0) {
-    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(A.rows_cap), A.h_v, DV / C2::WG_COLS),
-                       dim3(C2::THREADS), 0, stream, A);
+    const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
+    if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(C2::THREADS), 0, stream,
+                       A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
@@ -393,8 +412,10 @@ static hipError_t launch_fused_t(const PrefillArgs& A, hipStream_t stream) {
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.num_seqs > 0) {
-    hipLaunchKernelGGL((fused_pass_kernel<DK, DV, IO>), dim3(A.num_seqs, A.h_v, DV / CF::WG_COLS), dim3(CF::THREADS), 0,
-                       stream, A);
+    const int64_t gf = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / CF::WG_COLS));
+    if (gf > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fused_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(gf)), dim3(CF::THREADS), 0, stream,
+                       A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
