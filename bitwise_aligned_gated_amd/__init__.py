@@ -15,6 +15,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "GdnError", "Policy", "StatePool", "gdn_policy_digest", "gdn_policy_check",
+    "gdn_semantic_digest", "gdn_deployment_digest",
     "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
     "gdn_decode_step", "gdn_state_resync", "EXPORTS",
 ]
@@ -48,6 +49,8 @@ _SIGS = {
     "gdn_last_error": (ctypes.c_char_p, []),
     "gdn_policy_digest": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _u8p]),
     "gdn_sha256": (ctypes.c_int, [_P, _sz, _u8p]),
+    "gdn_semantic_digest": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _u8p]),
+    "gdn_deployment_digest": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _u8p]),
     "gdn_policy_check": (ctypes.c_int, [_u8p, _u8p]),
     "gdn_policy_validate": (ctypes.c_int, [ctypes.POINTER(_CPolicy)]),
     "gdn_state_bytes": (_sz, [ctypes.POINTER(_CPolicy), _i32]),
@@ -86,6 +89,7 @@ class Policy:
     chunk: int = 64
     io: str = "bf16"            # "f32" or "bf16"
     schedule: int = 1
+    boundary: str = "f32"       # boundary dtype: "f32" (exact resync) or "bf16" (rounding resync)
 
     @property
     def io_dtype(self) -> int:
@@ -96,8 +100,8 @@ class Policy:
         return {"f32": torch.float32, "bf16": torch.bfloat16}[self.io]
 
     def c(self) -> _CPolicy:
-        return _CPolicy(self.h_k, self.h_v, self.dk, self.dv, self.chunk, self.io_dtype, GDN_F32,
-                        self.schedule)
+        return _CPolicy(self.h_k, self.h_v, self.dk, self.dv, self.chunk, self.io_dtype,
+                        {"f32": GDN_F32, "bf16": GDN_BF16}[self.boundary], self.schedule)
 
     def validate(self):
         _check(_lib.gdn_policy_validate(ctypes.byref(self.c())))
@@ -106,6 +110,18 @@ class Policy:
 def gdn_policy_digest(policy: Policy) -> bytes:
     out = (ctypes.c_uint8 * 32)()
     _check(_lib.gdn_policy_digest(ctypes.byref(policy.c()), out))
+    return bytes(out)
+
+
+def gdn_semantic_digest(policy: Policy) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.gdn_semantic_digest(ctypes.byref(policy.c()), out))
+    return bytes(out)
+
+
+def gdn_deployment_digest(policy: Policy) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    _check(_lib.gdn_deployment_digest(ctypes.byref(policy.c()), out))
     return bytes(out)
 
 

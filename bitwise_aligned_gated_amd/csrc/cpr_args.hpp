@@ -26,7 +26,8 @@ struct PrefillArgs {
   int32_t h_k;
   int32_t h_v;
   int32_t chunk;
-  void* const* events;        // nullable: 3 hipEvent_t recorded around the passes
+  int32_t round_boundary;     // 1: bf16 boundary dtype (round the state at chunk starts)
+  void* const* events;        // nullable: hipEvent_t recorded around the kernels
 };
 
 struct DecodeArgs {
@@ -46,6 +47,7 @@ struct DecodeArgs {
   int32_t h_k;
   int32_t h_v;
   int32_t chunk;
+  int32_t round_boundary;     // 1: bf16 boundary dtype (round the state at chunk starts)
   void* const* events;        // nullable: 2 hipEvent_t recorded around the step kernel
 };
 

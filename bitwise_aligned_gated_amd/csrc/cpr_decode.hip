@@ -79,7 +79,12 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kern
   const float a = A.a[static_cast<int64_t>(e) * A.h_v + h];
   const float b = A.b[static_cast<int64_t>(e) * A.h_v + h];
 
-  if (A.boundary != nullptr && p >= 0 && p % A.chunk == 0) {    // resynchronise: commit the state
+  const bool at_chunk_start = p % A.chunk == 0;
+  if (A.round_boundary && at_chunk_start) {                      // resynchronise: re-base on bf16
+#pragma unroll
+    for (int c = 0; c < NC; ++c) resync_round(s[c]);
+  }
+  if (A.boundary != nullptr && at_chunk_start) {                 // commit the chunk-start state
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       state_store(A.boundary + head + static_cast<int64_t>(col0 + cs + SLOTS * c) * DK + g * kLeaf, s[c]);
@@ -115,9 +120,10 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) resync_kernel(De
   using Cfg = DecodeCfg<DK, DV>;
   const int e = blockIdx.x, h = blockIdx.y;
   const int32_t slot = A.slot_ids[e];
-  if (slot < 0 || slot >= A.num_slots || A.boundary == nullptr) return;
+  if (slot < 0 || slot >= A.num_slots) return;
   const int64_t p = A.pos[slot];
   if (p < 0 || p % A.chunk != 0) return;
+  if (A.boundary == nullptr && !A.round_boundary) return;
   const int tid = threadIdx.x, cs = tid / Cfg::G, g = tid % Cfg::G;
   const int col0 = blockIdx.z * Cfg::WG_COLS;
   const int64_t head = (static_cast<int64_t>(slot) * A.h_v + h) * DV * DK;
@@ -126,9 +132,13 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) resync_kernel(De
     const int64_t off = head + static_cast<int64_t>(col0 + cs + Cfg::SLOTS * c) * DK + g * kLeaf;
     float s[kLeaf];
     load_f32x8(A.state + off, s);
-    store_f32x8(A.boundary + off, s);
+    if (A.round_boundary) {
+      resync_round(s);
+      store_f32x8(A.state + off, s);
+    }
+    if (A.boundary != nullptr) store_f32x8(A.boundary + off, s);
   }
-  if (h == 0 && blockIdx.z == 0 && tid == 0) A.boundary_pos[slot] = p;
+  if (A.boundary != nullptr && h == 0 && blockIdx.z == 0 && tid == 0) A.boundary_pos[slot] = p;
 }
 
 template <int DK, int DV, int IO>
@@ -147,7 +157,7 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
 template <int DK, int DV>
 static hipError_t launch_resync_t(const DecodeArgs& A, hipStream_t stream) {
   using Cfg = DecodeCfg<DK, DV>;
-  if (A.batch == 0 || A.boundary == nullptr) return hipSuccess;
+  if (A.batch == 0 || (A.boundary == nullptr && !A.round_boundary)) return hipSuccess;
   hipLaunchKernelGGL((resync_kernel<DK, DV>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS), 0, stream, A);
   return hipGetLastError();
 }

@@ -58,7 +58,8 @@ int validate_policy(const gdn_policy* p) {
   if (p->dk <= 0 || p->dv <= 0) return fail(GDN_EINVAL, "head dims must be positive (dk=%d dv=%d)", p->dk, p->dv);
   if (p->chunk <= 0) return fail(GDN_EINVAL, "chunk must be positive (got %d)", p->chunk);
   if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16) return fail(GDN_EINVAL, "io_dtype %d unknown", p->io_dtype);
-  if (p->state_dtype != GDN_F32) return fail(GDN_EUNSUPPORTED, "only the fp32 state/boundary dtype is built");
+  if (p->state_dtype != GDN_F32 && p->state_dtype != GDN_BF16)
+    return fail(GDN_EINVAL, "boundary dtype %d unknown", p->state_dtype);
   if (p->schedule != cpr::kSchedule)
     return fail(GDN_EUNSUPPORTED, "schedule %d not built (only %d)", p->schedule, cpr::kSchedule);
   if (!supported_dims(p->dk, p->dv))
@@ -166,8 +167,36 @@ int gdn_policy_digest(const gdn_policy* p, uint8_t out[32]) {
   put_le32(bytes, p->io_dtype);
   put_le32(bytes, p->state_dtype);
   put_le32(bytes, p->schedule);
+  // chunk moves bits only when the boundary dtype rounds; otherwise it is a deployment setting
+  put_le32(bytes, p->state_dtype == GDN_F32 ? 0 : p->chunk);
   put_le32(bytes, cpr::kLeaf);
   put_le32(bytes, 0);  // GQA rule: value head h reads key head h / (h_v / h_k)
+  Sha256 s;
+  s.update(reinterpret_cast<const uint8_t*>(bytes.data()), bytes.size());
+  s.final(out);
+  return ok();
+}
+
+int gdn_semantic_digest(const gdn_policy* p, uint8_t out[32]) {
+  if (p == nullptr || out == nullptr) return fail(GDN_EINVAL, "gdn_semantic_digest: NULL pointer");
+  std::string bytes = "cpr-gdn-semantic-v1";
+  put_le32(bytes, 1);  // the gated delta rule with o_t = S_t^T q_t
+  put_le32(bytes, p->h_k);
+  put_le32(bytes, p->h_v);
+  put_le32(bytes, p->dk);
+  put_le32(bytes, p->dv);
+  put_le32(bytes, 0);  // GQA rule: value head h reads key head h / (h_v / h_k)
+  Sha256 s;
+  s.update(reinterpret_cast<const uint8_t*>(bytes.data()), bytes.size());
+  s.final(out);
+  return ok();
+}
+
+int gdn_deployment_digest(const gdn_policy* p, uint8_t out[32]) {
+  if (p == nullptr || out == nullptr) return fail(GDN_EINVAL, "gdn_deployment_digest: NULL pointer");
+  std::string bytes = "cpr-gdn-deploy-v1";
+  put_le32(bytes, p->state_dtype == GDN_F32 ? p->chunk : 0);  // with bf16 boundaries chunk is policy
+  put_le32(bytes, cpr::kMappingVersion);
   Sha256 s;
   s.update(reinterpret_cast<const uint8_t*>(bytes.data()), bytes.size());
   s.final(out);
@@ -312,6 +341,7 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
   A.num_slots = st->num_slots;
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.round_boundary = P.state_dtype == GDN_BF16;
   A.events = events;
   const hipError_t e = cpr::launch_prefill(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_prefill launch");
@@ -350,6 +380,7 @@ int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs
   A.num_slots = st->num_slots;
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.round_boundary = P.state_dtype == GDN_BF16;
   A.events = events;
   const hipError_t e = cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_prefill_fused launch");
@@ -375,6 +406,7 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const
   A.batch = batch;
   A.num_slots = st->num_slots;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.round_boundary = P.state_dtype == GDN_BF16;
   A.events = events;
   const hipError_t e = cpr::launch_decode(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
@@ -396,6 +428,7 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
   A.batch = n;
   A.num_slots = st->num_slots;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.round_boundary = P.state_dtype == GDN_BF16;
   const hipError_t e = cpr::launch_resync(P.dk, P.dv, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_state_resync launch");
   return ok();

@@ -218,6 +218,11 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
       if constexpr (has_rows(MODE)) {
         if (--nb == 0) {                                   // the new state enters a chunk start
           nb = A.chunk;
+          // resynchronise where a token at this position follows (pass 2 applies it after pass 1)
+          if (A.round_boundary && (MODE == kBoundary || t0 + tt + 1 < te)) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) resync_round(s[c]);
+          }
           if (rows_on && row < row_end && row < A.rows_cap) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
@@ -280,6 +285,7 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kBoundary>::THREADS)) boundar
 #pragma unroll
     for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
   }
+  if (A.round_boundary && m.p0 % A.chunk == 0) resync_round(s[0]);   // the first token is a chunk start
   store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s[0]);
   if (m.nrows < 2) return;
   // tokens up to the last recorded chunk start; the first chunk start is C - p0 % C tokens in
@@ -359,6 +365,7 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass
     for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
   }
   if (m.len > 0) {
+    if (A.round_boundary && m.p0 % A.chunk == 0) resync_round(s[0]);
     if (A.chunk_states != nullptr && row0 < A.rows_cap)
       store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s[0]);
     const int64_t C = A.chunk;

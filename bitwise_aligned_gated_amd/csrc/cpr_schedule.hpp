@@ -5,5 +5,9 @@ namespace cpr {
 
 constexpr int kSchedule = 1;  // schedule version (see cpr_step.hpp)
 constexpr int kLeaf = 8;      // rows per leaf of the pinned dot product
+// Version of the kernels' work mapping (lanes per column, columns per lane, tile sizes, workgroup
+// order).  The schedule fixes leaves and tree, so the mapping never moves a bit; it enters only
+// the deployment digest.
+constexpr int kMappingVersion = 3;
 
 }  // namespace cpr

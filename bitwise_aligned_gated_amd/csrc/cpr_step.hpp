@@ -96,4 +96,13 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short h) {
   return __builtin_bit_cast(float, static_cast<unsigned int>(h) << 16);
 }
 
+// Resynchronisation to a bf16 boundary dtype: every state element rounded to the nearest bf16
+// (ties to even).  Applied to the state entering a chunk-start position, just before that
+// position's token, by every path; with the fp32 boundary dtype nothing is applied.
+template <int N>
+__device__ __forceinline__ void resync_round(float (&s)[N]) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) s[r] = bf16_to_f32(f32_to_bf16_rne(s[r]));
+}
+
 }  // namespace cpr

@@ -70,8 +70,13 @@ extern "C" {
 /* The numerical policy of a state pool ("The execution contract": the constants an
  * implementation pins).  h_k, h_v: key and value heads (h_v a multiple of h_k; value head h reads
  * key head h / (h_v / h_k)).  dk, dv: head dims; builds support dk = dv in {16, 32, 64, 128}.
- * chunk: boundary spacing C >= 1.  io_dtype: GDN_F32 or GDN_BF16.  state_dtype: GDN_F32 (the only
- * boundary dtype; with it, resynchronisation is exact).  schedule: 1, the pinned per-token schedule:
+ * chunk: boundary spacing C >= 1.  io_dtype: GDN_F32 or GDN_BF16.
+ * state_dtype: the boundary dtype.  The state is always stored and updated in fp32; at every
+ * chunk start (just before the token at a position that is a multiple of C is applied) it is
+ * resynchronised to the boundary dtype: GDN_F32 changes nothing, GDN_BF16 rounds every element
+ * to the nearest bf16 (ties to even).  Every path applies the same rounding at the same
+ * positions; the state after a call's last token is left unrounded.
+ * schedule: 1, the pinned per-token schedule:
  *   for every value column j independently, in fp32 with IEEE denormals and round-to-nearest-even,
  *   (1) leaf partials over consecutive 8-row leaves of the d_k rows: p = S[r0][j]*k[r0], then
  *       p = fma(S[r][j], k[r], p) for r = r0+1 .. r0+7;
@@ -80,8 +85,8 @@ extern "C" {
  *   (3) w_j = fma(-a, u_j, v_j);  c_j = b * w_j;
  *   (4) S[r][j] = fma(k[r], c_j, a * S[r][j]) for every row r;
  *   (5) o_j = steps (1)-(2) applied to the updated S and q.
- * chunk is a deployment setting: it decides which states are materialised, never a value, so it
- * is left out of the policy digest. */
+ * With fp32 boundaries chunk is a deployment setting (it decides which states are materialised,
+ * never a value) and is left out of the policy digest; with bf16 boundaries it is numerical. */
 typedef struct gdn_policy {
   int32_t h_k;
   int32_t h_v;
@@ -101,10 +106,22 @@ typedef struct gdn_state gdn_state;
 const char* gdn_last_error(void);
 
 /* SHA-256 (FIPS 180-4) of the policy's canonical bytes: the ASCII tag "cpr-gdn-policy-v1"
- * followed by h_k, h_v, dk, dv, io_dtype, state_dtype, schedule, the leaf size (8) and the GQA
- * rule (0 = repeat-interleave) as little-endian int32.  chunk is excluded.  Writes 32 bytes.
+ * followed by h_k, h_v, dk, dv, io_dtype, state_dtype, schedule, chunk (0 when state_dtype is
+ * GDN_F32), the leaf size (8) and the GQA rule (0 = repeat-interleave) as little-endian int32.
+ * Writes 32 bytes.
  * ("The execution contract": digests exchanged at start-up.)  Host-only; needs no GPU. */
 int gdn_policy_digest(const gdn_policy* policy, uint8_t out[32]);
+
+/* The other two digests of "The execution contract", same form (SHA-256 of an ASCII tag and
+ * little-endian int32 fields):
+ *   semantic    what is computed: tag "cpr-gdn-semantic-v1", recurrence id (1), h_k, h_v, dk, dv,
+ *               GQA rule (0).  Equal semantic digests mean the same mathematical function.
+ *   deployment  settings that provably move no bit: tag "cpr-gdn-deploy-v1", chunk (0 when the
+ *               boundary dtype is bf16, where chunk is numerical policy), and the kernels' work-
+ *               mapping version.  Peers may differ here and still agree bitwise.
+ * Host-only. */
+int gdn_semantic_digest(const gdn_policy* policy, uint8_t out[32]);
+int gdn_deployment_digest(const gdn_policy* policy, uint8_t out[32]);
 
 /* SHA-256 (FIPS 180-4) of n host bytes into out[32]; the primitive behind the policy digest and
  * the identity digests of outputs ("The execution contract": SHA-256 identity digests).
@@ -210,9 +227,11 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
 
 /* Resynchronise listed slots (same section: decode re-bases its state once per chunk).  For a
  * slot at a chunk start (pos % C == 0) the state is re-based on the boundary state in the
- * policy's boundary dtype; with the fp32 boundary dtype that state is already exact, so values are
- * unchanged and the state is committed: copied, with pos, into the pool's boundary record if it
- * has one.  Slots that are not at a chunk start are left alone.  slot_ids device int32 [n]. */
+ * policy's boundary dtype (fp32: no change; bf16: the state is rounded in place, as a decode step
+ * would do before applying the token) and committed: copied, with pos, into the pool's boundary
+ * record if it has one.  Slots that are not at a chunk start are left alone.  Rounding is
+ * idempotent, so a decode step after an explicit resync changes nothing further.
+ * slot_ids device int32 [n]. */
 int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* stream);
 
 #ifdef __cplusplus

@@ -4,6 +4,7 @@ Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline le
 ``bench.py``.  The GPU product path never imports, calls or links anything here.
 """
 from .gdn_oracle import (bf16_bits_to_f64, boundary_positions, gdn_varlen, num_boundary_rows,
-                         recurrence)
+                         recurrence, round_to_bf16)
 
-__all__ = ["bf16_bits_to_f64", "boundary_positions", "gdn_varlen", "num_boundary_rows", "recurrence"]
+__all__ = ["bf16_bits_to_f64", "boundary_positions", "gdn_varlen", "num_boundary_rows", "recurrence",
+           "round_to_bf16"]

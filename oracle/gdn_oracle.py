@@ -26,19 +26,35 @@ Everything here is fp64 on inputs widened exactly from their fp32/bf16 bits.
 Chunk bookkeeping (which states are recorded) follows the same page: a chunk covers absolute
 positions [cC, (c+1)C) counted from the sequence's first token, and the recorded "boundary" states
 are the states at the start of each chunk the call touches (the first one being the state the
-call starts from).  Recording them does not change any value.
+call starts from).  With fp32 boundaries recording them changes no value.
+
+Boundary dtype.  Section "The execution contract" of the same article lists boundary dtypes among
+the constants a numerical policy pins.  With a bf16 boundary dtype the state is re-synchronised
+to bf16 at every chunk start: just before the token at a position that is a multiple of C is
+applied, every element of S is rounded to bf16.  The rounding decision is taken in the kernels'
+precision (the fp64 value rounded to fp32, then to bf16, each to nearest even).  The state after
+a call's last token is not rounded; whoever applies the next token does it.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrence", "boundary_positions", "num_boundary_rows", "gdn_varlen", "bf16_bits_to_f64"]
+__all__ = ["recurrence", "boundary_positions", "num_boundary_rows", "gdn_varlen", "bf16_bits_to_f64",
+           "round_to_bf16"]
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact value of bf16 bit patterns (uint16) as fp64."""
     w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return w.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Each element rounded to fp32 and then to bf16 (round to nearest even both times), as fp64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
 def boundary_positions(pos0: int, length: int, chunk: int) -> list:
@@ -56,13 +72,18 @@ def num_boundary_rows(pos0: int, length: int, chunk: int) -> int:
     return len(boundary_positions(pos0, length, chunk))
 
 
-def recurrence(q, k, v, a, b, S0=None, pos0: int = 0, chunk: int = 64):
+def recurrence(q, k, v, a, b, S0=None, pos0: int = 0, chunk: int = 64, boundary: str = "f32"):
     """The gated delta rule for one (sequence, value head), token by token, in fp64.
 
-    q, k: [T, d_k]; v: [T, d_v]; a, b: [T]; S0: [d_k, d_v] or None (zero state).
+    q, k: [T, d_k]; v: [T, d_v]; a, b: [T]; S0: [d_k, d_v] or None (zero state);
+    boundary: "f32" (chunk starts change nothing) or "bf16" (S is rounded to bf16 before the
+    token at every chunk-start position is applied).
     Returns (o [T, d_v], S_T [d_k, d_v], boundary states [R, d_k, d_v]) where the boundary
-    states are the states entering the positions listed by ``boundary_positions``.
+    states are the states entering the positions listed by ``boundary_positions`` (after the
+    rounding, at a chunk start).
     """
+    if boundary not in ("f32", "bf16"):
+        raise ValueError(boundary)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -75,6 +96,8 @@ def recurrence(q, k, v, a, b, S0=None, pos0: int = 0, chunk: int = 64):
     recorded = []
     for t in range(T):
         p = pos0 + t
+        if boundary == "bf16" and p % chunk == 0:
+            S = round_to_bf16(S)                    # resynchronise at the chunk start
         if t == 0 or p % chunk == 0:
             recorded.append(S.copy())
         u = S.T @ k[t]                              # u_t = S_{t-1}^T k_t
@@ -85,7 +108,8 @@ def recurrence(q, k, v, a, b, S0=None, pos0: int = 0, chunk: int = 64):
     return o, S, R
 
 
-def gdn_varlen(q, k, v, a, b, cu_seqlens, h_k: int, h_v: int, S0=None, pos0=None, chunk: int = 64):
+def gdn_varlen(q, k, v, a, b, cu_seqlens, h_k: int, h_v: int, S0=None, pos0=None, chunk: int = 64,
+               boundary: str = "f32"):
     """The recurrence over a packed batch of sequences.
 
     q, k: [N, H_k, d_k]; v: [N, H_v, d_v]; a, b: [N, H_v] (any float dtype, widened to fp64);
@@ -112,7 +136,7 @@ def gdn_varlen(q, k, v, a, b, cu_seqlens, h_k: int, h_v: int, S0=None, pos0=None
             g = h // group
             s0 = None if S0 is None else S0[i, h]
             o_h, s_h, r_h = recurrence(q[t0:t1, g], k[t0:t1, g], v[t0:t1, h], a[t0:t1, h], b[t0:t1, h],
-                                       S0=s0, pos0=p0, chunk=chunk)
+                                       S0=s0, pos0=p0, chunk=chunk, boundary=boundary)
             o[t0:t1, h] = o_h
             S_fin[i, h] = s_h
             per_head.append(r_h)

@@ -57,12 +57,36 @@ def test_sha256_matches_hashlib(n):
 
 def test_policy_digest_is_sha256_of_canonical_bytes():
     p = cpr.Policy(16, 32, 128, 128, chunk=64, io="bf16")
-    canon = b"cpr-gdn-policy-v1" + struct.pack("<9i", 16, 32, 128, 128, 1, 0, 1, 8, 0)
+    canon = b"cpr-gdn-policy-v1" + struct.pack("<10i", 16, 32, 128, 128, 1, 0, 1, 0, 8, 0)
     assert cpr.gdn_policy_digest(p) == hashlib.sha256(canon).digest()
+    # with bf16 boundaries the chunk size moves bits and enters the digest
+    pb = cpr.Policy(16, 32, 128, 128, chunk=64, io="bf16", boundary="bf16")
+    canon_b = b"cpr-gdn-policy-v1" + struct.pack("<10i", 16, 32, 128, 128, 1, 1, 1, 64, 8, 0)
+    assert cpr.gdn_policy_digest(pb) == hashlib.sha256(canon_b).digest()
+    assert cpr.gdn_policy_digest(pb) != cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128, chunk=32, boundary="bf16"))
     # chunk is a deployment setting and does not enter the digest; dtypes and shapes do
     assert cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128, chunk=16)) == cpr.gdn_policy_digest(p)
     assert cpr.gdn_policy_digest(cpr.Policy(16, 32, 128, 128, io="f32")) != cpr.gdn_policy_digest(p)
     assert cpr.gdn_policy_digest(cpr.Policy(8, 32, 128, 128)) != cpr.gdn_policy_digest(p)
+
+
+def test_semantic_and_deployment_digests():
+    p = cpr.Policy(16, 32, 128, 128, chunk=64, io="bf16")
+    sem = b"cpr-gdn-semantic-v1" + struct.pack("<6i", 1, 16, 32, 128, 128, 0)
+    assert cpr.gdn_semantic_digest(p) == hashlib.sha256(sem).digest()
+    # the semantic digest ignores everything that only affects rounding or deployment
+    for other in (cpr.Policy(16, 32, 128, 128, chunk=16, io="f32"), cpr.Policy(16, 32, 128, 128, boundary="bf16")):
+        assert cpr.gdn_semantic_digest(other) == cpr.gdn_semantic_digest(p)
+    assert cpr.gdn_semantic_digest(cpr.Policy(16, 32, 64, 64)) != cpr.gdn_semantic_digest(p)
+    dep = cpr.gdn_deployment_digest(p)
+    assert dep[:0] == b"" and len(dep) == 32
+    # fp32 boundaries: chunk is a deployment setting (deployment digest moves, policy digest not)
+    p16 = cpr.Policy(16, 32, 128, 128, chunk=16)
+    assert cpr.gdn_deployment_digest(p16) != dep and cpr.gdn_policy_digest(p16) == cpr.gdn_policy_digest(p)
+    # bf16 boundaries: chunk is numerical (policy digest moves, deployment digest not)
+    b64, b16 = cpr.Policy(16, 32, 128, 128, chunk=64, boundary="bf16"), cpr.Policy(16, 32, 128, 128, chunk=16, boundary="bf16")
+    assert cpr.gdn_deployment_digest(b64) == cpr.gdn_deployment_digest(b16)
+    assert cpr.gdn_policy_digest(b64) != cpr.gdn_policy_digest(b16)
 
 
 def test_policy_check_refuses_mismatch():

@@ -234,3 +234,46 @@ def test_varlen_packing_and_gqa_mapping():
     o2, _, _ = gdn_varlen(q, k, v2, a2, b2, cu, hk, hv, chunk=16)
     assert np.array_equal(o2[:, 0], o2[:, 1])
     assert not np.allclose(o2[:, 0], o2[:, 3])
+
+
+# --- bf16 boundary dtype ---------------------------------------------------------------------
+
+def test_round_to_bf16_matches_torch():
+    import torch
+    from oracle import round_to_bf16
+    x = np.random.default_rng(30).standard_normal(100000) * 10.0 ** np.random.default_rng(31).integers(-30, 30, 100000)
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_to_bf16(x), ref)
+
+
+def test_bf16_boundary_rounds_exactly_at_chunk_starts():
+    """bf16 mode = f32 mode run to the chunk start, the state rounded there, f32 mode from it on;
+    every recorded chunk-start state is bf16-representable; the final state is not rounded."""
+    from oracle import round_to_bf16
+    q, k, v, a, b, S0 = _rand(32, 150, 8, 8)
+    C = 32
+    o, S, R = recurrence(q, k, v, a, b, S0=S0, pos0=5, chunk=C, boundary="bf16")
+    # by hand: position 5 is not a chunk start; 32, 64, 96, 128 are
+    cur, outs, t = S0, [], 0
+    for stop in (27, 59, 91, 123, 150):
+        ob, cur, _ = recurrence(q[t:stop], k[t:stop], v[t:stop], a[t:stop], b[t:stop], S0=cur)
+        outs.append(ob)
+        if stop < 150:
+            cur = round_to_bf16(cur)
+        t = stop
+    assert np.array_equal(np.concatenate(outs), o) and np.array_equal(cur, S)
+    for row in R[1:]:
+        assert np.array_equal(round_to_bf16(row), row)
+    assert np.array_equal(R[0], S0)                      # 5 is not a chunk start: no rounding
+    assert not np.array_equal(round_to_bf16(S), S)       # the final state is left unrounded
+
+
+def test_bf16_boundary_is_identity_on_representable_states():
+    """With a = 1, b = 0 the state never changes; if S_0 is bf16-representable, rounding is exact
+    and bf16 mode equals f32 mode bit for bit."""
+    from oracle import round_to_bf16
+    q, k, v, a, b, S0 = _rand(33, 100, 8, 8)
+    S0 = round_to_bf16(S0)
+    o1, S1, _ = recurrence(q, k, v, np.ones(100), np.zeros(100), S0=S0, chunk=16, boundary="bf16")
+    o2, S2, _ = recurrence(q, k, v, np.ones(100), np.zeros(100), S0=S0, chunk=16)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
