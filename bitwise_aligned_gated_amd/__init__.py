@@ -17,7 +17,8 @@ __all__ = [
     "LIB_PATH", "GdnError", "Policy", "StatePool", "gdn_policy_digest", "gdn_policy_check",
     "gdn_semantic_digest", "gdn_deployment_digest",
     "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
-    "gdn_decode_step", "gdn_state_resync", "EXPORTS",
+    "gdn_prefill_fused", "gdn_decode_step", "gdn_state_resync", "gdn_backward", "gdn_backward_workspace_bytes",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpr_gdn.so")
@@ -66,6 +67,9 @@ _SIGS = {
     "gdn_prefill_fused": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
     "gdn_decode_step": (ctypes.c_int, [_P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_state_resync": (ctypes.c_int, [_P, _P, _i32, _P]),
+    "gdn_backward_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i64, _i32]),
+    "gdn_backward": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _P, _i32, _i64, _P, _P, _P, _P, _P, _P, _i64, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
@@ -337,3 +341,60 @@ def gdn_state_resync(pool: StatePool, slot_ids, stream=None):
     dev = pool.device
     ids = _ids(slot_ids, 0, dev)
     _check(_lib.gdn_state_resync(pool.handle, ids.data_ptr(), ids.numel(), _stream_ptr(stream)))
+
+
+def gdn_backward_workspace_bytes(policy: Policy, total_tokens: int, num_seqs: int) -> int:
+    r = _lib.gdn_backward_workspace_bytes(ctypes.byref(policy.c()), total_tokens, num_seqs)
+    if r < 0:
+        _check(GDN_EINVAL)
+    return int(r)
+
+
+def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state=None,
+                 want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None):
+    """Gradients of a trainer forward (C gdn_backward) from its inputs and chunk-state stash.
+
+    Returns a dict of fp32 device tensors dq, dk [N, H_k, d_k], dv [N, H_v, d_v], da, db [N, H_v]
+    and, when want_d_state0, d_state0 [num_seqs, H_v, d_v, d_k].  `out` may supply any of them."""
+    P = policy
+    dev = q.device
+    N = q.shape[0]
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
+        cu_d = _dev(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev, align=4)
+    else:
+        cu_h = _host_i32(cu_seqlens)
+        gdn_check_cu_seqlens(cu_h, N)
+        cu_d = cu_h.to(dev)
+    B = cu_d.numel() - 1
+    io = P.torch_io
+    _dev(q, "q", io, (N, P.h_k, P.dk), dev)
+    _dev(k, "k", io, (N, P.h_k, P.dk), dev)
+    _dev(v, "v", io, (N, P.h_v, P.dv), dev)
+    _dev(a, "a", torch.float32, (N, P.h_v), dev, align=4)
+    _dev(b, "b", torch.float32, (N, P.h_v), dev, align=4)
+    _dev(d_o, "d_o", io, (N, P.h_v, P.dv), dev)
+    _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    if d_state is not None:
+        _dev(d_state, "d_state", torch.float32, (B, P.h_v, P.dv, P.dk), dev)
+    out = dict(out or {})
+    shapes = {"dq": (N, P.h_k, P.dk), "dk": (N, P.h_k, P.dk), "dv": (N, P.h_v, P.dv), "da": (N, P.h_v),
+              "db": (N, P.h_v)}
+    if want_d_state0:
+        shapes["d_state0"] = (B, P.h_v, P.dv, P.dk)
+    for name, shape in shapes.items():
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=torch.float32, device=dev)
+        _dev(out[name], name, torch.float32, shape, dev)
+    need = gdn_backward_workspace_bytes(P, N, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+    d0 = out.get("d_state0")
+    _check(_lib.gdn_backward(ctypes.byref(P.c()), cu_d.data_ptr(), B, N, q.data_ptr(), k.data_ptr(),
+                             v.data_ptr(), a.data_ptr(), b.data_ptr(), chunk_states.data_ptr(),
+                             chunk_states.shape[0], d_o.data_ptr(),
+                             None if d_state is None else d_state.data_ptr(),
+                             out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(),
+                             out["da"].data_ptr(), out["db"].data_ptr(), None if d0 is None else d0.data_ptr(),
+                             workspace.data_ptr(), workspace.numel(), _stream_ptr(stream), _events(events, 4)))
+    return out

@@ -51,4 +51,32 @@ struct DecodeArgs {
   void* const* events;        // nullable: 2 hipEvent_t recorded around the step kernel
 };
 
+// Gradients of a forward that started every sequence at position 0 (the trainer's case).
+struct BackwardArgs {
+  const int32_t* cu;          // [num_seqs + 1]
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a;
+  const float* b;
+  const void* d_o;            // [N][H_v][dv], io dtype
+  const float* d_state;       // nullable: [num_seqs][H_v][dv][dk] gradient of the final states
+  const float* chunk_states;  // the forward's stash: [rows][H_v][dv][dk]
+  float* adjoint;             // workspace: [rows_cap][H_v][dv][dk], dL/dS at every chunk end
+  float* partial;             // workspace: [N][H_v][column groups][2 dk + 2]
+  float* dq;                  // [N][H_k][dk]
+  float* dk;                  // [N][H_k][dk]
+  float* dv;                  // [N][H_v][dv]
+  float* da;                  // [N][H_v]
+  float* db;                  // [N][H_v]
+  float* d_state0;            // nullable: [num_seqs][H_v][dv][dk]
+  int64_t total_tokens;
+  int64_t rows_cap;
+  int32_t num_seqs;
+  int32_t h_k;
+  int32_t h_v;
+  int32_t chunk;
+  void* const* events;        // nullable: 4 hipEvent_t around the three kernels
+};
+
 }  // namespace cpr

@@ -200,6 +200,18 @@ __device__ __forceinline__ SeqMeta seq_meta(const PrefillArgs& A, int j) {
   return m;
 }
 
+// The same metadata for a gradient pass: every sequence started at position 0, no slots.
+__device__ __forceinline__ SeqMeta seq_meta(const BackwardArgs& A, int j) {
+  SeqMeta m;
+  m.tok0 = 0; m.p0 = 0; m.len = 0; m.slot = 0; m.nrows = 0;
+  const int32_t c0 = A.cu[j], c1 = A.cu[j + 1];
+  if (c0 < 0 || c1 < c0 || static_cast<int64_t>(c1) > A.total_tokens) return m;
+  m.tok0 = c0;
+  m.len = c1 - c0;
+  m.nrows = m.len == 0 ? 0 : 1 + (m.len - 1) / A.chunk;
+  return m;
+}
+
 // Block-wide sum of one int64 per thread.  All threads must call; result valid in every thread.
 // `red` is __shared__ scratch of at least (blockDim.x + 63) / 64 entries.
 // Blocks narrower than a wave must have a power-of-two size so the butterfly stays on live lanes.
@@ -241,7 +253,8 @@ __device__ __forceinline__ int64_t block_excl_scan_i64(int64_t x, int64_t* red, 
 }
 
 // First boundary row of sequence i (sum of the rows of sequences 0 .. i-1).  Block-wide.
-__device__ inline int64_t plan_row_offset(const PrefillArgs& A, int i, int64_t* red) {
+template <class Args>
+__device__ inline int64_t plan_row_offset(const Args& A, int i, int64_t* red) {
   int64_t acc = 0;
   for (int base = 0; base < i; base += blockDim.x) {
     const int j = base + static_cast<int>(threadIdx.x);
@@ -253,8 +266,8 @@ __device__ inline int64_t plan_row_offset(const PrefillArgs& A, int i, int64_t* 
 
 // Which (sequence, row within it) owns global boundary row w.  Block-wide; returns false when w
 // is past the last row (the block has no work).  `red` needs (blockDim.x+63)/64 + 2 entries.
-__device__ inline bool plan_find_row(const PrefillArgs& A, int64_t w, int* seq, int64_t* row_in_seq,
-                                     int64_t* red) {
+template <class Args>
+__device__ inline bool plan_find_row(const Args& A, int64_t w, int* seq, int64_t* row_in_seq, int64_t* red) {
   int64_t* found = red + ((blockDim.x + 63) >> 6);   // [0]: sequence, [1]: row in it
   if (threadIdx.x == 0) found[0] = -1;
   int64_t offset = 0;

@@ -434,4 +434,77 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
   return ok();
 }
 
+static int64_t backward_rows(int64_t total_tokens, int32_t num_seqs, int32_t chunk) {
+  return total_tokens / chunk + num_seqs;   // sum over sequences of ceil(L_i / C), bounded
+}
+
+static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs) {
+  if (gdn_policy_validate(policy) != GDN_OK) return -1;
+  if (total_tokens < 0 || num_seqs < 0) {
+    fail(GDN_EINVAL, "gdn_backward_workspace_bytes: negative sizes");
+    return -1;
+  }
+  const gdn_policy& P = *policy;
+  const int ncg = cpr::backward_column_groups(P.dk, P.dv);
+  const int64_t plane = int64_t(P.dk) * P.dv;
+  const int64_t adj = backward_rows(total_tokens, num_seqs, P.chunk) * P.h_v * plane * 4;
+  const int64_t part = total_tokens * P.h_v * ncg * (2 * int64_t(P.dk) + 2) * 4;
+  ok();
+  return align256(adj) + align256(part);
+}
+
+int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                 const void* q, const void* k, const void* v, const float* a, const float* b,
+                 const float* chunk_states, int64_t chunk_state_rows, const void* d_o, const float* d_state,
+                 float* dq, float* dk, float* dv, float* da, float* db, float* d_state0, void* workspace,
+                 size_t workspace_bytes, void* stream, void* const* events) {
+  if (int rc = gdn_policy_validate(policy); rc != GDN_OK) return rc;
+  const gdn_policy& P = *policy;
+  if (P.state_dtype != GDN_F32)
+    return fail(GDN_EUNSUPPORTED, "gdn_backward: only the fp32 boundary dtype has a backward");
+  if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "gdn_backward: chunk %d > 64", P.chunk);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_backward: negative sizes");
+  if (total_tokens >= (int64_t(1) << 31))
+    return fail(GDN_EINVAL, "gdn_backward: total_tokens must fit int32 cu_seqlens");
+  if (num_seqs > 0 && cu_seqlens == nullptr) return fail(GDN_EINVAL, "gdn_backward: cu_seqlens is NULL");
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr ||
+                           d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || da == nullptr ||
+                           db == nullptr))
+    return fail(GDN_EINVAL, "gdn_backward: token tensor NULL");
+  const int64_t rows = backward_rows(total_tokens, num_seqs, P.chunk);
+  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "gdn_backward: chunk_states is NULL");
+  if (num_seqs > 0 && chunk_state_rows < rows)
+    return fail(GDN_EINVAL, "gdn_backward: chunk_state_rows %lld < %lld", (long long)chunk_state_rows,
+                (long long)rows);
+  if (rows * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_backward: too many chunks for one launch");
+  const int64_t need = gdn_backward_workspace_bytes(policy, total_tokens, num_seqs);
+  if (need < 0) return GDN_EINVAL;
+  if (int64_t(workspace_bytes) < need || (need > 0 && workspace == nullptr))
+    return fail(GDN_EINVAL, "gdn_backward: workspace of %lld bytes < %lld", (long long)workspace_bytes,
+                (long long)need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return fail(GDN_EINVAL, "gdn_backward: workspace must be 16-byte aligned");
+  const int64_t plane = int64_t(P.dk) * P.dv;
+  cpr::BackwardArgs A;
+  A.cu = cu_seqlens;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b;
+  A.d_o = d_o;
+  A.d_state = d_state;
+  A.chunk_states = chunk_states;
+  A.adjoint = static_cast<float*>(workspace);
+  A.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * P.h_v * plane * 4));
+  A.dq = dq; A.dk = dk; A.dv = dv; A.da = da; A.db = db;
+  A.d_state0 = d_state0;
+  A.total_tokens = total_tokens;
+  A.rows_cap = rows;
+  A.num_seqs = num_seqs;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.events = events;
+  const hipError_t e = cpr::launch_backward(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_backward launch");
+  return ok();
+}
+
 }  // extern "C"

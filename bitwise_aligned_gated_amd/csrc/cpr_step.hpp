@@ -68,6 +68,18 @@ __device__ __forceinline__ float pinned_dot(const float (&s)[NL * kLeaf], const 
   return lane_tree<G>(p[0]);
 }
 
+// The state update of one token on one column slice held by this lane (steps 1-4 of the
+// schedule); u, w and c are returned for the gradient pass, which replays the forward with them.
+template <int NL, int G>
+__device__ __forceinline__ void cpr_update(float (&s)[NL * kLeaf], const float (&k)[NL * kLeaf], float v, float a,
+                                           float b, float& u, float& w, float& c) {
+  u = pinned_dot<NL, G>(s, k);
+  w = __builtin_fmaf(-a, u, v);
+  c = b * w;
+#pragma unroll
+  for (int r = 0; r < NL * kLeaf; ++r) s[r] = __builtin_fmaf(k[r], c, a * s[r]);
+}
+
 // One token applied to one column slice held by this lane.
 //   s   this lane's NL*8 rows of column j (updated in place)
 //   k   the same rows of k_t; q the same rows of q_t (read only when WITH_OUT)
@@ -76,11 +88,8 @@ __device__ __forceinline__ float pinned_dot(const float (&s)[NL * kLeaf], const 
 template <int NL, int G, bool WITH_OUT>
 __device__ __forceinline__ float cpr_step(float (&s)[NL * kLeaf], const float (&k)[NL * kLeaf],
                                           const float (&q)[NL * kLeaf], float v, float a, float b) {
-  const float u = pinned_dot<NL, G>(s, k);
-  const float w = __builtin_fmaf(-a, u, v);
-  const float c = b * w;
-#pragma unroll
-  for (int r = 0; r < NL * kLeaf; ++r) s[r] = __builtin_fmaf(k[r], c, a * s[r]);
+  float u, w, c;
+  cpr_update<NL, G>(s, k, v, a, b, u, w, c);
   if constexpr (WITH_OUT) return pinned_dot<NL, G>(s, q);
   return 0.0f;
 }

@@ -34,6 +34,7 @@ __all__ = [
 
 # purposes, so that streams never collide
 _P_Q, _P_K, _P_V, _P_A, _P_B, _P_LEN, _P_PACK = 1, 2, 3, 4, 5, 6, 7
+_P_DO, _P_DS, _P_S0 = 8, 9, 10
 
 
 def _seed_of(seed: int, purpose: int, sub: int) -> int:
@@ -181,6 +182,27 @@ def make_inputs(seed: int, lengths, h_k: int, h_v: int, dk: int, dv: int, chunk:
     return GdnInputs(name, h_k, h_v, dk, dv, chunk, io, cu_from_lengths(lengths), q.contiguous(),
                      k.contiguous(), v.contiguous(), a.contiguous(), b.contiguous(),
                      {"seed": seed, "sub": sub, "device": str(dev)})
+
+
+def make_cotangents(x: GdnInputs, seed: int, with_d_state: bool = True, with_s0: bool = False,
+                    device=None) -> dict:
+    """Upstream gradients for a backward over x: d_o ~ N(0, 1) in x's io dtype [N, H_v, d_v];
+    d_state ~ N(0, 1) fp32 [B, H_v, d_v, d_k] (state layout, or None); and, for a forward that
+    continues from given states, s0 ~ N(0, 1/d_k) fp32 in the same layout (or None)."""
+    dev = torch.device(device) if device is not None else x.device
+    f64 = torch.float64
+    n, B = x.total_tokens, x.num_seqs
+
+    def normal(purpose, shape):
+        return torch.randn(shape, generator=_gen(seed, purpose, 0, dev), device=dev, dtype=f64)
+
+    out = {"d_o": normal(_P_DO, (n, x.h_v, x.dv)).to(torch.float32).to(_io_dtype(x.io)).contiguous(),
+           "d_state": None, "s0": None}
+    if with_d_state:
+        out["d_state"] = normal(_P_DS, (B, x.h_v, x.dv, x.dk)).to(torch.float32).contiguous()
+    if with_s0:
+        out["s0"] = (normal(_P_S0, (B, x.h_v, x.dv, x.dk)) / x.dk ** 0.5).to(torch.float32).contiguous()
+    return out
 
 
 # ---------------------------------------------------------------------------------------------

@@ -234,6 +234,45 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
  * slot_ids device int32 [n]. */
 int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* stream);
 
+/* ---- trainer backward ------------------------------------------------------------------------
+ * The per-layer table of section "Solving the linear-attention headache" times CPR for the
+ * trainer's forward and backward.  The gradients are those of the recurrence above for a loss L,
+ * given dO = dL/do and, optionally, dL/dS_T of every sequence's final state:
+ *   G = dL/dS_t runs backward in time; per token, with Gh = G + q_t dO_t^T,
+ *   dq_t = S_t dO_t,  dc = Gh^T k_t,  dw = b_t dc,  du = -a_t dw,  dv_t = dw,  db_t = <dc, w_t>,
+ *   dk_t = Gh c_t + S_{t-1} du,  da_t = <Gh, S_{t-1}> - <dw, u_t>,  G <- a_t Gh + k_t du^T,
+ * and dL/dS_0 is G after the first token; dq and dk of a key head sum its value heads'.
+ * It is evaluated the CPR way: an adjoint pass walks each sequence backward and keeps G at every
+ * chunk end; a chunk-parallel pass replays each chunk's forward states from the forward's stash
+ * and computes the per-token gradients; a final pass adds the per-column-group partial sums.
+ * Every sum has a fixed order, so the gradients are bitwise reproducible for any batch
+ * composition or packing. */
+
+/* Workspace bytes gdn_backward needs for total_tokens tokens in num_seqs sequences (-1 on bad
+ * input): dL/dS at every chunk end plus per-token partial sums of dq, dk, da and db. */
+int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
+
+/* Gradients of a trainer forward (gdn_prefill or gdn_prefill_fused over the same packed batch,
+ * every sequence starting at position 0: from_state 0, or 1 from slots at position 0).
+ *   policy        the forward's policy; the fp32 boundary dtype and chunk <= 64 are supported
+ *                 (GDN_EUNSUPPORTED otherwise).
+ *   cu_seqlens, total_tokens, q, k, v, a, b   the forward's inputs (device, layouts above).
+ *   chunk_states  the forward's stash, chunk_state_rows >= total_tokens / C + num_seqs (any
+ *                 forward stash qualifies): row 0 of a sequence is its initial state S_0.
+ *   d_o           device, io dtype, [N][H_v][d_v]: dL/do.
+ *   d_state       device fp32 [num_seqs][H_v][d_v][d_k] (state layout) or NULL (zero): dL/dS_T.
+ *   dq, dk        device fp32 [N][H_k][d_k];  dv  fp32 [N][H_v][d_v];  da, db  fp32 [N][H_v].
+ *   d_state0      device fp32 [num_seqs][H_v][d_v][d_k] or NULL: dL/dS_0 (for a forward that
+ *                 continued from slots).
+ *   workspace     device, 16-byte aligned, workspace_bytes >= gdn_backward_workspace_bytes().
+ * Outputs are fully overwritten for every token of every well-formed sequence.  Three kernels on
+ * `stream`; events: NULL, or 4 hipEvent_t recorded before, between and after them. */
+int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                 const void* q, const void* k, const void* v, const float* a, const float* b,
+                 const float* chunk_states, int64_t chunk_state_rows, const void* d_o, const float* d_state,
+                 float* dq, float* dk, float* dv, float* da, float* db, float* d_state0,
+                 void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -182,3 +182,41 @@ def test_prefill_argument_errors_before_launch():
     finally:
         assert lib.gdn_state_free(h) == 0
     assert lib.gdn_state_free(None) == 0
+
+
+def test_backward_workspace_bytes():
+    # adjoint rows (N/C + B) * H_v * dk * dv * 4, then partials N * H_v * groups * (2 dk + 2) * 4,
+    # each padded to 256 bytes; dk = 128 uses 8 column groups of 16, dk = 16 one group
+    p = cpr.Policy(16, 32, 128, 128, chunk=64)
+    adj = (10240 // 64 + 4) * 32 * 128 * 128 * 4
+    part = 10240 * 32 * 8 * 258 * 4
+    assert cpr.gdn_backward_workspace_bytes(p, 10240, 4) == adj + part
+    p = cpr.Policy(1, 2, 16, 16, chunk=8, io="f32")
+    adj, part = (100 // 8 + 3) * 2 * 16 * 16 * 4, 100 * 2 * 1 * 34 * 4
+    assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == -(-adj // 256) * 256 + -(-part // 256) * 256
+    with pytest.raises(cpr.GdnError):
+        cpr.gdn_backward_workspace_bytes(p, -1, 3)
+
+
+def test_backward_argument_errors_before_launch():
+    """gdn_backward's host checks (no GPU needed; the fake addresses are never dereferenced)."""
+    lib = cpr._lib
+    fake = 0x10000
+
+    def call(pol, rows=99, ws_bytes=1 << 40, num_seqs=2, total=100, ws=fake, d_o=fake):
+        return lib.gdn_backward(ctypes.byref(pol.c()), fake, num_seqs, total, fake, fake, fake, fake, fake, fake,
+                                rows, d_o, None, fake, fake, fake, fake, fake, None, ws, ws_bytes, None, None)
+
+    f32 = cpr.Policy(2, 4, 16, 16, chunk=64, io="f32")
+    assert call(cpr.Policy(2, 4, 16, 16, chunk=64, io="f32", boundary="bf16")) == 2
+    assert b"boundary" in lib.gdn_last_error()
+    assert call(cpr.Policy(2, 4, 16, 16, chunk=128, io="f32")) == 2
+    assert call(cpr.Policy(2, 3, 16, 16, chunk=64, io="f32")) == 1            # H_v not a multiple of H_k
+    assert call(f32, rows=2) == 1 and b"chunk_state_rows" in lib.gdn_last_error()   # needs 100/64 + 2 = 3
+    assert call(f32, ws_bytes=16) == 1 and b"workspace" in lib.gdn_last_error()
+    assert call(f32, ws=fake + 4) == 1 and b"aligned" in lib.gdn_last_error()
+    assert call(f32, d_o=None) == 1
+    assert call(f32, num_seqs=-1) == 1
+    # empty work launches nothing and succeeds
+    assert lib.gdn_backward(ctypes.byref(f32.c()), None, 0, 0, None, None, None, None, None, None, 0, None, None,
+                            None, None, None, None, None, None, None, 0, None, None) == 0

@@ -1,0 +1,191 @@
+"""Trainer backward on the GPU (gdn_backward) against the fp64 adjoint oracle, plus bitwise
+determinism and packing invariance of the gradients.
+
+Tolerance.  Every gradient is produced in fp32 from exactly representable inputs (bf16 io only
+changes what the inputs are, not the arithmetic), so the bound is the fp32 one, read relative to
+the gradient's own scale, which reaches ~1e2 for dk at d_k = 128:
+    max |got - ref| <= 1e-4 * max(1, max |ref|)   and   ||got - ref|| / ||ref|| <= 1e-5
+per gradient tensor of a sequence (dq, dk per key head; dv, da, db, dS_0 per value head).  fp32
+autograd of the same recurrence on the CPU lands at ~2e-7 normwise and ~1.5e-7 of the scale at
+these sizes, so both bounds leave a wide margin while still catching any wrong term.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from oracle import gdn_varlen_backward, recurrence_backward
+from tests.gpu_util import lib, normwise, policy_of, say, sha
+
+pytestmark = pytest.mark.gpu
+
+REL_MAX = 1e-4
+NORMWISE = 1e-5
+GRADS = ("dq", "dk", "dv", "da", "db")
+
+
+def _close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return
+    err = float(np.max(np.abs(got - ref)))
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    assert err <= REL_MAX * scale, f"{what}: max-abs {err:.3e} > {REL_MAX} * {scale:.3e}"
+    assert normwise(got, ref) <= NORMWISE, f"{what}: normwise {normwise(got, ref):.3e}"
+
+
+def _forward(x, s0=None, fused=False):
+    """Trainer forward on the GPU; returns the chunk-state stash."""
+    cpr = lib()
+    xd = x.to("cuda")
+    pool = cpr.StatePool(policy_of(x), max(x.num_seqs, 1))
+    if s0 is not None:
+        pool.state[: x.num_seqs].copy_(s0)
+    fn = cpr.gdn_prefill_fused if fused else cpr.gdn_prefill
+    rows = cpr.gdn_chunk_rows_bound(x.total_tokens, x.num_seqs, x.chunk)
+    cs = torch.empty((max(rows, 1), x.h_v, x.dv, x.dk), dtype=torch.float32, device="cuda")
+    fn(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, from_state=s0 is not None, chunk_states=cs)
+    return cs
+
+
+def _backward(x, ct, cs, want_d_state0=True):
+    cpr = lib()
+    xd = x.to("cuda")
+    d_state = None if ct["d_state"] is None else ct["d_state"].to("cuda")
+    g = cpr.gdn_backward(policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs, ct["d_o"].to("cuda"),
+                         d_state=d_state, want_d_state0=want_d_state0)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(x, ct):
+    cpu = x.to("cpu")
+    dO = ct["d_o"].cpu().double().numpy()
+    dS = None if ct["d_state"] is None else ct["d_state"].cpu().double().numpy().transpose(0, 1, 3, 2)
+    S0 = None if ct["s0"] is None else ct["s0"].cpu().double().numpy().transpose(0, 1, 3, 2)
+    return gdn_varlen_backward(cpu.widen("q"), cpu.widen("k"), cpu.widen("v"), cpu.widen("a"), cpu.widen("b"),
+                               dO, x.cu_seqlens, x.h_k, x.h_v, S0=S0, dS_T=dS)
+
+
+def _compare_all(x, g, ref):
+    names = GRADS + ("dS0",)
+    for i in range(x.num_seqs):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        for n, r in zip(names, ref):
+            if n == "dS0":
+                got = g["d_state0"][i].cpu().double().numpy().transpose(0, 2, 1)
+                _close(got, r[i], f"seq {i} dS0")
+            else:
+                got = g[n][t0:t1].cpu().double().numpy()
+                _close(got, r[t0:t1], f"seq {i} {n}")
+
+
+CASES = [
+    # dim, io, chunk, with d_state, with S0
+    (16, "f32", 16, True, True),
+    (16, "f32", 64, False, False),
+    (32, "f32", 8, True, False),
+    (64, "bf16", 32, True, True),
+    (128, "bf16", 64, True, True),
+    (128, "f32", 20, False, True),
+]
+
+
+@pytest.mark.parametrize("dim,io,chunk,with_ds,with_s0", CASES)
+def test_backward_matches_oracle(dim, io, chunk, with_ds, with_s0):
+    lens = [1, 64, 65, 200, 0, 33]
+    x = gi.make_inputs(61, lens, h_k=2, h_v=4, dk=dim, dv=dim, chunk=chunk, io=io)
+    ct = gi.make_cotangents(x, 62, with_d_state=with_ds, with_s0=with_s0)
+    say(f"backward vs oracle dim={dim} io={io} C={chunk} dS={with_ds} S0={with_s0}")
+    cs = _forward(x, None if ct["s0"] is None else ct["s0"].to("cuda"))
+    g = _backward(x, ct, cs)
+    _compare_all(x, g, _oracle(x, ct))
+
+
+def test_backward_gqa_ratio_four():
+    x = gi.make_inputs(63, [150, 64, 9], h_k=2, h_v=8, dk=64, dv=64, chunk=64, io="bf16")
+    ct = gi.make_cotangents(x, 64)
+    say("backward vs oracle GQA 4:1")
+    g = _backward(x, ct, _forward(x))
+    _compare_all(x, g, _oracle(x, ct))
+
+
+def test_backward_deterministic_and_packing_invariant():
+    lens = [300, 1, 128, 77, 0, 190]
+    x = gi.make_inputs(65, lens, h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    ct = gi.make_cotangents(x, 66, with_s0=True)
+    say("backward determinism and packing")
+    s0 = ct["s0"].to("cuda")
+    cs = _forward(x, s0)
+    g1 = _backward(x, ct, cs)
+    g2 = _backward(x, ct, _forward(x, s0, fused=True))     # stash of the one-pass forward
+    for n in GRADS + ("d_state0",):
+        assert sha(g1[n]) == sha(g2[n]), n
+    for i, L in enumerate(lens):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        xi = x.select([i])
+        cti = {"d_o": ct["d_o"][t0:t1].contiguous(), "d_state": ct["d_state"][i:i + 1].contiguous(),
+               "s0": ct["s0"][i:i + 1].contiguous()}
+        gi_ = _backward(xi, cti, _forward(xi, cti["s0"].to("cuda")))
+        for n in GRADS:
+            assert sha(gi_[n]) == sha(g1[n][t0:t1]), (i, n)
+        assert sha(gi_["d_state0"][0]) == sha(g1["d_state0"][i]), i
+
+
+def test_backward_chunk_size_changes_no_forward_bits_but_gradients_stay_close():
+    """The forward's bits do not depend on the chunk size (fp32 boundaries); the backward's
+    chunk-parallel sums do, within the fp32 tolerance, and each chunk size is reproducible."""
+    x = gi.make_inputs(67, [257], h_k=1, h_v=2, dk=32, dv=32, chunk=64, io="f32")
+    ct = gi.make_cotangents(x, 68)
+    say("backward across chunk sizes")
+    ref = _oracle(x, ct)
+    for C in (8, 32, 64):
+        xc = gi.GdnInputs(x.name, x.h_k, x.h_v, x.dk, x.dv, C, x.io, x.cu_seqlens, x.q, x.k, x.v, x.a, x.b,
+                          x.meta)
+        g = _backward(xc, ct, _forward(xc))
+        _compare_all(xc, g, ref)
+        g2 = _backward(xc, ct, _forward(xc))
+        assert all(sha(g[n]) == sha(g2[n]) for n in GRADS)
+
+
+def test_backward_trainer_10240_varlen():
+    """The trainer workload (10240 tokens packed varlen, 32 value heads over 16 key heads,
+    d = 128, chunk 64, bf16): sampled oracle parity on every sequence for key head 5 (value
+    heads 10 and 11), finite gradients everywhere, and packing invariance for one sequence."""
+    cpr = lib()
+    x = gi.config3(device="cuda")
+    ct = gi.make_cotangents(x, 69, device="cuda")
+    say(f"backward trainer 10240 lengths={x.lengths.tolist()}")
+    cs = _forward(x)
+    g = _backward(x, ct, cs)
+    for n in GRADS + ("d_state0",):
+        assert bool(torch.isfinite(g[n]).all()), n
+    cpu = x.to("cpu")
+    dO = ct["d_o"].cpu().double().numpy()
+    dS = ct["d_state"].cpu().double().numpy()
+    kh = 5
+    for i in range(x.num_seqs):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        rows = slice(t0, t1)
+        dq = dk = 0
+        for h in (2 * kh, 2 * kh + 1):
+            r = recurrence_backward(cpu.widen("q", rows)[:, kh], cpu.widen("k", rows)[:, kh],
+                                    cpu.widen("v", rows)[:, h], cpu.widen("a", rows)[:, h],
+                                    cpu.widen("b", rows)[:, h], dO[t0:t1, h], None, dS[i, h].T)
+            dq, dk = dq + r[0], dk + r[1]
+            _close(g["dv"][t0:t1, h].cpu().double().numpy(), r[2], f"seq {i} dv h{h}")
+            _close(g["da"][t0:t1, h].cpu().double().numpy(), r[3], f"seq {i} da h{h}")
+            _close(g["db"][t0:t1, h].cpu().double().numpy(), r[4], f"seq {i} db h{h}")
+            _close(g["d_state0"][i, h].cpu().double().numpy().T, r[5], f"seq {i} dS0 h{h}")
+        _close(g["dq"][t0:t1, kh].cpu().double().numpy(), dq, f"seq {i} dq")
+        _close(g["dk"][t0:t1, kh].cpu().double().numpy(), dk, f"seq {i} dk")
+    # packing: the last sequence alone gives the same bits
+    i = x.num_seqs - 1
+    t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+    xi = x.select([i])
+    cti = {"d_o": ct["d_o"][t0:t1].contiguous(), "d_state": ct["d_state"][i:i + 1].contiguous(), "s0": None}
+    gi_ = _backward(xi, cti, _forward(xi))
+    for n in GRADS:
+        assert sha(gi_[n]) == sha(g[n][t0:t1]), n
+    assert cpr.gdn_backward_workspace_bytes(policy_of(x), x.total_tokens, x.num_seqs) > 0
