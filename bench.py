@@ -30,6 +30,7 @@ METRIC = "CPR-GDN prefill tok/s (5×2048) + decode µs/step (256×1), % HBM peak
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 FLOP/clk/CU)
 FP32_UNPACKED_PEAK_TFLOPS = 78.6  # the same without packed fp32 (disabled in this build)
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle) worker
@@ -116,6 +117,21 @@ def prefill_flops(lengths, h_v, dk, dv, chunk):
     return p1_tokens * h_v * 5 * dk * dv, p2_tokens * h_v * 7 * dk * dv, p1_tokens
 
 
+def backward_flops(lengths, h_v, dk, dv, chunk):
+    """Algorithmic FLOPs of the trainer backward's kernels, per value head and token:
+    adjoint  G + q dO^T (2), dc = (.)^T k (2) and a G + k du^T (3): 7 dk dv over every token;
+    replay   the forward step without output: 5 dk dv;
+    chunk gradients (matrix cores), per chunk of L tokens: three L x d x d products
+             (dO S0^T, dU S0^T, C G_L^T) and five L x L x d products (dO C^T, dU C^T and the three
+             decay-masked products with K, Q, K): 6 L d^2 + 10 L^2 d."""
+    n = sum(lengths)
+    chunks = []
+    for L in lengths:
+        chunks += [chunk] * (L // chunk) + ([L % chunk] if L % chunk else [])
+    mfma = sum(6 * c * dk * dv + 10 * c * c * dk for c in chunks) * h_v
+    return n * h_v * 7 * dk * dv, n * h_v * 5 * dk * dv, mfma
+
+
 def decode_bytes(batch, h_k, h_v, dk, dv, io_bytes=2):
     """Algorithmic HBM bytes of one decode step: the state read and written once, the token's
     q, k (per key head), v, a, b read and o written."""
@@ -131,6 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-trainer", action="store_true", help="skip the trainer forward+backward workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--copy-calibration", action="store_true",
@@ -284,6 +301,61 @@ def main():
                          "traffic": traffic.get("decode_step"), "bytes_per_step": dbytes},
         }
 
+    # ---------------------------------------------------------------- trainer forward + backward
+    trainer = None
+    if not args.no_trainer:
+        xt = gi.config3(device=dev)
+        ct = gi.make_cotangents(xt, 69, device=dev)
+        Nt, Bt = xt.total_tokens, xt.num_seqs
+        tpool = cpr.StatePool(P, Bt, device=dev)
+        tcs = torch.empty((cpr.gdn_chunk_rows_bound(Nt, Bt, P.chunk), P.h_v, P.dv, P.dk), dtype=torch.float32,
+                          device=dev)
+        to = torch.empty((Nt, P.h_v, P.dv), dtype=torch.bfloat16, device=dev)
+        tcu = torch.from_numpy(xt.cu_seqlens).to(dev)
+        tids = torch.arange(Bt, dtype=torch.int32, device=dev)
+        ws = torch.empty(cpr.gdn_backward_workspace_bytes(P, Nt, Bt), dtype=torch.uint8, device=dev)
+        grads = {"dq": torch.empty((Nt, P.h_k, P.dk), device=dev), "dk": torch.empty((Nt, P.h_k, P.dk), device=dev),
+                 "dv": torch.empty((Nt, P.h_v, P.dv), device=dev), "da": torch.empty((Nt, P.h_v), device=dev),
+                 "db": torch.empty((Nt, P.h_v), device=dev)}
+
+        def train_step(fe=None, be=None):
+            cpr.gdn_prefill(tpool, tcu, xt.q, xt.k, xt.v, xt.a, xt.b, slot_ids=tids, o=to, chunk_states=tcs,
+                            events=fe)
+            cpr.gdn_backward(P, tcu, xt.q, xt.k, xt.v, xt.a, xt.b, tcs, ct["d_o"], d_state=ct["d_state"],
+                             workspace=ws, out=grads, events=be)
+
+        for _ in range(args.warmup):
+            train_step()
+        tev = [([hip.event() for _ in range(3)], [hip.event() for _ in range(4)]) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            train_step(*tev[i])
+        torch.cuda.synchronize()
+        t_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        avg = lambda pairs: statistics.mean(hip.ms(a, b) for a, b in pairs)
+        fwd_ms = avg([(f[0], f[2]) for f, _ in tev])
+        adj_ms = avg([(b[0], b[1]) for _, b in tev])
+        rep_ms = avg([(b[1], b[2]) for _, b in tev])
+        grad_ms = avg([(b[2], b[3]) for _, b in tev])
+        fa, fr, fg = backward_flops([int(l) for l in xt.lengths], P.h_v, P.dk, P.dv, P.chunk)
+        trainer = {
+            "workload": f"trainer forward+backward, {Nt} tokens packed varlen {xt.lengths.tolist()} (config 3 "
+                        "layout), stash reused by the backward",
+            "ms_per_step": round(t_ms, 4), "forward_ms": round(fwd_ms, 4),
+            "backward_ms": round(adj_ms + rep_ms + grad_ms, 4),
+            "kernels": {"adjoint": {"avg_ms": round(adj_ms, 4), "tflops": round(fa / (adj_ms * 1e-3) / 1e12, 3),
+                                    "bound": "alu", "peak_unpacked": FP32_UNPACKED_PEAK_TFLOPS},
+                        "replay": {"avg_ms": round(rep_ms, 4), "tflops": round(fr / (rep_ms * 1e-3) / 1e12, 3),
+                                   "bound": "alu", "peak_unpacked": FP32_UNPACKED_PEAK_TFLOPS},
+                        "grad_chunk": {"avg_ms": round(grad_ms, 4), "tflops": round(fg / (grad_ms * 1e-3) / 1e12, 3),
+                                       "bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
+                                       "frac": round(fg / (grad_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}},
+            "workspace_bytes": int(ws.numel()),
+            "h100_fwd_bwd_ms": 7.386,
+        }
+        del tpool, tcs, to, ws, grads, xt, ct
+
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
     if pool is not None:
@@ -331,8 +403,10 @@ def main():
                     "one_pass_variant": fused},
         "roofline": roofline,
         "decode": decode,
+        "trainer": trainer,
         "cpu_baseline": cpu,
-        "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "decode_256x1_cpr": 0.0846},
+        "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "decode_256x1_cpr": 0.0846,
+                                          "trainer_fwd_bwd_10240_cpr": 7.386},
                     "note": "pages' H100 figures; head layout not stated there"},
     }
     print(json.dumps(out, default=lambda v: v.item() if hasattr(v, "item") else str(v)), flush=True)

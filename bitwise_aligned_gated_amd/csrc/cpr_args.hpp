@@ -62,8 +62,10 @@ struct BackwardArgs {
   const void* d_o;            // [N][H_v][dv], io dtype
   const float* d_state;       // nullable: [num_seqs][H_v][dv][dk] gradient of the final states
   const float* chunk_states;  // the forward's stash: [rows][H_v][dv][dk]
-  float* adjoint;             // workspace: [rows_cap][H_v][dv][dk], dL/dS at every chunk end
-  float* partial;             // workspace: [N][H_v][column groups][2 dk + 2]
+  float* adjoint;             // workspace [adj_rows][H_v][dv][dk]: dL/dS at every chunk boundary
+  float* dc;                  // workspace [N][H_v][dv]: (G_t + q_t dO_t^T)^T k_t
+  float* cc;                  // workspace [N][H_v][dv]: c_t of the forward
+  float* ww;                  // workspace [N][H_v][dv]: w_t of the forward
   float* dq;                  // [N][H_k][dk]
   float* dk;                  // [N][H_k][dk]
   float* dv;                  // [N][H_v][dv]
@@ -71,7 +73,8 @@ struct BackwardArgs {
   float* db;                  // [N][H_v]
   float* d_state0;            // nullable: [num_seqs][H_v][dv][dk]
   int64_t total_tokens;
-  int64_t rows_cap;
+  int64_t rows_cap;           // chunk rows any plan can use
+  int64_t adj_rows;           // rows_cap + num_seqs (each sequence has one boundary more than chunks)
   int32_t num_seqs;
   int32_t h_k;
   int32_t h_v;

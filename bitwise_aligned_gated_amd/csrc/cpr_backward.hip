@@ -1,24 +1,34 @@
-// cpr_backward.hip -- gradients of the gated delta rule for the trainer, evaluated the CPR way.
+// cpr_backward.hip -- gradients of the gated delta rule for the trainer.
 //
 // The per-layer table of "Solving the linear-attention headache" (IsoExec articles) times CPR for
-// the trainer's forward and backward.  The backward mirrors the forward's two passes:
-//   adjoint pass   G = dL/dS runs backward in time, G_{t-1} = a_t (G_t + q_t dO_t^T) + k_t du_t^T
-//                  with du_t = -a_t b_t (G_t + q_t dO_t^T)^T k_t.  It needs no forward state and
-//                  is column-independent, so, like pass 1, it runs each sequence's columns from the
-//                  last token back to the end of chunk 0 and stores G at every chunk end.
-//   gradient pass  one workgroup per (chunk, value head, column group): the chunk's forward states
-//                  are replayed from the stashed chunk-start state (checkpoints every SUB tokens,
-//                  the SUB states of a sub-chunk in registers), G is replayed from the stored
-//                  chunk-end adjoint, and every token's dq, dk, dv, da, db follow.  dv is a
-//                  per-column value and is stored directly; dq, dk, da, db sum over the value
-//                  columns, so each workgroup stores its columns' sum (fixed pairwise order).
-//   reduce         per (token, key head): dq, dk sum the partials of its value heads and column
-//                  groups, da, db of a value head sum its column groups, all in a fixed pairwise
-//                  order, so the gradients are bitwise reproducible for any batch or packing.
-// Arithmetic (fp32, IEEE, round to nearest even; leaves and trees as in the forward schedule):
-//   Ghat = fma(q_i, dO_j, G);  dc = tree(Ghat, k);  dw = b*dc;  du = (-a)*dw;
-//   G    = fma(k_i, du, a*Ghat);  dv_j = dw;  db_j = dc*w;  da_j = fma(-dw, u, tree(Ghat, S_{t-1}));
-//   dq_i = sum_j S_t[i][j]*dO_j;  dk_i = sum_j fma(S_{t-1}[i][j], du_j, Ghat[i][j]*c_j).
+// the trainer's forward and backward.  The pages give no backward; this is reverse-mode
+// differentiation of the recurrence
+//     u_t = S_{t-1}^T k_t,  w_t = v_t - a_t u_t,  c_t = b_t w_t,  S_t = a_t S_{t-1} + k_t c_t^T,
+//     o_t = S_t^T q_t,
+// evaluated in three kernels over the forward's stash of chunk-start states.
+//
+// adjoint (column-parallel, one token at a time, last token first)
+//     G = dL/dS satisfies G_{t-1} = a_t (I - b_t k_t k_t^T) Ghat_t with Ghat_t = G_t + q_t dO_t^T;
+//     it needs no forward state.  Each (sequence, value head, column group) walks its tokens
+//     backward and writes dc_t = Ghat_t^T k_t for every token, G at every chunk boundary, and
+//     dL/dS_0.
+// replay (column-parallel, one chunk per workgroup)
+//     the forward step of the shared pinned schedule from the stashed chunk-start state, writing
+//     c_t and w_t for every token: the same bits the forward computed.
+// chunk gradients (matrix cores, one workgroup per (chunk, key head))
+//     Inside a chunk with gate products Gam_t = a_1 ... a_t, every state and adjoint is the
+//     chunk-start (or chunk-end) matrix plus rank-one terms, so with dU_t = -a_t b_t dc_t
+//       dq_t = Gam_t S_0 dO_t + sum_{s<=t} (Gam_t/Gam_s) k_s (c_s . dO_t)
+//       dk_t = (Gam_L/Gam_t) G_L c_t + sum_{s>=t} (Gam_s/Gam_t) q_s (dO_s . c_t)
+//            + Gam_{t-1} S_0 dU_t + sum_{s<t} (Gam_{t-1}/Gam_s) k_s (c_s . dU_t)
+//            + sum_{s>t} (Gam_{s-1}/Gam_t) k_s (dU_s . c_t)
+//     which are dense products on 16x16x4 fp32 MFMA tiles with decay-masked L x L factors.  The
+//     remaining gradients are per token: dv_t = b_t dc_t, db_t = dc_t . w_t, and
+//     a_t da_t = <G_{t-1}, S_{t-1}> =: h_{t-1}, where h_0 = <G at the chunk start, S_0> and
+//     h_t = h_{t-1} - q_t . dq_t + v_t . (b_t dc_t) (the per-value-head dq), accumulated in fp64.
+//     dq and dk of a key head add its value heads in head order inside the workgroup.
+// Every sum has a fixed order, so the gradients are bitwise reproducible for any batch
+// composition or packing.
 #include <hip/hip_runtime.h>
 
 #include "cpr_common.hpp"
@@ -26,43 +36,39 @@
 
 namespace cpr {
 
+// ---- column-parallel passes ------------------------------------------------------------------
 template <int DK, int DV>
-struct BwdCfg {
+struct ColCfg {
   static constexpr int G = DK / kLeaf;                         // lanes per column, one leaf each
   static constexpr int R = kLeaf;
   static constexpr int WG_COLS = (256 / G < DV) ? 256 / G : DV;
   static constexpr int THREADS = WG_COLS * G;
   static constexpr int NCG = DV / WG_COLS;                     // column groups per value head
   static constexpr int TT = 16;                                // tokens per staged tile
-  static constexpr int SUB = 8;                                // tokens per replayed sub-chunk
-  static constexpr int MAXC = 64;                              // largest chunk supported
-  static constexpr int NSUB = MAXC / SUB;
-  static constexpr int PW = 2 * DK + 2;                        // partial: dq[DK], dk[DK], da, db
   static_assert(DV % WG_COLS == 0 && WG_COLS % 8 == 0, "shape");
 };
 
 template <int DK, int DV>
-struct alignas(16) BwdLds {
-  using Cfg = BwdCfg<DK, DV>;
+struct alignas(16) ColLds {
+  using Cfg = ColCfg<DK, DV>;
   float k[Cfg::TT][DK];
   float q[Cfg::TT][DK];
   float v[Cfg::TT][Cfg::WG_COLS];
   float d[Cfg::TT][Cfg::WG_COLS];       // dO
   float2 ab[Cfg::TT];
-  float rq[Cfg::WG_COLS][DK];           // per-column partials of dq and dk for one token
-  float rk[Cfg::WG_COLS][DK];
-  float2 rs[Cfg::WG_COLS];              // per-column da, db
+  float out0[Cfg::TT][Cfg::WG_COLS];    // per-token column values awaiting a coalesced store
+  float out1[Cfg::TT][Cfg::WG_COLS];
 };
 
-// Stage tokens [t0, t0 + n) (packed indices, n <= TT) into LDS: k and q of key head kh, v and dO of
-// the workgroup's columns of value head h, a and b.  Synchronous; the caller synchronises.
+// Stage tokens [t0, t0 + n) (packed indices, n <= TT): k (and q) of key head kh, v (and dO) of
+// the workgroup's columns of value head h, a and b.  The caller synchronises around it.
 template <int DK, int DV, int IO, bool WITH_Q>
-__device__ __forceinline__ void stage(const BackwardArgs& A, BwdLds<DK, DV>& L, int t0, int n, int kh, int h,
+__device__ __forceinline__ void stage(const BackwardArgs& A, ColLds<DK, DV>& L, int64_t t0, int n, int kh, int h,
                                       int col0) {
-  using Cfg = BwdCfg<DK, DV>;
+  using Cfg = ColCfg<DK, DV>;
   for (int u = threadIdx.x; u < n * (DK / 8); u += Cfg::THREADS) {
     const int tt = u / (DK / 8), c8 = u % (DK / 8);
-    const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_k + kh) * DK + c8 * 8;
+    const int64_t e = ((t0 + tt) * A.h_k + kh) * DK + c8 * 8;
     float x[8];
     widen8<IO>(load_raw8<IO>(A.k, e), x);
     store_f32x8(&L.k[tt][c8 * 8], x);
@@ -73,7 +79,7 @@ __device__ __forceinline__ void stage(const BackwardArgs& A, BwdLds<DK, DV>& L, 
   }
   for (int u = threadIdx.x; u < n * (Cfg::WG_COLS / 8); u += Cfg::THREADS) {
     const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
-    const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
+    const int64_t e = ((t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
     float x[8];
     widen8<IO>(load_raw8<IO>(A.v, e), x);
     store_f32x8(&L.v[tt][c8 * 8], x);
@@ -83,17 +89,29 @@ __device__ __forceinline__ void stage(const BackwardArgs& A, BwdLds<DK, DV>& L, 
     }
   }
   for (int u = threadIdx.x; u < n; u += Cfg::THREADS) {
-    const int64_t e = static_cast<int64_t>(t0 + u) * A.h_v + h;
+    const int64_t e = (t0 + u) * A.h_v + h;
     L.ab[u] = make_float2(A.a[e], A.b[e]);
   }
 }
 
-// ---- adjoint pass -------------------------------------------------------------------------------
+// Store the staged per-token column values of tokens [t0, t0 + n) to dst [N][H_v][DV] (fp32).
+template <int DK, int DV>
+__device__ __forceinline__ void store_cols(const BackwardArgs& A,
+                                           const float (&src)[ColCfg<DK, DV>::TT][ColCfg<DK, DV>::WG_COLS],
+                                           float* dst, int64_t t0, int n, int h, int col0) {
+  using Cfg = ColCfg<DK, DV>;
+  for (int e = threadIdx.x; e < n * Cfg::WG_COLS; e += Cfg::THREADS) {
+    const int tt = e / Cfg::WG_COLS, col = e % Cfg::WG_COLS;
+    dst[((t0 + tt) * A.h_v + h) * DV + col0 + col] = src[tt][col];
+  }
+}
+
+// adjoint: one workgroup per (sequence, value head, column group), grouped per key head.
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((BwdCfg<DK, DV>::THREADS)) adjoint_pass_kernel(BackwardArgs A) {
-  using Cfg = BwdCfg<DK, DV>;
-  constexpr int G = Cfg::G;
-  __shared__ BwdLds<DK, DV> L;
+__global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(BackwardArgs A) {
+  using Cfg = ColCfg<DK, DV>;
+  constexpr int G = Cfg::G, R = Cfg::R;
+  __shared__ ColLds<DK, DV> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int ratio = A.h_v / A.h_k;
   const GroupSlot gs = xcd_group(blockIdx.x, ratio * Cfg::NCG);
@@ -101,96 +119,58 @@ __global__ void __launch_bounds__((BwdCfg<DK, DV>::THREADS)) adjoint_pass_kernel
   const int i = static_cast<int>(gs.group / A.h_k), kh = static_cast<int>(gs.group % A.h_k);
   const int h = kh * ratio + gs.member / Cfg::NCG, cg = gs.member % Cfg::NCG;
   const SeqMeta m = seq_meta(A, i);
-  const int64_t row0 = plan_row_offset(A, i, red);
+  const int64_t brow0 = plan_row_offset(A, i, red) + i;   // boundary b of sequence i: row brow0 + b
   const int tid = threadIdx.x, lc = tid / G, g = tid % G;
   const int col0 = cg * Cfg::WG_COLS;
   const int64_t plane = static_cast<int64_t>(DV) * DK;
-  const int64_t off = static_cast<int64_t>(col0 + lc) * DK + g * Cfg::R;
-  float Gs[Cfg::R];
+  const int64_t off = static_cast<int64_t>(col0 + lc) * DK + g * R;
+  float Gs[R];
   if (A.d_state != nullptr) {
     load_f32x8(A.d_state + (static_cast<int64_t>(i) * A.h_v + h) * plane + off, Gs);
   } else {
 #pragma unroll
-    for (int r = 0; r < Cfg::R; ++r) Gs[r] = 0.0f;
-  }
-  if (m.len == 0) {                                          // nothing to go through: dS0 = dS_T
-    if (A.d_state0 != nullptr) store_f32x8(A.d_state0 + (static_cast<int64_t>(i) * A.h_v + h) * plane + off, Gs);
-    return;
+    for (int r = 0; r < R; ++r) Gs[r] = 0.0f;
   }
   const int C = A.chunk;
-  const int64_t last_row = row0 + m.nrows - 1;
-  if (last_row < A.rows_cap) store_f32x8(A.adjoint + (last_row * A.h_v + h) * plane + off, Gs);
-  // tokens from the last one down to the first token of chunk 1
-  const int first = C;
-  for (int t1 = m.len; t1 > first; t1 -= Cfg::TT) {
-    const int t0 = t1 - Cfg::TT > first ? t1 - Cfg::TT : first;
+  // the boundary at the last token (position len) holds dL/dS_T
+  if (brow0 + m.nrows < A.adj_rows) store_f32x8(A.adjoint + ((brow0 + m.nrows) * A.h_v + h) * plane + off, Gs);
+  for (int t1 = m.len; t1 > 0; t1 -= Cfg::TT) {
+    const int t0 = t1 - Cfg::TT > 0 ? t1 - Cfg::TT : 0;
+    const int n = t1 - t0;
     __syncthreads();
-    stage<DK, DV, IO, true>(A, L, static_cast<int>(m.tok0) + t0, t1 - t0, kh, h, col0);
+    stage<DK, DV, IO, true>(A, L, m.tok0 + t0, n, kh, h, col0);
     __syncthreads();
-    for (int tt = t1 - t0 - 1; tt >= 0; --tt) {
-      float kr[Cfg::R], qr[Cfg::R], gh[Cfg::R];
-      load_f32x8(&L.k[tt][g * Cfg::R], kr);
-      load_f32x8(&L.q[tt][g * Cfg::R], qr);
+    for (int tt = n - 1; tt >= 0; --tt) {
+      float kr[R], qr[R], gh[R];
+      load_f32x8(&L.k[tt][g * R], kr);
+      load_f32x8(&L.q[tt][g * R], qr);
       const float dO = L.d[tt][lc];
       const float2 ab = L.ab[tt];
 #pragma unroll
-      for (int r = 0; r < Cfg::R; ++r) gh[r] = __builtin_fmaf(qr[r], dO, Gs[r]);
+      for (int r = 0; r < R; ++r) gh[r] = __builtin_fmaf(qr[r], dO, Gs[r]);
       const float dc = pinned_dot<1, G>(gh, kr);
-      const float dw = ab.y * dc;
-      const float du = -ab.x * dw;
+      const float du = -ab.x * (ab.y * dc);
 #pragma unroll
-      for (int r = 0; r < Cfg::R; ++r) Gs[r] = __builtin_fmaf(kr[r], du, ab.x * gh[r]);
+      for (int r = 0; r < R; ++r) Gs[r] = __builtin_fmaf(kr[r], du, ab.x * gh[r]);
+      if (g == 0) L.out0[tt][lc] = dc;
       const int t = t0 + tt;
-      if (t % C == 0) {                                      // G is now dL/dS at the end of chunk t/C - 1
-        const int64_t row = row0 + t / C - 1;
-        if (row < A.rows_cap) store_f32x8(A.adjoint + (row * A.h_v + h) * plane + off, Gs);
+      if (t % C == 0) {                                      // G is now dL/dS at position t
+        const int64_t row = brow0 + t / C;
+        if (row < A.adj_rows) store_f32x8(A.adjoint + (row * A.h_v + h) * plane + off, Gs);
       }
     }
+    __syncthreads();
+    store_cols<DK, DV>(A, L.out0, A.dc, m.tok0 + t0, n, h, col0);
   }
+  if (A.d_state0 != nullptr) store_f32x8(A.d_state0 + (static_cast<int64_t>(i) * A.h_v + h) * plane + off, Gs);
 }
 
-// ---- gradient pass ------------------------------------------------------------------------------
-// Register checkpoints indexed by a block-uniform sub-chunk number, through constant indices only.
-template <int R, int N, int M = 0>
-__device__ __forceinline__ void ckpt_save(float (&cp)[N][R], int idx, const float (&s)[R]) {
-  if constexpr (M < N) {
-    if (idx == M) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) cp[M][r] = s[r];
-    } else {
-      ckpt_save<R, N, M + 1>(cp, idx, s);
-    }
-  }
-}
-
-template <int R, int N, int M = 0>
-__device__ __forceinline__ void ckpt_load(const float (&cp)[N][R], int idx, float (&s)[R]) {
-  if constexpr (M < N) {
-    if (idx == M) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) s[r] = cp[M][r];
-    } else {
-      ckpt_load<R, N, M + 1>(cp, idx, s);
-    }
-  }
-}
-
-// Sum x over the WG_COLS column slots in a fixed balanced pairwise order.
-template <int N>
-__device__ __forceinline__ float pair_sum(float (&x)[N]) {
-#pragma unroll
-  for (int w = 1; w < N; w *= 2) {
-#pragma unroll
-    for (int l = 0; l + w < N; l += 2 * w) x[l] = x[l] + x[l + w];
-  }
-  return x[0];
-}
-
+// replay: one workgroup per (chunk, value head, column group), grouped per key head.
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((BwdCfg<DK, DV>::THREADS)) grad_chunk_kernel(BackwardArgs A) {
-  using Cfg = BwdCfg<DK, DV>;
-  constexpr int G = Cfg::G, R = Cfg::R, SUB = Cfg::SUB, NCOL = Cfg::WG_COLS;
-  __shared__ BwdLds<DK, DV> L;
+__global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) replay_kernel(BackwardArgs A) {
+  using Cfg = ColCfg<DK, DV>;
+  constexpr int G = Cfg::G, R = Cfg::R;
+  __shared__ ColLds<DK, DV> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int ratio = A.h_v / A.h_k;
   const GroupSlot gs = xcd_group(blockIdx.x, ratio * Cfg::NCG);
@@ -202,174 +182,376 @@ __global__ void __launch_bounds__((BwdCfg<DK, DV>::THREADS)) grad_chunk_kernel(B
   int64_t c;
   if (!plan_find_row(A, w, &i, &c, red)) return;             // uniform across the block
   const SeqMeta m = seq_meta(A, i);
-  const int C = A.chunk;
-  const int tb = static_cast<int>(c) * C;
-  const int te = tb + C < m.len ? tb + C : m.len;
-  const int tok0 = static_cast<int>(m.tok0);
+  const int tb = static_cast<int>(c) * A.chunk;
+  const int te = tb + A.chunk < m.len ? tb + A.chunk : m.len;
   const int tid = threadIdx.x, lc = tid / G, g = tid % G;
   const int col0 = cg * Cfg::WG_COLS;
   const int64_t plane = static_cast<int64_t>(DV) * DK;
-  const int64_t off = static_cast<int64_t>(col0 + lc) * DK + g * R;
-
-  float s[R], Gs[R];
-  load_f32x8(A.chunk_states + (w * A.h_v + h) * plane + off, s);
-  load_f32x8(A.adjoint + (w * A.h_v + h) * plane + off, Gs);
-
-  // replay the chunk forward once, keeping the state entering every sub-chunk
-  float cp[Cfg::NSUB][R];
+  float s[R];
+  load_f32x8(A.chunk_states + (w * A.h_v + h) * plane + static_cast<int64_t>(col0 + lc) * DK + g * R, s);
   for (int t0 = tb; t0 < te; t0 += Cfg::TT) {
     const int n = te - t0 < Cfg::TT ? te - t0 : Cfg::TT;
     __syncthreads();
-    stage<DK, DV, IO, false>(A, L, tok0 + t0, n, kh, h, col0);
+    stage<DK, DV, IO, false>(A, L, m.tok0 + t0, n, kh, h, col0);
     __syncthreads();
     for (int tt = 0; tt < n; ++tt) {
-      const int j = t0 + tt - tb;
-      if (j % SUB == 0) ckpt_save<R, Cfg::NSUB>(cp, j / SUB, s);
       float kr[R], u, ww, cc;
       load_f32x8(&L.k[tt][g * R], kr);
       const float2 ab = L.ab[tt];
       cpr_update<1, G>(s, kr, L.v[tt][lc], ab.x, ab.y, u, ww, cc);
-    }
-  }
-
-  // sub-chunks from the last to the first: replay their states, then walk them backwards
-  const int nsub = (te - tb + SUB - 1) / SUB;
-  for (int sc = nsub - 1; sc >= 0; --sc) {
-    const int ts = tb + sc * SUB;
-    const int n = te - ts < SUB ? te - ts : SUB;
-    __syncthreads();
-    stage<DK, DV, IO, true>(A, L, tok0 + ts, n, kh, h, col0);
-    __syncthreads();
-    float st[SUB + 1][R], uu[SUB], wv[SUB], cv[SUB];
-    ckpt_load<R, Cfg::NSUB>(cp, sc, st[0]);
-#pragma unroll
-    for (int j = 0; j < SUB; ++j) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) st[j + 1][r] = st[j][r];
-      if (j < n) {
-        float kr[R];
-        load_f32x8(&L.k[j][g * R], kr);
-        const float2 ab = L.ab[j];
-        cpr_update<1, G>(st[j + 1], kr, L.v[j][lc], ab.x, ab.y, uu[j], wv[j], cv[j]);
+      if (g == 0) {
+        L.out0[tt][lc] = cc;
+        L.out1[tt][lc] = ww;
       }
     }
-#pragma unroll
-    for (int j = SUB - 1; j >= 0; --j) {
-      if (j < n) {
-        float kr[R], qr[R], gh[R], pq[R], pk[R];
-        load_f32x8(&L.k[j][g * R], kr);
-        load_f32x8(&L.q[j][g * R], qr);
-        const float dO = L.d[j][lc];
-        const float2 ab = L.ab[j];
-#pragma unroll
-        for (int r = 0; r < R; ++r) gh[r] = __builtin_fmaf(qr[r], dO, Gs[r]);
-#pragma unroll
-        for (int r = 0; r < R; ++r) pq[r] = st[j + 1][r] * dO;
-        const float dc = pinned_dot<1, G>(gh, kr);
-        const float dS = pinned_dot<1, G>(gh, st[j]);
-        const float dw = ab.y * dc;
-        const float du = -ab.x * dw;
-        const float da_col = __builtin_fmaf(-dw, uu[j], dS);
-        const float db_col = dc * wv[j];
-#pragma unroll
-        for (int r = 0; r < R; ++r) pk[r] = __builtin_fmaf(st[j][r], du, gh[r] * cv[j]);
-#pragma unroll
-        for (int r = 0; r < R; ++r) Gs[r] = __builtin_fmaf(kr[r], du, ab.x * gh[r]);
-        const int t = tok0 + ts + j;
-        if (g == 0) {
-          A.dv[(static_cast<int64_t>(t) * A.h_v + h) * DV + col0 + lc] = dw;
-          L.rs[lc] = make_float2(da_col, db_col);
-        }
-        store_f32x8(&L.rq[lc][g * R], pq);
-        store_f32x8(&L.rk[lc][g * R], pk);
-        __syncthreads();
-        float* part = A.partial + ((static_cast<int64_t>(t) * A.h_v + h) * Cfg::NCG + cg) * Cfg::PW;
-        for (int e = tid; e < Cfg::PW; e += Cfg::THREADS) {
-          float x[NCOL];
-          if (e < DK) {
-#pragma unroll
-            for (int l = 0; l < NCOL; ++l) x[l] = L.rq[l][e];
-          } else if (e < 2 * DK) {
-#pragma unroll
-            for (int l = 0; l < NCOL; ++l) x[l] = L.rk[l][e - DK];
-          } else if (e == 2 * DK) {
-#pragma unroll
-            for (int l = 0; l < NCOL; ++l) x[l] = L.rs[l].x;
-          } else {
-#pragma unroll
-            for (int l = 0; l < NCOL; ++l) x[l] = L.rs[l].y;
-          }
-          part[e] = pair_sum<NCOL>(x);
-        }
-        __syncthreads();
-      }
-    }
+    __syncthreads();
+    store_cols<DK, DV>(A, L.out0, A.cc, m.tok0 + t0, n, h, col0);
+    store_cols<DK, DV>(A, L.out1, A.ww, m.tok0 + t0, n, h, col0);
   }
-  if (c == 0 && A.d_state0 != nullptr)
-    store_f32x8(A.d_state0 + (static_cast<int64_t>(i) * A.h_v + h) * plane + off, Gs);
 }
 
-// ---- reduce ---------------------------------------------------------------------------------------
-// One workgroup per token.  dq and dk of a key head: each of its value heads' column-group
-// partials summed pairwise, then the value heads added in head order.  da and db of a value head:
-// its column-group partials summed pairwise.
-template <int DK, int DV>
-__global__ void __launch_bounds__(256) grad_reduce_kernel(BackwardArgs A) {
-  using Cfg = BwdCfg<DK, DV>;
-  constexpr int NCG = Cfg::NCG, PW = Cfg::PW;
-  const int64_t t = blockIdx.x;
-  if (t >= A.total_tokens) return;
-  const int ratio = A.h_v / A.h_k;
-  const float* pt = A.partial + t * A.h_v * NCG * PW;
-  for (int e = threadIdx.x; e < A.h_k * 2 * DK; e += blockDim.x) {
-    const int kh = e / (2 * DK), idx = e % (2 * DK);
-    float acc = 0.0f;
-    for (int m = 0; m < ratio; ++m) {
-      const float* p = pt + (kh * ratio + m) * NCG * PW + idx;
-      float x[NCG];
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) x[cg] = p[cg * PW];
-      const float s = pair_sum<NCG>(x);
-      acc = m == 0 ? s : acc + s;
-    }
-    float* out = idx < DK ? A.dq : A.dk;
-    out[(t * A.h_k + kh) * DK + idx % DK] = acc;
+// ---- chunk gradients on matrix cores --------------------------------------------------------
+// v_mfma_f32_16x16x4f32 on a wave of 64 lanes, lane l = j + 16 g (j < 16, g < 4):
+//   A (16 x 4): lane holds A[j][g];  B (4 x 16): lane holds B[g][j];
+//   D (16 x 16): lane holds D[4 g + r][j] in register r.
+// In a product over a k range, a lane of group g feeds the k values 16 p + 4 g + e (e < 4) of
+// panel p, so that its A elements are four consecutive columns of a row.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct MCfg {
+  static constexpr int L = 64;                  // token rows of a chunk tile: 4 waves x 16
+  static constexpr int SB = D + 4;              // row stride of D-wide matrices in LDS
+  static constexpr int SC = L + 4;              // row stride of C^T (D rows of L tokens)
+  static constexpr int SA = L + 4;              // row stride of the L x L products
+  static constexpr int NT = D / 16;             // 16-wide tiles across D
+  static constexpr int KP = D / 16;             // 16-deep k panels across D
+  static constexpr int BIG_ROWS = D > 2 * L ? D : 2 * L;
+  static constexpr int SMALL = (D * SC > 2 * L * SA) ? D * SC : 2 * L * SA;
+};
+
+template <int D>
+struct alignas(16) MLds {
+  using M = MCfg<D>;
+  float big[M::BIG_ROWS * M::SB];   // S0, then G_end, then K (rows 0..L-1) and Q (rows L..2L-1)
+  float small[M::SMALL];            // C^T [D][SC], then A1 = dO C^T and A2 = dU C^T [L][SA] each
+  double lgd[M::L + 1];             // sum of log a over the chunk's tokens before token t
+  float2 ab[M::L];
+  float xq[M::L];                   // q_t . dq_t of the current value head
+  float xv[M::L];                   // v_t . dW_t
+  double red[8];
+};
+
+template <int IO>
+__device__ __forceinline__ float4 load4(const void* base, int64_t elem) {
+  if constexpr (IO == IO_F32) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(base) + elem);
+    return make_float4(__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xFFFF0000u),
+                       __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xFFFF0000u));
   }
-  for (int e = threadIdx.x; e < A.h_v * 2; e += blockDim.x) {
-    const int h = e / 2, which = e % 2;
-    const float* p = pt + h * NCG * PW + 2 * DK + which;
-    float x[NCG];
+}
+
+__device__ __forceinline__ float comp(const float4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// Sum of one double per thread over a 256-thread block in a fixed order; every thread gets it.
+__device__ __forceinline__ double block_sum_f64(double x, double* red) {
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) x[cg] = p[cg * PW];
-    (which == 0 ? A.da : A.db)[t * A.h_v + h] = pair_sum<NCG>(x);
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <int D, int IO>
+__global__ void __launch_bounds__(256) grad_chunk_kernel(BackwardArgs A) {
+  using M = MCfg<D>;
+  constexpr int NT = M::NT, KP = M::KP, SB = M::SB, SC = M::SC, SA = M::SA, LT = M::L;
+  __shared__ MLds<D> S;
+  __shared__ int64_t red[6];
+  const int64_t w = blockIdx.x / A.h_k;
+  const int kh = static_cast<int>(blockIdx.x % A.h_k);
+  if (w >= A.rows_cap) return;                               // uniform across the block
+  int i;
+  int64_t c;
+  if (!plan_find_row(A, w, &i, &c, red)) return;             // uniform across the block
+  const SeqMeta m = seq_meta(A, i);
+  const int tb = static_cast<int>(c) * A.chunk;
+  const int L = A.chunk < m.len - tb ? A.chunk : m.len - tb; // tokens in this chunk, 1..64
+  const int64_t tok = m.tok0 + tb;
+  const int ratio = A.h_v / A.h_k;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lgp = lane >> 4;
+  const int row = 16 * wave + lj;                            // this lane's A row (token in chunk)
+  const bool rv = row < L;
+  const int64_t plane = static_cast<int64_t>(D) * D;
+  const int64_t gstart = w + i;                              // boundary rows around this chunk
+
+  f32x4 dq_sum[NT], acc_dk[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) dq_sum[n] = acc_dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int hh = 0; hh < ratio; ++hh) {
+    const int h = kh * ratio + hh;
+    __syncthreads();                                         // the previous head is done with LDS
+    // S0 -> big; C^T -> small (tokens past the chunk are zero); gates
+    const float* s0 = A.chunk_states + (w * A.h_v + h) * plane;
+    for (int e = tid; e < D * D / 4; e += 256) {
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      *reinterpret_cast<float4*>(&S.big[r * SB + 4 * c4]) = reinterpret_cast<const float4*>(s0 + r * D)[c4];
+    }
+    for (int e = tid; e < LT * D / 4; e += 256) {
+      const int t = e / (D / 4), c4 = e % (D / 4);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < L) x = reinterpret_cast<const float4*>(A.cc + ((tok + t) * A.h_v + h) * D)[c4];
+      S.small[(4 * c4 + 0) * SC + t] = x.x;
+      S.small[(4 * c4 + 1) * SC + t] = x.y;
+      S.small[(4 * c4 + 2) * SC + t] = x.z;
+      S.small[(4 * c4 + 3) * SC + t] = x.w;
+    }
+    if (tid < LT) {
+      float2 ab = make_float2(1.f, 0.f);
+      if (tid < L) ab = make_float2(A.a[(tok + tid) * A.h_v + h], A.b[(tok + tid) * A.h_v + h]);
+      S.ab[tid] = ab;
+      // log of the gate product up to and including token tid, an inclusive scan in fp64
+      double x = tid < L ? log(static_cast<double>(ab.x)) : 0.0;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      S.lgd[tid + 1] = x;
+      if (tid == 0) S.lgd[0] = 0.0;
+    }
+    __syncthreads();
+    // h_0 = <G at the chunk start, S0> in fp64
+    double hp = 0.0;
+    {
+      const float* g0 = A.adjoint + (gstart * A.h_v + h) * plane;
+      for (int e = tid; e < D * D / 4; e += 256) {
+        const int r = e / (D / 4), c4 = e % (D / 4);
+        const float4 gv = reinterpret_cast<const float4*>(g0 + r * D)[c4];
+        const float4 sv = *reinterpret_cast<const float4*>(&S.big[r * SB + 4 * c4]);
+        hp += static_cast<double>(gv.x) * sv.x + static_cast<double>(gv.y) * sv.y +
+              static_cast<double>(gv.z) * sv.z + static_cast<double>(gv.w) * sv.w;
+      }
+    }
+    const double h0 = block_sum_f64(hp, S.red);
+    const double lr0 = S.lgd[row], lr1 = S.lgd[row + 1];
+    const float2 abr = S.ab[row];
+    const float fq = rv ? __expf(static_cast<float>(lr1)) : 0.f;                 // Gam after the row
+    const float fu = rv ? __expf(static_cast<float>(lr0)) : 0.f;                 // Gam before it
+    const float fc = rv ? __expf(static_cast<float>(S.lgd[L] - lr1)) : 0.f;     // Gam_L / Gam_row
+    const float su = -abr.x * abr.y;                                              // dU = su * dc
+
+    // dq += Gam_t dO S0^T; dk += Gam_{t-1} dU S0^T; A1 = dO C^T; A2 = dU C^T
+    f32x4 acc_dq[NT], a1[4], a2[4];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc_dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 4; ++n) a1[n] = a2[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < KP; ++p) {
+      const int kb = 16 * p + 4 * lgp;
+      float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f), c4 = o4;
+      if (rv) {
+        o4 = load4<IO>(A.d_o, ((tok + row) * A.h_v + h) * D + kb);
+        c4 = *reinterpret_cast<const float4*>(A.dc + ((tok + row) * A.h_v + h) * D + kb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = kb + e;
+        const float ao = comp(o4, e), au = su * comp(c4, e);
+        const float aq = ao * fq, ak = au * fu;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float bs = S.big[k * SB + 16 * n + lj];
+          acc_dq[n] = mfma4(aq, bs, acc_dq[n]);
+          acc_dk[n] = mfma4(ak, bs, acc_dk[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const float bc = S.small[k * SC + 16 * n + lj];
+          a1[n] = mfma4(ao, bc, a1[n]);
+          a2[n] = mfma4(au, bc, a2[n]);
+        }
+      }
+    }
+    // dk += (Gam_L / Gam_t) C G_end^T
+    __syncthreads();                                         // S0 reads done
+    {
+      const float* ge = A.adjoint + ((gstart + 1) * A.h_v + h) * plane;
+      for (int e = tid; e < D * D / 4; e += 256) {
+        const int r = e / (D / 4), c4 = e % (D / 4);
+        *reinterpret_cast<float4*>(&S.big[r * SB + 4 * c4]) = reinterpret_cast<const float4*>(ge + r * D)[c4];
+      }
+    }
+    __syncthreads();
+    for (int p = 0; p < KP; ++p) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 16 * p + 4 * lgp + e;
+        const float ac = S.small[k * SC + row] * fc;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc_dk[n] = mfma4(ac, S.big[k * SB + 16 * n + lj], acc_dk[n]);
+      }
+    }
+    __syncthreads();                                         // C^T and G_end reads done
+    // A1, A2 -> small; K -> big rows [0, L); Q -> big rows [L, 2L) (zero past the chunk)
+    float* sa1 = S.small;
+    float* sa2 = S.small + LT * SA;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lgp + r;
+        sa1[t * SA + 16 * n + lj] = a1[n][r];
+        sa2[t * SA + 16 * n + lj] = a2[n][r];
+      }
+    for (int e = tid; e < 2 * LT * D / 4; e += 256) {
+      const int rr = e / (D / 4), c4 = e % (D / 4);
+      const int t = rr % LT;
+      const void* src = rr < LT ? A.k : A.q;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < L) x = rr < LT ? load4<IO>(A.k, ((tok + t) * A.h_k + kh) * D + 4 * c4)
+                             : load4<IO>(A.q, ((tok + t) * A.h_k + kh) * D + 4 * c4);
+      (void)src;
+      *reinterpret_cast<float4*>(&S.big[rr * SB + 4 * c4]) = x;
+    }
+    __syncthreads();
+    // dq += (M_incl . A1) K;  dk += (N_incl . A1^T) Q + (M_strict . A2 + N_strict . A2^T) K
+    for (int p = 0; p < LT / 16; ++p) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * p + 4 * lgp + e;
+        const double ls0 = S.lgd[s], ls1 = S.lgd[s + 1];
+        float aq = 0.f, ak1 = 0.f, ak2 = 0.f;
+        if (rv) {
+          if (s <= row) aq = sa1[row * SA + s] * __expf(static_cast<float>(lr1 - ls1));
+          if (s >= row) ak1 = sa1[s * SA + row] * __expf(static_cast<float>(ls1 - lr1));
+          if (s < row) ak2 = sa2[row * SA + s] * __expf(static_cast<float>(lr0 - ls1));
+          if (s > row) ak2 = sa2[s * SA + row] * __expf(static_cast<float>(ls0 - lr1));
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const float kbv = S.big[s * SB + 16 * n + lj];
+          const float qbv = S.big[(LT + s) * SB + 16 * n + lj];
+          acc_dq[n] = mfma4(aq, kbv, acc_dq[n]);
+          acc_dk[n] = mfma4(ak1, qbv, acc_dk[n]);
+          acc_dk[n] = mfma4(ak2, kbv, acc_dk[n]);
+        }
+      }
+    }
+    // per-token terms of this value head
+    {
+      // q_t . dq_t over this head's dq: rows 16 wave + 4 g + r, columns 16 n + j
+      float xr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lgp + r;
+        float x = 0.f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) x = __builtin_fmaf(acc_dq[n][r], S.big[(LT + t) * SB + 16 * n + lj], x);
+        xr[r] = lane_tree<16>(x);
+      }
+      if (lj == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S.xq[16 * wave + 4 * lgp + r] = xr[r];
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) dq_sum[n] += acc_dq[n];
+      // dv = b dc; v . dv; db = dc . w: four threads per token, D/4 columns each
+      const int t = tid >> 2, part = tid & 3;
+      float sv = 0.f, sd = 0.f;
+      if (t < L) {
+        const int64_t base = ((tok + t) * A.h_v + h) * D;
+        const float bt = S.ab[t].y;
+        for (int j4 = part * (D / 16); j4 < (part + 1) * (D / 16); ++j4) {
+          const float4 dc4 = reinterpret_cast<const float4*>(A.dc + base)[j4];
+          const float4 w4 = reinterpret_cast<const float4*>(A.ww + base)[j4];
+          const float4 v4 = load4<IO>(A.v, base + 4 * j4);
+          const float4 dv4 = make_float4(bt * dc4.x, bt * dc4.y, bt * dc4.z, bt * dc4.w);
+          reinterpret_cast<float4*>(A.dv + base)[j4] = dv4;
+          sv = __builtin_fmaf(v4.x, dv4.x, sv);
+          sv = __builtin_fmaf(v4.y, dv4.y, sv);
+          sv = __builtin_fmaf(v4.z, dv4.z, sv);
+          sv = __builtin_fmaf(v4.w, dv4.w, sv);
+          sd = __builtin_fmaf(dc4.x, w4.x, sd);
+          sd = __builtin_fmaf(dc4.y, w4.y, sd);
+          sd = __builtin_fmaf(dc4.z, w4.z, sd);
+          sd = __builtin_fmaf(dc4.w, w4.w, sd);
+        }
+      }
+      sv = dpp_pair_add<0xB1>(sv);
+      sv = dpp_pair_add<0x4E>(sv);
+      sd = dpp_pair_add<0xB1>(sd);
+      sd = dpp_pair_add<0x4E>(sd);
+      if (part == 0 && t < L) {
+        S.xv[t] = sv;
+        A.db[(tok + t) * A.h_v + h] = sd;
+      }
+    }
+    __syncthreads();
+    // h_{t-1} = h_0 - sum_{s<t} (q_s . dq_s - v_s . dv_s); da_t = h_{t-1} / a_t
+    if (tid < LT) {
+      const double x = tid < L ? static_cast<double>(S.xq[tid]) - static_cast<double>(S.xv[tid]) : 0.0;
+      double incl = x;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      double excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = 0.0;
+      if (tid < L) A.da[(tok + tid) * A.h_v + h] = static_cast<float>((h0 - excl) / static_cast<double>(S.ab[tid].x));
+    }
+  }
+  // dq and dk of the key head: rows 16 wave + 4 g + r, columns 16 n + j
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * wave + 4 * lgp + r;
+    if (t < L) {
+      const int64_t base = ((tok + t) * A.h_k + kh) * D;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        A.dq[base + 16 * n + lj] = dq_sum[n][r];
+        A.dk[base + 16 * n + lj] = acc_dk[n][r];
+      }
+    }
   }
 }
 
 template <int DK, int DV, int IO>
 static hipError_t launch_backward_t(const BackwardArgs& A, hipStream_t stream) {
-  using Cfg = BwdCfg<DK, DV>;
+  using Cfg = ColCfg<DK, DV>;
   const int ratio = A.h_v / A.h_k;
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.num_seqs > 0) {
     const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, ratio * Cfg::NCG);
     if (g1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((adjoint_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g1)), dim3(Cfg::THREADS), 0,
-                       stream, A);
+    hipLaunchKernelGGL((adjoint_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g1)), dim3(Cfg::THREADS), 0, stream,
+                       A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0 && A.rows_cap > 0) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, ratio * Cfg::NCG);
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((grad_chunk_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(Cfg::THREADS), 0, stream,
-                       A);
+    hipLaunchKernelGGL((replay_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(Cfg::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
-  if (A.total_tokens > 0) {
-    hipLaunchKernelGGL((grad_reduce_kernel<DK, DV>), dim3(static_cast<unsigned>(A.total_tokens)), dim3(256), 0, stream,
-                       A);
+  if (A.num_seqs > 0 && A.rows_cap > 0) {
+    const int64_t g3 = A.rows_cap * A.h_k;
+    if (g3 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((grad_chunk_kernel<DK, IO>), dim3(static_cast<unsigned>(g3)), dim3(256), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return record_event(A.events, 3, stream);
@@ -384,18 +566,6 @@ hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStr
   CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
 #undef CPR_CASE
   return hipErrorInvalidValue;
-}
-
-int backward_column_groups(int dk, int dv) {
-  if (dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128)) {
-    switch (dk) {
-      case 16: return BwdCfg<16, 16>::NCG;
-      case 32: return BwdCfg<32, 32>::NCG;
-      case 64: return BwdCfg<64, 64>::NCG;
-      default: return BwdCfg<128, 128>::NCG;
-    }
-  }
-  return 0;
 }
 
 }  // namespace cpr

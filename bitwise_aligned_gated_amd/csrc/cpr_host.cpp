@@ -447,12 +447,11 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
     return -1;
   }
   const gdn_policy& P = *policy;
-  const int ncg = cpr::backward_column_groups(P.dk, P.dv);
   const int64_t plane = int64_t(P.dk) * P.dv;
-  const int64_t adj = backward_rows(total_tokens, num_seqs, P.chunk) * P.h_v * plane * 4;
-  const int64_t part = total_tokens * P.h_v * ncg * (2 * int64_t(P.dk) + 2) * 4;
+  const int64_t adj = (backward_rows(total_tokens, num_seqs, P.chunk) + num_seqs) * P.h_v * plane * 4;
+  const int64_t per_token = total_tokens * P.h_v * int64_t(P.dv) * 4;
   ok();
-  return align256(adj) + align256(part);
+  return align256(adj) + 3 * align256(per_token);
 }
 
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -487,18 +486,24 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return fail(GDN_EINVAL, "gdn_backward: workspace must be 16-byte aligned");
   const int64_t plane = int64_t(P.dk) * P.dv;
+  const int64_t adj_bytes = align256((rows + num_seqs) * P.h_v * plane * 4);
+  const int64_t tok_bytes = align256(total_tokens * P.h_v * int64_t(P.dv) * 4);
+  char* ws = static_cast<char*>(workspace);
   cpr::BackwardArgs A;
   A.cu = cu_seqlens;
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b;
   A.d_o = d_o;
   A.d_state = d_state;
   A.chunk_states = chunk_states;
-  A.adjoint = static_cast<float*>(workspace);
-  A.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * P.h_v * plane * 4));
+  A.adjoint = reinterpret_cast<float*>(ws);
+  A.dc = reinterpret_cast<float*>(ws + adj_bytes);
+  A.cc = reinterpret_cast<float*>(ws + adj_bytes + tok_bytes);
+  A.ww = reinterpret_cast<float*>(ws + adj_bytes + 2 * tok_bytes);
   A.dq = dq; A.dk = dk; A.dv = dv; A.da = da; A.db = db;
   A.d_state0 = d_state0;
   A.total_tokens = total_tokens;
   A.rows_cap = rows;
+  A.adj_rows = rows + num_seqs;
   A.num_seqs = num_seqs;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.events = events;

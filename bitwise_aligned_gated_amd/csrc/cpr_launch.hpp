@@ -15,7 +15,5 @@ hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hi
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream);
-// Column groups per value head in the gradient pass (sizes the partial-sum workspace); 0 if unsupported.
-int backward_column_groups(int dk, int dv);
 
 }  // namespace cpr

@@ -185,15 +185,17 @@ def test_prefill_argument_errors_before_launch():
 
 
 def test_backward_workspace_bytes():
-    # adjoint rows (N/C + B) * H_v * dk * dv * 4, then partials N * H_v * groups * (2 dk + 2) * 4,
-    # each padded to 256 bytes; dk = 128 uses 8 column groups of 16, dk = 16 one group
+    # dL/dS at every chunk boundary: (N/C + B) chunk rows plus one more boundary per sequence,
+    # each H_v * dk * dv * 4 bytes; then three per-token arrays (dc, c, w) of N * H_v * dv * 4
+    # bytes; each part padded to 256 bytes
+    pad = lambda x: -(-x // 256) * 256
     p = cpr.Policy(16, 32, 128, 128, chunk=64)
-    adj = (10240 // 64 + 4) * 32 * 128 * 128 * 4
-    part = 10240 * 32 * 8 * 258 * 4
-    assert cpr.gdn_backward_workspace_bytes(p, 10240, 4) == adj + part
+    adj = (10240 // 64 + 4 + 4) * 32 * 128 * 128 * 4
+    tok = 10240 * 32 * 128 * 4
+    assert cpr.gdn_backward_workspace_bytes(p, 10240, 4) == pad(adj) + 3 * pad(tok)
     p = cpr.Policy(1, 2, 16, 16, chunk=8, io="f32")
-    adj, part = (100 // 8 + 3) * 2 * 16 * 16 * 4, 100 * 2 * 1 * 34 * 4
-    assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == -(-adj // 256) * 256 + -(-part // 256) * 256
+    adj, tok = (100 // 8 + 3 + 3) * 2 * 16 * 16 * 4, 100 * 2 * 16 * 4
+    assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == pad(adj) + 3 * pad(tok)
     with pytest.raises(cpr.GdnError):
         cpr.gdn_backward_workspace_bytes(p, -1, 3)
 
