@@ -82,15 +82,20 @@ class Hip:
         return float(out.value)
 
 
+# Sources the profiled forward kernels (prefill passes and decode step) are built from.
+FORWARD_SOURCES = ("cpr_args.hpp", "cpr_common.hpp", "cpr_decode.hip", "cpr_prefill.hip", "cpr_schedule.hpp",
+                   "cpr_step.hpp")
+
+
 def kernel_source_digest() -> str:
-    """SHA-256 over the HIP sources (name + bytes, sorted), to tie stored counters to a build."""
-    import glob
+    """SHA-256 over the forward kernels' sources (name + bytes, sorted), to tie stored counters to
+    the code they were taken on."""
     import hashlib
     csrc = os.path.join(ROOT, "bitwise_aligned_gated_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in sorted(FORWARD_SOURCES):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 

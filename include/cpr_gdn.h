@@ -242,20 +242,24 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
  *   dq_t = S_t dO_t,  dc = Gh^T k_t,  dw = b_t dc,  du = -a_t dw,  dv_t = dw,  db_t = <dc, w_t>,
  *   dk_t = Gh c_t + S_{t-1} du,  da_t = <Gh, S_{t-1}> - <dw, u_t>,  G <- a_t Gh + k_t du^T,
  * and dL/dS_0 is G after the first token; dq and dk of a key head sum its value heads'.
- * It is evaluated the CPR way: an adjoint pass walks each sequence backward and keeps G at every
- * chunk end; a chunk-parallel pass replays each chunk's forward states from the forward's stash
- * and computes the per-token gradients; a final pass adds the per-column-group partial sums.
- * Every sum has a fixed order, so the gradients are bitwise reproducible for any batch
- * composition or packing. */
+ * Three kernels evaluate it: an adjoint pass walks each sequence backward (G needs no forward
+ * state) and keeps dc for every token and G at every chunk boundary; a replay pass re-runs the
+ * pinned forward step of every chunk from the stash and keeps c and w; a chunk-gradient pass,
+ * one workgroup per (chunk, key head), forms dq and dk on fp32 matrix cores from the chunk-form
+ * expansion of S_t and G_t (chunk-start or chunk-end matrix plus decay-weighted rank-one terms),
+ * and da from a_t da_t = <G_{t-1}, S_{t-1}>, carried along the chunk in fp64.  Every sum has a
+ * fixed order, so the gradients are bitwise reproducible for any batch composition or packing. */
 
 /* Workspace bytes gdn_backward needs for total_tokens tokens in num_seqs sequences (-1 on bad
- * input): dL/dS at every chunk end plus per-token partial sums of dq, dk, da and db. */
+ * input): dL/dS at every chunk boundary (total_tokens / C + 2 num_seqs states) and three fp32
+ * per-token arrays of N * H_v * d_v (dc, c, w), each part padded to 256 bytes. */
 int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
 
 /* Gradients of a trainer forward (gdn_prefill or gdn_prefill_fused over the same packed batch,
  * every sequence starting at position 0: from_state 0, or 1 from slots at position 0).
  *   policy        the forward's policy; the fp32 boundary dtype and chunk <= 64 are supported
- *                 (GDN_EUNSUPPORTED otherwise).
+ *                 (GDN_EUNSUPPORTED otherwise).  Every gate a_t must be positive (da_t is
+ *                 obtained by dividing by a_t); the gate form exp(-softplus(x)) always is.
  *   cu_seqlens, total_tokens, q, k, v, a, b   the forward's inputs (device, layouts above).
  *   chunk_states  the forward's stash, chunk_state_rows >= total_tokens / C + num_seqs (any
  *                 forward stash qualifies): row 0 of a sequence is its initial state S_0.
