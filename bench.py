@@ -261,6 +261,33 @@ def main():
              == digest_two_pass}
     del fpool, of
 
+    # the chunkwise evaluation on matrix cores, both output modes ("native" in the pages' table,
+    # and the R2 reading); context only, not bit-identical to CPR
+    chunked = {}
+    cws = torch.empty(cpr.gdn_prefill_chunked_workspace_bytes(P, N, B), dtype=torch.uint8, device=dev)
+    for label, mode in (("native", cpr.GDN_CHUNKED_NATIVE), ("r2", cpr.GDN_CHUNKED_R2)):
+        cpool = cpr.StatePool(P, B, device=dev)
+        oc = torch.empty_like(o)
+        for _ in range(args.warmup):
+            cpr.gdn_prefill_chunked(cpool, cu, x.q, x.k, x.v, x.a, x.b, slot_ids=ids, outputs=mode, o=oc,
+                                    chunk_states=cs, workspace=cws)
+        cevs = [[hip.event() for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            cpr.gdn_prefill_chunked(cpool, cu, x.q, x.k, x.v, x.a, x.b, slot_ids=ids, outputs=mode, o=oc,
+                                    chunk_states=cs, workspace=cws, events=cevs[i])
+        torch.cuda.synchronize()
+        c_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        stage = [statistics.mean(hip.ms(e[j], e[j + 1]) for e in cevs) for j in range(3)]
+        d_o = (oc.float() - o.float()).norm() / o.float().norm()
+        chunked[label] = {"ms_per_step": round(c_ms, 4), "tok_s": round(N / (c_ms * 1e-3), 1),
+                          "stages_ms": {"prep": round(stage[0], 4), "state": round(stage[1], 4),
+                                        "output": round(stage[2], 4)},
+                          "normwise_o_vs_cpr": float(d_o), "cpr_over_this": round(ms_step / c_ms, 3)}
+        del cpool, oc
+    del cws
+
     # ---------------------------------------------------------------- decode workload
     decode = None
     if not args.no_decode:
@@ -405,13 +432,14 @@ def main():
                     "cpr_bytes": int(cpr_bytes), "hbm_frac": round(prefill_gbs / HBM_PEAK_GBS, 4),
                     "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                 for k, v in kernels.items()},
-                    "one_pass_variant": fused},
+                    "one_pass_variant": fused, "chunked_matrix_core": chunked},
         "roofline": roofline,
         "decode": decode,
         "trainer": trainer,
         "cpu_baseline": cpu,
-        "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "decode_256x1_cpr": 0.0846,
-                                          "trainer_fwd_bwd_10240_cpr": 7.386},
+        "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "prefill_5x2048_native": 0.844,
+                                          "decode_256x1_cpr": 0.0846, "decode_256x1_native": 0.0612,
+                                          "trainer_fwd_bwd_10240_cpr": 7.386, "trainer_fwd_bwd_10240_native": 5.177},
                     "note": "pages' H100 figures; head layout not stated there"},
     }
     print(json.dumps(out, default=lambda v: v.item() if hasattr(v, "item") else str(v)), flush=True)

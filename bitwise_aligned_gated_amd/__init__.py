@@ -18,6 +18,7 @@ __all__ = [
     "gdn_semantic_digest", "gdn_deployment_digest",
     "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
     "gdn_prefill_fused", "gdn_decode_step", "gdn_state_resync", "gdn_backward", "gdn_backward_workspace_bytes",
+    "gdn_prefill_chunked", "gdn_prefill_chunked_workspace_bytes", "GDN_CHUNKED_NATIVE", "GDN_CHUNKED_R2",
     "EXPORTS",
 ]
 
@@ -29,6 +30,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP, GDN_EPOLICY = 0, 1, 2, 3, 4
 GDN_F32, GDN_BF16 = 0, 1
+GDN_CHUNKED_NATIVE, GDN_CHUNKED_R2 = 0, 1
 _CODES = {1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED", 3: "GDN_EHIP", 4: "GDN_EPOLICY"}
 
 
@@ -68,6 +70,9 @@ _SIGS = {
     "gdn_decode_step": (ctypes.c_int, [_P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_state_resync": (ctypes.c_int, [_P, _P, _i32, _P]),
     "gdn_backward_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i64, _i32]),
+    "gdn_prefill_chunked_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i64, _i32]),
+    "gdn_prefill_chunked": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _i32,
+                                           _P, _sz, _P, _P]),
     "gdn_backward": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _P, _i32, _i64, _P, _P, _P, _P, _P, _P, _i64, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P, _P]),
 }
@@ -398,3 +403,33 @@ def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d
                              out["da"].data_ptr(), out["db"].data_ptr(), None if d0 is None else d0.data_ptr(),
                              workspace.data_ptr(), workspace.numel(), _stream_ptr(stream), _events(events, 4)))
     return out
+
+
+def gdn_prefill_chunked_workspace_bytes(policy: Policy, total_tokens: int, num_seqs: int) -> int:
+    r = _lib.gdn_prefill_chunked_workspace_bytes(ctypes.byref(policy.c()), total_tokens, num_seqs)
+    if r < 0:
+        _check(GDN_EUNSUPPORTED if policy.dk not in (32, 64, 128) else GDN_EINVAL)
+    return int(r)
+
+
+def gdn_prefill_chunked(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                        outputs: int = GDN_CHUNKED_NATIVE, o=None, chunk_states=None, workspace=None, stream=None,
+                        events=None):
+    """Chunkwise evaluation on matrix cores (C gdn_prefill_chunked): outputs=GDN_CHUNKED_NATIVE
+    or GDN_CHUNKED_R2.  Returns (o, chunk_states)."""
+    P, dev = pool.policy, pool.device
+    N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
+    bound = gdn_chunk_rows_bound(N, B, P.chunk)
+    if chunk_states is None:
+        chunk_states = torch.empty((max(bound, 1), P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)
+    _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    need = gdn_prefill_chunked_workspace_bytes(P, N, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+    _check(_lib.gdn_prefill_chunked(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                    o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0], int(outputs),
+                                    workspace.data_ptr(), workspace.numel(), _stream_ptr(stream),
+                                    _events(events, 4)))
+    return o, chunk_states

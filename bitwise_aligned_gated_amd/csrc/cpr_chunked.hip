@@ -1,0 +1,581 @@
+// cpr_chunked.hip -- the chunkwise (WY/UT) evaluation of the gated delta rule on bf16 matrix
+// cores, used two ways:
+//   native  every output from the chunk form: the pages' "native" column of the per-layer table
+//           in "Solving the linear-attention headache" (IsoExec articles), the evaluation CPR is
+//           compared against;
+//   R2      the chunk form computes only the states at chunk starts (a value-changing boundary
+//           pass); the outputs then come from the pinned per-token step started at those states
+//           (the CPR output pass), the other reading of the CPR passes.
+//
+// Algebra, per chunk of L tokens with gate products Gam_t = a_1 ... a_t and entering state S_0:
+//   the per-token write vectors c_t = b_t (v_t - a_t S_{t-1}^T k_t) satisfy
+//       (I + A) C = diag(b) V - diag(b Gam) K S_0,   A[s][r] = b_s (Gam_s/Gam_r) k_s . k_r (r < s),
+//   so with T = (I + A)^{-1}, W = T diag(b Gam) K and U = T diag(b) V:
+//       C = U - W S_0,   S_L = Gam_L S_0 + K^T diag(Gam_L / Gam) C,
+//       O = diag(Gam) Q S_0 + (M . Q K^T) C,   M[t][s] = Gam_t / Gam_s (s <= t).
+// Kernels: prep (per chunk and value head: T by forward substitution in fp32, then W and U),
+// state (per sequence, value head and column slice, sequential over the chunks: C and the next
+// state), output (per chunk and value head: O).  Products run on v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation; an operand that is not exactly bf16 is split into a bf16 high part and a
+// bf16 low part and the product taken as hi*hi + hi*lo + lo*hi, which keeps fp32-level accuracy.
+// Log gate products are summed in fp64; decay ratios are exp of their fp32 differences.
+#include <hip/hip_runtime.h>
+
+#include "cpr_common.hpp"
+#include "cpr_launch.hpp"
+
+namespace cpr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4c __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32_bf16 on a wave of 64 lanes, lane l = j + 16 g (j < 16, g < 4):
+//   A (16 x 32): lane holds A[j][8 g + e], e < 8;  B (32 x 16): lane holds B[8 g + e][j];
+//   D (16 x 16): lane holds D[4 g + r][j] in register r.
+// Both operands are read from arrays laid out with the contraction index contiguous (A as
+// [row][k], B as [column][k]), so a lane's eight elements are consecutive.
+__device__ __forceinline__ f32x4c mma(const bf16x8& a, const bf16x8& b, f32x4c c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split {
+  bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ Split split8(const float4& x0, const float4& x1) {
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  Split s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
+    s.hi[e] = h;
+    s.lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+  }
+  return s;
+}
+
+// Eight consecutive fp32 values (16-byte aligned) as a split operand.
+__device__ __forceinline__ Split frag_f32(const float* p) {
+  return split8(reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]);
+}
+
+// Eight consecutive bf16 values (16-byte aligned) as an exact operand.
+__device__ __forceinline__ bf16x8 frag_bf16(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ f32x4c mma_split(const Split& a, const Split& b, f32x4c c) {
+  c = mma(a.hi, b.hi, c);
+  c = mma(a.hi, b.lo, c);
+  return mma(a.lo, b.hi, c);
+}
+__device__ __forceinline__ f32x4c mma_split_a(const Split& a, const bf16x8& b, f32x4c c) {
+  c = mma(a.hi, b, c);
+  return mma(a.lo, b, c);
+}
+__device__ __forceinline__ f32x4c mma_split_b(const bf16x8& a, const Split& b, f32x4c c) {
+  c = mma(a, b.hi, c);
+  return mma(a, b.lo, c);
+}
+
+template <int D>
+struct ChunkCfg {
+  static constexpr int L = 64;                   // token rows of a chunk tile (4 waves x 16)
+  static constexpr int NS = 32;                  // state columns per state-pass workgroup
+  static constexpr int SB = D + 8;               // bf16 row stride of [L][D] tiles
+  static constexpr int ST = L + 8;               // bf16 row stride of [D][L] tiles
+  static constexpr int SF = L + 4;               // fp32 row stride of [L][L] / [NS][L] tiles
+  static constexpr int SS = D + 4;               // fp32 row stride of the [NS][D] state slice
+  static constexpr int WS_MAT = L * D;           // floats of one [L][D] workspace matrix
+  static constexpr int WS_LG = 72;               // doubles reserved for the log gate products
+};
+
+// Workspace of one (chunk row, value head): W [L][D], U [L][D], C^T [D][L] (fp32), then the
+// log gate products lgd[0..L] (fp64; lgd[t] = sum of log a over the chunk's first t tokens).
+template <int D>
+__host__ __device__ constexpr int64_t chunk_ws_floats() {
+  return 3 * ChunkCfg<D>::WS_MAT + 2 * ChunkCfg<D>::WS_LG;
+}
+
+// The token range [t0, t1) (within the sequence) of chunk row c of a sequence starting at p0.
+__device__ __forceinline__ void chunk_range(const SeqMeta& m, int64_t c, int C, int* t0, int* t1) {
+  const int64_t first = m.p0 / C;
+  const int64_t b0 = (first + c) * C - m.p0, b1 = (first + c + 1) * C - m.p0;
+  *t0 = static_cast<int>(b0 > 0 ? b0 : 0);
+  *t1 = static_cast<int>(b1 < m.len ? b1 : m.len);
+}
+
+// ---- prep: T, W, U per (chunk row, value head) ------------------------------------------------
+template <int D>
+struct alignas(16) PrepLds {
+  using M = ChunkCfg<D>;
+  __bf16 kt[D * M::ST];         // K^T (zero past the chunk)
+  float am[M::L * M::SF];       // A, then T
+  float tp[M::L * M::SF];       // T, then T diag(b Gam), then T diag(b)
+  union {
+    float ty[M::L * M::SF];     // blocked-inverse scratch
+    __bf16 vt[D * M::ST];       // then V^T
+  };
+  double lgd[M::L + 1];
+  float bb[M::L];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* ws) {
+  using M = ChunkCfg<D>;
+  constexpr int L = M::L, ST = M::ST, SF = M::SF, NT = D / 16;
+  __shared__ PrepLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio);
+  const int64_t w = gs.group / A.h_k;
+  const int kh = static_cast<int>(gs.group % A.h_k);
+  const int h = kh * ratio + gs.member;
+  if (w >= A.rows_cap) return;                                // uniform across the block
+  int i;
+  int64_t c;
+  if (!plan_find_row(A, w, &i, &c, red)) return;              // uniform across the block
+  const SeqMeta m = seq_meta(A, i);
+  int t0, t1;
+  chunk_range(m, c, A.chunk, &t0, &t1);
+  const int n = t1 - t0;                                      // tokens, 1..64
+  const int64_t tok = m.tok0 + t0;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lg = lane >> 4;
+  const __bf16* kin = static_cast<const __bf16*>(A.k);
+  const __bf16* vin = static_cast<const __bf16*>(A.v);
+
+  // K^T (zero past the chunk), gates and their log products
+  for (int e = tid; e < L * D / 8; e += 256) {
+    const int t = e / (D / 8), c8 = e % (D / 8);
+    bf16x8 kv = {};
+    if (t < n) kv = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) S.kt[(8 * c8 + x) * ST + t] = kv[x];
+  }
+  if (tid < L) {
+    float a = 1.f, b = 0.f;
+    if (tid < n) {
+      a = A.a[(tok + tid) * A.h_v + h];
+      b = A.b[(tok + tid) * A.h_v + h];
+    }
+    S.bb[tid] = b;
+    double x = tid < n ? log(static_cast<double>(a)) : 0.0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    S.lgd[tid + 1] = x;
+    if (tid == 0) S.lgd[0] = 0.0;
+  }
+  __syncthreads();
+
+  // A = strictly lower (b_s Gam_s / Gam_r) k_s . k_r, K rows read straight from memory
+  {
+    f32x4c acc[4] = {};
+    const int ra = 16 * wave + lj;
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) {
+      bf16x8 af = {};
+      if (ra < n) af = *reinterpret_cast<const bf16x8*>(kin + ((tok + ra) * A.h_k + kh) * D + 32 * p + 8 * lg);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int rb = 16 * nt + lj;
+        bf16x8 bfr = {};
+        if (rb < n) bfr = *reinterpret_cast<const bf16x8*>(kin + ((tok + rb) * A.h_k + kh) * D + 32 * p + 8 * lg);
+        acc[nt] = mma(af, bfr, acc[nt]);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * wave + 4 * lg + r, rr = 16 * nt + lj;
+        float v = 0.f;
+        if (rr < s && s < n) v = S.bb[s] * __expf(static_cast<float>(S.lgd[s + 1] - S.lgd[rr + 1])) * acc[nt][r];
+        S.am[s * SF + rr] = v;
+      }
+  }
+  __syncthreads();
+  // T = (I + A)^{-1} (unit lower triangular), blocked: the four 16 x 16 diagonal blocks by
+  // forward substitution, then the off-diagonal blocks level by level, X = -T_B A_BA T_A
+  if (tid < L) {
+    const int bk = tid >> 4, j = tid & 15, o0 = 16 * bk;
+    for (int s = 0; s < 16; ++s) {
+      float acc = s == j ? 1.f : 0.f;
+      for (int r = j; r < s; ++r) acc = __builtin_fmaf(-S.am[(o0 + s) * SF + o0 + r], S.tp[(o0 + r) * SF + o0 + j], acc);
+      S.tp[(o0 + s) * SF + o0 + j] = s < j ? 0.f : acc;
+    }
+  }
+  for (int e = tid; e < L * L; e += 256) {                     // zero the off-diagonal blocks
+    const int t = e / L, s = e % L;
+    if ((t >> 4) != (s >> 4)) S.tp[t * SF + s] = 0.f;
+  }
+  __syncthreads();
+  for (int half = 16; half < L; half *= 2) {
+    // pairs of half x half blocks at offsets (q, q + half), q = 0, 2 half, ...
+    const int npairs = L / (2 * half);
+    // Y = A_BA T_A
+    for (int e = tid; e < npairs * half * half; e += 256) {
+      const int pr = e / (half * half), t = (e / half) % half, s = e % half, q = 2 * half * pr;
+      float acc = 0.f;
+      for (int r = s; r < half; ++r) acc = __builtin_fmaf(S.am[(q + half + t) * SF + q + r], S.tp[(q + r) * SF + q + s], acc);
+      S.ty[(q + half + t) * SF + q + s] = acc;
+    }
+    __syncthreads();
+    // X = -T_B Y
+    for (int e = tid; e < npairs * half * half; e += 256) {
+      const int pr = e / (half * half), t = (e / half) % half, s = e % half, q = 2 * half * pr;
+      float acc = 0.f;
+      for (int r = 0; r <= t; ++r) acc = __builtin_fmaf(S.tp[(q + half + t) * SF + q + half + r], S.ty[(q + half + r) * SF + q + s], acc);
+      S.tp[(q + half + t) * SF + q + s] = -acc;
+    }
+    __syncthreads();
+  }
+  // keep T in am; tp = T diag(b Gam); V^T into the scratch's space (zero past the chunk)
+  for (int e = tid; e < L * L; e += 256) {
+    const int t = e / L, s = e % L;
+    const float tv = S.tp[t * SF + s];
+    S.am[t * SF + s] = tv;
+    S.tp[t * SF + s] = tv * (S.bb[s] * __expf(static_cast<float>(S.lgd[s + 1])));
+  }
+  for (int e = tid; e < L * D / 8; e += 256) {
+    const int t = e / (D / 8), c8 = e % (D / 8);
+    bf16x8 vv = {};
+    if (t < n) vv = *reinterpret_cast<const bf16x8*>(vin + ((tok + t) * A.h_v + h) * D + 8 * c8);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) S.vt[(8 * c8 + x) * ST + t] = vv[x];
+  }
+  __syncthreads();
+  float* wsb = ws + (w * A.h_v + h) * chunk_ws_floats<D>();
+  // W = T diag(b Gam) K, then U = T diag(b) V
+  for (int which = 0; which < 2; ++which) {
+    f32x4c acc[NT] = {};
+#pragma unroll
+    for (int p = 0; p < L / 32; ++p) {
+      const Split af = frag_f32(&S.tp[(16 * wave + lj) * SF + 32 * p + 8 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const __bf16* bt = which == 0 ? S.kt : S.vt;
+        acc[nt] = mma_split_a(af, frag_bf16(&bt[(16 * nt + lj) * ST + 32 * p + 8 * lg]), acc[nt]);
+      }
+    }
+    float* dst = wsb + which * M::WS_MAT;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * lg + r) * D + 16 * nt + lj] = acc[nt][r];
+    if (which == 0) {
+      __syncthreads();
+      for (int e = tid; e < L * L; e += 256) {
+        const int t = e / L, s = e % L;
+        S.tp[t * SF + s] = S.am[t * SF + s] * S.bb[s];
+      }
+      __syncthreads();
+    }
+  }
+  double* lgw = reinterpret_cast<double*>(wsb + 3 * M::WS_MAT);
+  for (int e = tid; e <= L; e += 256) lgw[e] = S.lgd[e];
+}
+
+// ---- state: sequential over chunks per (sequence, value head, column slice) ---------------------
+template <int D>
+struct alignas(16) StateLds {
+  using M = ChunkCfg<D>;
+  float st[M::NS * M::SS];      // S^T slice [column][d]
+  float ct[M::NS * M::SF];      // diag(Gam_L / Gam) C, transposed: [column][token]
+  __bf16 kt[D * M::ST];         // K^T of the chunk
+  double lgd[M::L + 1];
+};
+
+// One chunk's inputs of the state pass, loaded ahead into registers.
+template <int D>
+struct StateRegs {
+  using M = ChunkCfg<D>;
+  static constexpr int KU = (M::L * D / 8 + 255) / 256;        // bf16x8 units of K per thread
+  bf16x8 k[KU];
+  float4 w[D / 32][2];                                         // W fragments of this lane's row
+  float u[M::NS / 16][4];                                      // U at this lane's C positions
+  double lg;                                                   // lgd[tid] (threads 0..L)
+};
+
+template <int D>
+__device__ __forceinline__ void state_fetch(const PrefillArgs& A, const float* ws, const SeqMeta& m, int64_t row0,
+                                            int64_t c, int h, int kh, int j0, StateRegs<D>& R) {
+  using M = ChunkCfg<D>;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lg = lane >> 4;
+  int t0, t1;
+  chunk_range(m, c, A.chunk, &t0, &t1);
+  const int n = t1 - t0;
+  const int64_t tok = m.tok0 + t0;
+  const __bf16* kin = static_cast<const __bf16*>(A.k);
+#pragma unroll
+  for (int x = 0; x < StateRegs<D>::KU; ++x) {
+    const int e = tid + 256 * x, t = e / (D / 8), c8 = e % (D / 8);
+    R.k[x] = bf16x8{};
+    if (e < M::L * D / 8 && t < n) R.k[x] = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+  }
+  const float* wsb = ws + ((row0 + c) * A.h_v + h) * chunk_ws_floats<D>();
+#pragma unroll
+  for (int p = 0; p < D / 32; ++p) {
+    const float4* src = reinterpret_cast<const float4*>(wsb + (16 * wave + lj) * D + 32 * p + 8 * lg);
+    R.w[p][0] = src[0];
+    R.w[p][1] = src[1];
+  }
+#pragma unroll
+  for (int nt = 0; nt < M::NS / 16; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) R.u[nt][r] = wsb[M::WS_MAT + (16 * wave + 4 * lg + r) * D + j0 + 16 * nt + lj];
+  R.lg = tid <= M::L ? reinterpret_cast<const double*>(wsb + 3 * M::WS_MAT)[tid] : 0.0;
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* ws, int write_final) {
+  using M = ChunkCfg<D>;
+  constexpr int L = M::L, NS = M::NS, SS = M::SS, SF = M::SF, ST = M::ST;
+  constexpr int NSL = D / NS;                                  // column slices per value head
+  __shared__ StateLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio * NSL);
+  if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
+  const int i = static_cast<int>(gs.group / A.h_k), kh = static_cast<int>(gs.group % A.h_k);
+  const int h = kh * ratio + gs.member / NSL, sl = gs.member % NSL;
+  const SeqMeta m = seq_meta(A, i);
+  const int64_t row0 = plan_row_offset(A, i, red);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lg = lane >> 4;
+  const int64_t plane = static_cast<int64_t>(D) * D;
+  const int j0 = sl * NS;
+  if (m.slot < 0) return;                                      // uniform: nothing to do
+  // chunks whose workspace exists (rows beyond the launch's capacity are never planned)
+  const int64_t nrows = row0 + m.nrows <= A.rows_cap ? m.nrows : (A.rows_cap > row0 ? A.rows_cap - row0 : 0);
+  StateRegs<D> R;
+  if (nrows > 0) state_fetch<D>(A, ws, m, row0, 0, h, kh, j0, R);
+  // the entering state: the slot's (continuation) or zero
+  for (int e = tid; e < NS * D / 4; e += 256) {
+    const int jj = e / (D / 4), c4 = e % (D / 4);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (A.from_state) x = reinterpret_cast<const float4*>(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane +
+                                                          static_cast<int64_t>(j0 + jj) * D)[c4];
+    *reinterpret_cast<float4*>(&S.st[jj * SS + 4 * c4]) = x;
+  }
+  __syncthreads();
+  for (int64_t c = 0; c < nrows; ++c) {
+    const int64_t w = row0 + c;
+    int t0, t1;
+    chunk_range(m, c, A.chunk, &t0, &t1);
+    const int n = t1 - t0;
+    // the state entering this chunk -> its chunk-state row
+    for (int e = tid; e < NS * D / 4; e += 256) {
+      const int jj = e / (D / 4), c4 = e % (D / 4);
+      reinterpret_cast<float4*>(A.chunk_states + (w * A.h_v + h) * plane + static_cast<int64_t>(j0 + jj) * D)[c4] =
+          *reinterpret_cast<const float4*>(&S.st[jj * SS + 4 * c4]);
+    }
+    // commit the fetched K^T and log products
+#pragma unroll
+    for (int x = 0; x < StateRegs<D>::KU; ++x) {
+      const int e = tid + 256 * x, t = e / (D / 8), c8 = e % (D / 8);
+      if (e < L * D / 8) {
+#pragma unroll
+        for (int y = 0; y < 8; ++y) S.kt[(8 * c8 + y) * ST + t] = R.k[x][y];
+      }
+    }
+    if (tid <= L) S.lgd[tid] = R.lg;
+    // P = W S: rows 16 wave.., columns j0 + 16 nt + j
+    f32x4c acc[NS / 16] = {};
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) {
+      const Split af = split8(R.w[p][0], R.w[p][1]);
+#pragma unroll
+      for (int nt = 0; nt < NS / 16; ++nt) acc[nt] = mma_split(af, frag_f32(&S.st[(16 * nt + lj) * SS + 32 * p + 8 * lg]), acc[nt]);
+    }
+    float uc[NS / 16][4];
+#pragma unroll
+    for (int nt = 0; nt < NS / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) uc[nt][r] = R.u[nt][r];
+    __syncthreads();                                           // kt, lgd committed; st reads done
+    if (c + 1 < nrows) state_fetch<D>(A, ws, m, row0, c + 1, h, kh, j0, R);   // next chunk, in flight
+    // C = U - P; C^T to the workspace; diag(Gam_L / Gam) C^T to LDS
+    float* wsb = ws + (w * A.h_v + h) * chunk_ws_floats<D>();
+    const double lgL = S.lgd[n];
+#pragma unroll
+    for (int nt = 0; nt < NS / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lg + r, jj = 16 * nt + lj;
+        const float cv = uc[nt][r] - acc[nt][r];
+        wsb[2 * M::WS_MAT + (j0 + jj) * L + t] = cv;
+        S.ct[jj * SF + t] = t < n ? cv * __expf(static_cast<float>(lgL - S.lgd[t + 1])) : 0.f;
+      }
+    __syncthreads();
+    // S^T <- Gam_L S^T + (diag(Gam_L/Gam) C)^T K
+    const float gL = __expf(static_cast<float>(lgL));
+    constexpr int TILES = (NS / 16) * (D / 16);
+#pragma unroll
+    for (int q = 0; q < TILES / 4; ++q) {
+      const int tile = wave * (TILES / 4) + q;
+      const int jt = tile / (D / 16), dt = tile % (D / 16);
+      f32x4c u = {};
+#pragma unroll
+      for (int p = 0; p < L / 32; ++p)
+        u = mma_split_a(frag_f32(&S.ct[(16 * jt + lj) * SF + 32 * p + 8 * lg]),
+                        frag_bf16(&S.kt[(16 * dt + lj) * ST + 32 * p + 8 * lg]), u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float& sv = S.st[(16 * jt + 4 * lg + r) * SS + 16 * dt + lj];
+        sv = __builtin_fmaf(gL, sv, u[r]);
+      }
+    }
+    __syncthreads();
+  }
+  if (write_final || m.len == 0) {                             // an empty sequence keeps its entering state
+    for (int e = tid; e < NS * D / 4; e += 256) {
+      const int jj = e / (D / 4), c4 = e % (D / 4);
+      reinterpret_cast<float4*>(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane +
+                                static_cast<int64_t>(j0 + jj) * D)[c4] = *reinterpret_cast<const float4*>(&S.st[jj * SS + 4 * c4]);
+    }
+  }
+}
+
+// ---- output: O = diag(Gam) Q S_0 + (M . Q K^T) C per (chunk row, value head) ------------------------
+template <int D>
+struct alignas(16) OutLds {
+  using M = ChunkCfg<D>;
+  float qk[M::L * M::SF];       // M . Q K^T
+  double lgd[M::L + 1];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) chunk_output_kernel(PrefillArgs A, const float* ws) {
+  using M = ChunkCfg<D>;
+  constexpr int L = M::L, SF = M::SF, NT = D / 16;
+  __shared__ OutLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio);
+  const int64_t w = gs.group / A.h_k;
+  const int kh = static_cast<int>(gs.group % A.h_k);
+  const int h = kh * ratio + gs.member;
+  if (w >= A.rows_cap) return;                                // uniform across the block
+  int i;
+  int64_t c;
+  if (!plan_find_row(A, w, &i, &c, red)) return;              // uniform across the block
+  const SeqMeta m = seq_meta(A, i);
+  int t0, t1;
+  chunk_range(m, c, A.chunk, &t0, &t1);
+  const int n = t1 - t0;
+  const int64_t tok = m.tok0 + t0;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lg = lane >> 4;
+  const __bf16* qin = static_cast<const __bf16*>(A.q);
+  const __bf16* kin = static_cast<const __bf16*>(A.k);
+  const float* wsb = ws + (w * A.h_v + h) * chunk_ws_floats<D>();
+  const double* lgw = reinterpret_cast<const double*>(wsb + 3 * M::WS_MAT);
+  for (int e = tid; e <= L; e += 256) S.lgd[e] = lgw[e];
+  const int row = 16 * wave + lj;                              // this lane's A row
+  // Q fragments of this lane's row (exact bf16; zero past the chunk)
+  bf16x8 qf[D / 32];
+#pragma unroll
+  for (int p = 0; p < D / 32; ++p) {
+    qf[p] = bf16x8{};
+    if (row < n) qf[p] = *reinterpret_cast<const bf16x8*>(qin + ((tok + row) * A.h_k + kh) * D + 32 * p + 8 * lg);
+  }
+  __syncthreads();
+  // M . Q K^T -> LDS
+  {
+    f32x4c acc[4] = {};
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int s = 16 * nt + lj;
+        bf16x8 kf = {};
+        if (s < n) kf = *reinterpret_cast<const bf16x8*>(kin + ((tok + s) * A.h_k + kh) * D + 32 * p + 8 * lg);
+        acc[nt] = mma(qf[p], kf, acc[nt]);
+      }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lg + r, s = 16 * nt + lj;
+        float v = 0.f;
+        if (s <= t && t < n) v = __expf(static_cast<float>(S.lgd[t + 1] - S.lgd[s + 1])) * acc[nt][r];
+        S.qk[t * SF + s] = v;
+      }
+  }
+  __syncthreads();
+  // O = diag(Gam) Q S_0 + (M . Q K^T) C
+  const float* s0 = A.chunk_states + (w * A.h_v + h) * static_cast<int64_t>(D) * D;
+  const float* ctw = wsb + 2 * M::WS_MAT;                      // C^T [D][L]
+  unsigned short* o = static_cast<unsigned short*>(A.o);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4c acc = {};
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) acc = mma_split_b(qf[p], frag_f32(s0 + (16 * nt + lj) * D + 32 * p + 8 * lg), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= __expf(static_cast<float>(S.lgd[16 * wave + 4 * lg + r + 1]));
+#pragma unroll
+    for (int p = 0; p < L / 32; ++p)
+      acc = mma_split(frag_f32(&S.qk[row * SF + 32 * p + 8 * lg]), frag_f32(ctw + (16 * nt + lj) * L + 32 * p + 8 * lg), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * lg + r;
+      if (t < n) o[((tok + t) * A.h_v + h) * D + 16 * nt + lj] = f32_to_bf16_rne(acc[r]);
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_chunked_t(const PrefillArgs& A, float* ws, int mode, hipStream_t stream) {
+  using M = ChunkCfg<D>;
+  const int ratio = A.h_v / A.h_k;
+  hipError_t e = record_event(A.events, 0, stream);
+  if (e != hipSuccess) return e;
+  if (A.num_seqs > 0 && A.rows_cap > 0) {
+    const int64_t g = xcd_grid(A.rows_cap * A.h_k, ratio);
+    if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((chunk_prep_kernel<D>), dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, A, ws);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
+  if (A.num_seqs > 0) {
+    const int64_t g = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, ratio * (D / M::NS));
+    if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((chunk_state_kernel<D>), dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, A, ws,
+                       mode == 0 ? 1 : 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
+  if (mode == 0) {
+    if (A.num_seqs > 0 && A.rows_cap > 0) {
+      const int64_t g = xcd_grid(A.rows_cap * A.h_k, ratio);
+      hipLaunchKernelGGL((chunk_output_kernel<D>), dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, A,
+                         static_cast<const float*>(ws));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = launch_prefill_finish(A, stream)) != hipSuccess) return e;
+  } else {
+    // R2: the CPR output pass (pinned per-token step) from the chunk-form states just stored
+    if ((e = launch_output_pass(D, D, IO_BF16, A, stream)) != hipSuccess) return e;
+  }
+  return record_event(A.events, 3, stream);
+}
+
+hipError_t launch_prefill_chunked(int dk, int dv, int io, const PrefillArgs& A, void* ws, int mode, hipStream_t stream) {
+  if (io != IO_BF16 || dk != dv) return hipErrorInvalidValue;
+  float* w = static_cast<float*>(ws);
+  if (dk == 32) return launch_chunked_t<32>(A, w, mode, stream);
+  if (dk == 64) return launch_chunked_t<64>(A, w, mode, stream);
+  if (dk == 128) return launch_chunked_t<128>(A, w, mode, stream);
+  return hipErrorInvalidValue;
+}
+
+int64_t chunked_workspace_floats(int d) {
+  if (d == 32) return chunk_ws_floats<32>();
+  if (d == 64) return chunk_ws_floats<64>();
+  if (d == 128) return chunk_ws_floats<128>();
+  return 0;
+}
+
+}  // namespace cpr

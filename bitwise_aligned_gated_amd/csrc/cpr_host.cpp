@@ -512,4 +512,73 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   return ok();
 }
 
+int64_t gdn_prefill_chunked_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs) {
+  if (gdn_policy_validate(policy) != GDN_OK) return -1;
+  if (total_tokens < 0 || num_seqs < 0) {
+    fail(GDN_EINVAL, "gdn_prefill_chunked_workspace_bytes: negative sizes");
+    return -1;
+  }
+  const int64_t per = cpr::chunked_workspace_floats(policy->dk);
+  if (per == 0 || policy->dk != policy->dv) {
+    fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: head dims %d x %d not built", policy->dk, policy->dv);
+    return -1;
+  }
+  ok();
+  return gdn_chunk_rows_bound(total_tokens, num_seqs, policy->chunk) * policy->h_v * per * 4;
+}
+
+int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                        const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                        int32_t outputs, void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_prefill_chunked: state handle is NULL");
+  const gdn_policy& P = st->policy;
+  if (P.io_dtype != GDN_BF16) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: bf16 io only");
+  if (P.state_dtype != GDN_F32) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: fp32 boundary dtype only");
+  if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: chunk %d > 64", P.chunk);
+  if (outputs != GDN_CHUNKED_NATIVE && outputs != GDN_CHUNKED_R2)
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: outputs must be GDN_CHUNKED_NATIVE or GDN_CHUNKED_R2");
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill_chunked: negative sizes");
+  if (total_tokens >= (int64_t(1) << 31))
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: total_tokens must fit int32 cu_seqlens");
+  if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: cu_seqlens/slot_ids NULL");
+  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "gdn_prefill_chunked: from_state must be 0 or 1");
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr || o == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: token tensor NULL");
+  const int64_t bound = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
+  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "gdn_prefill_chunked: chunk_states is NULL");
+  if (chunk_state_rows < bound)
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: chunk_state_rows %lld < bound %lld", (long long)chunk_state_rows,
+                (long long)bound);
+  if (bound * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: too many chunks for one launch");
+  const int64_t need = gdn_prefill_chunked_workspace_bytes(&P, total_tokens, num_seqs);
+  if (need < 0) return GDN_EUNSUPPORTED;
+  if (int64_t(workspace_bytes) < need || (need > 0 && workspace == nullptr))
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: workspace of %lld bytes < %lld", (long long)workspace_bytes,
+                (long long)need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: workspace must be 16-byte aligned");
+  cpr::PrefillArgs A;
+  A.cu = cu_seqlens;
+  A.slot_ids = slot_ids;
+  A.pos = st->pos;
+  A.pos_out = st->pos;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
+  A.state = st->state;
+  A.chunk_states = chunk_states;
+  A.total_tokens = total_tokens;
+  A.rows_cap = bound;
+  A.num_seqs = num_seqs;
+  A.num_slots = st->num_slots;
+  A.from_state = from_state;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.round_boundary = 0;
+  A.events = events;
+  const hipError_t e = cpr::launch_prefill_chunked(P.dk, P.dv, 1, A, workspace, outputs,
+                                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
+  return ok();
+}
+
 }  // extern "C"

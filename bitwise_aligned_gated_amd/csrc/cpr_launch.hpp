@@ -15,5 +15,15 @@ hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hi
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream);
+// The position update that ends every prefill, and the CPR output pass (with that update) alone,
+// started from chunk states already stored.
+hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream);
+hipError_t launch_output_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+// Chunkwise evaluation on matrix cores: mode 0 native outputs, mode 1 chunk-form boundary states
+// followed by the CPR output pass.  ws holds chunked_workspace_floats(d) floats per chunk row and
+// value head.
+hipError_t launch_prefill_chunked(int dk, int dv, int io, const PrefillArgs& A, void* ws, int mode,
+                                  hipStream_t stream);
+int64_t chunked_workspace_floats(int d);
 
 }  // namespace cpr

@@ -444,6 +444,37 @@ hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hi
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream) {
+  if (A.num_seqs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_finish_kernel, dim3((A.num_seqs + 255) / 256), dim3(256), 0, stream, A);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int IO>
+static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream) {
+  using C2 = PassCfg<DK, DV, kOutput>;
+  if (A.num_seqs > 0 && A.rows_cap > 0) {
+    const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
+    if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(C2::THREADS), 0, stream,
+                       A);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_prefill_finish(A, stream);
+}
+
+hipError_t launch_output_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
+#define CPR_CASE(D, IOV) \
+  if (dk == D && dv == D && io == IOV) return launch_output_pass_t<D, D, IOV>(A, stream);
+  CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
+  CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
+  CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)
+  CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
+#undef CPR_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
 #define CPR_CASE(D, IOV) \
   if (dk == D && dv == D && io == IOV) return launch_prefill_t<D, D, IOV>(A, stream);

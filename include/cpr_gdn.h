@@ -234,6 +234,36 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
  * slot_ids device int32 [n]. */
 int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* stream);
 
+/* ---- chunkwise evaluation on matrix cores --------------------------------------------------
+ * The per-layer table of section "Solving the linear-attention headache" compares CPR with a
+ * "native" evaluation: the chunkwise (WY/UT) form of the gated delta rule on matrix units.  Per
+ * chunk of L tokens with gate products G_t = a_1...a_t and entering state S_0, the write vectors
+ * c_t solve (I + A) C = diag(b) V - diag(b G) K S_0 with A[s][r] = b_s (G_s/G_r) k_s.k_r (r < s);
+ * with T = (I + A)^{-1}, W = T diag(b G) K and U = T diag(b) V:  C = U - W S_0,
+ * S_L = G_L S_0 + K^T diag(G_L/G) C  and  O = diag(G) Q S_0 + (M . Q K^T) C, M[t][s] = G_t/G_s
+ * (s <= t).  The products run on bf16 matrix cores with fp32 accumulation, operands that are not
+ * exact bf16 split into a high and a low bf16 part.  Results agree with the recurrence to the
+ * bf16 output tolerance, not bit for bit with the CPR entry points.
+ *   outputs GDN_CHUNKED_NATIVE  o and the final states from the chunk form;
+ *   outputs GDN_CHUNKED_R2      the chunk form gives only the states at chunk starts; o and the
+ *                               final state come from the pinned per-token step started at those
+ *                               states (the other reading of CPR's first pass: its boundary states
+ *                               differ from the per-token ones, so resynchronisation changes
+ *                               values).
+ * Requirements: bf16 io, fp32 boundary dtype, chunk <= 64, dk = dv in {32, 64, 128}, every gate
+ * a_t > 0 (GDN_EUNSUPPORTED otherwise).  Arguments as gdn_prefill, plus a caller-owned device
+ * workspace (16-byte aligned) of gdn_prefill_chunked_workspace_bytes().  chunk_states receives
+ * the states entering every chunk, in gdn_chunk_rows' layout.
+ * events: NULL, or 4 hipEvent_t recorded before and between the three stages and at the end. */
+#define GDN_CHUNKED_NATIVE 0
+#define GDN_CHUNKED_R2 1
+int64_t gdn_prefill_chunked_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
+int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state,
+                        const void* q, const void* k, const void* v, const float* a, const float* b,
+                        void* o, float* chunk_states, int64_t chunk_state_rows, int32_t outputs,
+                        void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 /* ---- trainer backward ------------------------------------------------------------------------
  * The per-layer table of section "Solving the linear-attention headache" times CPR for the
  * trainer's forward and backward.  The gradients are those of the recurrence above for a loss L,

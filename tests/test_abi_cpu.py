@@ -222,3 +222,35 @@ def test_backward_argument_errors_before_launch():
     # empty work launches nothing and succeeds
     assert lib.gdn_backward(ctypes.byref(f32.c()), None, 0, 0, None, None, None, None, None, None, 0, None, None,
                             None, None, None, None, None, None, None, 0, None, None) == 0
+
+
+def test_chunked_workspace_and_argument_errors():
+    """gdn_prefill_chunked's host checks (no GPU needed; fake addresses are never dereferenced)."""
+    lib = cpr._lib
+    p = cpr.Policy(2, 4, 128, 128, chunk=64, io="bf16")
+    # per (chunk row, value head): W, U and C^T (64 x d fp32 each) and 72 doubles of log products
+    per = (3 * 64 * 128 + 144) * 4
+    assert cpr.gdn_prefill_chunked_workspace_bytes(p, 1000, 3) == cpr.gdn_chunk_rows_bound(1000, 3, 64) * 4 * per
+    assert lib.gdn_prefill_chunked_workspace_bytes(ctypes.byref(cpr.Policy(2, 4, 16, 16, io="bf16").c()), 10, 1) == -1
+    fake = 0x10000
+    msgs = []
+
+    def call(pol, outputs=0, ws_bytes=1 << 40, ws=fake, rows=99):
+        h = ctypes.c_void_p()
+        nbytes = lib.gdn_state_bytes(ctypes.byref(pol.c()), 3)
+        assert lib.gdn_state_alloc(ctypes.byref(pol.c()), 3, fake, fake, nbytes, None, None, ctypes.byref(h)) == 0
+        try:
+            rc = lib.gdn_prefill_chunked(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, rows,
+                                         outputs, ws, ws_bytes, None, None)
+            msgs.append(lib.gdn_last_error())
+            return rc
+        finally:
+            lib.gdn_state_free(h)
+
+    assert call(cpr.Policy(2, 4, 64, 64, io="f32")) == 2                     # bf16 io only
+    assert call(cpr.Policy(2, 4, 64, 64, io="bf16", boundary="bf16")) == 2   # fp32 boundaries only
+    assert call(cpr.Policy(2, 4, 64, 64, chunk=128, io="bf16")) == 2
+    assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), outputs=2) == 1
+    assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), ws_bytes=64) == 1 and b"workspace" in msgs[-1]
+    assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), ws=fake + 8) == 1
+    assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), rows=2) == 1
