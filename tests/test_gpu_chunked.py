@@ -8,9 +8,11 @@ so it agrees to fp32-level rounding before o is rounded to bf16.
 
 R2: the chunk form gives the states at chunk starts, the pinned per-token step gives everything
 in between.  So (1) R2's o for a chunk is bit for bit what the CPR path produces when started
-from R2's state at that chunk start, which is what a decode that resynchronises to the chunk form
-at every chunk start produces; (2) R2's chunk-start states differ from the per-token ones (the
-resynchronisation changes values), while both stay within tolerance of the oracle.
+from R2's state at that chunk start, which is what a decode produces between chunk starts;
+(2) at a chunk start such a decode resynchronises by re-running the chunk form over the chunk it
+just finished, from the previous chunk-start state (the native mode's final state), and lands
+exactly on R2's next chunk-start state; (3) R2's chunk-start states differ from the per-token
+ones (the resynchronisation changes values), while both stay within tolerance of the oracle.
 """
 import numpy as np
 import pytest
@@ -92,7 +94,7 @@ def test_chunked_packing_invariance(mode):
 
 
 def test_r2_outputs_are_the_per_token_step_from_chunk_form_states():
-    """(1) and (2) of the module docstring on one 300-token sequence."""
+    """(1), (2) and (3) of the module docstring on one 300-token sequence."""
     cpr = lib()
     x = gi.make_inputs(85, [300], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
     say("R2 structure")
@@ -111,6 +113,18 @@ def test_r2_outputs_are_the_per_token_step_from_chunk_form_states():
         assert sha(oc) == sha(o[t0:t1]), c
         if t1 == 300:
             assert sha(pc.state[0]) == sha(pool.state[0])
+    # the resynchronisation a decode performs at a chunk start: the chunk form re-run over the
+    # chunk just finished, from the previous chunk-start state, lands exactly on R2's state
+    for c in range(300 // C):
+        part = x.token_slice(c * C, (c + 1) * C)
+        pc = cpr.StatePool(policy_of(x), 1)
+        pc.state[0].copy_(cs[c])
+        pc.pos.fill_(c * C)
+        pd = part.to("cuda")
+        cpr.gdn_prefill_chunked(pc, part.cu_seqlens, pd.q, pd.k, pd.v, pd.a, pd.b, from_state=True,
+                                outputs=cpr.GDN_CHUNKED_NATIVE)
+        torch.cuda.synchronize()
+        assert sha(pc.state[0]) == sha(cs[c + 1]), c
     # the chunk-form states differ from the per-token (CPR) states at every chunk start after 0
     ref_pool = cpr.StatePool(policy_of(x), 1)
     xd = x.to("cuda")
