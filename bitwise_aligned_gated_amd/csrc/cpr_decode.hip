@@ -25,14 +25,14 @@ constexpr int64_t kPosMask = (int64_t(1) << kPosBits) - 1;
 #define CPR_DECODE_MAX_NC 8   // columns per lane: 8 -> one workgroup per (slot, value head) at d = 128
 #endif
 #ifndef CPR_DECODE_NT
-#define CPR_DECODE_NT 0       // 1: streaming (non-temporal) state loads and stores
+#define CPR_DECODE_NT 0       // streaming (non-temporal) state access: bit 0 loads, bit 1 stores
 #endif
 
 __device__ __forceinline__ void state_load(const float* p, float (&x)[8]) {
-  if constexpr (CPR_DECODE_NT) load_f32x8_nt(p, x); else load_f32x8(p, x);
+  if constexpr ((CPR_DECODE_NT & 1) != 0) load_f32x8_nt(p, x); else load_f32x8(p, x);
 }
 __device__ __forceinline__ void state_store(float* p, const float (&x)[8]) {
-  if constexpr (CPR_DECODE_NT) store_f32x8_nt(p, x); else store_f32x8(p, x);
+  if constexpr ((CPR_DECODE_NT & 2) != 0) store_f32x8_nt(p, x); else store_f32x8(p, x);
 }
 
 template <int DK, int DV>

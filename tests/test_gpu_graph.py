@@ -1,0 +1,103 @@
+"""Graph capture ("What it actually costs": the method keeps working under graph capture): the
+library's calls allocate nothing, never synchronise and record no memset, so a decode step and a
+continuation prefill captured in a HIP graph replay to exactly the bytes of eager calls.
+
+Each test replays its graph several times, with eager work and synchronisations between the
+replays, and compares every replay with the eager result bit for bit.  The replays cross chunk
+starts, so the resynchronisation commit runs inside the graph too.
+"""
+import pytest
+import torch
+
+import gdn_inputs as gi
+from tests.gpu_util import lib, policy_of, say, sha
+
+pytestmark = pytest.mark.gpu
+
+
+def _pools(x, n_slots, boundary):
+    cpr = lib()
+    pol = policy_of(x)
+    return cpr.StatePool(pol, n_slots, boundary=boundary), cpr.StatePool(pol, n_slots, boundary=boundary)
+
+
+@pytest.mark.parametrize("boundary", ["f32", "bf16"])
+def test_decode_step_graph_replays_match_eager(boundary):
+    cpr = lib()
+    B, steps = 8, 70
+    prompts = gi.make_inputs(91, [5, 60, 63, 64, 1, 100, 127, 33], h_k=2, h_v=4, dk=128, dv=128, chunk=64,
+                             io="bf16")
+    toks = gi.make_inputs(92, [steps] * B, h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16").to("cuda")
+    say(f"graph: decode, boundary={boundary}")
+    pol = cpr.Policy(2, 4, 128, 128, 64, "bf16", boundary=boundary)
+    eager = cpr.StatePool(pol, B, boundary=True)
+    graphed = cpr.StatePool(pol, B, boundary=True)
+    pd = prompts.to("cuda")
+    for pool in (eager, graphed):
+        cpr.gdn_prefill(pool, prompts.cu_seqlens, pd.q, pd.k, pd.v, pd.a, pd.b)
+    torch.cuda.synchronize()
+    # step t of slot i is token i * steps + t of the packed decode batch
+    idx = lambda t: torch.arange(B, device="cuda") * steps + t
+    sq, sk, sv = toks.q[idx(0)].clone(), toks.k[idx(0)].clone(), toks.v[idx(0)].clone()
+    sa, sb = toks.a[idx(0)].clone(), toks.b[idx(0)].clone()
+    so = torch.empty((B, 4, 128), dtype=torch.bfloat16, device="cuda")
+    ids = torch.arange(B, dtype=torch.int32, device="cuda")
+    # warm up the capture stream on a throwaway pool, then capture one step on the graphed pool
+    scratch = cpr.StatePool(pol, B, boundary=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cpr.gdn_decode_step(scratch, sq, sk, sv, sa, sb, slot_ids=ids, o=so)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cpr.gdn_decode_step(graphed, sq, sk, sv, sa, sb, slot_ids=ids, o=so)
+    torch.cuda.synchronize()
+    for t in range(steps):
+        sq.copy_(toks.q[idx(t)]); sk.copy_(toks.k[idx(t)]); sv.copy_(toks.v[idx(t)])
+        sa.copy_(toks.a[idx(t)]); sb.copy_(toks.b[idx(t)])
+        g.replay()
+        oe = cpr.gdn_decode_step(eager, toks.q[idx(t)], toks.k[idx(t)], toks.v[idx(t)], toks.a[idx(t)],
+                                 toks.b[idx(t)], slot_ids=ids)
+        torch.cuda.synchronize()
+        assert sha(so) == sha(oe), t
+        assert sha(graphed.state) == sha(eager.state) and graphed.pos.tolist() == eager.pos.tolist(), t
+    assert sha(graphed.boundary) == sha(eager.boundary)
+    assert graphed.boundary_pos.tolist() == eager.boundary_pos.tolist()
+
+
+def test_continuation_prefill_graph_replays_match_eager():
+    cpr = lib()
+    n, reps = 3, 4
+    x = gi.make_inputs(93, [40] * n * reps, h_k=2, h_v=4, dk=64, dv=64, chunk=32, io="bf16").to("cuda")
+    say("graph: continuation prefill")
+    eager, graphed = _pools(x, n, boundary=False)
+    ids = torch.arange(n, dtype=torch.int32, device="cuda")
+    cu = torch.tensor([0, 40, 80, 120], dtype=torch.int32, device="cuda")
+    part = lambda r: slice(r * n * 40, (r + 1) * n * 40)
+    sq, sk, sv = x.q[part(0)].clone(), x.k[part(0)].clone(), x.v[part(0)].clone()
+    sa, sb = x.a[part(0)].clone(), x.b[part(0)].clone()
+    so = torch.empty((n * 40, 4, 64), dtype=torch.bfloat16, device="cuda")
+    rows = cpr.gdn_chunk_rows_bound(n * 40, n, 32)
+    cs = torch.empty((rows, 4, 64, 64), device="cuda")
+    scratch = cpr.StatePool(policy_of(x), n)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        cpr.gdn_prefill(scratch, cu, sq, sk, sv, sa, sb, slot_ids=ids, from_state=True, o=so, chunk_states=cs)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cpr.gdn_prefill(graphed, cu, sq, sk, sv, sa, sb, slot_ids=ids, from_state=True, o=so, chunk_states=cs)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        sq.copy_(x.q[part(r)]); sk.copy_(x.k[part(r)]); sv.copy_(x.v[part(r)])
+        sa.copy_(x.a[part(r)]); sb.copy_(x.b[part(r)])
+        g.replay()
+        oe, _ = cpr.gdn_prefill(eager, cu, x.q[part(r)], x.k[part(r)], x.v[part(r)], x.a[part(r)], x.b[part(r)],
+                                slot_ids=ids, from_state=True)
+        torch.cuda.synchronize()
+        assert sha(so) == sha(oe), r
+        assert sha(graphed.state) == sha(eager.state) and graphed.pos.tolist() == eager.pos.tolist() == [40 * (r + 1)] * n
