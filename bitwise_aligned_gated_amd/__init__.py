@@ -19,6 +19,7 @@ __all__ = [
     "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
     "gdn_prefill_fused", "gdn_decode_step", "gdn_state_resync", "gdn_backward", "gdn_backward_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_chunked_workspace_bytes", "GDN_CHUNKED_NATIVE", "GDN_CHUNKED_R2",
+    "gdn_trainer_forward",
     "EXPORTS",
 ]
 
@@ -74,7 +75,9 @@ _SIGS = {
     "gdn_prefill_chunked": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _i32,
                                            _P, _sz, _P, _P]),
     "gdn_backward": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _P, _i32, _i64, _P, _P, _P, _P, _P, _P, _i64, _P,
-                                    _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P, _P]),
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P, _P]),
+    "gdn_trainer_forward": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P,
+                                           _P]),
 }
 EXPORTS = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
@@ -320,6 +323,26 @@ def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_
     return o, chunk_states
 
 
+def gdn_trainer_forward(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                        o=None, chunk_states=None, cw=None, stream=None, events=None):
+    """Trainer forward (C gdn_trainer_forward): gdn_prefill that also keeps every token's c and w
+    for gdn_backward.  Returns (o, chunk_states, cw)."""
+    P, dev = pool.policy, pool.device
+    N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
+    bound = gdn_chunk_rows_bound(N, B, P.chunk)
+    if chunk_states is None:
+        chunk_states = torch.empty((max(bound, 1), P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)
+    _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    if cw is None:
+        cw = torch.empty((2, N, P.h_v, P.dv), dtype=torch.float32, device=dev)
+    _dev(cw, "cw", torch.float32, (2, N, P.h_v, P.dv), dev)
+    _check(_lib.gdn_trainer_forward(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                    o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0], cw.data_ptr(),
+                                    _stream_ptr(stream), _events(events, 3)))
+    return o, chunk_states, cw
+
+
 def gdn_decode_step(pool: StatePool, q, k, v, a, b, slot_ids=None, o=None, stream=None, events=None):
     """One token for each listed slot (C gdn_decode_step).  Returns o [batch, H_v, dv]."""
     P, dev = pool.policy, pool.device
@@ -356,7 +379,7 @@ def gdn_backward_workspace_bytes(policy: Policy, total_tokens: int, num_seqs: in
 
 
 def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state=None,
-                 want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None):
+                 want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None, cw=None):
     """Gradients of a trainer forward (C gdn_backward) from its inputs and chunk-state stash.
 
     Returns a dict of fp32 device tensors dq, dk [N, H_k, d_k], dv [N, H_v, d_v], da, db [N, H_v]
@@ -379,6 +402,8 @@ def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d
     _dev(b, "b", torch.float32, (N, P.h_v), dev, align=4)
     _dev(d_o, "d_o", io, (N, P.h_v, P.dv), dev)
     _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    if cw is not None:
+        _dev(cw, "cw", torch.float32, (2, N, P.h_v, P.dv), dev)
     if d_state is not None:
         _dev(d_state, "d_state", torch.float32, (B, P.h_v, P.dv, P.dk), dev)
     out = dict(out or {})
@@ -397,7 +422,7 @@ def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d
     d0 = out.get("d_state0")
     _check(_lib.gdn_backward(ctypes.byref(P.c()), cu_d.data_ptr(), B, N, q.data_ptr(), k.data_ptr(),
                              v.data_ptr(), a.data_ptr(), b.data_ptr(), chunk_states.data_ptr(),
-                             chunk_states.shape[0], d_o.data_ptr(),
+                             chunk_states.shape[0], None if cw is None else cw.data_ptr(), d_o.data_ptr(),
                              None if d_state is None else d_state.data_ptr(),
                              out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(),
                              out["da"].data_ptr(), out["db"].data_ptr(), None if d0 is None else d0.data_ptr(),

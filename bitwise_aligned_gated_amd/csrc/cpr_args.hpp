@@ -27,6 +27,7 @@ struct PrefillArgs {
   int32_t h_v;
   int32_t chunk;
   int32_t round_boundary;     // 1: bf16 boundary dtype (round the state at chunk starts)
+  float* cw;                  // nullable: [2][N][H_v][dv] fp32, every token's c then w (trainer forward)
   void* const* events;        // nullable: hipEvent_t recorded around the kernels
 };
 
@@ -79,6 +80,7 @@ struct BackwardArgs {
   int32_t h_k;
   int32_t h_v;
   int32_t chunk;
+  int32_t have_cw;            // 1: cc and ww came from the trainer forward (no replay needed)
   void* const* events;        // nullable: 4 hipEvent_t around the three kernels
 };
 

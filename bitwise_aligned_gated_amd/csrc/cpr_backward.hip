@@ -14,7 +14,8 @@
 //     dL/dS_0.
 // replay (column-parallel, one chunk per workgroup)
 //     the forward step of the shared pinned schedule from the stashed chunk-start state, writing
-//     c_t and w_t for every token: the same bits the forward computed.
+//     c_t and w_t for every token: the same bits the forward computed.  Skipped when the trainer
+//     forward kept them.
 // chunk gradients (matrix cores, one workgroup per (chunk, key head))
 //     Inside a chunk with gate products Gam_t = a_1 ... a_t, every state and adjoint is the
 //     chunk-start (or chunk-end) matrix plus rank-one terms, so with dU_t = -a_t b_t dc_t
@@ -541,7 +542,7 @@ static hipError_t launch_backward_t(const BackwardArgs& A, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
-  if (A.num_seqs > 0 && A.rows_cap > 0) {
+  if (A.num_seqs > 0 && A.rows_cap > 0 && !A.have_cw) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, ratio * Cfg::NCG);
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((replay_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(Cfg::THREADS), 0, stream, A);

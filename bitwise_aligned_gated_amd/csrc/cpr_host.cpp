@@ -308,25 +308,25 @@ int gdn_chunk_rows(const int32_t* cu, const int64_t* pos0, int32_t num_seqs, int
   return ok();
 }
 
-int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
-                const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
-                void* stream, void* const* events) {
-  if (st == nullptr) return fail(GDN_EINVAL, "gdn_prefill: state handle is NULL");
-  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill: negative sizes");
-  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "gdn_prefill: total_tokens must fit int32 cu_seqlens");
+static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                        const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                        float* cw, void* stream, void* const* events, const char* who) {
+  if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", who);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", who);
+  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", who);
   if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill: cu_seqlens/slot_ids NULL");
-  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "gdn_prefill: from_state must be 0 or 1");
+    return fail(GDN_EINVAL, "%s: cu_seqlens/slot_ids NULL", who);
+  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "%s: from_state must be 0 or 1", who);
   if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr || o == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill: token tensor NULL");
+    return fail(GDN_EINVAL, "%s: token tensor NULL", who);
   const gdn_policy& P = st->policy;
   const int64_t bound = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
-  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "gdn_prefill: chunk_states is NULL");
+  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "%s: chunk_states is NULL", who);
   if (chunk_state_rows < bound)
-    return fail(GDN_EINVAL, "gdn_prefill: chunk_state_rows %lld < bound %lld", (long long)chunk_state_rows,
+    return fail(GDN_EINVAL, "%s: chunk_state_rows %lld < bound %lld", who, (long long)chunk_state_rows,
                 (long long)bound);
-  if (bound > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_prefill: too many chunks for one launch");
+  if (bound > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "%s: too many chunks for one launch", who);
   cpr::PrefillArgs A;
   A.cu = cu_seqlens;
   A.slot_ids = slot_ids;
@@ -342,10 +342,28 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = P.state_dtype == GDN_BF16;
+  A.cw = cw;
   A.events = events;
   const hipError_t e = cpr::launch_prefill(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "gdn_prefill launch");
+  if (e != hipSuccess) return hip_fail(e, who);
   return ok();
+}
+
+int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                void* stream, void* const* events) {
+  return prefill_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, chunk_states,
+                      chunk_state_rows, nullptr, stream, events, "gdn_prefill");
+}
+
+int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                        const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                        float* cw, void* stream, void* const* events) {
+  if (total_tokens > 0 && cw == nullptr) return fail(GDN_EINVAL, "gdn_trainer_forward: cw is NULL");
+  return prefill_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, chunk_states,
+                      chunk_state_rows, cw, stream, events, "gdn_trainer_forward");
 }
 
 int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -381,6 +399,7 @@ int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = P.state_dtype == GDN_BF16;
+  A.cw = nullptr;
   A.events = events;
   const hipError_t e = cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_prefill_fused launch");
@@ -456,7 +475,8 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
 
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                  const void* q, const void* k, const void* v, const float* a, const float* b,
-                 const float* chunk_states, int64_t chunk_state_rows, const void* d_o, const float* d_state,
+                 const float* chunk_states, int64_t chunk_state_rows, const float* cw, const void* d_o,
+                 const float* d_state,
                  float* dq, float* dk, float* dv, float* da, float* db, float* d_state0, void* workspace,
                  size_t workspace_bytes, void* stream, void* const* events) {
   if (int rc = gdn_policy_validate(policy); rc != GDN_OK) return rc;
@@ -499,6 +519,11 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   A.dc = reinterpret_cast<float*>(ws + adj_bytes);
   A.cc = reinterpret_cast<float*>(ws + adj_bytes + tok_bytes);
   A.ww = reinterpret_cast<float*>(ws + adj_bytes + 2 * tok_bytes);
+  A.have_cw = cw != nullptr;
+  if (cw != nullptr) {                       // the trainer forward's c and w: no replay needed
+    A.cc = const_cast<float*>(cw);
+    A.ww = const_cast<float*>(cw) + total_tokens * P.h_v * int64_t(P.dv);
+  }
   A.dq = dq; A.dk = dk; A.dv = dv; A.da = da; A.db = db;
   A.d_state0 = d_state0;
   A.total_tokens = total_tokens;
@@ -574,6 +599,7 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = 0;
+  A.cw = nullptr;
   A.events = events;
   const hipError_t e = cpr::launch_prefill_chunked(P.dk, P.dv, 1, A, workspace, outputs,
                                                    static_cast<hipStream_t>(stream));

@@ -199,9 +199,14 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
       float vv[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) vv[c] = L.v[tt][cp * NC + c];
-      float o[NC];
+      float o[NC], wv[NC], cv[NC];
+      if constexpr (MODE == kOutput) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) o[c] = cpr_step<NL, G, OUT>(s[c], kr, qr, vv[c], ab.x, ab.y);
+        for (int c = 0; c < NC; ++c) o[c] = cpr_step_wc<NL, G>(s[c], kr, qr, vv[c], ab.x, ab.y, wv[c], cv[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) o[c] = cpr_step<NL, G, OUT>(s[c], kr, qr, vv[c], ab.x, ab.y);
+      }
       if constexpr (MODE == kOutput) {
         if (g == 0) {
           const int64_t oe = (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + cp * NC;
@@ -210,6 +215,14 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
           } else {
 #pragma unroll
             for (int c = 0; c < NC; ++c) store1<IO>(A.o, oe + c, o[c]);
+          }
+          if (A.cw != nullptr) {                           // the trainer forward keeps c and w
+            const int64_t wofs = A.total_tokens * A.h_v * DV;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              A.cw[oe + c] = cv[c];
+              A.cw[wofs + oe + c] = wv[c];
+            }
           }
         }
       } else if constexpr (MODE == kFused) {

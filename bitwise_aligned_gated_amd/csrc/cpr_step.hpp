@@ -94,6 +94,17 @@ __device__ __forceinline__ float cpr_step(float (&s)[NL * kLeaf], const float (&
   return 0.0f;
 }
 
+// The same step with output that also returns w and c (the values a trainer forward keeps for
+// the backward).
+template <int NL, int G>
+__device__ __forceinline__ float cpr_step_wc(float (&s)[NL * kLeaf], const float (&k)[NL * kLeaf],
+                                             const float (&q)[NL * kLeaf], float v, float a, float b, float& w,
+                                             float& c) {
+  float u;
+  cpr_update<NL, G>(s, k, v, a, b, u, w, c);
+  return pinned_dot<NL, G>(s, q);
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite values), the one conversion every kernel uses.
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
   unsigned int u = __builtin_bit_cast(unsigned int, f);

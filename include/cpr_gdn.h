@@ -197,6 +197,17 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
                 void* o, float* chunk_states, int64_t chunk_state_rows, void* stream,
                 void* const* events);
 
+/* The trainer forward ([A]'s "trainer_fwd" case): gdn_prefill, bit for bit in o, final states
+ * and chunk states, that also keeps what the backward would otherwise recompute:
+ *   cw  device fp32 [2][N][H_v][d_v]: every token's c_t = b_t w_t (block 0) and
+ *       w_t = v_t - a_t S_{t-1}^T k_t (block 1), as the pinned step computed them.
+ * Pass it to gdn_backward.  events as gdn_prefill. */
+int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state,
+                        const void* q, const void* k, const void* v, const float* a, const float* b,
+                        void* o, float* chunk_states, int64_t chunk_state_rows, float* cw, void* stream,
+                        void* const* events);
+
 /* One-pass prefill: the same recurrence and the same outputs, final states and chunk-start rows
  * as gdn_prefill, bit for bit, evaluated by a single kernel that runs every token of a sequence
  * in order (the per-layer table of section "Solving the linear-attention headache" calls this
@@ -285,14 +296,17 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
  * per-token arrays of N * H_v * d_v (dc, c, w), each part padded to 256 bytes. */
 int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
 
-/* Gradients of a trainer forward (gdn_prefill or gdn_prefill_fused over the same packed batch,
- * every sequence starting at position 0: from_state 0, or 1 from slots at position 0).
+/* Gradients of a trainer forward (gdn_trainer_forward, gdn_prefill or gdn_prefill_fused over the
+ * same packed batch, every sequence starting at position 0: from_state 0, or 1 from slots at
+ * position 0).
  *   policy        the forward's policy; the fp32 boundary dtype and chunk <= 64 are supported
  *                 (GDN_EUNSUPPORTED otherwise).  Every gate a_t must be positive (da_t is
  *                 obtained by dividing by a_t); the gate form exp(-softplus(x)) always is.
  *   cu_seqlens, total_tokens, q, k, v, a, b   the forward's inputs (device, layouts above).
  *   chunk_states  the forward's stash, chunk_state_rows >= total_tokens / C + num_seqs (any
  *                 forward stash qualifies): row 0 of a sequence is its initial state S_0.
+ *   cw            NULL, or gdn_trainer_forward's c and w: then the replay of the forward is
+ *                 skipped (the gradients are the same bits either way).
  *   d_o           device, io dtype, [N][H_v][d_v]: dL/do.
  *   d_state       device fp32 [num_seqs][H_v][d_v][d_k] (state layout) or NULL (zero): dL/dS_T.
  *   dq, dk        device fp32 [N][H_k][d_k];  dv  fp32 [N][H_v][d_v];  da, db  fp32 [N][H_v].
@@ -303,7 +317,8 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
  * `stream`; events: NULL, or 4 hipEvent_t recorded before, between and after them. */
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                  const void* q, const void* k, const void* v, const float* a, const float* b,
-                 const float* chunk_states, int64_t chunk_state_rows, const void* d_o, const float* d_state,
+                 const float* chunk_states, int64_t chunk_state_rows, const float* cw, const void* d_o,
+                 const float* d_state,
                  float* dq, float* dk, float* dv, float* da, float* db, float* d_state0,
                  void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 

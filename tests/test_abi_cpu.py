@@ -207,7 +207,7 @@ def test_backward_argument_errors_before_launch():
 
     def call(pol, rows=99, ws_bytes=1 << 40, num_seqs=2, total=100, ws=fake, d_o=fake):
         return lib.gdn_backward(ctypes.byref(pol.c()), fake, num_seqs, total, fake, fake, fake, fake, fake, fake,
-                                rows, d_o, None, fake, fake, fake, fake, fake, None, ws, ws_bytes, None, None)
+                                rows, None, d_o, None, fake, fake, fake, fake, fake, None, ws, ws_bytes, None, None)
 
     f32 = cpr.Policy(2, 4, 16, 16, chunk=64, io="f32")
     assert call(cpr.Policy(2, 4, 16, 16, chunk=64, io="f32", boundary="bf16")) == 2
@@ -221,7 +221,7 @@ def test_backward_argument_errors_before_launch():
     assert call(f32, num_seqs=-1) == 1
     # empty work launches nothing and succeeds
     assert lib.gdn_backward(ctypes.byref(f32.c()), None, 0, 0, None, None, None, None, None, None, 0, None, None,
-                            None, None, None, None, None, None, None, 0, None, None) == 0
+                            None, None, None, None, None, None, None, None, 0, None, None) == 0
 
 
 def test_chunked_workspace_and_argument_errors():

@@ -189,3 +189,30 @@ def test_backward_trainer_10240_varlen():
     for n in GRADS:
         assert sha(gi_[n]) == sha(g[n][t0:t1]), n
     assert cpr.gdn_backward_workspace_bytes(policy_of(x), x.total_tokens, x.num_seqs) > 0
+
+
+@pytest.mark.parametrize("dim,io", [(16, "f32"), (128, "bf16")])
+def test_trainer_forward_stash_gives_the_same_gradients(dim, io):
+    """gdn_trainer_forward equals gdn_prefill bit for bit (o, final states, chunk states), and the
+    c and w it keeps are the bits the backward's replay recomputes: the gradients with and
+    without the kept values are identical."""
+    cpr = lib()
+    x = gi.make_inputs(70, [1, 64, 65, 200, 0, 33], h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io=io)
+    ct = gi.make_cotangents(x, 71)
+    say(f"trainer forward stash dim={dim} io={io}")
+    xd = x.to("cuda")
+    p1 = cpr.StatePool(policy_of(x), x.num_seqs)
+    p2 = cpr.StatePool(policy_of(x), x.num_seqs)
+    o1, cs1 = cpr.gdn_prefill(p1, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    o2, cs2, cw = cpr.gdn_trainer_forward(p2, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    torch.cuda.synchronize()
+    n = int(cpr.gdn_chunk_rows(x.cu_seqlens, x.chunk)[-1])
+    assert sha(o1) == sha(o2) and sha(p1.state) == sha(p2.state) and sha(cs1[:n]) == sha(cs2[:n])
+    d_state = ct["d_state"].to("cuda")
+    g1 = cpr.gdn_backward(policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs1, ct["d_o"].to("cuda"),
+                          d_state=d_state, want_d_state0=True)
+    g2 = cpr.gdn_backward(policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs2, ct["d_o"].to("cuda"),
+                          d_state=d_state, want_d_state0=True, cw=cw)
+    torch.cuda.synchronize()
+    for name in GRADS + ("d_state0",):
+        assert sha(g1[name]) == sha(g2[name]), name
