@@ -27,7 +27,7 @@
 //     remaining gradients are per token: dv_t = b_t dc_t, db_t = dc_t . w_t, and
 //     a_t da_t = <G_{t-1}, S_{t-1}> =: h_{t-1}, where h_0 = <G at the chunk start, S_0> and
 //     h_t = h_{t-1} - q_t . dq_t + v_t . (b_t dc_t) (the per-value-head dq), accumulated in fp64.
-//     dq and dk of a key head add its value heads in head order inside the workgroup.
+//     dq and dk of a key head add its value heads' totals in head order inside the workgroup.
 // Every sum has a fixed order, so the gradients are bitwise reproducible for any batch
 // composition or packing.
 #include <hip/hip_runtime.h>
@@ -107,6 +107,84 @@ __device__ __forceinline__ void store_cols(const BackwardArgs& A,
   }
 }
 
+// One tile's inputs of the adjoint, loaded ahead into registers (raw io units).
+template <int DK, int DV, int IO>
+struct AdjRegs {
+  using Cfg = ColCfg<DK, DV>;
+  static constexpr int KU = (Cfg::TT * DK / 8 + Cfg::THREADS - 1) / Cfg::THREADS;
+  static constexpr int VU = (Cfg::TT * Cfg::WG_COLS / 8 + Cfg::THREADS - 1) / Cfg::THREADS;
+  static constexpr int AU = (2 * Cfg::TT + Cfg::THREADS - 1) / Cfg::THREADS;
+  Raw8<IO> k[KU], q[KU], v[VU], d[VU];
+  float ab[AU];
+};
+
+// Fetch tokens [t0, t0 + n) (packed indices, n <= TT); units past n are zero.
+template <int DK, int DV, int IO>
+__device__ __forceinline__ void adj_fetch(const BackwardArgs& A, AdjRegs<DK, DV, IO>& R, int64_t t0, int n, int kh,
+                                          int h, int col0) {
+  using Cfg = ColCfg<DK, DV>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int x = 0; x < AdjRegs<DK, DV, IO>::KU; ++x) {
+    const int u = tid + x * Cfg::THREADS, tt = u / (DK / 8), c8 = u % (DK / 8);
+    const bool ok = u < Cfg::TT * DK / 8 && tt < n;
+    const int64_t e = ((t0 + tt) * A.h_k + kh) * DK + c8 * 8;
+    R.k[x] = ok ? load_raw8<IO>(A.k, e) : zero_raw8<IO>();
+    R.q[x] = ok ? load_raw8<IO>(A.q, e) : zero_raw8<IO>();
+  }
+#pragma unroll
+  for (int x = 0; x < AdjRegs<DK, DV, IO>::VU; ++x) {
+    const int u = tid + x * Cfg::THREADS, tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
+    const bool ok = u < Cfg::TT * Cfg::WG_COLS / 8 && tt < n;
+    const int64_t e = ((t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
+    R.v[x] = ok ? load_raw8<IO>(A.v, e) : zero_raw8<IO>();
+    R.d[x] = ok ? load_raw8<IO>(A.d_o, e) : zero_raw8<IO>();
+  }
+#pragma unroll
+  for (int x = 0; x < AdjRegs<DK, DV, IO>::AU; ++x) {
+    const int u = tid + x * Cfg::THREADS, tt = u % Cfg::TT;
+    const bool ok = u < 2 * Cfg::TT && tt < n;
+    const float* src = u < Cfg::TT ? A.a : A.b;
+    R.ab[x] = ok ? src[(t0 + tt) * A.h_v + h] : 0.0f;
+  }
+}
+
+template <int DK, int DV, int IO>
+__device__ __forceinline__ void adj_commit(const AdjRegs<DK, DV, IO>& R, ColLds<DK, DV>& L) {
+  using Cfg = ColCfg<DK, DV>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int x = 0; x < AdjRegs<DK, DV, IO>::KU; ++x) {
+    const int u = tid + x * Cfg::THREADS, tt = u / (DK / 8), c8 = u % (DK / 8);
+    if (u < Cfg::TT * DK / 8) {
+      float y[8];
+      widen8<IO>(R.k[x], y);
+      store_f32x8(&L.k[tt][c8 * 8], y);
+      widen8<IO>(R.q[x], y);
+      store_f32x8(&L.q[tt][c8 * 8], y);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < AdjRegs<DK, DV, IO>::VU; ++x) {
+    const int u = tid + x * Cfg::THREADS, tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
+    if (u < Cfg::TT * Cfg::WG_COLS / 8) {
+      float y[8];
+      widen8<IO>(R.v[x], y);
+      store_f32x8(&L.v[tt][c8 * 8], y);
+      widen8<IO>(R.d[x], y);
+      store_f32x8(&L.d[tt][c8 * 8], y);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < AdjRegs<DK, DV, IO>::AU; ++x) {
+    const int u = tid + x * Cfg::THREADS;
+    if (u < Cfg::TT)
+      L.ab[u].x = R.ab[x];
+    else if (u < 2 * Cfg::TT)
+      L.ab[u - Cfg::TT].y = R.ab[x];
+  }
+}
+
 // adjoint: one workgroup per (sequence, value head, column group), grouped per key head.
 template <int DK, int DV, int IO>
 __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(BackwardArgs A) {
@@ -135,12 +213,23 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
   const int C = A.chunk;
   // the boundary at the last token (position len) holds dL/dS_T
   if (brow0 + m.nrows < A.adj_rows) store_f32x8(A.adjoint + ((brow0 + m.nrows) * A.h_v + h) * plane + off, Gs);
+  // tiles of TT tokens from the last one back: the tile ending at t1 starts at max(t1 - TT, 0);
+  // the next tile's inputs are fetched into registers while this one runs
+  AdjRegs<DK, DV, IO> Rg;
+  if (m.len > 0) {
+    const int t0 = m.len - Cfg::TT > 0 ? m.len - Cfg::TT : 0;
+    adj_fetch<DK, DV, IO>(A, Rg, m.tok0 + t0, m.len - t0, kh, h, col0);
+    adj_commit<DK, DV, IO>(Rg, L);
+  }
+  __syncthreads();
   for (int t1 = m.len; t1 > 0; t1 -= Cfg::TT) {
     const int t0 = t1 - Cfg::TT > 0 ? t1 - Cfg::TT : 0;
     const int n = t1 - t0;
-    __syncthreads();
-    stage<DK, DV, IO, true>(A, L, m.tok0 + t0, n, kh, h, col0);
-    __syncthreads();
+    const bool more = t0 > 0;
+    if (more) {
+      const int p0 = t0 - Cfg::TT > 0 ? t0 - Cfg::TT : 0;
+      adj_fetch<DK, DV, IO>(A, Rg, m.tok0 + p0, t0 - p0, kh, h, col0);
+    }
     for (int tt = n - 1; tt >= 0; --tt) {
       float kr[R], qr[R], gh[R];
       load_f32x8(&L.k[tt][g * R], kr);
@@ -162,6 +251,8 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
     }
     __syncthreads();
     store_cols<DK, DV>(A, L.out0, A.dc, m.tok0 + t0, n, h, col0);
+    if (more) adj_commit<DK, DV, IO>(Rg, L);
+    __syncthreads();
   }
   if (A.d_state0 != nullptr) store_f32x8(A.d_state0 + (static_cast<int64_t>(i) * A.h_v + h) * plane + off, Gs);
 }
@@ -227,19 +318,29 @@ template <int D>
 struct MCfg {
   static constexpr int L = 64;                  // token rows of a chunk tile: 4 waves x 16
   static constexpr int SB = D + 4;              // row stride of D-wide matrices in LDS
-  static constexpr int SC = L + 4;              // row stride of C^T (D rows of L tokens)
+  static constexpr int SC = L + 4;              // row stride of C^T (rows of L tokens)
   static constexpr int SA = L + 4;              // row stride of the L x L products
   static constexpr int NT = D / 16;             // 16-wide tiles across D
-  static constexpr int KP = D / 16;             // 16-deep k panels across D
-  static constexpr int BIG_ROWS = D > 2 * L ? D : 2 * L;
-  static constexpr int SMALL = (D * SC > 2 * L * SA) ? D * SC : 2 * L * SA;
+  static constexpr int HR = D < 64 ? D : 64;    // rows of a D x D matrix (and of C^T) staged at once
+  static constexpr int NH = D / HR;             // staged parts per matrix
 };
 
+// LDS of the chunk-gradient kernel: the products with S0 and G_end stream those matrices (and
+// C^T) in parts of HR rows; the decay-masked products then hold A1, A2 and K (later Q).
 template <int D>
 struct alignas(16) MLds {
   using M = MCfg<D>;
-  float big[M::BIG_ROWS * M::SB];   // S0, then G_end, then K (rows 0..L-1) and Q (rows L..2L-1)
-  float small[M::SMALL];            // C^T [D][SC], then A1 = dO C^T and A2 = dU C^T [L][SA] each
+  union {
+    struct {
+      float mat[M::HR * M::SB];     // rows [j0, j0 + HR) of S0 or G_end ([dv][dk] layout)
+      float ct[M::HR * M::SC];      // rows [j0, j0 + HR) of C^T
+    } p;
+    struct {
+      float a1[M::L * M::SA];       // dO C^T
+      float a2[M::L * M::SA];       // dU C^T
+      float kq[M::L * M::SB];       // K, then Q (zero past the chunk)
+    } m;
+  } u;
   double lgd[M::L + 1];             // sum of log a over the chunk's tokens before token t
   float2 ab[M::L];
   float xq[M::L];                   // q_t . dq_t of the current value head
@@ -272,10 +373,44 @@ __device__ __forceinline__ double block_sum_f64(double x, double* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-template <int D, int IO>
-__global__ void __launch_bounds__(256) grad_chunk_kernel(BackwardArgs A) {
+// Stage rows [j0, j0 + HR) of a D x D fp32 matrix in [dv][dk] layout into S.u.p.mat, and the same
+// rows of C^T (C [t][j] of this chunk, zero past its n tokens) into S.u.p.ct.
+template <int D>
+__device__ __forceinline__ void stage_part(MLds<D>& S, const float* mat, const float* cc, int64_t tok, int n,
+                                           int h_v, int h, int j0) {
   using M = MCfg<D>;
-  constexpr int NT = M::NT, KP = M::KP, SB = M::SB, SC = M::SC, SA = M::SA, LT = M::L;
+  for (int e = threadIdx.x; e < M::HR * D / 4; e += 256) {
+    const int r = e / (D / 4), c4 = e % (D / 4);
+    *reinterpret_cast<float4*>(&S.u.p.mat[r * M::SB + 4 * c4]) =
+        reinterpret_cast<const float4*>(mat + static_cast<int64_t>(j0 + r) * D)[c4];
+  }
+  for (int e = threadIdx.x; e < M::L * M::HR / 4; e += 256) {
+    const int t = e / (M::HR / 4), c4 = e % (M::HR / 4);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < n) x = *reinterpret_cast<const float4*>(cc + ((tok + t) * h_v + h) * D + j0 + 4 * c4);
+    S.u.p.ct[(4 * c4 + 0) * M::SC + t] = x.x;
+    S.u.p.ct[(4 * c4 + 1) * M::SC + t] = x.y;
+    S.u.p.ct[(4 * c4 + 2) * M::SC + t] = x.z;
+    S.u.p.ct[(4 * c4 + 3) * M::SC + t] = x.w;
+  }
+}
+
+// K or Q rows of the chunk (io dtype, zero past its n tokens) into S.u.m.kq.
+template <int D, int IO>
+__device__ __forceinline__ void stage_kq(MLds<D>& S, const void* src, int64_t tok, int n, int h_k, int kh) {
+  using M = MCfg<D>;
+  for (int e = threadIdx.x; e < M::L * D / 4; e += 256) {
+    const int t = e / (D / 4), c4 = e % (D / 4);
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < n) x = load4<IO>(src, ((tok + t) * h_k + kh) * D + 4 * c4);
+    *reinterpret_cast<float4*>(&S.u.m.kq[t * M::SB + 4 * c4]) = x;
+  }
+}
+
+template <int D, int IO>
+__global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
+  using M = MCfg<D>;
+  constexpr int NT = M::NT, SB = M::SB, SC = M::SC, SA = M::SA, LT = M::L, HR = M::HR, NH = M::NH;
   __shared__ MLds<D> S;
   __shared__ int64_t red[6];
   const int64_t w = blockIdx.x / A.h_k;
@@ -295,28 +430,9 @@ __global__ void __launch_bounds__(256) grad_chunk_kernel(BackwardArgs A) {
   const int64_t plane = static_cast<int64_t>(D) * D;
   const int64_t gstart = w + i;                              // boundary rows around this chunk
 
-  f32x4 dq_sum[NT], acc_dk[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) dq_sum[n] = acc_dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   for (int hh = 0; hh < ratio; ++hh) {
     const int h = kh * ratio + hh;
     __syncthreads();                                         // the previous head is done with LDS
-    // S0 -> big; C^T -> small (tokens past the chunk are zero); gates
-    const float* s0 = A.chunk_states + (w * A.h_v + h) * plane;
-    for (int e = tid; e < D * D / 4; e += 256) {
-      const int r = e / (D / 4), c4 = e % (D / 4);
-      *reinterpret_cast<float4*>(&S.big[r * SB + 4 * c4]) = reinterpret_cast<const float4*>(s0 + r * D)[c4];
-    }
-    for (int e = tid; e < LT * D / 4; e += 256) {
-      const int t = e / (D / 4), c4 = e % (D / 4);
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < L) x = reinterpret_cast<const float4*>(A.cc + ((tok + t) * A.h_v + h) * D)[c4];
-      S.small[(4 * c4 + 0) * SC + t] = x.x;
-      S.small[(4 * c4 + 1) * SC + t] = x.y;
-      S.small[(4 * c4 + 2) * SC + t] = x.z;
-      S.small[(4 * c4 + 3) * SC + t] = x.w;
-    }
     if (tid < LT) {
       float2 ab = make_float2(1.f, 0.f);
       if (tid < L) ab = make_float2(A.a[(tok + tid) * A.h_v + h], A.b[(tok + tid) * A.h_v + h]);
@@ -332,121 +448,130 @@ __global__ void __launch_bounds__(256) grad_chunk_kernel(BackwardArgs A) {
       if (tid == 0) S.lgd[0] = 0.0;
     }
     __syncthreads();
-    // h_0 = <G at the chunk start, S0> in fp64
-    double hp = 0.0;
-    {
-      const float* g0 = A.adjoint + (gstart * A.h_v + h) * plane;
-      for (int e = tid; e < D * D / 4; e += 256) {
-        const int r = e / (D / 4), c4 = e % (D / 4);
-        const float4 gv = reinterpret_cast<const float4*>(g0 + r * D)[c4];
-        const float4 sv = *reinterpret_cast<const float4*>(&S.big[r * SB + 4 * c4]);
-        hp += static_cast<double>(gv.x) * sv.x + static_cast<double>(gv.y) * sv.y +
-              static_cast<double>(gv.z) * sv.z + static_cast<double>(gv.w) * sv.w;
-      }
-    }
-    const double h0 = block_sum_f64(hp, S.red);
     const double lr0 = S.lgd[row], lr1 = S.lgd[row + 1];
     const float2 abr = S.ab[row];
     const float fq = rv ? __expf(static_cast<float>(lr1)) : 0.f;                 // Gam after the row
     const float fu = rv ? __expf(static_cast<float>(lr0)) : 0.f;                 // Gam before it
     const float fc = rv ? __expf(static_cast<float>(S.lgd[L] - lr1)) : 0.f;     // Gam_L / Gam_row
     const float su = -abr.x * abr.y;                                              // dU = su * dc
+    const float* s0 = A.chunk_states + (w * A.h_v + h) * plane;
+    const float* g0 = A.adjoint + (gstart * A.h_v + h) * plane;
+    const float* ge = A.adjoint + ((gstart + 1) * A.h_v + h) * plane;
 
-    // dq += Gam_t dO S0^T; dk += Gam_{t-1} dU S0^T; A1 = dO C^T; A2 = dU C^T
-    f32x4 acc_dq[NT], a1[4], a2[4];
+    // dq += Gam_t dO S0^T; dk += Gam_{t-1} dU S0^T; A1 = dO C^T; A2 = dU C^T; h_0 = <G_start, S0>
+    f32x4 acc_dq[NT], acc_dk[NT], a1[4], a2[4];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc_dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NT; ++n) acc_dq[n] = acc_dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < 4; ++n) a1[n] = a2[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < KP; ++p) {
-      const int kb = 16 * p + 4 * lgp;
-      float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f), c4 = o4;
-      if (rv) {
-        o4 = load4<IO>(A.d_o, ((tok + row) * A.h_v + h) * D + kb);
-        c4 = *reinterpret_cast<const float4*>(A.dc + ((tok + row) * A.h_v + h) * D + kb);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = kb + e;
-        const float ao = comp(o4, e), au = su * comp(c4, e);
-        const float aq = ao * fq, ak = au * fu;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const float bs = S.big[k * SB + 16 * n + lj];
-          acc_dq[n] = mfma4(aq, bs, acc_dq[n]);
-          acc_dk[n] = mfma4(ak, bs, acc_dk[n]);
-        }
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const float bc = S.small[k * SC + 16 * n + lj];
-          a1[n] = mfma4(ao, bc, a1[n]);
-          a2[n] = mfma4(au, bc, a2[n]);
-        }
-      }
-    }
-    // dk += (Gam_L / Gam_t) C G_end^T
-    __syncthreads();                                         // S0 reads done
-    {
-      const float* ge = A.adjoint + ((gstart + 1) * A.h_v + h) * plane;
-      for (int e = tid; e < D * D / 4; e += 256) {
+    double hp = 0.0;
+#pragma unroll 1
+    for (int part = 0; part < NH; ++part) {
+      const int j0 = part * HR;
+      __syncthreads();
+      stage_part<D>(S, s0, A.cc, tok, L, A.h_v, h, j0);
+      __syncthreads();
+      for (int e = tid; e < HR * D / 4; e += 256) {
         const int r = e / (D / 4), c4 = e % (D / 4);
-        *reinterpret_cast<float4*>(&S.big[r * SB + 4 * c4]) = reinterpret_cast<const float4*>(ge + r * D)[c4];
+        const float4 gv = reinterpret_cast<const float4*>(g0 + static_cast<int64_t>(j0 + r) * D)[c4];
+        const float4 sv = *reinterpret_cast<const float4*>(&S.u.p.mat[r * SB + 4 * c4]);
+        hp += static_cast<double>(gv.x) * sv.x + static_cast<double>(gv.y) * sv.y +
+              static_cast<double>(gv.z) * sv.z + static_cast<double>(gv.w) * sv.w;
+      }
+#pragma unroll 1
+      for (int p = 0; p < HR / 16; ++p) {
+        const int kl = 16 * p + 4 * lgp;                     // k within the part
+        float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f), c4 = o4;
+        if (rv) {
+          o4 = load4<IO>(A.d_o, ((tok + row) * A.h_v + h) * D + j0 + kl);
+          c4 = *reinterpret_cast<const float4*>(A.dc + ((tok + row) * A.h_v + h) * D + j0 + kl);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = kl + e;
+          const float ao = comp(o4, e), au = su * comp(c4, e);
+          const float aq = ao * fq, ak = au * fu;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const float bs = S.u.p.mat[k * SB + 16 * n + lj];
+            acc_dq[n] = mfma4(aq, bs, acc_dq[n]);
+            acc_dk[n] = mfma4(ak, bs, acc_dk[n]);
+          }
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            const float bc = S.u.p.ct[k * SC + 16 * n + lj];
+            a1[n] = mfma4(ao, bc, a1[n]);
+            a2[n] = mfma4(au, bc, a2[n]);
+          }
+        }
       }
     }
-    __syncthreads();
-    for (int p = 0; p < KP; ++p) {
+    const double h0 = block_sum_f64(hp, S.red);
+    // dk += (Gam_L / Gam_t) C G_end^T
+#pragma unroll 1
+    for (int part = 0; part < NH; ++part) {
+      const int j0 = part * HR;
+      __syncthreads();
+      stage_part<D>(S, ge, A.cc, tok, L, A.h_v, h, j0);
+      __syncthreads();
+#pragma unroll 1
+      for (int p = 0; p < HR / 16; ++p) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int k = 16 * p + 4 * lgp + e;
-        const float ac = S.small[k * SC + row] * fc;
+        for (int e = 0; e < 4; ++e) {
+          const int k = 16 * p + 4 * lgp + e;
+          const float ac = S.u.p.ct[k * SC + row] * fc;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc_dk[n] = mfma4(ac, S.big[k * SB + 16 * n + lj], acc_dk[n]);
+          for (int n = 0; n < NT; ++n) acc_dk[n] = mfma4(ac, S.u.p.mat[k * SB + 16 * n + lj], acc_dk[n]);
+        }
       }
     }
     __syncthreads();                                         // C^T and G_end reads done
-    // A1, A2 -> small; K -> big rows [0, L); Q -> big rows [L, 2L) (zero past the chunk)
-    float* sa1 = S.small;
-    float* sa2 = S.small + LT * SA;
+    // A1, A2 -> LDS; K rows -> LDS
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wave + 4 * lgp + r;
-        sa1[t * SA + 16 * n + lj] = a1[n][r];
-        sa2[t * SA + 16 * n + lj] = a2[n][r];
+        S.u.m.a1[t * SA + 16 * n + lj] = a1[n][r];
+        S.u.m.a2[t * SA + 16 * n + lj] = a2[n][r];
       }
-    for (int e = tid; e < 2 * LT * D / 4; e += 256) {
-      const int rr = e / (D / 4), c4 = e % (D / 4);
-      const int t = rr % LT;
-      const void* src = rr < LT ? A.k : A.q;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < L) x = rr < LT ? load4<IO>(A.k, ((tok + t) * A.h_k + kh) * D + 4 * c4)
-                             : load4<IO>(A.q, ((tok + t) * A.h_k + kh) * D + 4 * c4);
-      (void)src;
-      *reinterpret_cast<float4*>(&S.big[rr * SB + 4 * c4]) = x;
-    }
+    stage_kq<D, IO>(S, A.k, tok, L, A.h_k, kh);
     __syncthreads();
-    // dq += (M_incl . A1) K;  dk += (N_incl . A1^T) Q + (M_strict . A2 + N_strict . A2^T) K
+    // dq += (M_incl . A1) K;  dk += (M_strict . A2 + N_strict . A2^T) K
+#pragma unroll 1
     for (int p = 0; p < LT / 16; ++p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = 16 * p + 4 * lgp + e;
         const double ls0 = S.lgd[s], ls1 = S.lgd[s + 1];
-        float aq = 0.f, ak1 = 0.f, ak2 = 0.f;
+        float aq = 0.f, ak2 = 0.f;
         if (rv) {
-          if (s <= row) aq = sa1[row * SA + s] * __expf(static_cast<float>(lr1 - ls1));
-          if (s >= row) ak1 = sa1[s * SA + row] * __expf(static_cast<float>(ls1 - lr1));
-          if (s < row) ak2 = sa2[row * SA + s] * __expf(static_cast<float>(lr0 - ls1));
-          if (s > row) ak2 = sa2[s * SA + row] * __expf(static_cast<float>(ls0 - lr1));
+          if (s <= row) aq = S.u.m.a1[row * SA + s] * __expf(static_cast<float>(lr1 - ls1));
+          if (s < row) ak2 = S.u.m.a2[row * SA + s] * __expf(static_cast<float>(lr0 - ls1));
+          if (s > row) ak2 = S.u.m.a2[s * SA + row] * __expf(static_cast<float>(ls0 - lr1));
         }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const float kbv = S.big[s * SB + 16 * n + lj];
-          const float qbv = S.big[(LT + s) * SB + 16 * n + lj];
+          const float kbv = S.u.m.kq[s * SB + 16 * n + lj];
           acc_dq[n] = mfma4(aq, kbv, acc_dq[n]);
-          acc_dk[n] = mfma4(ak1, qbv, acc_dk[n]);
           acc_dk[n] = mfma4(ak2, kbv, acc_dk[n]);
         }
+      }
+    }
+    __syncthreads();
+    stage_kq<D, IO>(S, A.q, tok, L, A.h_k, kh);
+    __syncthreads();
+    // dk += (N_incl . A1^T) Q
+#pragma unroll 1
+    for (int p = 0; p < LT / 16; ++p) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 16 * p + 4 * lgp + e;
+        const double ls1 = S.lgd[s + 1];
+        float ak1 = 0.f;
+        if (rv && s >= row) ak1 = S.u.m.a1[s * SA + row] * __expf(static_cast<float>(ls1 - lr1));
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc_dk[n] = mfma4(ak1, S.u.m.kq[s * SB + 16 * n + lj], acc_dk[n]);
       }
     }
     // per-token terms of this value head
@@ -458,15 +583,29 @@ __global__ void __launch_bounds__(256) grad_chunk_kernel(BackwardArgs A) {
         const int t = 16 * wave + 4 * lgp + r;
         float x = 0.f;
 #pragma unroll
-        for (int n = 0; n < NT; ++n) x = __builtin_fmaf(acc_dq[n][r], S.big[(LT + t) * SB + 16 * n + lj], x);
+        for (int n = 0; n < NT; ++n) x = __builtin_fmaf(acc_dq[n][r], S.u.m.kq[t * SB + 16 * n + lj], x);
         xr[r] = lane_tree<16>(x);
       }
       if (lj == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.xq[16 * wave + 4 * lgp + r] = xr[r];
       }
+      // this head's dq and dk added to the key head's, heads in order (the same thread owns the
+      // same elements for every head)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) dq_sum[n] += acc_dq[n];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * lgp + r;
+        if (t < L) {
+          const int64_t base = ((tok + t) * A.h_k + kh) * D;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            float* pq = A.dq + base + 16 * n + lj;
+            float* pk = A.dk + base + 16 * n + lj;
+            *pq = hh == 0 ? acc_dq[n][r] : *pq + acc_dq[n][r];
+            *pk = hh == 0 ? acc_dk[n][r] : *pk + acc_dk[n][r];
+          }
+        }
+      }
       // dv = b dc; v . dv; db = dc . w: four threads per token, D/4 columns each
       const int t = tid >> 2, part = tid & 3;
       float sv = 0.f, sd = 0.f;
@@ -511,19 +650,6 @@ __global__ void __launch_bounds__(256) grad_chunk_kernel(BackwardArgs A) {
       double excl = __shfl_up(incl, 1, 64);
       if (lane == 0) excl = 0.0;
       if (tid < L) A.da[(tok + tid) * A.h_v + h] = static_cast<float>((h0 - excl) / static_cast<double>(S.ab[tid].x));
-    }
-  }
-  // dq and dk of the key head: rows 16 wave + 4 g + r, columns 16 n + j
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 16 * wave + 4 * lgp + r;
-    if (t < L) {
-      const int64_t base = ((tok + t) * A.h_k + kh) * D;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        A.dq[base + 16 * n + lj] = dq_sum[n][r];
-        A.dk[base + 16 * n + lj] = acc_dk[n][r];
-      }
     }
   }
 }
