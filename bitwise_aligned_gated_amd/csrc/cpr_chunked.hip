@@ -38,6 +38,12 @@ __device__ __forceinline__ f32x4c mma(const bf16x8& a, const bf16x8& b, f32x4c c
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x4f32 (same lane layout with one A and one B element per lane: A[j][g], B[g][j])
+// for the small fp32 products of the triangular inverse.
+__device__ __forceinline__ f32x4c mma_f32(float a, float b, f32x4c c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 struct Split {
   bf16x8 hi, lo;
 };
@@ -105,6 +111,25 @@ __device__ __forceinline__ void chunk_range(const SeqMeta& m, int64_t c, int C, 
   *t1 = static_cast<int>(b1 < m.len ? b1 : m.len);
 }
 
+// Rows t < n of an io-bf16 [tokens][D] operand (row t at src + (tok + t) * stride), written
+// transposed into dst [D][ST] (zero for t >= n).  Each thread takes two consecutive tokens of one
+// 8-column unit, so consecutive threads store consecutive 32-bit words.
+template <int D, int ST>
+__device__ __forceinline__ void stage_transposed(__bf16* dst, const __bf16* src, int64_t tok, int64_t stride, int n) {
+  constexpr int L = 64;
+  for (int e = threadIdx.x; e < (L / 2) * (D / 8); e += 256) {
+    const int tp = e % (L / 2), c8 = e / (L / 2), t = 2 * tp;
+    bf16x8 x0 = {}, x1 = {};
+    if (t < n) x0 = *reinterpret_cast<const bf16x8*>(src + (tok + t) * stride + 8 * c8);
+    if (t + 1 < n) x1 = *reinterpret_cast<const bf16x8*>(src + (tok + t + 1) * stride + 8 * c8);
+#pragma unroll
+    for (int y = 0; y < 8; ++y) {
+      __bf16 pr[2] = {x0[y], x1[y]};
+      *reinterpret_cast<unsigned*>(&dst[(8 * c8 + y) * ST + t]) = __builtin_bit_cast(unsigned, pr);
+    }
+  }
+}
+
 // ---- prep: T, W, U per (chunk row, value head) ------------------------------------------------
 template <int D>
 struct alignas(16) PrepLds {
@@ -145,13 +170,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* w
   const __bf16* vin = static_cast<const __bf16*>(A.v);
 
   // K^T (zero past the chunk), gates and their log products
-  for (int e = tid; e < L * D / 8; e += 256) {
-    const int t = e / (D / 8), c8 = e % (D / 8);
-    bf16x8 kv = {};
-    if (t < n) kv = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) S.kt[(8 * c8 + x) * ST + t] = kv[x];
-  }
+  stage_transposed<D, ST>(S.kt, kin + kh * D, tok, static_cast<int64_t>(A.h_k) * D, n);
   if (tid < L) {
     float a = 1.f, b = 0.f;
     if (tid < n) {
@@ -199,13 +218,18 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* w
   __syncthreads();
   // T = (I + A)^{-1} (unit lower triangular), blocked: the four 16 x 16 diagonal blocks by
   // forward substitution, then the off-diagonal blocks level by level, X = -T_B A_BA T_A
-  if (tid < L) {
+  if (tid < L) {                                               // column j of block bk in registers
     const int bk = tid >> 4, j = tid & 15, o0 = 16 * bk;
+    float tc[16];
+#pragma unroll
     for (int s = 0; s < 16; ++s) {
       float acc = s == j ? 1.f : 0.f;
-      for (int r = j; r < s; ++r) acc = __builtin_fmaf(-S.am[(o0 + s) * SF + o0 + r], S.tp[(o0 + r) * SF + o0 + j], acc);
-      S.tp[(o0 + s) * SF + o0 + j] = s < j ? 0.f : acc;
+#pragma unroll
+      for (int r = 0; r < s; ++r) acc = __builtin_fmaf(-S.am[(o0 + s) * SF + o0 + r], tc[r], acc);   // tc[r] = 0 for r < j
+      tc[s] = s < j ? 0.f : acc;
     }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) S.tp[(o0 + s) * SF + o0 + j] = tc[s];
   }
   for (int e = tid; e < L * L; e += 256) {                     // zero the off-diagonal blocks
     const int t = e / L, s = e % L;
@@ -213,22 +237,29 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* w
   }
   __syncthreads();
   for (int half = 16; half < L; half *= 2) {
-    // pairs of half x half blocks at offsets (q, q + half), q = 0, 2 half, ...
-    const int npairs = L / (2 * half);
+    // pairs of half x half blocks at offsets (q, q + half), q = 0, 2 half, ...; 16 x 16 tiles of
+    // the off-diagonal block, one wave per tile, on fp32 matrix cores
+    const int tps = (half / 16) * (half / 16), ntiles = (L / (2 * half)) * tps;
     // Y = A_BA T_A
-    for (int e = tid; e < npairs * half * half; e += 256) {
-      const int pr = e / (half * half), t = (e / half) % half, s = e % half, q = 2 * half * pr;
-      float acc = 0.f;
-      for (int r = s; r < half; ++r) acc = __builtin_fmaf(S.am[(q + half + t) * SF + q + r], S.tp[(q + r) * SF + q + s], acc);
-      S.ty[(q + half + t) * SF + q + s] = acc;
+    for (int tile = wave; tile < ntiles; tile += 4) {
+      const int q = 2 * half * (tile / tps), it = (tile % tps) / (half / 16), jt = tile % (half / 16);
+      f32x4c acc = {};
+      for (int kk = 0; kk < half / 4; ++kk)
+        acc = mma_f32(S.am[(q + half + 16 * it + lj) * SF + q + 4 * kk + lg],
+                      S.tp[(q + 4 * kk + lg) * SF + q + 16 * jt + lj], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.ty[(q + half + 16 * it + 4 * lg + r) * SF + q + 16 * jt + lj] = acc[r];
     }
     __syncthreads();
     // X = -T_B Y
-    for (int e = tid; e < npairs * half * half; e += 256) {
-      const int pr = e / (half * half), t = (e / half) % half, s = e % half, q = 2 * half * pr;
-      float acc = 0.f;
-      for (int r = 0; r <= t; ++r) acc = __builtin_fmaf(S.tp[(q + half + t) * SF + q + half + r], S.ty[(q + half + r) * SF + q + s], acc);
-      S.tp[(q + half + t) * SF + q + s] = -acc;
+    for (int tile = wave; tile < ntiles; tile += 4) {
+      const int q = 2 * half * (tile / tps), it = (tile % tps) / (half / 16), jt = tile % (half / 16);
+      f32x4c acc = {};
+      for (int kk = 0; kk < half / 4; ++kk)
+        acc = mma_f32(S.tp[(q + half + 16 * it + lj) * SF + q + half + 4 * kk + lg],
+                      S.ty[(q + half + 4 * kk + lg) * SF + q + 16 * jt + lj], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.tp[(q + half + 16 * it + 4 * lg + r) * SF + q + 16 * jt + lj] = -acc[r];
     }
     __syncthreads();
   }
@@ -239,13 +270,7 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* w
     S.am[t * SF + s] = tv;
     S.tp[t * SF + s] = tv * (S.bb[s] * __expf(static_cast<float>(S.lgd[s + 1])));
   }
-  for (int e = tid; e < L * D / 8; e += 256) {
-    const int t = e / (D / 8), c8 = e % (D / 8);
-    bf16x8 vv = {};
-    if (t < n) vv = *reinterpret_cast<const bf16x8*>(vin + ((tok + t) * A.h_v + h) * D + 8 * c8);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) S.vt[(8 * c8 + x) * ST + t] = vv[x];
-  }
+  stage_transposed<D, ST>(S.vt, vin + static_cast<int64_t>(h) * D, tok, static_cast<int64_t>(A.h_v) * D, n);
   __syncthreads();
   float* wsb = ws + (w * A.h_v + h) * chunk_ws_floats<D>();
   // W = T diag(b Gam) K, then U = T diag(b) V
@@ -292,8 +317,8 @@ struct alignas(16) StateLds {
 template <int D>
 struct StateRegs {
   using M = ChunkCfg<D>;
-  static constexpr int KU = (M::L * D / 8 + 255) / 256;        // bf16x8 units of K per thread
-  bf16x8 k[KU];
+  static constexpr int KU = ((M::L / 2) * (D / 8) + 255) / 256;   // token pairs of 8 K columns per thread
+  bf16x8 k[2 * KU];
   float4 w[D / 32][2];                                         // W fragments of this lane's row
   float u[M::NS / 16][4];                                      // U at this lane's C positions
   double lg;                                                   // lgd[tid] (threads 0..L)
@@ -311,9 +336,12 @@ __device__ __forceinline__ void state_fetch(const PrefillArgs& A, const float* w
   const __bf16* kin = static_cast<const __bf16*>(A.k);
 #pragma unroll
   for (int x = 0; x < StateRegs<D>::KU; ++x) {
-    const int e = tid + 256 * x, t = e / (D / 8), c8 = e % (D / 8);
-    R.k[x] = bf16x8{};
-    if (e < M::L * D / 8 && t < n) R.k[x] = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+    const int e = tid + 256 * x, t = 2 * (e % (M::L / 2)), c8 = e / (M::L / 2);
+    R.k[2 * x] = R.k[2 * x + 1] = bf16x8{};
+    if (e < (M::L / 2) * (D / 8)) {
+      if (t < n) R.k[2 * x] = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+      if (t + 1 < n) R.k[2 * x + 1] = *reinterpret_cast<const bf16x8*>(kin + ((tok + t + 1) * A.h_k + kh) * D + 8 * c8);
+    }
   }
   const float* wsb = ws + ((row0 + c) * A.h_v + h) * chunk_ws_floats<D>();
 #pragma unroll
@@ -371,13 +399,16 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* 
       reinterpret_cast<float4*>(A.chunk_states + (w * A.h_v + h) * plane + static_cast<int64_t>(j0 + jj) * D)[c4] =
           *reinterpret_cast<const float4*>(&S.st[jj * SS + 4 * c4]);
     }
-    // commit the fetched K^T and log products
+    // commit the fetched K^T (two consecutive tokens per thread: 32-bit stores) and log products
 #pragma unroll
     for (int x = 0; x < StateRegs<D>::KU; ++x) {
-      const int e = tid + 256 * x, t = e / (D / 8), c8 = e % (D / 8);
-      if (e < L * D / 8) {
+      const int e = tid + 256 * x, tp = e % (L / 2), c8 = e / (L / 2);
+      if (e < (L / 2) * (D / 8)) {
 #pragma unroll
-        for (int y = 0; y < 8; ++y) S.kt[(8 * c8 + y) * ST + t] = R.k[x][y];
+        for (int y = 0; y < 8; ++y) {
+          __bf16 pr[2] = {R.k[2 * x][y], R.k[2 * x + 1][y]};
+          *reinterpret_cast<unsigned*>(&S.kt[(8 * c8 + y) * ST + 2 * tp]) = __builtin_bit_cast(unsigned, pr);
+        }
       }
     }
     if (tid <= L) S.lgd[tid] = R.lg;
