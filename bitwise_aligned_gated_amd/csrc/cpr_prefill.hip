@@ -80,36 +80,41 @@ struct TileLds {
 };
 
 // Fetch packed tokens [t0, t0 + n) (n <= TT) of key head kh / value head h into registers.
-// Units past n are zero-filled and never read from memory.
+// The tile's base addresses are uniform and each lane's offsets within a tile do not depend on
+// t0, so per unit the loop pays one compare and a load.  Units past n keep what they held (they
+// are committed to LDS but no token reads them) and are never read from memory.
 template <int DK, int DV, int IO, int MODE>
 __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV, IO, MODE>& R, int t0, int n,
                                            int kh, int h, int col0) {
   using Cfg = PassCfg<DK, DV, MODE>;
+  constexpr int64_t ES = IO == IO_F32 ? 4 : 2;
   const int tid = threadIdx.x;
+  const char* kb = static_cast<const char*>(A.k) + (static_cast<int64_t>(t0) * A.h_k + kh) * DK * ES;
+  const char* qb = static_cast<const char*>(A.q) + (static_cast<int64_t>(t0) * A.h_k + kh) * DK * ES;
+  const char* vb = static_cast<const char*>(A.v) + ((static_cast<int64_t>(t0) * A.h_v + h) * DV + col0) * ES;
 #pragma unroll
   for (int i = 0; i < Cfg::K_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
     const int tt = u / (DK / 8), c8 = u % (DK / 8);
-    const bool ok = u < Cfg::K_UNITS && tt < n;
-    const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_k + kh) * DK + c8 * 8;
-    R.k[i] = ok ? load_raw8<IO>(A.k, e) : zero_raw8<IO>();
-    if constexpr (has_out(MODE)) R.q[i] = ok ? load_raw8<IO>(A.q, e) : zero_raw8<IO>();
+    const uint32_t off = static_cast<uint32_t>(tt * A.h_k * DK + c8 * 8);
+    if (u < Cfg::K_UNITS && tt < n) {
+      R.k[i] = load_raw8<IO>(kb, off);
+      if constexpr (has_out(MODE)) R.q[i] = load_raw8<IO>(qb, off);
+    }
   }
 #pragma unroll
   for (int i = 0; i < Cfg::V_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
     const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
-    const bool ok = u < Cfg::V_UNITS && tt < n;
-    const int64_t e = (static_cast<int64_t>(t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
-    R.v[i] = ok ? load_raw8<IO>(A.v, e) : zero_raw8<IO>();
+    const uint32_t off = static_cast<uint32_t>(tt * A.h_v * DV + c8 * 8);
+    if (u < Cfg::V_UNITS && tt < n) R.v[i] = load_raw8<IO>(vb, off);
   }
 #pragma unroll
   for (int i = 0; i < Cfg::AB_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
     const int tt = u % Cfg::TT;
-    const bool ok = u < 2 * Cfg::TT && tt < n;
-    const float* src = u < Cfg::TT ? A.a : A.b;
-    R.ab[i] = ok ? src[static_cast<int64_t>(t0 + tt) * A.h_v + h] : 0.0f;
+    const float* src = (u < Cfg::TT ? A.a : A.b) + static_cast<int64_t>(t0) * A.h_v + h;
+    if (u < 2 * Cfg::TT && tt < n) R.ab[i] = src[static_cast<uint32_t>(tt * A.h_v)];
   }
 }
 
@@ -182,7 +187,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
   int64_t row = row0 + 1;                              // row the next chunk-start state goes to
   const bool rows_on = has_rows(MODE) && A.chunk_states != nullptr;
 
-  TileRegs<DK, DV, IO, MODE> Rg;
+  TileRegs<DK, DV, IO, MODE> Rg = {};
   fetch_tile<DK, DV, IO, MODE>(A, Rg, tok0 + tb, te - tb < Cfg::TT ? te - tb : Cfg::TT, kh, h, col0);
   commit_tile<DK, DV, IO, MODE>(Rg, L);
   __syncthreads();
@@ -248,7 +253,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
       }
     };
     if (MODE != kOutput && n == Cfg::TT) {    // one-leaf lanes, full tile: unrolled, immediate offsets
-#pragma unroll 4
+#pragma unroll
       for (int tt = 0; tt < Cfg::TT; ++tt) token(tt);
     } else {
       for (int tt = 0; tt < n; ++tt) token(tt);
