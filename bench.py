@@ -114,11 +114,16 @@ def measured_traffic():
     return {k: v["bytes"] for k, v in tr.get("kernels", {}).items()}
 
 
-def prefill_flops(lengths, h_v, dk, dv, chunk):
-    """Algorithmic FLOPs of the two passes.  Per token-head: pass 1 (state only) 5*dk*dv
-    (u = S^T k: 2 dk dv; a*S: dk dv; k c^T added: 2 dk dv); pass 2 adds o = S^T q: 7*dk*dv."""
-    p1_tokens = sum(max(0, ((L - 1) // chunk) * chunk) for L in lengths if L > 0)
+def prefill_flops(lengths, h_v, dk, dv, chunk, stash=True):
+    """Algorithmic FLOPs of the two passes.  Per token-head, the step is u = S^T k (2 dk dv), a*S
+    (dk dv) and k c^T added (2 dk dv); the output o = S^T q adds 2 dk dv.
+    With the c stash: pass 1 runs every token without output (5 dk dv) and pass 2 applies the kept
+    c with output (a*S, k c^T, o: 5 dk dv).  Without it: pass 1 runs the tokens up to each
+    sequence's last chunk start (5 dk dv) and pass 2 the whole step with output (7 dk dv)."""
     p2_tokens = sum(lengths)
+    if stash:
+        return p2_tokens * h_v * 5 * dk * dv, p2_tokens * h_v * 5 * dk * dv, p2_tokens
+    p1_tokens = sum(max(0, ((L - 1) // chunk) * chunk) for L in lengths if L > 0)
     return p1_tokens * h_v * 5 * dk * dv, p2_tokens * h_v * 7 * dk * dv, p1_tokens
 
 
@@ -197,9 +202,11 @@ def main():
     o = torch.empty((N, P.h_v, P.dv), dtype=torch.bfloat16, device=dev)
     cu = torch.from_numpy(x.cu_seqlens).to(dev)
     ids = torch.arange(B, dtype=torch.int32, device=dev)
+    stash = torch.empty((N, P.h_v, P.dv), dtype=torch.float32, device=dev)   # every token's c
 
-    def step(events=None):
-        cpr.gdn_prefill(spool, cu, x.q, x.k, x.v, x.a, x.b, slot_ids=ids, o=o, chunk_states=cs, events=events)
+    def step(events=None, c_stash=stash, pool=spool, out=o):
+        cpr.gdn_prefill(pool, cu, x.q, x.k, x.v, x.a, x.b, slot_ids=ids, o=out, chunk_states=cs, c_stash=c_stash,
+                        events=events)
 
     for _ in range(args.warmup):
         step()
@@ -227,19 +234,46 @@ def main():
                 "traffic": traffic.get(dom),
                 "peak_unpacked": FP32_UNPACKED_PEAK_TFLOPS,
                 "frac_unpacked": round(kernels[dom]["tflops"] / FP32_UNPACKED_PEAK_TFLOPS, 4)}
-    # prefill HBM fraction (the metric's "% HBM peak"): algorithmic bytes of the whole CPR step
+    # prefill HBM fraction (the metric's "% HBM peak"): algorithmic bytes of the whole CPR step.
+    # Pass 1 reads k, v, a, b of every token and writes the chunk-start states and each token's c;
+    # pass 2 reads q, k, a, the chunk states and c, and writes o and the final states.
     io = 2
-    in_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4)
-    pass1_reread = p1_tokens * (P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4)
     n_rows = int(cpr.gdn_chunk_rows(x.cu_seqlens, P.chunk)[-1])
     bstate = n_rows * P.h_v * P.dk * P.dv * 4
-    cpr_bytes = in_bytes + pass1_reread + 2 * bstate + N * P.h_v * P.dv * io + B * P.h_v * P.dk * P.dv * 4
+    c_bytes = N * P.h_v * P.dv * 4
+    pass1_bytes = N * (P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4) + bstate + c_bytes
+    pass2_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * 4) + bstate + c_bytes + N * P.h_v * P.dv * io \
+        + B * P.h_v * P.dk * P.dv * 4
+    cpr_bytes = pass1_bytes + pass2_bytes
     prefill_gbs = cpr_bytes / (ms_step * 1e-3) / 1e9
 
     # parity of the timed prefill output against the oracle (computed in the CPU leg below)
     o_host = o.float().cpu().numpy()
     S_host = spool.state.cpu().numpy()
     digest_two_pass = hashlib.sha256(o.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
+
+    # the same call without the c stash (pass 2 predicts every c again): context, same bits
+    npool = cpr.StatePool(P, B, device=dev)
+    on = torch.empty_like(o)
+    for _ in range(args.warmup):
+        step(c_stash=None, pool=npool, out=on)
+    nevs = [[hip.event() for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(nevs[i], c_stash=None, pool=npool, out=on)
+    torch.cuda.synchronize()
+    n_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    nf1, nf2, _ = prefill_flops([int(l) for l in x.lengths], P.h_v, P.dk, P.dv, P.chunk, stash=False)
+    n1 = statistics.mean(hip.ms(e[0], e[1]) for e in nevs)
+    n2 = statistics.mean(hip.ms(e[1], e[2]) for e in nevs)
+    no_stash = {"ms_per_step": round(n_ms, 4), "tok_s": round(N / (n_ms * 1e-3), 1),
+                "boundary_pass_ms": round(n1, 4), "output_pass_ms": round(n2, 4),
+                "boundary_pass_tflops": round(nf1 / (n1 * 1e-3) / 1e12, 3),
+                "output_pass_tflops": round(nf2 / (n2 * 1e-3) / 1e12, 3),
+                "bitwise_equal_to_stash": hashlib.sha256(on.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
+                == digest_two_pass and bool(torch.equal(npool.state, spool.state))}
+    del npool, on
 
     # the one-pass variant on the same workload ("recurrent everywhere" in the pages' table);
     # context only: the timed step above is the two-pass CPR prefill
@@ -434,7 +468,7 @@ def main():
                     "cpr_bytes": int(cpr_bytes), "hbm_frac": round(prefill_gbs / HBM_PEAK_GBS, 4),
                     "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                 for k, v in kernels.items()},
-                    "one_pass_variant": fused, "chunked_matrix_core": chunked},
+                    "without_c_stash": no_stash, "one_pass_variant": fused, "chunked_matrix_core": chunked},
         "roofline": roofline,
         "decode": decode,
         "trainer": trainer,

@@ -66,7 +66,7 @@ _SIGS = {
     "gdn_check_cu_seqlens": (ctypes.c_int, [_P, _i32, _i64]),
     "gdn_chunk_rows_bound": (_i64, [_i64, _i32, _i32]),
     "gdn_chunk_rows": (ctypes.c_int, [_P, _P, _i32, _i32, _P]),
-    "gdn_prefill": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
+    "gdn_prefill": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P, _P]),
     "gdn_prefill_fused": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
     "gdn_decode_step": (ctypes.c_int, [_P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_state_resync": (ctypes.c_int, [_P, _P, _i32, _P]),
@@ -305,10 +305,13 @@ def gdn_prefill_fused(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None,
 
 
 def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
-                o=None, chunk_states=None, stream=None, events=None):
+                o=None, chunk_states=None, c_stash=True, stream=None, events=None):
     """Prefill / trainer forward over a packed batch (C gdn_prefill).
 
     cu_seqlens: host sequence (checked on the host, then copied) or a device int32 tensor.
+    c_stash: True allocates the [N][H_v][dv] fp32 scratch in which pass 1 keeps every token's c for
+    pass 2; a tensor is used as that scratch; None or False passes NULL (pass 2 predicts c again).
+    The bits of every result are the same either way.
     Returns (o, chunk_states); chunk_states is allocated with the bound's row count when None."""
     P, dev = pool.policy, pool.device
     N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
@@ -316,9 +319,14 @@ def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_
     if chunk_states is None:
         chunk_states = torch.empty((max(bound, 1), P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)
     _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    if c_stash is True:
+        c_stash = torch.empty((N, P.h_v, P.dv), dtype=torch.float32, device=dev) if N > 0 else None
+    if c_stash is not None and c_stash is not False:
+        _dev(c_stash, "c_stash", torch.float32, (N, P.h_v, P.dv), dev)
+    stash_ptr = c_stash.data_ptr() if isinstance(c_stash, torch.Tensor) else None
     _check(_lib.gdn_prefill(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
                             q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
-                            o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0],
+                            o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0], stash_ptr,
                             _stream_ptr(stream), _events(events, 3)))
     return o, chunk_states
 

@@ -27,7 +27,8 @@ struct PrefillArgs {
   int32_t h_v;
   int32_t chunk;
   int32_t round_boundary;     // 1: bf16 boundary dtype (round the state at chunk starts)
-  float* cw;                  // nullable: [2][N][H_v][dv] fp32, every token's c then w (trainer forward)
+  float* c_stash;             // nullable: [N][H_v][dv] fp32, every token's c (pass 1 writes, pass 2 reads)
+  float* w_stash;             // nullable (needs c_stash): [N][H_v][dv] fp32, every token's w
   void* const* events;        // nullable: hipEvent_t recorded around the kernels
 };
 

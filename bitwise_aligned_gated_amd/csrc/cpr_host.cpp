@@ -311,7 +311,7 @@ int gdn_chunk_rows(const int32_t* cu, const int64_t* pos0, int32_t num_seqs, int
 static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                         const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
                         const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
-                        float* cw, void* stream, void* const* events, const char* who) {
+                        float* c_stash, float* w_stash, void* stream, void* const* events, const char* who) {
   if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", who);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", who);
   if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", who);
@@ -327,6 +327,7 @@ static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
     return fail(GDN_EINVAL, "%s: chunk_state_rows %lld < bound %lld", who, (long long)chunk_state_rows,
                 (long long)bound);
   if (bound > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "%s: too many chunks for one launch", who);
+  if (reinterpret_cast<uintptr_t>(c_stash) % 16 != 0) return fail(GDN_EINVAL, "%s: c stash must be 16-byte aligned", who);
   cpr::PrefillArgs A;
   A.cu = cu_seqlens;
   A.slot_ids = slot_ids;
@@ -342,7 +343,8 @@ static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = P.state_dtype == GDN_BF16;
-  A.cw = cw;
+  A.c_stash = total_tokens > 0 ? c_stash : nullptr;
+  A.w_stash = total_tokens > 0 ? w_stash : nullptr;
   A.events = events;
   const hipError_t e = cpr::launch_prefill(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, who);
@@ -352,9 +354,9 @@ static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
 int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                 const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
                 const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
-                void* stream, void* const* events) {
+                float* c_stash, void* stream, void* const* events) {
   return prefill_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, chunk_states,
-                      chunk_state_rows, nullptr, stream, events, "gdn_prefill");
+                      chunk_state_rows, c_stash, nullptr, stream, events, "gdn_prefill");
 }
 
 int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -362,8 +364,10 @@ int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
                         const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
                         float* cw, void* stream, void* const* events) {
   if (total_tokens > 0 && cw == nullptr) return fail(GDN_EINVAL, "gdn_trainer_forward: cw is NULL");
+  // pass 1 keeps every token's c in block 0 and w in block 1; pass 2 applies the kept c
+  float* w = cw == nullptr || st == nullptr ? nullptr : cw + total_tokens * st->policy.h_v * int64_t(st->policy.dv);
   return prefill_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, chunk_states,
-                      chunk_state_rows, cw, stream, events, "gdn_trainer_forward");
+                      chunk_state_rows, cw, w, stream, events, "gdn_trainer_forward");
 }
 
 int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -399,7 +403,8 @@ int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = P.state_dtype == GDN_BF16;
-  A.cw = nullptr;
+  A.c_stash = nullptr;
+  A.w_stash = nullptr;
   A.events = events;
   const hipError_t e = cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_prefill_fused launch");
@@ -599,7 +604,8 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.from_state = from_state;
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = 0;
-  A.cw = nullptr;
+  A.c_stash = nullptr;
+  A.w_stash = nullptr;
   A.events = events;
   const hipError_t e = cpr::launch_prefill_chunked(P.dk, P.dv, 1, A, workspace, outputs,
                                                    static_cast<hipStream_t>(stream));

@@ -35,13 +35,19 @@ namespace cpr {
 
 // What a token loop does: pass 1 stores chunk-start states, pass 2 writes outputs, the fused
 // one-pass variant does both (it runs a whole sequence like pass 1, with outputs like pass 2).
-enum : int { kBoundary = 0, kOutput = 1, kFused = 2 };
-constexpr bool has_out(int mode) { return mode != kBoundary; }
-constexpr bool has_rows(int mode) { return mode != kOutput; }
+// With a stash, pass 1 runs every token and also keeps each token's write value c (and w when
+// asked), and pass 2 applies the kept c instead of predicting it again: the same values enter
+// the same update, so the bits do not change, and pass 2 skips the prediction's dot product.
+enum : int { kBoundary = 0, kOutput = 1, kFused = 2, kOutputC = 3, kBoundaryC = 4 };
+constexpr bool has_out(int mode) { return mode == kOutput || mode == kFused || mode == kOutputC; }
+constexpr bool has_rows(int mode) { return mode == kBoundary || mode == kFused || mode == kBoundaryC; }
+constexpr bool is_wide(int mode) { return mode == kOutput || mode == kOutputC; }
+constexpr bool reads_c(int mode) { return mode == kOutputC; }      // c from the stash instead of v, b
+constexpr bool keeps_c(int mode) { return mode == kBoundaryC; }    // writes the stash
 
 template <int DK, int DV, int MODE>
 struct PassCfg {
-  static constexpr bool WIDE = MODE == kOutput;   // parallel over chunks: fewer, longer lanes
+  static constexpr bool WIDE = is_wide(MODE);     // parallel over chunks: fewer, longer lanes
   static constexpr int G = WIDE ? (DK / kLeaf < 4 ? DK / kLeaf : 4) : DK / kLeaf;  // lanes per column
   static constexpr int NL = DK / (kLeaf * G);                                  // leaves per lane
   static constexpr int R = NL * kLeaf;                                         // rows per lane
@@ -49,12 +55,13 @@ struct PassCfg {
   static constexpr int WG_MAX_COLS = 256 / G * NC;                             // 4 waves
   static constexpr int WG_COLS = WG_MAX_COLS < DV ? WG_MAX_COLS : DV;
   static constexpr int THREADS = WG_COLS / NC * G;
-  static constexpr int TT = MODE == kBoundary ? 32 : 16;     // tokens per tile (LDS: all resident)
+  static constexpr int TT = (MODE == kBoundary || MODE == kBoundaryC) ? 32 : 16;  // tokens per tile
   static constexpr int K_UNITS = TT * DK / 8;          // 8-element units of a k (or q) tile
   static constexpr int V_UNITS = TT * WG_COLS / 8;
   static constexpr int K_PER_T = (K_UNITS + THREADS - 1) / THREADS;
   static constexpr int V_PER_T = (V_UNITS + THREADS - 1) / THREADS;
-  static constexpr int AB_PER_T = (2 * TT + THREADS - 1) / THREADS;
+  static constexpr int NAB = reads_c(MODE) ? TT : 2 * TT;        // gates per tile: a (and b)
+  static constexpr int AB_PER_T = (NAB + THREADS - 1) / THREADS;
   static_assert(DK % (kLeaf * G) == 0 && DV % WG_COLS == 0 && WG_COLS % 8 == 0, "shape");
   static_assert(THREADS % 64 == 0 || (THREADS & (THREADS - 1)) == 0, "block size");
 };
@@ -65,7 +72,7 @@ struct TileRegs {
   using Cfg = PassCfg<DK, DV, MODE>;
   Raw8<IO> k[Cfg::K_PER_T];
   Raw8<IO> q[has_out(MODE) ? Cfg::K_PER_T : 1];
-  Raw8<IO> v[Cfg::V_PER_T];
+  Raw8<reads_c(MODE) ? IO_F32 : IO> v[Cfg::V_PER_T];   // v, or the stashed c (fp32)
   float ab[Cfg::AB_PER_T];
 };
 
@@ -74,9 +81,11 @@ struct TileLds {
   using Cfg = PassCfg<DK, DV, MODE>;
   float k[Cfg::TT][DK];
   float q[has_out(MODE) ? Cfg::TT : 1][DK];
-  float v[Cfg::TT][Cfg::WG_COLS];
+  float v[Cfg::TT][Cfg::WG_COLS];                       // v, or the stashed c
   float o[MODE == kFused ? Cfg::TT : 1][Cfg::WG_COLS];  // fused: outputs gathered for row stores
-  float2 ab[Cfg::TT];   // (a, b) of each token
+  float cs[keeps_c(MODE) ? Cfg::TT : 1][Cfg::WG_COLS];  // stash: c and w gathered for row stores
+  float ws[keeps_c(MODE) ? Cfg::TT : 1][Cfg::WG_COLS];
+  float2 ab[Cfg::TT];   // (a, b) of each token (stashed c: a only)
 };
 
 // Fetch packed tokens [t0, t0 + n) (n <= TT) of key head kh / value head h into registers.
@@ -91,7 +100,9 @@ __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV
   const int tid = threadIdx.x;
   const char* kb = static_cast<const char*>(A.k) + (static_cast<int64_t>(t0) * A.h_k + kh) * DK * ES;
   const char* qb = static_cast<const char*>(A.q) + (static_cast<int64_t>(t0) * A.h_k + kh) * DK * ES;
-  const char* vb = static_cast<const char*>(A.v) + ((static_cast<int64_t>(t0) * A.h_v + h) * DV + col0) * ES;
+  const char* vb = reads_c(MODE)
+                       ? reinterpret_cast<const char*>(A.c_stash + (static_cast<int64_t>(t0) * A.h_v + h) * DV + col0)
+                       : static_cast<const char*>(A.v) + ((static_cast<int64_t>(t0) * A.h_v + h) * DV + col0) * ES;
 #pragma unroll
   for (int i = 0; i < Cfg::K_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
@@ -107,14 +118,21 @@ __device__ __forceinline__ void fetch_tile(const PrefillArgs& A, TileRegs<DK, DV
     const int u = tid + i * Cfg::THREADS;
     const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
     const uint32_t off = static_cast<uint32_t>(tt * A.h_v * DV + c8 * 8);
-    if (u < Cfg::V_UNITS && tt < n) R.v[i] = load_raw8<IO>(vb, off);
+    if (u < Cfg::V_UNITS && tt < n) R.v[i] = load_raw8<reads_c(MODE) ? IO_F32 : IO>(vb, off);
   }
+  const float* ga = A.a + static_cast<int64_t>(t0) * A.h_v + h;
+  const float* gb = A.b + static_cast<int64_t>(t0) * A.h_v + h;
 #pragma unroll
   for (int i = 0; i < Cfg::AB_PER_T; ++i) {
     const int u = tid + i * Cfg::THREADS;
     const int tt = u % Cfg::TT;
-    const float* src = (u < Cfg::TT ? A.a : A.b) + static_cast<int64_t>(t0) * A.h_v + h;
-    if (u < 2 * Cfg::TT && tt < n) R.ab[i] = src[static_cast<uint32_t>(tt * A.h_v)];
+    const uint32_t off = static_cast<uint32_t>(tt * A.h_v);
+    if (tt < n) {                    // lanes [0, TT) fetch a, lanes [TT, 2 TT) fetch b
+      if (u < Cfg::TT)
+        R.ab[i] = ga[off];
+      else if (u < Cfg::NAB)
+        R.ab[i] = gb[off];
+    }
   }
 }
 
@@ -142,7 +160,7 @@ __device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, MODE>& R,
     if (u < Cfg::V_UNITS) {
       const int tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
       float x[8];
-      widen8<IO>(R.v[i], x);
+      widen8<reads_c(MODE) ? IO_F32 : IO>(R.v[i], x);
       store_f32x8(&L.v[tt][c8 * 8], x);
     }
   }
@@ -151,7 +169,7 @@ __device__ __forceinline__ void commit_tile(const TileRegs<DK, DV, IO, MODE>& R,
     const int u = tid + i * Cfg::THREADS;
     if (u < Cfg::TT)
       L.ab[u].x = R.ab[i];
-    else if (u < 2 * Cfg::TT)
+    else if (u < Cfg::NAB)
       L.ab[u - Cfg::TT].y = R.ab[i];
   }
 }
@@ -186,6 +204,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
   int nb = __builtin_amdgcn_readfirstlane(first_nb);   // tokens until the next chunk start
   int64_t row = row0 + 1;                              // row the next chunk-start state goes to
   const bool rows_on = has_rows(MODE) && A.chunk_states != nullptr;
+  const bool keep_w = A.w_stash != nullptr;
 
   TileRegs<DK, DV, IO, MODE> Rg = {};
   fetch_tile<DK, DV, IO, MODE>(A, Rg, tok0 + tb, te - tb < Cfg::TT ? te - tb : Cfg::TT, kh, h, col0);
@@ -196,23 +215,41 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
     const int t1 = t0 + Cfg::TT;
     const bool more = t1 < te;
     if (more) fetch_tile<DK, DV, IO, MODE>(A, Rg, tok0 + t1, te - t1 < Cfg::TT ? te - t1 : Cfg::TT, kh, h, col0);
+    // Stash modes hand each token's c (and w) to LDS at the start of the next token, so that the
+    // lane-masked write does not split a token's own arithmetic.
+    float pc = 0.0f, pw = 0.0f;
+    int ptt = -1;
+    auto hand_over = [&]() {
+      if constexpr (keeps_c(MODE)) {
+        if (ptt >= 0 && g == 0) {
+          L.cs[ptt][cp] = pc;
+          if (keep_w) L.ws[ptt][cp] = pw;
+        }
+      }
+    };
     auto token = [&](int tt) {
       float kr[R], qr[R];
       lds_read<R>(&L.k[tt][g * R], kr);
       if constexpr (OUT) lds_read<R>(&L.q[tt][g * R], qr);
       const float2 ab = L.ab[tt];
+      hand_over();
       float vv[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) vv[c] = L.v[tt][cp * NC + c];
-      float o[NC], wv[NC], cv[NC];
-      if constexpr (MODE == kOutput) {
+      float o[NC];
+      if constexpr (MODE == kOutputC) {                    // vv holds the stashed c
 #pragma unroll
-        for (int c = 0; c < NC; ++c) o[c] = cpr_step_wc<NL, G>(s[c], kr, qr, vv[c], ab.x, ab.y, wv[c], cv[c]);
+        for (int c = 0; c < NC; ++c) o[c] = cpr_step_given_c<NL, G>(s[c], kr, qr, ab.x, vv[c]);
+      } else if constexpr (MODE == kBoundaryC) {
+        float u;
+        cpr_update<NL, G>(s[0], kr, vv[0], ab.x, ab.y, u, pw, pc);
+        ptt = tt;
+        o[0] = 0.0f;
       } else {
 #pragma unroll
         for (int c = 0; c < NC; ++c) o[c] = cpr_step<NL, G, OUT>(s[c], kr, qr, vv[c], ab.x, ab.y);
       }
-      if constexpr (MODE == kOutput) {
+      if constexpr (is_wide(MODE)) {
         if (g == 0) {
           const int64_t oe = (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + cp * NC;
           if constexpr (NC == 2) {
@@ -220,14 +257,6 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
           } else {
 #pragma unroll
             for (int c = 0; c < NC; ++c) store1<IO>(A.o, oe + c, o[c]);
-          }
-          if (A.cw != nullptr) {                           // the trainer forward keeps c and w
-            const int64_t wofs = A.total_tokens * A.h_v * DV;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              A.cw[oe + c] = cv[c];
-              A.cw[wofs + oe + c] = wv[c];
-            }
           }
         }
       } else if constexpr (MODE == kFused) {
@@ -252,12 +281,14 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
         }
       }
     };
-    if (MODE != kOutput && n == Cfg::TT) {    // one-leaf lanes, full tile: unrolled, immediate offsets
+    if (!is_wide(MODE) && n == Cfg::TT) {    // one-leaf lanes, full tile: unrolled, immediate offsets
 #pragma unroll
       for (int tt = 0; tt < Cfg::TT; ++tt) token(tt);
     } else {
       for (int tt = 0; tt < n; ++tt) token(tt);
     }
+    hand_over();
+    ptt = -1;
     __syncthreads();
     if constexpr (MODE == kFused) {                    // the tile's outputs, 8 columns per unit
       for (int u = tid; u < n * (Cfg::WG_COLS / 8); u += Cfg::THREADS) {
@@ -268,16 +299,27 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
         store8<IO>(A.o, (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8, x);
       }
     }
+    if constexpr (keeps_c(MODE)) {                     // the tile's c (and w), 4 columns per unit
+      for (int u = tid; u < n * (Cfg::WG_COLS / 4); u += Cfg::THREADS) {
+        const int tt = u / (Cfg::WG_COLS / 4), c4 = u % (Cfg::WG_COLS / 4);
+        const int64_t e = (static_cast<int64_t>(tok0 + t0 + tt) * A.h_v + h) * DV + col0 + c4 * 4;
+        *reinterpret_cast<float4*>(A.c_stash + e) = *reinterpret_cast<const float4*>(&L.cs[tt][c4 * 4]);
+        if (A.w_stash != nullptr)
+          *reinterpret_cast<float4*>(A.w_stash + e) = *reinterpret_cast<const float4*>(&L.ws[tt][c4 * 4]);
+      }
+    }
     if (more) commit_tile<DK, DV, IO, MODE>(Rg, L);
     __syncthreads();
   }
 }
 
-template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PassCfg<DK, DV, kBoundary>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
-  using Cfg = PassCfg<DK, DV, kBoundary>;
+// MODE kBoundary: tokens up to the last chunk start; kBoundaryC: every token, keeping c (and w).
+template <int DK, int DV, int IO, int MODE>
+__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, MODE>;
   static_assert(Cfg::R == kLeaf && Cfg::NC == 1, "pass 1 holds one leaf of one column per lane");
-  __shared__ TileLds<DK, DV, kBoundary> L;
+  static_assert(MODE == kBoundary || MODE == kBoundaryC, "pass 1 modes");
+  __shared__ TileLds<DK, DV, MODE> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   // group = (sequence, key head); members = its value heads x column groups
   const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
@@ -305,19 +347,21 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kBoundary>::THREADS)) boundar
   }
   if (A.round_boundary && m.p0 % A.chunk == 0) resync_round(s[0]);   // the first token is a chunk start
   store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s[0]);
-  if (m.nrows < 2) return;
-  // tokens up to the last recorded chunk start; the first chunk start is C - p0 % C tokens in
+  if (MODE == kBoundary && m.nrows < 2) return;
+  // tokens up to the last recorded chunk start (or all of them); the first chunk start is
+  // C - p0 % C tokens in
   const int64_t C = A.chunk;
   const int first_nb = static_cast<int>(C - m.p0 % C);
-  const int last = static_cast<int>((m.p0 / C + m.nrows - 1) * C - m.p0);
-  run_tokens<DK, DV, IO, kBoundary>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, row0 + m.nrows,
-                                    first_nb);
+  const int last = MODE == kBoundaryC ? m.len : static_cast<int>((m.p0 / C + m.nrows - 1) * C - m.p0);
+  run_tokens<DK, DV, IO, MODE>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, row0 + m.nrows, first_nb);
 }
 
-template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PassCfg<DK, DV, kOutput>::THREADS)) output_pass_kernel(PrefillArgs A) {
-  using Cfg = PassCfg<DK, DV, kOutput>;
-  __shared__ TileLds<DK, DV, kOutput> L;
+// MODE kOutput: every step predicts c from v; kOutputC: c comes from pass 1's stash.
+template <int DK, int DV, int IO, int MODE>
+__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) output_pass_kernel(PrefillArgs A) {
+  using Cfg = PassCfg<DK, DV, MODE>;
+  static_assert(MODE == kOutput || MODE == kOutputC, "pass 2 modes");
+  __shared__ TileLds<DK, DV, MODE> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   // group = (boundary row, key head); members = its value heads x column groups
   const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
@@ -343,8 +387,8 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kOutput>::THREADS)) output_pa
 #pragma unroll
     for (int r = 0; r < Cfg::R; r += 8) load_f32x8(src + off + r, *reinterpret_cast<float(*)[8]>(&s[cc][r]));
   }
-  run_tokens<DK, DV, IO, kOutput>(A, L, s, static_cast<int>(m.tok0), static_cast<int>(tb), static_cast<int>(te), h,
-                                  cg, 0, 0, 0);
+  run_tokens<DK, DV, IO, MODE>(A, L, s, static_cast<int>(m.tok0), static_cast<int>(tb), static_cast<int>(te), h, cg,
+                               0, 0, 0);
   if (c == m.nrows - 1) {
     float* dst = A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane;
 #pragma unroll
@@ -411,16 +455,24 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
   if (A.num_seqs > 0) {
     const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
     if (g1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g1)), dim3(C1::THREADS), 0, stream,
-                       A);
+    if (A.c_stash != nullptr)
+      hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO, kBoundaryC>), dim3(static_cast<unsigned>(g1)),
+                         dim3(C1::THREADS), 0, stream, A);
+    else
+      hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO, kBoundary>), dim3(static_cast<unsigned>(g1)),
+                         dim3(C1::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0 && A.rows_cap > 0) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(C2::THREADS), 0, stream,
-                       A);
+    if (A.c_stash != nullptr)
+      hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO, kOutputC>), dim3(static_cast<unsigned>(g2)),
+                         dim3(C2::THREADS), 0, stream, A);
+    else
+      hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO, kOutput>), dim3(static_cast<unsigned>(g2)),
+                         dim3(C2::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
@@ -474,8 +526,8 @@ static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream)
   if (A.num_seqs > 0 && A.rows_cap > 0) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(C2::THREADS), 0, stream,
-                       A);
+    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO, kOutput>), dim3(static_cast<unsigned>(g2)), dim3(C2::THREADS), 0,
+                       stream, A);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

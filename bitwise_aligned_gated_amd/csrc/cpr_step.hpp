@@ -68,16 +68,22 @@ __device__ __forceinline__ float pinned_dot(const float (&s)[NL * kLeaf], const 
   return lane_tree<G>(p[0]);
 }
 
+// The update's last step on one column slice held by this lane: S[r][j] = fma(k[r], c, a*S[r][j]).
+template <int N>
+__device__ __forceinline__ void cpr_apply(float (&s)[N], const float (&k)[N], float a, float c) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) s[r] = __builtin_fmaf(k[r], c, a * s[r]);
+}
+
 // The state update of one token on one column slice held by this lane (steps 1-4 of the
-// schedule); u, w and c are returned for the gradient pass, which replays the forward with them.
+// schedule); u, w and c are returned for the passes that keep them.
 template <int NL, int G>
 __device__ __forceinline__ void cpr_update(float (&s)[NL * kLeaf], const float (&k)[NL * kLeaf], float v, float a,
                                            float b, float& u, float& w, float& c) {
   u = pinned_dot<NL, G>(s, k);
   w = __builtin_fmaf(-a, u, v);
   c = b * w;
-#pragma unroll
-  for (int r = 0; r < NL * kLeaf; ++r) s[r] = __builtin_fmaf(k[r], c, a * s[r]);
+  cpr_apply(s, k, a, c);
 }
 
 // One token applied to one column slice held by this lane.
@@ -94,14 +100,12 @@ __device__ __forceinline__ float cpr_step(float (&s)[NL * kLeaf], const float (&
   return 0.0f;
 }
 
-// The same step with output that also returns w and c (the values a trainer forward keeps for
-// the backward).
+// The same step with output when c_t[j] is already known (kept by an earlier pass that ran this
+// very step on the same state): the update's last step and the output, the same bits as cpr_step.
 template <int NL, int G>
-__device__ __forceinline__ float cpr_step_wc(float (&s)[NL * kLeaf], const float (&k)[NL * kLeaf],
-                                             const float (&q)[NL * kLeaf], float v, float a, float b, float& w,
-                                             float& c) {
-  float u;
-  cpr_update<NL, G>(s, k, v, a, b, u, w, c);
+__device__ __forceinline__ float cpr_step_given_c(float (&s)[NL * kLeaf], const float (&k)[NL * kLeaf],
+                                                  const float (&q)[NL * kLeaf], float a, float c) {
+  cpr_apply(s, k, a, c);
   return pinned_dot<NL, G>(s, q);
 }
 

@@ -187,6 +187,13 @@ int gdn_chunk_rows(const int32_t* cu_seqlens_host, const int64_t* pos0_host, int
  *                layout gdn_chunk_rows describes (row 0 of a sequence is its initial state).
  *                For engine prefill this is scratch; for the trainer forward it is the stash the
  *                caller keeps.  chunk_state_rows must be >= gdn_chunk_rows_bound(N, num_seqs, C).
+ *   c_stash      NULL, or device fp32 scratch [N][H_v][d_v] (16-byte aligned).  When given, the
+ *                boundary pass runs every token (not only up to the last chunk start) and keeps
+ *                each token's write value c_t = b_t w_t there, and the output pass applies the
+ *                kept c_t instead of computing the prediction S^T k_t again: about a quarter less
+ *                arithmetic in the output pass for N*H_v*d_v*8 more bytes of traffic.  The
+ *                update is fed the very value it would compute, so o, final states and chunk
+ *                states are bit for bit the same with or without it.  Contents on return: c.
  * On return (stream order) each slot holds its sequence's final state and pos[slot] = p_i + L_i.
  * Launches the boundary pass, the output pass and a position update on `stream`.
  * events: NULL, or 3 hipEvent_t (as void*) recorded on `stream` before the boundary pass, between
@@ -194,13 +201,15 @@ int gdn_chunk_rows(const int32_t* cu_seqlens_host, const int64_t* pos0_host, int
 int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                 const int32_t* slot_ids, int32_t from_state,
                 const void* q, const void* k, const void* v, const float* a, const float* b,
-                void* o, float* chunk_states, int64_t chunk_state_rows, void* stream,
+                void* o, float* chunk_states, int64_t chunk_state_rows, float* c_stash, void* stream,
                 void* const* events);
 
 /* The trainer forward ([A]'s "trainer_fwd" case): gdn_prefill, bit for bit in o, final states
  * and chunk states, that also keeps what the backward would otherwise recompute:
  *   cw  device fp32 [2][N][H_v][d_v]: every token's c_t = b_t w_t (block 0) and
- *       w_t = v_t - a_t S_{t-1}^T k_t (block 1), as the pinned step computed them.
+ *       w_t = v_t - a_t S_{t-1}^T k_t (block 1), as the pinned step computed them.  Block 0
+ *       serves as gdn_prefill's c_stash: the boundary pass writes both blocks and the output
+ *       pass applies block 0.
  * Pass it to gdn_backward.  events as gdn_prefill. */
 int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                         const int32_t* slot_ids, int32_t from_state,
@@ -213,8 +222,8 @@ int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
  * in order (the per-layer table of section "Solving the linear-attention headache" calls this
  * evaluation "recurrent everywhere").  It does no second pass, so it suits batches whose
  * (sequence, value head, column) chains already fill the GPU; gdn_prefill's chunk-parallel
- * pass suits few long sequences.  Arguments as gdn_prefill, except that chunk_states may be NULL
- * (no stash is written; chunk_state_rows is then ignored).
+ * pass suits few long sequences.  Arguments as gdn_prefill, except that there is no c_stash and
+ * chunk_states may be NULL (no stash is written; chunk_state_rows is then ignored).
  * events: NULL, or 2 hipEvent_t recorded before and after the kernel. */
 int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                       const int32_t* slot_ids, int32_t from_state,

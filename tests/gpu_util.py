@@ -37,14 +37,14 @@ def sha(t: torch.Tensor) -> str:
 
 
 def prefill(x: gi.GdnInputs, chunk=None, pool=None, slot_ids=None, from_state=False, boundary=False,
-            chunk_states=None):
+            chunk_states=None, c_stash=True):
     """Run gdn_prefill over x (tensors moved to the GPU). Returns (o, pool, chunk_states)."""
     cpr = lib()
     xd = x.to("cuda")
     if pool is None:
         pool = cpr.StatePool(policy_of(x, chunk), max(x.num_seqs, 1), boundary=boundary)
     o, cs = cpr.gdn_prefill(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, slot_ids=slot_ids,
-                            from_state=from_state, chunk_states=chunk_states)
+                            from_state=from_state, chunk_states=chunk_states, c_stash=c_stash)
     torch.cuda.synchronize()
     return o, pool, cs
 

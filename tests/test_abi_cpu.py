@@ -159,16 +159,19 @@ def test_prefill_argument_errors_before_launch():
         # boundary without boundary_pos
         assert lib.gdn_state_alloc(ctypes.byref(pol), 3, fake, fake, nbytes, fake, None, ctypes.byref(h2)) == 1
         # too few chunk-state rows: bound(100 tokens, 2 seqs, C=64) = 1 + 4 = 5
-        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 4, None, None)
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 4, None, None, None)
         assert rc == 1 and b"chunk_state_rows" in lib.gdn_last_error()
-        rc = lib.gdn_prefill(h, fake, -1, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+        rc = lib.gdn_prefill(h, fake, -1, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None, None)
         assert rc == 1
-        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 2, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 2, fake, fake, fake, fake, fake, fake, fake, 99, None, None, None)
         assert rc == 1
-        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, None, fake, fake, fake, fake, fake, fake, 99, None, None)
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, None, fake, fake, fake, fake, fake, fake, 99, None, None, None)
         assert rc == 1
-        rc = lib.gdn_prefill(None, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+        rc = lib.gdn_prefill(None, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None, None)
         assert rc == 1
+        # a c stash that is not 16-byte aligned
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, fake + 4, None, None)
+        assert rc == 1 and b"c stash" in lib.gdn_last_error()
         rc = lib.gdn_decode_step(h, fake, -1, fake, fake, fake, fake, fake, fake, None, None)
         assert rc == 1
         rc = lib.gdn_decode_step(h, None, 3, fake, fake, fake, fake, fake, fake, None, None)

@@ -219,6 +219,51 @@ def test_fused_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dim", [16, 32, 64, 128])
+def test_c_stash_changes_no_bit(dim, io):
+    """gdn_prefill with the c stash (pass 1 runs every token and keeps its c, pass 2 applies the
+    kept c) against the same call without it: o, final states and chunk states bit for bit.  The
+    stash then holds every token's c, exactly the block the trainer forward keeps."""
+    cpr = lib()
+    x = gi.make_inputs(23, LENS, h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io=io)
+    say(f"c stash vs none dim={dim} io={io}")
+    stash = torch.full((x.total_tokens, x.h_v, x.dv), float("nan"), device="cuda")
+    o1, pool1, cs1 = prefill(x, c_stash=stash)
+    o2, pool2, cs2 = prefill(x, c_stash=None)
+    assert sha(o1) == sha(o2)
+    assert sha(pool1.state) == sha(pool2.state) and pool1.pos.tolist() == pool2.pos.tolist()
+    n = int(cpr.gdn_chunk_rows(x.cu_seqlens, 32)[-1])
+    assert sha(cs1[:n]) == sha(cs2[:n])
+    assert not bool(torch.isnan(stash).any())
+    xd = x.to("cuda")
+    pool3 = cpr.StatePool(policy_of(x), max(x.num_seqs, 1))
+    o3, cs3, cw = cpr.gdn_trainer_forward(pool3, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    torch.cuda.synchronize()
+    assert sha(cw[0]) == sha(stash) and sha(o3) == sha(o1) and sha(cs3[:n]) == sha(cs1[:n])
+
+
+@pytest.mark.parametrize("boundary", ["f32", "bf16"])
+def test_c_stash_continuation_changes_no_bit(boundary):
+    """The stash path continuing from a state (positions not on a chunk start), with both boundary
+    dtypes: the same bits as the path without the stash and as one run over all tokens."""
+    cpr = lib()
+    x = gi.make_inputs(24, [300], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    say(f"c stash continuation boundary={boundary}")
+    pol = cpr.Policy(2, 4, 128, 128, 64, "bf16", boundary=boundary)
+    results = []
+    for stash in (True, None):
+        pool = cpr.StatePool(pol, 1)
+        o1, _, _ = prefill(x.token_slice(0, 77), pool=pool, c_stash=stash)
+        o2, _, cs2 = prefill(x.token_slice(77, 300), pool=pool, from_state=True, c_stash=stash)
+        n = int(cpr.gdn_chunk_rows([0, 223], 64, [77])[-1])      # rows past n are never written
+        results.append((sha(torch.cat([o1, o2])), sha(pool.state), sha(cs2[:n])))
+    full = cpr.StatePool(pol, 1)
+    o_full, _, _ = prefill(x, pool=full)
+    assert results[0] == results[1]
+    assert results[0][0] == sha(o_full) and results[0][1] == sha(full.state)
+
+
 @pytest.mark.parametrize("chunk", [1, 16, 64, 1000])
 def test_fused_continuation_matches(chunk):
     cpr = lib()
