@@ -245,6 +245,8 @@ def main():
     pass2_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * 4) + bstate + c_bytes + N * P.h_v * P.dv * io \
         + B * P.h_v * P.dk * P.dv * 4
     cpr_bytes = pass1_bytes + pass2_bytes
+    kernels["boundary_pass"]["bytes"] = int(pass1_bytes)
+    kernels["output_pass"]["bytes"] = int(pass2_bytes)
     prefill_gbs = cpr_bytes / (ms_step * 1e-3) / 1e9
 
     # parity of the timed prefill output against the oracle (computed in the CPU leg below)
