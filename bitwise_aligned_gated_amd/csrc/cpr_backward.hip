@@ -52,7 +52,7 @@ struct ColCfg {
 template <int DK, int DV>
 struct alignas(16) ColLds {
   using Cfg = ColCfg<DK, DV>;
-  float k[Cfg::TT][DK];
+  float k[Cfg::TT][DK];                 // lane-interleaved rows (kq_slot)
   float q[Cfg::TT][DK];
   float v[Cfg::TT][Cfg::WG_COLS];
   float d[Cfg::TT][Cfg::WG_COLS];       // dO
@@ -72,10 +72,10 @@ __device__ __forceinline__ void stage(const BackwardArgs& A, ColLds<DK, DV>& L, 
     const int64_t e = ((t0 + tt) * A.h_k + kh) * DK + c8 * 8;
     float x[8];
     widen8<IO>(load_raw8<IO>(A.k, e), x);
-    store_f32x8(&L.k[tt][c8 * 8], x);
+    store_kq8<Cfg::G, Cfg::R>(&L.k[tt][0], c8 * 8, x);
     if constexpr (WITH_Q) {
       widen8<IO>(load_raw8<IO>(A.q, e), x);
-      store_f32x8(&L.q[tt][c8 * 8], x);
+      store_kq8<Cfg::G, Cfg::R>(&L.q[tt][0], c8 * 8, x);
     }
   }
   for (int u = threadIdx.x; u < n * (Cfg::WG_COLS / 8); u += Cfg::THREADS) {
@@ -159,9 +159,9 @@ __device__ __forceinline__ void adj_commit(const AdjRegs<DK, DV, IO>& R, ColLds<
     if (u < Cfg::TT * DK / 8) {
       float y[8];
       widen8<IO>(R.k[x], y);
-      store_f32x8(&L.k[tt][c8 * 8], y);
+      store_kq8<Cfg::G, Cfg::R>(&L.k[tt][0], c8 * 8, y);
       widen8<IO>(R.q[x], y);
-      store_f32x8(&L.q[tt][c8 * 8], y);
+      store_kq8<Cfg::G, Cfg::R>(&L.q[tt][0], c8 * 8, y);
     }
   }
 #pragma unroll
@@ -232,8 +232,8 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
     }
     for (int tt = n - 1; tt >= 0; --tt) {
       float kr[R], qr[R], gh[R];
-      load_f32x8(&L.k[tt][g * R], kr);
-      load_f32x8(&L.q[tt][g * R], qr);
+      lds_read_kq<G, R>(&L.k[tt][0], g, kr);
+      lds_read_kq<G, R>(&L.q[tt][0], g, qr);
       const float dO = L.d[tt][lc];
       const float2 ab = L.ab[tt];
 #pragma unroll
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) replay_kernel(Backw
     __syncthreads();
     for (int tt = 0; tt < n; ++tt) {
       float kr[R], u, ww, cc;
-      load_f32x8(&L.k[tt][g * R], kr);
+      lds_read_kq<G, R>(&L.k[tt][0], g, kr);
       const float2 ab = L.ab[tt];
       cpr_update<1, G>(s, kr, L.v[tt][lc], ab.x, ab.y, u, ww, cc);
       if (g == 0) {

@@ -139,6 +139,33 @@ __device__ __forceinline__ void store_f32x8(float* p, const float (&x)[8]) {
   reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// ---- lane-interleaved k / q tile rows in LDS -------------------------------------------------
+// A staged k (or q) row is kept lane-interleaved: lane g of a column reads its rows
+// [g R, g R + R) as R/4 float4s, and float4 i of lane g sits at slot i G + g, so the G lanes'
+// i-th reads cover G consecutive float4s (no LDS bank conflicts) instead of G strided ones.
+template <int G, int R>
+__device__ __forceinline__ int kq_slot(int row) {
+  return ((row % R) / 4 * G + row / R) * 4 + row % 4;
+}
+
+// Rows [r0, r0 + 8) of a lane-interleaved tile row (r0 a multiple of 8; R a multiple of 8, so the
+// eight rows belong to one lane and form two of its float4s).
+template <int G, int R>
+__device__ __forceinline__ void store_kq8(float* row, int r0, const float (&x)[8]) {
+  reinterpret_cast<float4*>(row + kq_slot<G, R>(r0))[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4*>(row + kq_slot<G, R>(r0 + 4))[0] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// Lane g's R rows of a lane-interleaved tile row.
+template <int G, int R>
+__device__ __forceinline__ void lds_read_kq(const float* row, int g, float (&x)[R]) {
+#pragma unroll
+  for (int i = 0; i < R / 4; ++i) {
+    const float4 f = reinterpret_cast<const float4*>(row)[i * G + g];
+    x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
+  }
+}
+
 // Record events[i] on the stream when the caller asked for timing events.
 inline hipError_t record_event(void* const* events, int i, hipStream_t stream) {
   if (events == nullptr || events[i] == nullptr) return hipSuccess;

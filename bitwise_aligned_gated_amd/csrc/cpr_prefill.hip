@@ -76,14 +76,6 @@ struct TileRegs {
   float ab[Cfg::AB_PER_T];
 };
 
-// A k (or q) row of the tile is kept lane-interleaved: lane g of a column reads its rows
-// [g R, g R + R) as R/4 float4s, and float4 i of lane g sits at slot i G + g, so the G lanes'
-// i-th reads cover G consecutive float4s (no LDS bank conflicts) instead of G strided ones.
-template <int G, int R>
-__device__ __forceinline__ int kq_slot(int row) {
-  return ((row % R) / 4 * G + row / R) * 4 + row % 4;
-}
-
 template <int DK, int DV, int MODE>
 struct TileLds {
   using Cfg = PassCfg<DK, DV, MODE>;
@@ -95,24 +87,6 @@ struct TileLds {
   float ws[keeps_c(MODE) ? Cfg::TT : 1][Cfg::WG_COLS];
   float2 ab[Cfg::TT];   // (a, b) of each token (stashed c: a only)
 };
-
-// Rows [r0, r0 + 8) of a lane-interleaved tile row (r0 a multiple of 8; R a multiple of 8, so the
-// eight rows belong to one lane and form two of its float4s).
-template <int G, int R>
-__device__ __forceinline__ void store_kq8(float* row, int r0, const float (&x)[8]) {
-  reinterpret_cast<float4*>(row + kq_slot<G, R>(r0))[0] = make_float4(x[0], x[1], x[2], x[3]);
-  reinterpret_cast<float4*>(row + kq_slot<G, R>(r0 + 4))[0] = make_float4(x[4], x[5], x[6], x[7]);
-}
-
-// Lane g's R rows of a lane-interleaved tile row.
-template <int G, int R>
-__device__ __forceinline__ void lds_read_kq(const float* row, int g, float (&x)[R]) {
-#pragma unroll
-  for (int i = 0; i < R / 4; ++i) {
-    const float4 f = reinterpret_cast<const float4*>(row)[i * G + g];
-    x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
-  }
-}
 
 // Fetch packed tokens [t0, t0 + n) (n <= TT) of key head kh / value head h into registers.
 // The tile's base addresses are uniform and each lane's offsets within a tile do not depend on
