@@ -118,34 +118,49 @@ struct AdjRegs {
   float ab[AU];
 };
 
-// Fetch tokens [t0, t0 + n) (packed indices, n <= TT); units past n are zero.
+// Fetch tokens [t0, t0 + n) (packed indices, n <= TT).  Tile bases are uniform and each lane's
+// offsets within a tile do not depend on t0; units past n keep what they held (no token reads
+// them) and are never read from memory.
 template <int DK, int DV, int IO>
 __device__ __forceinline__ void adj_fetch(const BackwardArgs& A, AdjRegs<DK, DV, IO>& R, int64_t t0, int n, int kh,
                                           int h, int col0) {
   using Cfg = ColCfg<DK, DV>;
+  constexpr int64_t ES = IO == IO_F32 ? 4 : 2;
   const int tid = threadIdx.x;
+  const char* kb = static_cast<const char*>(A.k) + (t0 * A.h_k + kh) * DK * ES;
+  const char* qb = static_cast<const char*>(A.q) + (t0 * A.h_k + kh) * DK * ES;
+  const char* vb = static_cast<const char*>(A.v) + ((t0 * A.h_v + h) * DV + col0) * ES;
+  const char* db = static_cast<const char*>(A.d_o) + ((t0 * A.h_v + h) * DV + col0) * ES;
+  const float* ga = A.a + t0 * A.h_v + h;
+  const float* gb = A.b + t0 * A.h_v + h;
 #pragma unroll
   for (int x = 0; x < AdjRegs<DK, DV, IO>::KU; ++x) {
     const int u = tid + x * Cfg::THREADS, tt = u / (DK / 8), c8 = u % (DK / 8);
-    const bool ok = u < Cfg::TT * DK / 8 && tt < n;
-    const int64_t e = ((t0 + tt) * A.h_k + kh) * DK + c8 * 8;
-    R.k[x] = ok ? load_raw8<IO>(A.k, e) : zero_raw8<IO>();
-    R.q[x] = ok ? load_raw8<IO>(A.q, e) : zero_raw8<IO>();
+    const uint32_t off = static_cast<uint32_t>(tt * A.h_k * DK + c8 * 8);
+    if (u < Cfg::TT * DK / 8 && tt < n) {
+      R.k[x] = load_raw8<IO>(kb, off);
+      R.q[x] = load_raw8<IO>(qb, off);
+    }
   }
 #pragma unroll
   for (int x = 0; x < AdjRegs<DK, DV, IO>::VU; ++x) {
     const int u = tid + x * Cfg::THREADS, tt = u / (Cfg::WG_COLS / 8), c8 = u % (Cfg::WG_COLS / 8);
-    const bool ok = u < Cfg::TT * Cfg::WG_COLS / 8 && tt < n;
-    const int64_t e = ((t0 + tt) * A.h_v + h) * DV + col0 + c8 * 8;
-    R.v[x] = ok ? load_raw8<IO>(A.v, e) : zero_raw8<IO>();
-    R.d[x] = ok ? load_raw8<IO>(A.d_o, e) : zero_raw8<IO>();
+    const uint32_t off = static_cast<uint32_t>(tt * A.h_v * DV + c8 * 8);
+    if (u < Cfg::TT * Cfg::WG_COLS / 8 && tt < n) {
+      R.v[x] = load_raw8<IO>(vb, off);
+      R.d[x] = load_raw8<IO>(db, off);
+    }
   }
 #pragma unroll
   for (int x = 0; x < AdjRegs<DK, DV, IO>::AU; ++x) {
     const int u = tid + x * Cfg::THREADS, tt = u % Cfg::TT;
-    const bool ok = u < 2 * Cfg::TT && tt < n;
-    const float* src = u < Cfg::TT ? A.a : A.b;
-    R.ab[x] = ok ? src[(t0 + tt) * A.h_v + h] : 0.0f;
+    const uint32_t off = static_cast<uint32_t>(tt * A.h_v);
+    if (tt < n) {                    // lanes [0, TT) fetch a, lanes [TT, 2 TT) fetch b
+      if (u < Cfg::TT)
+        R.ab[x] = ga[off];
+      else if (u < 2 * Cfg::TT)
+        R.ab[x] = gb[off];
+    }
   }
 }
 
@@ -215,7 +230,7 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
   if (brow0 + m.nrows < A.adj_rows) store_f32x8(A.adjoint + ((brow0 + m.nrows) * A.h_v + h) * plane + off, Gs);
   // tiles of TT tokens from the last one back: the tile ending at t1 starts at max(t1 - TT, 0);
   // the next tile's inputs are fetched into registers while this one runs
-  AdjRegs<DK, DV, IO> Rg;
+  AdjRegs<DK, DV, IO> Rg = {};
   if (m.len > 0) {
     const int t0 = m.len - Cfg::TT > 0 ? m.len - Cfg::TT : 0;
     adj_fetch<DK, DV, IO>(A, Rg, m.tok0 + t0, m.len - t0, kh, h, col0);
@@ -230,25 +245,42 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
       const int p0 = t0 - Cfg::TT > 0 ? t0 - Cfg::TT : 0;
       adj_fetch<DK, DV, IO>(A, Rg, m.tok0 + p0, t0 - p0, kh, h, col0);
     }
-    for (int tt = n - 1; tt >= 0; --tt) {
+    // token t0 + tt leaves G at dL/dS of position t0 + tt, a boundary when that is a multiple of
+    // C; rem counts down to it.  Each token's dc goes to LDS at the start of the next one, so that
+    // the lane-masked write does not split a token's own arithmetic.
+    int rem = __builtin_amdgcn_readfirstlane((t1 - 1) % C);
+    int64_t brow = brow0 + (t1 - 1) / C;
+    float pdc = 0.0f;
+    int ptt = -1;
+    auto token = [&](int tt) {
       float kr[R], qr[R], gh[R];
       lds_read_kq<G, R>(&L.k[tt][0], g, kr);
       lds_read_kq<G, R>(&L.q[tt][0], g, qr);
       const float dO = L.d[tt][lc];
       const float2 ab = L.ab[tt];
+      if (ptt >= 0 && g == 0) L.out0[ptt][lc] = pdc;
 #pragma unroll
       for (int r = 0; r < R; ++r) gh[r] = __builtin_fmaf(qr[r], dO, Gs[r]);
       const float dc = pinned_dot<1, G>(gh, kr);
       const float du = -ab.x * (ab.y * dc);
 #pragma unroll
       for (int r = 0; r < R; ++r) Gs[r] = __builtin_fmaf(kr[r], du, ab.x * gh[r]);
-      if (g == 0) L.out0[tt][lc] = dc;
-      const int t = t0 + tt;
-      if (t % C == 0) {                                      // G is now dL/dS at position t
-        const int64_t row = brow0 + t / C;
-        if (row < A.adj_rows) store_f32x8(A.adjoint + (row * A.h_v + h) * plane + off, Gs);
+      pdc = dc;
+      ptt = tt;
+      if (rem == 0) {                                        // G is now dL/dS at a chunk boundary
+        if (brow < A.adj_rows) store_f32x8(A.adjoint + (brow * A.h_v + h) * plane + off, Gs);
+        rem = C;
+        --brow;
       }
+      --rem;
+    };
+    if (n == Cfg::TT) {                                      // full tile: unrolled, immediate offsets
+#pragma unroll
+      for (int tt = Cfg::TT - 1; tt >= 0; --tt) token(tt);
+    } else {
+      for (int tt = n - 1; tt >= 0; --tt) token(tt);
     }
+    if (g == 0) L.out0[ptt][lc] = pdc;
     __syncthreads();
     store_cols<DK, DV>(A, L.out0, A.dc, m.tok0 + t0, n, h, col0);
     if (more) adj_commit<DK, DV, IO>(Rg, L);
