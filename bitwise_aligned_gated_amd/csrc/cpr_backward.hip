@@ -355,7 +355,31 @@ struct MCfg {
   static constexpr int NT = D / 16;             // 16-wide tiles across D
   static constexpr int HR = D < 64 ? D : 64;    // rows of a D x D matrix (and of C^T) staged at once
   static constexpr int NH = D / HR;             // staged parts per matrix
+  // With DIRECT staging (D = 128, bf16 io) the S0 / G_end rows are loaded straight into LDS,
+  // 64 lanes x 16 bytes = two rows per load; pairs of rows sit PP floats apart, so the four rows
+  // one MFMA operand read touches (r, r + 4, r + 8, r + 12) start 16 banks apart.  Otherwise rows
+  // go through registers with a padded row stride SB (the fp32-io kernel has no registers to
+  // spare for the wider dO loads and the direct path together).
+  static constexpr int PP = 2 * D + 8;
+  static_assert(HR / 2 * PP <= HR * SB || D != 128, "the direct layout fits the padded one");
 };
+
+template <int D, int IO>
+constexpr bool direct_staging() {
+  return D == 128 && IO == IO_BF16;
+}
+
+// Offset of row r of the staged matrix part, and of row r0 + e from row r0 (r0 even, e < 4).
+template <int D, bool DIRECT>
+__device__ __forceinline__ int mrow(int r) {
+  using M = MCfg<D>;
+  if constexpr (DIRECT) return (r >> 1) * M::PP + (r & 1) * D;
+  return r * M::SB;
+}
+template <int D, bool DIRECT>
+constexpr int mrow_step(int e) {
+  return DIRECT ? (e >> 1) * MCfg<D>::PP + (e & 1) * D : e * MCfg<D>::SB;
+}
 
 // LDS of the chunk-gradient kernel: the products with S0 and G_end stream those matrices (and
 // C^T) in parts of HR rows; the decay-masked products then hold A1, A2 and K (later Q).
@@ -405,16 +429,29 @@ __device__ __forceinline__ double block_sum_f64(double x, double* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// Stage rows [j0, j0 + HR) of a D x D fp32 matrix in [dv][dk] layout into S.u.p.mat, and the same
+// Stage rows [j0, j0 + HR) of a D x D fp32 matrix in [dv][dk] layout into S.u.p.mat (row r at
+// mrow(r)), and the same
 // rows of C^T (C [t][j] of this chunk, zero past its n tokens) into S.u.p.ct.
-template <int D>
+template <int D, bool DIRECT>
 __device__ __forceinline__ void stage_part(MLds<D>& S, const float* mat, const float* cc, int64_t tok, int n,
                                            int h_v, int h, int j0) {
   using M = MCfg<D>;
-  for (int e = threadIdx.x; e < M::HR * D / 4; e += 256) {
-    const int r = e / (D / 4), c4 = e % (D / 4);
-    *reinterpret_cast<float4*>(&S.u.p.mat[r * M::SB + 4 * c4]) =
-        reinterpret_cast<const float4*>(mat + static_cast<int64_t>(j0 + r) * D)[c4];
+  if constexpr (DIRECT) {
+    // wave w loads row pairs w, w + 4, ...: lane l takes 16 bytes of row 2 p + l / 32, which the
+    // load writes to LDS at the pair's base + 16 l
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float* src = mat + static_cast<int64_t>(j0 + (lane >> 5)) * D + 4 * (lane & 31);
+#if defined(__HIP_DEVICE_COMPILE__)   // a device builtin; the host pass only needs the declaration
+#pragma unroll 1
+    for (int p = wave; p < M::HR / 2; p += 4)
+      __builtin_amdgcn_global_load_lds(src + static_cast<int64_t>(2 * p) * D, &S.u.p.mat[p * M::PP], 16, 0, 0);
+#endif
+  } else {
+    for (int e = threadIdx.x; e < M::HR * D / 4; e += 256) {
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      *reinterpret_cast<float4*>(&S.u.p.mat[r * M::SB + 4 * c4]) =
+          reinterpret_cast<const float4*>(mat + static_cast<int64_t>(j0 + r) * D)[c4];
+    }
   }
   for (int e = threadIdx.x; e < M::L * M::HR / 4; e += 256) {
     const int t = e / (M::HR / 4), c4 = e % (M::HR / 4);
@@ -425,6 +462,7 @@ __device__ __forceinline__ void stage_part(MLds<D>& S, const float* mat, const f
     S.u.p.ct[(4 * c4 + 2) * M::SC + t] = x.z;
     S.u.p.ct[(4 * c4 + 3) * M::SC + t] = x.w;
   }
+  if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into LDS have landed
 }
 
 // K or Q rows of the chunk (io dtype, zero past its n tokens) into S.u.m.kq.
@@ -443,6 +481,7 @@ template <int D, int IO>
 __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
   using M = MCfg<D>;
   constexpr int NT = M::NT, SB = M::SB, SC = M::SC, SA = M::SA, LT = M::L, HR = M::HR, NH = M::NH;
+  constexpr bool DS = direct_staging<D, IO>();
   __shared__ MLds<D> S;
   __shared__ int64_t red[6];
   const int64_t w = blockIdx.x / A.h_k;
@@ -501,18 +540,19 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
     for (int part = 0; part < NH; ++part) {
       const int j0 = part * HR;
       __syncthreads();
-      stage_part<D>(S, s0, A.cc, tok, L, A.h_v, h, j0);
+      stage_part<D, DS>(S, s0, A.cc, tok, L, A.h_v, h, j0);
       __syncthreads();
       for (int e = tid; e < HR * D / 4; e += 256) {
         const int r = e / (D / 4), c4 = e % (D / 4);
         const float4 gv = reinterpret_cast<const float4*>(g0 + static_cast<int64_t>(j0 + r) * D)[c4];
-        const float4 sv = *reinterpret_cast<const float4*>(&S.u.p.mat[r * SB + 4 * c4]);
+        const float4 sv = *reinterpret_cast<const float4*>(&S.u.p.mat[mrow<D, DS>(r) + 4 * c4]);
         hp += static_cast<double>(gv.x) * sv.x + static_cast<double>(gv.y) * sv.y +
               static_cast<double>(gv.z) * sv.z + static_cast<double>(gv.w) * sv.w;
       }
 #pragma unroll 1
       for (int p = 0; p < HR / 16; ++p) {
         const int kl = 16 * p + 4 * lgp;                     // k within the part
+        const int mk = mrow<D, DS>(kl);
         float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f), c4 = o4;
         if (rv) {
           o4 = load4<IO>(A.d_o, ((tok + row) * A.h_v + h) * D + j0 + kl);
@@ -525,7 +565,7 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
           const float aq = ao * fq, ak = au * fu;
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            const float bs = S.u.p.mat[k * SB + 16 * n + lj];
+            const float bs = S.u.p.mat[mk + mrow_step<D, DS>(e) + 16 * n + lj];
             acc_dq[n] = mfma4(aq, bs, acc_dq[n]);
             acc_dk[n] = mfma4(ak, bs, acc_dk[n]);
           }
@@ -544,16 +584,18 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
     for (int part = 0; part < NH; ++part) {
       const int j0 = part * HR;
       __syncthreads();
-      stage_part<D>(S, ge, A.cc, tok, L, A.h_v, h, j0);
+      stage_part<D, DS>(S, ge, A.cc, tok, L, A.h_v, h, j0);
       __syncthreads();
 #pragma unroll 1
       for (int p = 0; p < HR / 16; ++p) {
+        const int mk = mrow<D, DS>(16 * p + 4 * lgp);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = 16 * p + 4 * lgp + e;
           const float ac = S.u.p.ct[k * SC + row] * fc;
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc_dk[n] = mfma4(ac, S.u.p.mat[k * SB + 16 * n + lj], acc_dk[n]);
+          for (int n = 0; n < NT; ++n)
+            acc_dk[n] = mfma4(ac, S.u.p.mat[mk + mrow_step<D, DS>(e) + 16 * n + lj], acc_dk[n]);
         }
       }
     }
