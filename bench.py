@@ -159,6 +159,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-trainer", action="store_true", help="skip the trainer forward+backward workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the oracle")
+    ap.add_argument("--no-long", action="store_true", help="skip the single 65536-token sequence")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB fp32 copy kernel (torch.neg) 3 times, a known-size "
@@ -324,6 +325,43 @@ def main():
         del cpool, oc
     del cws
 
+    # one 65536-token sequence (the invariance workload's X): where pass 1's chain of sequential
+    # steps is the critical path, the two-pass prefill against the one-pass variant; context only
+    long_seq = None
+    if not args.no_long:
+        xl = gi.config4_x(device=dev)
+        NL = xl.total_tokens
+        cul = torch.from_numpy(xl.cu_seqlens).to(dev)
+        idl = torch.zeros(1, dtype=torch.int32, device=dev)
+        ol = torch.empty((NL, P.h_v, P.dv), dtype=torch.bfloat16, device=dev)
+        csl = torch.empty((cpr.gdn_chunk_rows_bound(NL, 1, P.chunk), P.h_v, P.dv, P.dk), dtype=torch.float32,
+                          device=dev)
+        stl = torch.empty((NL, P.h_v, P.dv), dtype=torch.float32, device=dev)
+        lpool = cpr.StatePool(P, 1, device=dev)
+        runs = {"two_pass": lambda ev: cpr.gdn_prefill(lpool, cul, xl.q, xl.k, xl.v, xl.a, xl.b, slot_ids=idl, o=ol,
+                                                       chunk_states=csl, c_stash=stl, events=ev),
+                "one_pass": lambda ev: cpr.gdn_prefill_fused(lpool, cul, xl.q, xl.k, xl.v, xl.a, xl.b, slot_ids=idl,
+                                                             o=ol, events=ev)}
+        long_seq = {"workload": f"one sequence of {NL} tokens, the prefill head layout"}
+        digests = {}
+        for label, run in runs.items():
+            nev = 3 if label == "two_pass" else 2
+            run(None)
+            lev = [[hip.event() for _ in range(nev)] for _ in range(3)]
+            torch.cuda.synchronize()
+            for e in lev:
+                run(e)
+            torch.cuda.synchronize()
+            k_ms = [hip.ms(e[0], e[-1]) for e in lev]
+            entry = {"ms": round(statistics.median(k_ms), 4), "tok_s": round(NL / (statistics.median(k_ms) * 1e-3), 1)}
+            if label == "two_pass":
+                entry["boundary_pass_ms"] = round(statistics.median(hip.ms(e[0], e[1]) for e in lev), 4)
+                entry["output_pass_ms"] = round(statistics.median(hip.ms(e[1], e[2]) for e in lev), 4)
+            long_seq[label] = entry
+            digests[label] = hashlib.sha256(ol.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
+        long_seq["bitwise_equal"] = digests["two_pass"] == digests["one_pass"]
+        del xl, ol, csl, stl, lpool
+
     # ---------------------------------------------------------------- decode workload
     decode = None
     if not args.no_decode:
@@ -470,7 +508,8 @@ def main():
                     "cpr_bytes": int(cpr_bytes), "hbm_frac": round(prefill_gbs / HBM_PEAK_GBS, 4),
                     "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                 for k, v in kernels.items()},
-                    "without_c_stash": no_stash, "one_pass_variant": fused, "chunked_matrix_core": chunked},
+                    "without_c_stash": no_stash, "one_pass_variant": fused, "chunked_matrix_core": chunked,
+                    "long_sequence": long_seq},
         "roofline": roofline,
         "decode": decode,
         "trainer": trainer,

@@ -217,15 +217,26 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
         }
       }
     };
-    auto token = [&](int tt) {
-      float kr[R], qr[R];
-      lds_read_kq<G, R>(&L.k[tt][0], g, kr);
-      if constexpr (OUT) lds_read_kq<G, R>(&L.q[tt][0], g, qr);
-      const float2 ab = L.ab[tt];
-      hand_over();
-      float vv[NC];
+    // A token's inputs from the tile.  Pass 1 reads token tt + 1's while token tt computes, so
+    // that a lone sequence's chain does not wait on LDS at every token (the one-pass variant
+    // would need more registers than five waves per SIMD allow).
+    struct In {
+      float kr[R], qr[R], vv[NC];
+      float2 ab;
+    };
+    auto read_in = [&](int tt, In& x) {
+      lds_read_kq<G, R>(&L.k[tt][0], g, x.kr);
+      if constexpr (OUT) lds_read_kq<G, R>(&L.q[tt][0], g, x.qr);
+      x.ab = L.ab[tt];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) vv[c] = L.v[tt][cp * NC + c];
+      for (int c = 0; c < NC; ++c) x.vv[c] = L.v[tt][cp * NC + c];
+    };
+    auto token = [&](int tt, In& x) {
+      float (&kr)[R] = x.kr;
+      float (&qr)[R] = x.qr;
+      float (&vv)[NC] = x.vv;
+      const float2 ab = x.ab;
+      hand_over();
       float o[NC];
       if constexpr (MODE == kOutputC) {                    // vv holds the stashed c
 #pragma unroll
@@ -271,11 +282,36 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
         }
       }
     };
-    if (!is_wide(MODE) && n == Cfg::TT) {    // one-leaf lanes, full tile: unrolled, immediate offsets
+    if constexpr (MODE == kBoundary || MODE == kBoundaryC) {
+      In nx;
+      read_in(0, nx);
+      if (n == Cfg::TT) {                      // full tile: unrolled, immediate offsets
 #pragma unroll
-      for (int tt = 0; tt < Cfg::TT; ++tt) token(tt);
+        for (int tt = 0; tt < Cfg::TT; ++tt) {
+          In cur = nx;
+          if (tt + 1 < Cfg::TT) read_in(tt + 1, nx);
+          token(tt, cur);
+        }
+      } else {
+        for (int tt = 0; tt < n; ++tt) {
+          In cur = nx;
+          if (tt + 1 < n) read_in(tt + 1, nx);
+          token(tt, cur);
+        }
+      }
+    } else if (!is_wide(MODE) && n == Cfg::TT) {   // one-leaf lanes, full tile: unrolled
+#pragma unroll
+      for (int tt = 0; tt < Cfg::TT; ++tt) {
+        In cur;
+        read_in(tt, cur);
+        token(tt, cur);
+      }
     } else {
-      for (int tt = 0; tt < n; ++tt) token(tt);
+      for (int tt = 0; tt < n; ++tt) {
+        In cur;
+        read_in(tt, cur);
+        token(tt, cur);
+      }
     }
     hand_over();
     ptt = -1;
