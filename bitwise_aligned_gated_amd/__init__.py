@@ -17,7 +17,7 @@ __all__ = [
     "LIB_PATH", "GdnError", "Policy", "StatePool", "gdn_policy_digest", "gdn_policy_check",
     "gdn_semantic_digest", "gdn_deployment_digest",
     "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
-    "gdn_prefill_fused", "gdn_decode_step", "gdn_state_resync", "gdn_backward", "gdn_backward_workspace_bytes",
+    "gdn_prefill_fused", "gdn_prefill_overlapped", "gdn_decode_step", "gdn_state_resync", "gdn_backward", "gdn_backward_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_chunked_workspace_bytes", "GDN_CHUNKED_NATIVE", "GDN_CHUNKED_R2",
     "gdn_trainer_forward",
     "EXPORTS",
@@ -68,6 +68,7 @@ _SIGS = {
     "gdn_chunk_rows": (ctypes.c_int, [_P, _P, _i32, _i32, _P]),
     "gdn_prefill": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P, _P]),
     "gdn_prefill_fused": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
+    "gdn_prefill_overlapped": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P]),
     "gdn_decode_step": (ctypes.c_int, [_P, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
     "gdn_state_resync": (ctypes.c_int, [_P, _P, _i32, _P]),
     "gdn_backward_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i64, _i32]),
@@ -301,6 +302,23 @@ def gdn_prefill_fused(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None,
                                   q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
                                   o.data_ptr(), None if chunk_states is None else chunk_states.data_ptr(), rows,
                                   _stream_ptr(stream), _events(events, 2)))
+    return o, chunk_states
+
+
+def gdn_prefill_overlapped(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                           o=None, chunk_states=None, stream=None, events=None):
+    """Overlapped prefill (C gdn_prefill_overlapped): pass 1 and the chunk outputs in one launch;
+    bitwise equal to gdn_prefill.  chunk_states None: no stash.  Returns (o, chunk_states)."""
+    P, dev = pool.policy, pool.device
+    N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
+    rows = 0
+    if chunk_states is not None:
+        _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+        rows = chunk_states.shape[0]
+    _check(_lib.gdn_prefill_overlapped(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
+                                       q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                       o.data_ptr(), None if chunk_states is None else chunk_states.data_ptr(),
+                                       rows, _stream_ptr(stream), _events(events, 2)))
     return o, chunk_states
 
 

@@ -370,23 +370,25 @@ int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
                       chunk_state_rows, cw, w, stream, events, "gdn_trainer_forward");
 }
 
-int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                      const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
-                      const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
-                      void* stream, void* const* events) {
-  if (st == nullptr) return fail(GDN_EINVAL, "gdn_prefill_fused: state handle is NULL");
-  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill_fused: negative sizes");
+// The single-launch prefills: the one-pass kernel, or pass 1 with the chunk outputs overlapped
+// (chunks up to the overlap kernel's limit; longer chunks take the one-pass kernel, same bits).
+static int onepass_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                        const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                        void* stream, void* const* events, bool overlap, const char* who) {
+  if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", who);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", who);
   if (total_tokens >= (int64_t(1) << 31))
-    return fail(GDN_EINVAL, "gdn_prefill_fused: total_tokens must fit int32 cu_seqlens");
+    return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", who);
   if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill_fused: cu_seqlens/slot_ids NULL");
-  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "gdn_prefill_fused: from_state must be 0 or 1");
+    return fail(GDN_EINVAL, "%s: cu_seqlens/slot_ids NULL", who);
+  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "%s: from_state must be 0 or 1", who);
   if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr || o == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill_fused: token tensor NULL");
+    return fail(GDN_EINVAL, "%s: token tensor NULL", who);
   const gdn_policy& P = st->policy;
   const int64_t bound = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
   if (chunk_states != nullptr && chunk_state_rows < bound)
-    return fail(GDN_EINVAL, "gdn_prefill_fused: chunk_state_rows %lld < bound %lld", (long long)chunk_state_rows,
+    return fail(GDN_EINVAL, "%s: chunk_state_rows %lld < bound %lld", who, (long long)chunk_state_rows,
                 (long long)bound);
   cpr::PrefillArgs A;
   A.cu = cu_seqlens;
@@ -406,9 +408,27 @@ int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs
   A.c_stash = nullptr;
   A.w_stash = nullptr;
   A.events = events;
-  const hipError_t e = cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "gdn_prefill_fused launch");
+  const hipError_t e = overlap && P.chunk <= cpr::overlap_max_chunk()
+                           ? cpr::launch_prefill_overlap(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream))
+                           : cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, who);
   return ok();
+}
+
+int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                      const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                      void* stream, void* const* events) {
+  return onepass_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, chunk_states,
+                      chunk_state_rows, stream, events, false, "gdn_prefill_fused");
+}
+
+int gdn_prefill_overlapped(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                           const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                           const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                           void* stream, void* const* events) {
+  return onepass_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, chunk_states,
+                      chunk_state_rows, stream, events, true, "gdn_prefill_overlapped");
 }
 
 int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const void* q, const void* k,

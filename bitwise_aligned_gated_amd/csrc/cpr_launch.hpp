@@ -12,6 +12,9 @@ struct BackwardArgs;
 // Each returns hipErrorInvalidValue for a (dk, dv, io) combination that is not compiled in.
 hipError_t launch_prefill(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
 hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+// Pass 1 and the chunk outputs in one workgroup per column group (chunks up to overlap_max_chunk()).
+hipError_t launch_prefill_overlap(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+int overlap_max_chunk();
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream);

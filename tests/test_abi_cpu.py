@@ -172,6 +172,14 @@ def test_prefill_argument_errors_before_launch():
         # a c stash that is not 16-byte aligned
         rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, fake + 4, None, None)
         assert rc == 1 and b"c stash" in lib.gdn_last_error()
+        # the single-launch prefills share the prefill checks
+        for fn in (lib.gdn_prefill_fused, lib.gdn_prefill_overlapped):
+            rc = fn(None, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+            assert rc == 1 and b"state handle" in lib.gdn_last_error()
+            rc = fn(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 4, None, None)
+            assert rc == 1 and b"chunk_state_rows" in lib.gdn_last_error()
+            rc = fn(h, fake, 2, 100, fake, 3, fake, fake, fake, fake, fake, fake, fake, 99, None, None)
+            assert rc == 1 and b"from_state" in lib.gdn_last_error()
         rc = lib.gdn_decode_step(h, fake, -1, fake, fake, fake, fake, fake, fake, None, None)
         assert rc == 1
         rc = lib.gdn_decode_step(h, None, 3, fake, fake, fake, fake, fake, fake, None, None)

@@ -208,6 +208,17 @@ def test_long_sequence_invariant_to_chunk(long_x, chunk):
     assert sha(o) == so and sha(pool.state) == sS
 
 
+def test_long_sequence_overlapped(long_x):
+    x, so, sS, _ = long_x
+    say("long: overlapped prefill")
+    cpr = lib()
+    pool = cpr.StatePool(policy_of(x), 1)
+    xd = x.to("cuda")
+    o, _ = cpr.gdn_prefill_overlapped(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    torch.cuda.synchronize()
+    assert sha(o) == so and sha(pool.state) == sS
+
+
 def test_long_sequence_decoded_65536_steps(long_x):
     x, so, sS, _ = long_x
     say("long: 65536 decode steps")

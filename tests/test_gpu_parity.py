@@ -187,7 +187,7 @@ def test_repeat_runs_are_identical():
         assert [sha(prefill(x)[0])] == first
 
 
-def _fused(x, chunk=None, pool=None, from_state=False, stash=True):
+def _fused(x, chunk=None, pool=None, from_state=False, stash=True, overlapped=False):
     cpr = lib()
     xd = x.to("cuda")
     if pool is None:
@@ -196,8 +196,8 @@ def _fused(x, chunk=None, pool=None, from_state=False, stash=True):
     if stash:
         rows = cpr.gdn_chunk_rows_bound(x.total_tokens, x.num_seqs, pool.policy.chunk)
         cs = torch.full((max(rows, 1), x.h_v, x.dv, x.dk), float("nan"), device="cuda")
-    o, cs = cpr.gdn_prefill_fused(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, from_state=from_state,
-                                  chunk_states=cs)
+    run = cpr.gdn_prefill_overlapped if overlapped else cpr.gdn_prefill_fused
+    o, cs = run(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, from_state=from_state, chunk_states=cs)
     torch.cuda.synchronize()
     return o, pool, cs
 
@@ -278,5 +278,46 @@ def test_fused_continuation_matches(chunk):
     rows = cpr.gdn_chunk_rows([0, 223], chunk, [77]).numpy()
     full_rows = cpr.gdn_chunk_rows([0, 300], chunk).numpy()
     # rows after the hand-over state are the same chunk-start states as in one run
+    k0 = int(full_rows[-1]) - (int(rows[-1]) - 1)
+    assert sha(cs2[1:int(rows[-1])]) == sha(cs_full[k0:int(full_rows[-1])])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dim", [16, 32, 64, 128])
+def test_overlapped_prefill_is_bitwise_equal_to_two_pass(dim, io):
+    """The overlapped prefill (pass 1 and the chunk outputs in one workgroup) against gdn_prefill:
+    o, final states, positions and chunk-start rows bit for bit, nothing written past the rows."""
+    cpr = lib()
+    x = gi.make_inputs(26, LENS, h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io=io)
+    say(f"overlapped vs two-pass dim={dim} io={io}")
+    o2, pool2, cs2 = prefill(x)
+    o1, pool1, cs1 = _fused(x, overlapped=True)
+    assert sha(o1) == sha(o2)
+    assert sha(pool1.state) == sha(pool2.state) and pool1.pos.tolist() == pool2.pos.tolist()
+    n = int(cpr.gdn_chunk_rows(x.cu_seqlens, 32)[-1])
+    assert sha(cs1[:n]) == sha(cs2[:n])
+    assert bool(torch.isnan(cs1[n:]).all())
+    o3, pool3, _ = _fused(x, stash=False, overlapped=True)
+    assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
+
+
+@pytest.mark.parametrize("boundary", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [1, 16, 64, 100])
+def test_overlapped_continuation_matches(chunk, boundary):
+    """Continuing from a state at a position off the chunk grid, both boundary dtypes; a chunk
+    above 64 tokens takes the one-pass kernel and must give the same bits as well."""
+    cpr = lib()
+    x = gi.make_inputs(27, [300], h_k=2, h_v=4, dk=128, dv=128, chunk=chunk, io="bf16")
+    say(f"overlapped continuation C={chunk} boundary={boundary}")
+    pol = cpr.Policy(2, 4, 128, 128, chunk, "bf16", boundary=boundary)
+    full = cpr.StatePool(pol, 1)
+    o_full, _, cs_full = prefill(x, pool=full)
+    pool = cpr.StatePool(pol, 1)
+    o1, _, _ = _fused(x.token_slice(0, 77), pool=pool, overlapped=True)
+    o2, _, cs2 = _fused(x.token_slice(77, 300), pool=pool, from_state=True, overlapped=True)
+    assert sha(torch.cat([o1, o2])) == sha(o_full)
+    assert sha(pool.state) == sha(full.state) and int(pool.pos[0]) == 300
+    rows = cpr.gdn_chunk_rows([0, 223], chunk, [77]).numpy()
+    full_rows = cpr.gdn_chunk_rows([0, 300], chunk).numpy()
     k0 = int(full_rows[-1]) - (int(rows[-1]) - 1)
     assert sha(cs2[1:int(rows[-1])]) == sha(cs_full[k0:int(full_rows[-1])])
