@@ -232,12 +232,12 @@ int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs
                       void* const* events);
 
 /* Overlapped prefill: the same results as gdn_prefill, bit for bit, from a single launch in
- * which each (sequence, value head, column group) workgroup runs pass 1 on one wave and produces
- * the outputs of every chunk pass 1 has finished on a second wave of the same workgroup, while
- * pass 1 goes on (section "Solving the linear-attention headache": the parallel fill-in of a
- * chunk's outputs needs only the state at its start).  It suits a few long sequences, where pass
- * 1 alone cannot fill the GPU and pass 2 would otherwise run after it.  The state entering each
- * chunk and its tokens' write values c_t pass between the two waves through LDS, so nothing is
+ * which each (sequence, value head, column group) workgroup runs pass 1 on some of its waves and
+ * produces the outputs of every chunk pass 1 has finished on other waves of the same workgroup,
+ * while pass 1 goes on (section "Solving the linear-attention headache": the parallel fill-in of
+ * a chunk's outputs needs only the state at its start).  It suits a few long sequences, where
+ * pass 1 alone cannot fill the GPU and pass 2 would otherwise run after it.  The state entering
+ * each chunk and its tokens' write values c_t pass between the waves through LDS, so nothing is
  * written to HBM for the hand-off.  Chunks above 64 tokens take the one-pass kernel instead (the
  * same bits).  Arguments as gdn_prefill_fused.  events: NULL, or 2 hipEvent_t recorded before and
  * after the kernel. */
