@@ -194,7 +194,7 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- prefill (the timed step)
-    x = gi.config1(device=dev)
+    x = gi.prefill_5x2048(device=dev)
     P = cpr.Policy(x.h_k, x.h_v, x.dk, x.dv, x.chunk, x.io)
     N, B = x.total_tokens, x.num_seqs
     spool = cpr.StatePool(P, B, device=dev)
@@ -330,7 +330,7 @@ def main():
     # variants; context only
     long_seq = None
     if not args.no_long:
-        xl = gi.config4_x(device=dev)
+        xl = gi.long_sequence(device=dev)
         NL = xl.total_tokens
         cul = torch.from_numpy(xl.cu_seqlens).to(dev)
         idl = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -368,12 +368,12 @@ def main():
     # ---------------------------------------------------------------- decode workload
     decode = None
     if not args.no_decode:
-        prompts = gi.config2_prompts(device=dev)
+        prompts = gi.decode_prompts(device=dev)
         nb = prompts.num_seqs
         dpool = cpr.StatePool(P, nb, device=dev)
         cpr.gdn_prefill(dpool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
         del prompts
-        toks = [gi.config2_decode_tokens(s, nb, device=dev) for s in range(args.decode_steps)]
+        toks = [gi.decode_tokens(s, nb, device=dev) for s in range(args.decode_steps)]
         od = torch.empty((nb, P.h_v, P.dv), dtype=torch.bfloat16, device=dev)
         dids = torch.arange(nb, dtype=torch.int32, device=dev)
         wpool = cpr.StatePool(P, nb, device=dev)          # warm-up on a copy; the real states stay put
@@ -413,7 +413,7 @@ def main():
     # ---------------------------------------------------------------- trainer forward + backward
     trainer = None
     if not args.no_trainer:
-        xt = gi.config3(device=dev)
+        xt = gi.trainer_10240(device=dev)
         ct = gi.make_cotangents(xt, 69, device=dev)
         Nt, Bt = xt.total_tokens, xt.num_seqs
         tpool = cpr.StatePool(P, Bt, device=dev)
@@ -451,8 +451,9 @@ def main():
         grad_ms = avg([(b[2], b[3]) for _, b in tev])
         fa, _, fg = backward_flops([int(l) for l in xt.lengths], P.h_v, P.dk, P.dv, P.chunk)
         trainer = {
-            "workload": f"trainer forward+backward, {Nt} tokens packed varlen {xt.lengths.tolist()} (config 3 "
-                        "layout); the forward keeps its chunk states and every token's c and w for the backward",
+            "workload": f"trainer forward+backward, {Nt} tokens packed varlen {xt.lengths.tolist()} (H_k=16, "
+                        "H_v=32, dk=dv=128, chunk=64, bf16 io); the forward keeps its chunk states and every "
+                        "token's c and w for the backward",
             "ms_per_step": round(t_ms, 4), "forward_ms": round(fwd_ms, 4),
             "backward_ms": round(adj_ms + rep_ms + grad_ms, 4),
             "kernels": {"adjoint": {"avg_ms": round(adj_ms, 4), "tflops": round(fa / (adj_ms * 1e-3) / 1e12, 3),
@@ -504,7 +505,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "prefill 5x2048 (config 1): H_k=16, H_v=32, dk=dv=128, chunk=64, "
+        "config": {"workload": "prefill 5x2048: H_k=16, H_v=32, dk=dv=128, chunk=64, "
                                "bf16 q/k/v/o, fp32 a/b/state",
                    "global_batch": B, "seq_len": int(x.lengths[0]), "parallelism": "single-gpu"},
         "prefill": {"boundary_pass_ms": round(p1_ms, 4), "output_pass_ms": round(p2_ms, 4),

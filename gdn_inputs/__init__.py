@@ -28,8 +28,8 @@ import torch
 
 __all__ = [
     "GdnInputs", "make_inputs", "f32_to_bf16_bits", "bf16_bits_to_f32", "cu_from_lengths",
-    "config0", "config1", "config2_prompt_lengths", "config2_prompts", "config2_decode_tokens",
-    "config3_lengths", "config3", "config4_x", "config4_lengths", "config4_batch",
+    "tiny_fp32", "prefill_5x2048", "decode_prompt_lengths", "decode_prompts", "decode_tokens",
+    "trainer_lengths", "trainer_10240", "long_sequence", "neighbour_lengths", "long_in_batch",
 ]
 
 # purposes, so that streams never collide
@@ -212,35 +212,35 @@ def make_cotangents(x: GdnInputs, seed: int, with_d_state: bool = True, with_s0:
 BIG = dict(h_k=16, h_v=32, dk=128, dv=128, chunk=64)
 
 
-def config0(device="cpu") -> GdnInputs:
+def tiny_fp32(device="cpu") -> GdnInputs:
     """Tiny fp32 case: one 256-token sequence, 2 heads, d_k = d_v = 16, chunk 64."""
     return make_inputs(0, [256], h_k=2, h_v=2, dk=16, dv=16, chunk=64, io="f32",
                        name="tiny-fp32-1x256", device=device)
 
 
-def config1(num_seqs: int = 5, seqlen: int = 2048, device="cpu") -> GdnInputs:
+def prefill_5x2048(num_seqs: int = 5, seqlen: int = 2048, device="cpu") -> GdnInputs:
     """Rollout prefill: 5 sequences x 2048 tokens, bf16 q/k/v."""
     return make_inputs(1, [seqlen] * num_seqs, io="bf16", name=f"prefill-{num_seqs}x{seqlen}",
                        device=device, **BIG)
 
 
-def config2_prompt_lengths(num_seqs: int = 256, max_len: int = 2048) -> np.ndarray:
+def decode_prompt_lengths(num_seqs: int = 256, max_len: int = 2048) -> np.ndarray:
     return _np_rng(2, _P_LEN).integers(1, max_len + 1, size=num_seqs)
 
 
-def config2_prompts(num_seqs: int = 256, max_len: int = 2048, device="cpu") -> GdnInputs:
+def decode_prompts(num_seqs: int = 256, max_len: int = 2048, device="cpu") -> GdnInputs:
     """Ragged prompts that seed the decode states (lengths uniform in [1, max_len])."""
-    return make_inputs(2, config2_prompt_lengths(num_seqs, max_len), io="bf16",
+    return make_inputs(2, decode_prompt_lengths(num_seqs, max_len), io="bf16",
                        name=f"decode-prompts-{num_seqs}", device=device, **BIG)
 
 
-def config2_decode_tokens(step: int, num_seqs: int = 256, device="cpu") -> GdnInputs:
+def decode_tokens(step: int, num_seqs: int = 256, device="cpu") -> GdnInputs:
     """The tokens of decode step ``step`` (one per sequence), drawn from their own streams."""
     return make_inputs(2, [1] * num_seqs, io="bf16", name=f"decode-step{step}", sub=1000 + step,
                        device=device, **BIG)
 
 
-def config3_lengths(total: int = 10240, lo: int = 64, hi: int = 4096, seed: int = 3) -> list:
+def trainer_lengths(total: int = 10240, lo: int = 64, hi: int = 4096, seed: int = 3) -> list:
     """Lengths in [lo, hi] summing exactly to ``total`` (draw while more than hi remains)."""
     rng = _np_rng(seed, _P_LEN)
     rem, out = total, []
@@ -253,27 +253,27 @@ def config3_lengths(total: int = 10240, lo: int = 64, hi: int = 4096, seed: int 
     return out
 
 
-def config3(device="cpu") -> GdnInputs:
+def trainer_10240(device="cpu") -> GdnInputs:
     """Trainer forward: 10240 tokens packed varlen, lengths in [64, 4096]."""
-    return make_inputs(3, config3_lengths(), io="bf16", name="trainer-10240-varlen", device=device, **BIG)
+    return make_inputs(3, trainer_lengths(), io="bf16", name="trainer-10240-varlen", device=device, **BIG)
 
 
-def config4_x(seqlen: int = 65536, device="cpu") -> GdnInputs:
+def long_sequence(seqlen: int = 65536, device="cpu") -> GdnInputs:
     """The long sequence X of the invariance sweep (large head layout, bf16)."""
     return make_inputs(4, [seqlen], io="bf16", name=f"long-{seqlen}", device=device, **BIG)
 
 
-def config4_lengths(n_neighbours: int, sub: int, max_len: int = 8192) -> np.ndarray:
+def neighbour_lengths(n_neighbours: int, sub: int, max_len: int = 8192) -> np.ndarray:
     return _np_rng(4, _P_LEN, sub).integers(1, max_len + 1, size=n_neighbours)
 
 
-def config4_batch(x: GdnInputs, batch: int, sub: int, max_len: int = 8192):
+def long_in_batch(x: GdnInputs, batch: int, sub: int, max_len: int = 8192):
     """Embed the single sequence ``x`` among ``batch - 1`` random neighbours.
 
     Returns (inputs, index of x in the batch)."""
     if batch == 1:
         return x, 0
-    lens = config4_lengths(batch - 1, sub, max_len)
+    lens = neighbour_lengths(batch - 1, sub, max_len)
     nb = make_inputs(4, lens, io=x.io, name="neighbours", sub=100 + sub, h_k=x.h_k, h_v=x.h_v,
                      dk=x.dk, dv=x.dv, chunk=x.chunk, device=x.device)
     pos = int(_np_rng(4, _P_PACK, sub).integers(0, batch))

@@ -154,7 +154,7 @@ def test_backward_trainer_10240_varlen():
     d = 128, chunk 64, bf16): sampled oracle parity on every sequence for key head 5 (value
     heads 10 and 11), finite gradients everywhere, and packing invariance for one sequence."""
     cpr = lib()
-    x = gi.config3(device="cuda")
+    x = gi.trainer_10240(device="cuda")
     ct = gi.make_cotangents(x, 69, device="cuda")
     say(f"backward trainer 10240 lengths={x.lengths.tolist()}")
     cs = _forward(x)

@@ -140,7 +140,7 @@ def test_chunked_prefill_5x2048_sampled():
     """The 5 x 2048 rollout workload through both modes: oracle samples on two (sequence, value
     head) pairs per sequence, finite everywhere."""
     cpr = lib()
-    x = gi.config1(device="cuda")
+    x = gi.prefill_5x2048(device="cuda")
     for mode, outputs in (("native", cpr.GDN_CHUNKED_NATIVE), ("r2", cpr.GDN_CHUNKED_R2)):
         say(f"chunked {mode} 5x2048")
         o, pool, cs = _chunked(x, outputs)

@@ -34,7 +34,7 @@ def _decode_seq(pool, x, slot=0, on_step=None):
 
 def test_prefill_5x2048():
     cpr = lib()
-    x = gi.config1(device="cuda")
+    x = gi.prefill_5x2048(device="cuda")
     say("prefill 5x2048: packed run")
     o, pool, cs = prefill(x)
     rows = cpr.gdn_chunk_rows(x.cu_seqlens, 64).numpy()
@@ -100,13 +100,13 @@ def _with_generated(prompts: gi.GdnInputs, steps):
 
 def test_decode_256x1_128_steps_equals_one_prefill():
     cpr = lib()
-    prompts = gi.config2_prompts(device="cuda")
+    prompts = gi.decode_prompts(device="cuda")
     n = prompts.num_seqs
     say(f"decode: prefill {n} prompts ({prompts.total_tokens} tokens)")
     P = policy_of(prompts)
     pool = cpr.StatePool(P, n, boundary=True)
     cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
-    steps = [gi.config2_decode_tokens(s, n, device="cuda") for s in range(128)]
+    steps = [gi.decode_tokens(s, n, device="cuda") for s in range(128)]
     say("decode: 128 steps")
     outs = []
     for s in steps:
@@ -140,7 +140,7 @@ def test_decode_256x1_128_steps_equals_one_prefill():
 
 def test_trainer_forward_10240_varlen_with_stash():
     cpr = lib()
-    x = gi.config3(device="cuda")
+    x = gi.trainer_10240(device="cuda")
     say(f"trainer: lengths {list(x.lengths)}")
     rows = cpr.gdn_chunk_rows(x.cu_seqlens, 64).numpy()
     stash = torch.empty((int(rows[-1]) + 2 * x.num_seqs + x.total_tokens // 64, x.h_v, x.dv, x.dk),
@@ -175,7 +175,7 @@ def test_trainer_forward_10240_varlen_with_stash():
 
 @pytest.fixture(scope="module")
 def long_x():
-    x = gi.config4_x(device="cuda")
+    x = gi.long_sequence(device="cuda")
     say("long: X alone")
     o, pool, _ = prefill(x)
     return x, sha(o), sha(pool.state), o
@@ -192,7 +192,7 @@ def test_long_sequence_matches_oracle(long_x):
 @pytest.mark.parametrize("batch", [2, 8, 64])
 def test_long_sequence_invariant_to_neighbours(long_x, batch):
     x, so, sS, _ = long_x
-    y, pos = gi.config4_batch(x, batch, sub=batch)
+    y, pos = gi.long_in_batch(x, batch, sub=batch)
     say(f"long: X among {batch - 1} neighbours at position {pos} ({y.total_tokens} tokens)")
     o, pool, _ = prefill(y)
     t0 = int(y.cu_seqlens[pos])

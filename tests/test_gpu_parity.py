@@ -16,9 +16,9 @@ from tests.gpu_util import (check_close, decode_all, gpu_state_math, lib, oracle
 pytestmark = pytest.mark.gpu
 
 
-def test_config0_prefill_matches_oracle():
-    x = gi.config0()
-    say("config0 prefill vs oracle")
+def test_tiny_prefill_matches_oracle():
+    x = gi.tiny_fp32()
+    say("tiny fp32 prefill vs oracle")
     o, pool, cs = prefill(x)
     ref_o, ref_S, ref_R = oracle_all(x)
     check_close("f32", o.cpu().double().numpy(), ref_o, "o")
@@ -29,10 +29,10 @@ def test_config0_prefill_matches_oracle():
     assert int(pool.pos[0]) == 256
 
 
-def test_config0_decode_bitwise_equals_prefill():
+def test_tiny_decode_bitwise_equals_prefill():
     cpr = lib()
-    x = gi.config0()
-    say("config0 prefill vs 256 decode steps")
+    x = gi.tiny_fp32()
+    say("tiny fp32 prefill vs 256 decode steps")
     o_p, pool_p, cs = prefill(x)
     pool_d = cpr.StatePool(policy_of(x), 1, boundary=True)
     o_d = decode_all(x, pool_d)

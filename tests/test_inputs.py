@@ -17,16 +17,16 @@ def test_bf16_encoding_matches_torch_rne():
 
 
 def test_generator_is_deterministic_and_streams_differ():
-    a = gi.config0()
-    b = gi.config0()
+    a = gi.tiny_fp32()
+    b = gi.tiny_fp32()
     assert a.digest() == b.digest()
     assert not torch.equal(a.q, a.k)
     c = gi.make_inputs(0, [256], 2, 2, 16, 16, io="f32", sub=1)
     assert c.digest() != a.digest()
 
 
-def test_config0_shapes_and_distributions():
-    x = gi.config0()
+def test_tiny_shapes_and_distributions():
+    x = gi.tiny_fp32()
     assert x.q.shape == (256, 2, 16) and x.v.shape == (256, 2, 16) and x.a.shape == (256, 2)
     assert x.q.dtype == torch.float32 and x.a.dtype == torch.float32
     assert bool((x.a > 0).all() and (x.a < 1).all() and (x.b > 0).all() and (x.b < 1).all())
@@ -54,20 +54,20 @@ def test_select_and_concat():
     assert torch.equal(z.q, x.q[3:73]) and list(z.cu_seqlens) == [0, 70]
 
 
-def test_config3_lengths():
-    L = gi.config3_lengths()
+def test_trainer_lengths():
+    L = gi.trainer_lengths()
     assert sum(L) == 10240 and all(64 <= l <= 4096 for l in L)
 
 
-def test_config2_prompt_lengths():
-    L = gi.config2_prompt_lengths()
+def test_decode_prompt_lengths():
+    L = gi.decode_prompt_lengths()
     assert len(L) == 256 and L.min() >= 1 and L.max() <= 2048
 
 
 @pytest.mark.parametrize("batch", [1, 2, 5])
-def test_config4_embedding_keeps_x(batch):
+def test_long_in_batch_keeps_x(batch):
     x = gi.make_inputs(4, [300], h_k=1, h_v=2, dk=16, dv=16, io="bf16")
-    y, pos = gi.config4_batch(x, batch, sub=batch, max_len=50)
+    y, pos = gi.long_in_batch(x, batch, sub=batch, max_len=50)
     assert y.num_seqs == batch
     t0 = int(y.cu_seqlens[pos])
     assert y.lengths[pos] == 300
