@@ -308,7 +308,8 @@ def gdn_prefill_fused(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None,
 def gdn_prefill_overlapped(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
                            o=None, chunk_states=None, stream=None, events=None):
     """Overlapped prefill (C gdn_prefill_overlapped): pass 1 and the chunk outputs in one launch;
-    bitwise equal to gdn_prefill.  chunk_states None: no stash.  Returns (o, chunk_states)."""
+    bitwise equal to gdn_prefill.  More workgroups than CUs, or chunks above 64 tokens, run the
+    one-pass kernel instead.  chunk_states None: no stash.  Returns (o, chunk_states)."""
     P, dev = pool.policy, pool.device
     N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
     rows = 0

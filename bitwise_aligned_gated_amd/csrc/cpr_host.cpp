@@ -408,7 +408,8 @@ static int onepass_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.c_stash = nullptr;
   A.w_stash = nullptr;
   A.events = events;
-  const hipError_t e = overlap && P.chunk <= cpr::overlap_max_chunk()
+  const bool overlapped = overlap && P.chunk <= cpr::overlap_max_chunk() && cpr::overlap_fits(P.dk, P.dv, A);
+  const hipError_t e = overlapped
                            ? cpr::launch_prefill_overlap(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream))
                            : cpr::launch_prefill_fused(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, who);

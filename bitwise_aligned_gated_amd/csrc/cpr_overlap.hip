@@ -384,6 +384,26 @@ static hipError_t launch_overlap_t(const PrefillArgs& A, hipStream_t stream) {
 
 int overlap_max_chunk() { return OvCfg<128, 128>::CMAX; }
 
+// The kernel's LDS holds one workgroup per CU, so a grid larger than the CU count would run in
+// rounds, each as long as the longest sequence; the one-pass kernel is faster there.
+bool overlap_fits(int dk, int dv, const PrefillArgs& A) {
+  int ncg = 0;
+  if (dk == dv) {
+    switch (dk) {
+      case 16: ncg = OvCfg<16, 16>::NCG; break;
+      case 32: ncg = OvCfg<32, 32>::NCG; break;
+      case 64: ncg = OvCfg<64, 64>::NCG; break;
+      case 128: ncg = OvCfg<128, 128>::NCG; break;
+      default: return false;
+    }
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  return static_cast<int64_t>(A.num_seqs) * A.h_v * ncg <= cus;
+}
+
 hipError_t launch_prefill_overlap(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
 #define CPR_CASE(D, IOV) \
   if (dk == D && dv == D && io == IOV) return launch_overlap_t<D, D, IOV>(A, stream);

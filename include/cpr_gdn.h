@@ -238,8 +238,10 @@ int gdn_prefill_fused(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs
  * a chunk's outputs needs only the state at its start).  It suits a few long sequences, where
  * pass 1 alone cannot fill the GPU and pass 2 would otherwise run after it.  The state entering
  * each chunk and its tokens' write values c_t pass between the waves through LDS, so nothing is
- * written to HBM for the hand-off.  Chunks above 64 tokens take the one-pass kernel instead (the
- * same bits).  Arguments as gdn_prefill_fused.  events: NULL, or 2 hipEvent_t recorded before and
+ * written to HBM for the hand-off.  Each workgroup (one per sequence, value head and group of
+ * 16 columns at d = 16 or 128, 32 at d = 32 or 64) needs a CU of its own: when there are more
+ * workgroups than the device has CUs, or a chunk exceeds 64 tokens, the call runs the one-pass
+ * kernel instead (the same bits).  Arguments as gdn_prefill_fused.  events: NULL, or 2 hipEvent_t recorded before and
  * after the kernel. */
 int gdn_prefill_overlapped(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                            const int32_t* slot_ids, int32_t from_state,

@@ -301,6 +301,20 @@ def test_overlapped_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
 
 
+def test_overlapped_prefill_beyond_one_workgroup_per_cu():
+    """A batch whose overlapped grid exceeds the CU count (40 sequences x 4 value heads x 8
+    column groups) runs the one-pass kernel instead: still the same bits as gdn_prefill."""
+    cpr = lib()
+    lens = [(37 * i) % 150 + 1 for i in range(40)]
+    x = gi.make_inputs(28, lens, h_k=2, h_v=4, dk=128, dv=128, chunk=32, io="bf16")
+    say("overlapped beyond one workgroup per CU")
+    o2, pool2, cs2 = prefill(x)
+    o1, pool1, cs1 = _fused(x, overlapped=True)
+    assert sha(o1) == sha(o2) and sha(pool1.state) == sha(pool2.state)
+    n = int(cpr.gdn_chunk_rows(x.cu_seqlens, 32)[-1])
+    assert sha(cs1[:n]) == sha(cs2[:n])
+
+
 @pytest.mark.parametrize("boundary", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [1, 16, 64, 100])
 def test_overlapped_continuation_matches(chunk, boundary):
