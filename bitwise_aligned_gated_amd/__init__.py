@@ -63,6 +63,7 @@ _SIGS = {
     "gdn_state_free": (ctypes.c_int, [_P]),
     "gdn_state_data": (_P, [_P]),
     "gdn_state_positions": (_P, [_P]),
+    "gdn_state_set_max_workgroups": (ctypes.c_int, [_P, _i64]),
     "gdn_check_cu_seqlens": (ctypes.c_int, [_P, _i32, _i64]),
     "gdn_chunk_rows_bound": (_i64, [_i64, _i32, _i32]),
     "gdn_chunk_rows": (ctypes.c_int, [_P, _P, _i32, _i32, _P]),
@@ -244,6 +245,11 @@ class StatePool:
     @property
     def handle(self):
         return self._h
+
+    def set_max_workgroups(self, n: int) -> None:
+        """Cap the compute kernels of later calls at n workgroups (C gdn_state_set_max_workgroups);
+        0 restores one workgroup per work item.  Results are bitwise the same either way."""
+        _check(_lib.gdn_state_set_max_workgroups(self._h, int(n)))
 
     def close(self):
         if getattr(self, "_h", None):

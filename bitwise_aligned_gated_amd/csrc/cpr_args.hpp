@@ -30,6 +30,8 @@ struct PrefillArgs {
   float* c_stash;             // nullable: [N][H_v][dv] fp32, every token's c (pass 1 writes, pass 2 reads)
   float* w_stash;             // nullable (needs c_stash): [N][H_v][dv] fp32, every token's w
   void* const* events;        // nullable: hipEvent_t recorded around the kernels
+  int64_t grid_items;         // set per launch: the kernel's work items (one per natural workgroup)
+  int64_t max_wgs;            // 0: one workgroup per item; else at most this many, taking items in turn
 };
 
 struct DecodeArgs {
@@ -51,6 +53,8 @@ struct DecodeArgs {
   int32_t chunk;
   int32_t round_boundary;     // 1: bf16 boundary dtype (round the state at chunk starts)
   void* const* events;        // nullable: 2 hipEvent_t recorded around the step kernel
+  int64_t grid_items;         // set per launch: the kernel's work items
+  int64_t max_wgs;            // 0: one workgroup per item; else at most this many, taking items in turn
 };
 
 // Gradients of a forward that started every sequence at position 0 (the trainer's case).

@@ -184,6 +184,28 @@ inline int64_t xcd_grid(int64_t n_groups, int group_size) {
   return (n_groups + kXcds - 1) / kXcds * kXcds * group_size;
 }
 
+// Launch shape of a kernel with `items` work items: one workgroup each, or at most max_wgs
+// workgroups that take items b, b + gridDim.x, ... in turn.  Every item's arithmetic is the same
+// either way, so the shape moves no bit.
+template <typename Args>
+inline Args with_items(const Args& A, int64_t items) {
+  Args B = A;
+  B.grid_items = items;
+  return B;
+}
+// Launch `items` work items: the natural kernel with one workgroup per item, or, when the caller
+// capped the grid below that, the strided kernel with max_wgs workgroups.
+template <typename Args>
+inline hipError_t launch_items(void (*natural)(Args), void (*strided)(Args), int64_t items, unsigned threads,
+                               hipStream_t stream, const Args& A) {
+  if (items > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (A.max_wgs > 0 && A.max_wgs < items)
+    hipLaunchKernelGGL(strided, dim3(static_cast<unsigned>(A.max_wgs)), dim3(threads), 0, stream, with_items(A, items));
+  else
+    hipLaunchKernelGGL(natural, dim3(static_cast<unsigned>(items)), dim3(threads), 0, stream, with_items(A, items));
+  return hipGetLastError();
+}
+
 struct GroupSlot {
   int64_t group;
   int member;

@@ -46,17 +46,20 @@ struct DecodeCfg {
   static_assert(DV % SLOTS == 0 && NC_ALL % NC == 0, "shape");
 };
 
-// One workgroup per (entry, value head, column group): every lane first issues the streaming
+// One work item per (entry, value head, column group): every lane first issues the streaming
 // loads of all its NC columns (NC x 32 bytes of state), then runs the step on each column; lane
 // (slot, g) owns columns col0 + slot + SLOTS * c, so each load instruction of a wave covers whole
 // 512-byte columns.
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kernel(DecodeArgs A) {
+__device__ __forceinline__ void decode_step_item(const DecodeArgs& A, int64_t vb) {
   using Cfg = DecodeCfg<DK, DV>;
-  constexpr int G = Cfg::G, NC = Cfg::NC, SLOTS = Cfg::SLOTS;
+  constexpr int G = Cfg::G, NC = Cfg::NC, SLOTS = Cfg::SLOTS, NCG = DV / Cfg::WG_COLS;
   __shared__ float o_lds[Cfg::WG_COLS];
-  const int e = blockIdx.x, h = blockIdx.y;
-  const int col0 = blockIdx.z * Cfg::WG_COLS;
+  // items in (entry, value head, column group) order, entries fastest
+  const int per_entry = A.h_v * NCG;
+  const int e = static_cast<int>(vb % A.batch), h = static_cast<int>(vb / A.batch % A.h_v);
+  const int z = static_cast<int>(vb / A.batch / A.h_v);
+  const int col0 = z * Cfg::WG_COLS;
   const int32_t slot = A.slot_ids[e];
   if (slot < 0 || slot >= A.num_slots) return;                  // uniform across the block
   // the low 48 bits are the position; the high bits count this step's finished workgroups
@@ -88,7 +91,7 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kern
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       state_store(A.boundary + head + static_cast<int64_t>(col0 + cs + SLOTS * c) * DK + g * kLeaf, s[c]);
-    if (h == 0 && blockIdx.z == 0 && tid == 0) A.boundary_pos[slot] = p;
+    if (h == 0 && z == 0 && tid == 0) A.boundary_pos[slot] = p;
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -106,12 +109,26 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kern
     store8<IO>(A.o, vo + tid * 8, x);
   }
   if (tid == 0) {
-    // Every workgroup of this slot read pos above, before its own increment here, so the last
+    // Every work item of this slot read pos above, before its own increment here, so the last
     // one to finish can advance the position and clear the counter without racing a reader.
-    const unsigned long long done = static_cast<unsigned long long>(gridDim.y) * gridDim.z;
+    const unsigned long long done = static_cast<unsigned long long>(per_entry);
     const unsigned long long old =
         atomicAdd(reinterpret_cast<unsigned long long*>(A.pos + slot), 1ull << kPosBits);
     if ((old >> kPosBits) == done - 1) A.pos[slot] = static_cast<int64_t>(old & kPosMask) + 1;
+  }
+}
+
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_kernel(DecodeArgs A) {
+  decode_step_item<DK, DV, IO>(A, blockIdx.x);
+}
+
+// The same items under a capped grid: each workgroup takes items b, b + gridDim.x, ...
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((DecodeCfg<DK, DV>::THREADS)) decode_step_strided_kernel(DecodeArgs A) {
+  for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
+    if (vb != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
+    decode_step_item<DK, DV, IO>(A, vb);
   }
 }
 
@@ -147,9 +164,11 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.batch > 0) {
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV, IO>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS), 0,
-                       stream, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t items = static_cast<int64_t>(A.batch) * A.h_v * (DV / Cfg::WG_COLS);
+    if (items > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    e = launch_items(decode_step_kernel<DK, DV, IO>, decode_step_strided_kernel<DK, DV, IO>, items, Cfg::THREADS, stream,
+                     A);
+    if (e != hipSuccess) return e;
   }
   return record_event(A.events, 1, stream);
 }

@@ -21,6 +21,7 @@ struct gdn_state {
   float* boundary;
   int64_t* boundary_pos;
   bool owns;
+  int64_t max_wgs;   // launch-shape cap of the compute kernels (0: one workgroup per work item)
 };
 
 namespace {
@@ -256,6 +257,7 @@ int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, i
   st->boundary = boundary;
   st->boundary_pos = boundary_pos;
   st->owns = self;
+  st->max_wgs = 0;
   *out = st;
   return ok();
 }
@@ -267,6 +269,14 @@ int gdn_state_free(gdn_state* st) {
     (void)hipFree(st->pos);
   }
   delete st;
+  return ok();
+}
+
+int gdn_state_set_max_workgroups(gdn_state* st, int64_t max_workgroups) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_state_set_max_workgroups: state handle is NULL");
+  if (max_workgroups < 0 || max_workgroups > 0x7FFFFFFF)
+    return fail(GDN_EINVAL, "gdn_state_set_max_workgroups: %lld is outside [0, 2^31)", (long long)max_workgroups);
+  st->max_wgs = max_workgroups;
   return ok();
 }
 
@@ -328,7 +338,8 @@ static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
                 (long long)bound);
   if (bound > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "%s: too many chunks for one launch", who);
   if (reinterpret_cast<uintptr_t>(c_stash) % 16 != 0) return fail(GDN_EINVAL, "%s: c stash must be 16-byte aligned", who);
-  cpr::PrefillArgs A;
+  cpr::PrefillArgs A{};
+  A.max_wgs = st->max_wgs;
   A.cu = cu_seqlens;
   A.slot_ids = slot_ids;
   A.pos = st->pos;
@@ -390,7 +401,8 @@ static int onepass_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   if (chunk_states != nullptr && chunk_state_rows < bound)
     return fail(GDN_EINVAL, "%s: chunk_state_rows %lld < bound %lld", who, (long long)chunk_state_rows,
                 (long long)bound);
-  cpr::PrefillArgs A;
+  cpr::PrefillArgs A{};
+  A.max_wgs = st->max_wgs;
   A.cu = cu_seqlens;
   A.slot_ids = slot_ids;
   A.pos = st->pos;
@@ -441,7 +453,8 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const
                     b == nullptr || o == nullptr))
     return fail(GDN_EINVAL, "gdn_decode_step: NULL pointer");
   const gdn_policy& P = st->policy;
-  cpr::DecodeArgs A;
+  cpr::DecodeArgs A{};
+  A.max_wgs = st->max_wgs;
   A.slot_ids = slot_ids;
   A.pos = st->pos;
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b; A.o = o;
@@ -463,7 +476,8 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
   if (n < 0) return fail(GDN_EINVAL, "gdn_state_resync: negative count");
   if (n > 0 && slot_ids == nullptr) return fail(GDN_EINVAL, "gdn_state_resync: slot_ids is NULL");
   const gdn_policy& P = st->policy;
-  cpr::DecodeArgs A;
+  cpr::DecodeArgs A{};
+  A.max_wgs = st->max_wgs;
   std::memset(&A, 0, sizeof A);
   A.slot_ids = slot_ids;
   A.pos = st->pos;
@@ -610,7 +624,8 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
                 (long long)need);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return fail(GDN_EINVAL, "gdn_prefill_chunked: workspace must be 16-byte aligned");
-  cpr::PrefillArgs A;
+  cpr::PrefillArgs A{};
+  A.max_wgs = st->max_wgs;
   A.cu = cu_seqlens;
   A.slot_ids = slot_ids;
   A.pos = st->pos;

@@ -94,13 +94,13 @@ struct OvIn {
 };
 
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((OvCfg<DK, DV>::THREADS)) overlap_kernel(PrefillArgs A) {
+__device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
   using O = OvCfg<DK, DV>;
   constexpr int G = O::G, CW = O::CW, P = O::P, G2 = O::G2, NL2 = O::NL2, R2 = O::R2, TH = O::TH, TT = O::TT;
   __shared__ OvLds<DK, DV> L;
   __shared__ int64_t red[(O::THREADS + 63) / 64 + 2];
   const int ratio = A.h_v / A.h_k;
-  const GroupSlot gs = xcd_group(blockIdx.x, ratio * O::NCG);
+  const GroupSlot gs = xcd_group(vb, ratio * O::NCG);
   if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
   const int i = static_cast<int>(gs.group / A.h_k), kh = static_cast<int>(gs.group % A.h_k);
   const int h = kh * ratio + gs.member / O::NCG, col0 = (gs.member % O::NCG) * CW;
@@ -367,6 +367,20 @@ __global__ void __launch_bounds__((OvCfg<DK, DV>::THREADS)) overlap_kernel(Prefi
 }
 
 template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((OvCfg<DK, DV>::THREADS)) overlap_kernel(PrefillArgs A) {
+  overlap_item<DK, DV, IO>(A, blockIdx.x);
+}
+
+// The same items under a capped grid: each workgroup takes items b, b + gridDim.x, ...
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((OvCfg<DK, DV>::THREADS)) overlap_strided_kernel(PrefillArgs A) {
+  for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
+    if (vb != blockIdx.x) __syncthreads();                 // every wave is done with the previous item
+    overlap_item<DK, DV, IO>(A, vb);
+  }
+}
+
+template <int DK, int DV, int IO>
 static hipError_t launch_overlap_t(const PrefillArgs& A, hipStream_t stream) {
   using O = OvCfg<DK, DV>;
   hipError_t e = record_event(A.events, 0, stream);
@@ -374,9 +388,8 @@ static hipError_t launch_overlap_t(const PrefillArgs& A, hipStream_t stream) {
   if (A.num_seqs > 0) {
     const int64_t grid = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * O::NCG);
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((overlap_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(grid)), dim3(O::THREADS), 0, stream,
-                       A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_items(overlap_kernel<DK, DV, IO>, overlap_strided_kernel<DK, DV, IO>, grid, O::THREADS, stream, A);
+    if (e != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   return launch_prefill_finish(A, stream);
@@ -401,7 +414,8 @@ bool overlap_fits(int dk, int dv, const PrefillArgs& A) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return false;
-  return static_cast<int64_t>(A.num_seqs) * A.h_v * ncg <= cus;
+  const int64_t items = static_cast<int64_t>(A.num_seqs) * A.h_v * ncg;
+  return (A.max_wgs > 0 && A.max_wgs < items ? A.max_wgs : items) <= cus;
 }
 
 hipError_t launch_prefill_overlap(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {

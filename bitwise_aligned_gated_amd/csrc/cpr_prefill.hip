@@ -341,7 +341,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
 
 // MODE kBoundary: tokens up to the last chunk start; kBoundaryC: every token, keeping c (and w).
 template <int DK, int DV, int IO, int MODE>
-__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
+__device__ __forceinline__ void boundary_pass_item(const PrefillArgs& A, int64_t vb) {
   using Cfg = PassCfg<DK, DV, MODE>;
   static_assert(Cfg::R == kLeaf && Cfg::NC == 1, "pass 1 holds one leaf of one column per lane");
   static_assert(MODE == kBoundary || MODE == kBoundaryC, "pass 1 modes");
@@ -349,7 +349,7 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) boundary_pas
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   // group = (sequence, key head); members = its value heads x column groups
   const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
-  const GroupSlot gs = xcd_group(blockIdx.x, ratio * ncg);
+  const GroupSlot gs = xcd_group(vb, ratio * ncg);
   if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
   const int i = static_cast<int>(gs.group / A.h_k);
   const int h = static_cast<int>(gs.group % A.h_k) * ratio + gs.member / ncg, cg = gs.member % ncg;
@@ -382,16 +382,30 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) boundary_pas
   run_tokens<DK, DV, IO, MODE>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, row0 + m.nrows, first_nb);
 }
 
+template <int DK, int DV, int IO, int MODE>
+__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) boundary_pass_kernel(PrefillArgs A) {
+  boundary_pass_item<DK, DV, IO, MODE>(A, blockIdx.x);
+}
+
+// The same items under a capped grid: each workgroup takes items b, b + gridDim.x, ...
+template <int DK, int DV, int IO, int MODE>
+__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) boundary_pass_strided_kernel(PrefillArgs A) {
+  for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
+    if (vb != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
+    boundary_pass_item<DK, DV, IO, MODE>(A, vb);
+  }
+}
+
 // MODE kOutput: every step predicts c from v; kOutputC: c comes from pass 1's stash.
 template <int DK, int DV, int IO, int MODE>
-__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) output_pass_kernel(PrefillArgs A) {
+__device__ __forceinline__ void output_pass_item(const PrefillArgs& A, int64_t vb) {
   using Cfg = PassCfg<DK, DV, MODE>;
   static_assert(MODE == kOutput || MODE == kOutputC, "pass 2 modes");
   __shared__ TileLds<DK, DV, MODE> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   // group = (boundary row, key head); members = its value heads x column groups
   const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
-  const GroupSlot gs = xcd_group(blockIdx.x, ratio * ncg);
+  const GroupSlot gs = xcd_group(vb, ratio * ncg);
   const int64_t w = gs.group / A.h_k;
   const int h = static_cast<int>(gs.group % A.h_k) * ratio + gs.member / ncg, cg = gs.member % ncg;
   if (w >= A.rows_cap) return;                               // uniform across the block
@@ -426,15 +440,29 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) output_pass_
   }
 }
 
+template <int DK, int DV, int IO, int MODE>
+__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) output_pass_kernel(PrefillArgs A) {
+  output_pass_item<DK, DV, IO, MODE>(A, blockIdx.x);
+}
+
+// The same items under a capped grid: each workgroup takes items b, b + gridDim.x, ...
+template <int DK, int DV, int IO, int MODE>
+__global__ void __launch_bounds__((PassCfg<DK, DV, MODE>::THREADS)) output_pass_strided_kernel(PrefillArgs A) {
+  for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
+    if (vb != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
+    output_pass_item<DK, DV, IO, MODE>(A, vb);
+  }
+}
+
 // The one-pass variant: every token of a sequence in one launch, with outputs, and (when a stash
 // is given) the same chunk-start rows as pass 1.  Same step, same bits as the two passes.
 template <int DK, int DV, int IO>
-__global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass_kernel(PrefillArgs A) {
+__device__ __forceinline__ void fused_pass_item(const PrefillArgs& A, int64_t vb) {
   using Cfg = PassCfg<DK, DV, kFused>;
   __shared__ TileLds<DK, DV, kFused> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   const int ratio = A.h_v / A.h_k, ncg = DV / Cfg::WG_COLS;
-  const GroupSlot gs = xcd_group(blockIdx.x, ratio * ncg);
+  const GroupSlot gs = xcd_group(vb, ratio * ncg);
   if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
   const int i = static_cast<int>(gs.group / A.h_k);
   const int h = static_cast<int>(gs.group % A.h_k) * ratio + gs.member / ncg, cg = gs.member % ncg;
@@ -464,6 +492,20 @@ __global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass
   store_f32x8(slot_state, s[0]);
 }
 
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass_kernel(PrefillArgs A) {
+  fused_pass_item<DK, DV, IO>(A, blockIdx.x);
+}
+
+// The same items under a capped grid: each workgroup takes items b, b + gridDim.x, ...
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((PassCfg<DK, DV, kFused>::THREADS)) fused_pass_strided_kernel(PrefillArgs A) {
+  for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
+    if (vb != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
+    fused_pass_item<DK, DV, IO>(A, vb);
+  }
+}
+
 __global__ void prefill_finish_kernel(PrefillArgs A) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= A.num_seqs) return;
@@ -482,24 +524,24 @@ static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
     const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
     if (g1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     if (A.c_stash != nullptr)
-      hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO, kBoundaryC>), dim3(static_cast<unsigned>(g1)),
-                         dim3(C1::THREADS), 0, stream, A);
+      e = launch_items(boundary_pass_kernel<DK, DV, IO, kBoundaryC>, boundary_pass_strided_kernel<DK, DV, IO, kBoundaryC>,
+                       g1, C1::THREADS, stream, A);
     else
-      hipLaunchKernelGGL((boundary_pass_kernel<DK, DV, IO, kBoundary>), dim3(static_cast<unsigned>(g1)),
-                         dim3(C1::THREADS), 0, stream, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = launch_items(boundary_pass_kernel<DK, DV, IO, kBoundary>, boundary_pass_strided_kernel<DK, DV, IO, kBoundary>,
+                       g1, C1::THREADS, stream, A);
+    if (e != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0 && A.rows_cap > 0) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     if (A.c_stash != nullptr)
-      hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO, kOutputC>), dim3(static_cast<unsigned>(g2)),
-                         dim3(C2::THREADS), 0, stream, A);
+      e = launch_items(output_pass_kernel<DK, DV, IO, kOutputC>, output_pass_strided_kernel<DK, DV, IO, kOutputC>, g2,
+                       C2::THREADS, stream, A);
     else
-      hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO, kOutput>), dim3(static_cast<unsigned>(g2)),
-                         dim3(C2::THREADS), 0, stream, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = launch_items(output_pass_kernel<DK, DV, IO, kOutput>, output_pass_strided_kernel<DK, DV, IO, kOutput>, g2,
+                       C2::THREADS, stream, A);
+    if (e != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0) {
@@ -517,9 +559,8 @@ static hipError_t launch_fused_t(const PrefillArgs& A, hipStream_t stream) {
   if (A.num_seqs > 0) {
     const int64_t gf = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / CF::WG_COLS));
     if (gf > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fused_pass_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(gf)), dim3(CF::THREADS), 0, stream,
-                       A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = launch_items(fused_pass_kernel<DK, DV, IO>, fused_pass_strided_kernel<DK, DV, IO>, gf, CF::THREADS, stream, A);
+    if (e != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0) {
@@ -552,9 +593,8 @@ static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream)
   if (A.num_seqs > 0 && A.rows_cap > 0) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((output_pass_kernel<DK, DV, IO, kOutput>), dim3(static_cast<unsigned>(g2)), dim3(C2::THREADS), 0,
-                       stream, A);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_items(output_pass_kernel<DK, DV, IO, kOutput>,
+                                      output_pass_strided_kernel<DK, DV, IO, kOutput>, g2, C2::THREADS, stream, A);
     if (e != hipSuccess) return e;
   }
   return launch_prefill_finish(A, stream);

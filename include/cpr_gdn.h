@@ -158,6 +158,16 @@ int gdn_state_free(gdn_state* st);
 float* gdn_state_data(gdn_state* st);
 int64_t* gdn_state_positions(gdn_state* st);
 
+/* Launch shape of later calls on this pool (section "Making kernels parallelism-invariant":
+ * identical bits however the work is split).  max_workgroups = 0, the default, launches one
+ * workgroup per work item.  A positive value caps the workgroups of the compute kernels at that
+ * number, and each workgroup takes work items in turn.  The capped kernels are the two prefill
+ * passes, the one-pass and overlapped prefill and the decode step.  No output or state changes
+ * by a bit; a small cap only runs the work with less parallelism.  The position-update, resync,
+ * chunkwise and backward kernels keep their natural shapes.  GDN_EINVAL for a NULL handle, a
+ * negative value or one of 2^31 or more.  Host-only. */
+int gdn_state_set_max_workgroups(gdn_state* st, int64_t max_workgroups);
+
 /* Host-side check of a cu_seqlens array (host copy): GDN_OK if cu[0] == 0, non-decreasing and
  * cu[num_seqs] == total_tokens; GDN_EINVAL otherwise. */
 int gdn_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens);

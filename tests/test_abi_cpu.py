@@ -190,6 +190,12 @@ def test_prefill_argument_errors_before_launch():
         assert lib.gdn_decode_step(h, None, 0, None, None, None, None, None, None, None, None) == 0
         assert lib.gdn_state_resync(h, None, 0, None) == 0
         assert lib.gdn_last_error() == b""
+        # launch-shape cap: 0 and positive values below 2^31 are accepted
+        for n in (0, 1, 7, 0x7FFFFFFF):
+            assert lib.gdn_state_set_max_workgroups(h, n) == 0
+        for n in (-1, 1 << 31):
+            assert lib.gdn_state_set_max_workgroups(h, n) == 1 and b"max_workgroups" in lib.gdn_last_error()
+        assert lib.gdn_state_set_max_workgroups(None, 4) == 1 and b"state handle" in lib.gdn_last_error()
     finally:
         assert lib.gdn_state_free(h) == 0
     assert lib.gdn_state_free(None) == 0

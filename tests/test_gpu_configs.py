@@ -219,6 +219,55 @@ def test_long_sequence_overlapped(long_x):
     assert sha(o) == so and sha(pool.state) == sS
 
 
+@pytest.mark.parametrize("cap", [1, 7, 64, 256, 1024, 4096])
+def test_long_sequence_under_a_grid_cap(long_x, cap):
+    """X through the two-pass prefill with the compute kernels capped at `cap` workgroups, each
+    taking work items in turn ("Making kernels parallelism-invariant": identical bits however the
+    work is split): the natural launch's o and final S, bit for bit."""
+    x, so, sS, _ = long_x
+    say(f"long: two-pass prefill under a grid cap of {cap}")
+    pool = lib().StatePool(policy_of(x), 1)
+    pool.set_max_workgroups(cap)
+    o, pool, _ = prefill(x, pool=pool)
+    assert sha(o) == so and sha(pool.state) == sS
+
+
+@pytest.mark.parametrize("cap", [7, 100])
+def test_long_sequence_one_pass_and_overlapped_under_a_grid_cap(long_x, cap):
+    x, so, sS, _ = long_x
+    cpr = lib()
+    xd = x.to("cuda")
+    for run in (cpr.gdn_prefill_fused, cpr.gdn_prefill_overlapped):
+        say(f"long: {run.__name__} under a grid cap of {cap}")
+        pool = cpr.StatePool(policy_of(x), 1)
+        pool.set_max_workgroups(cap)
+        o, _ = run(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+        torch.cuda.synchronize()
+        assert sha(o) == so and sha(pool.state) == sS
+
+
+@pytest.mark.parametrize("cap", [1, 7, 64])
+def test_decode_under_a_grid_cap(cap):
+    """Ragged prompts, then 70 decode steps that cross chunk starts, with the decode step capped
+    at `cap` workgroups: every output, state, position and boundary record as in the natural
+    launch."""
+    cpr = lib()
+    lens = [(53 * i) % 190 + 1 for i in range(16)]
+    prompts = gi.make_inputs(31, lens, io="bf16", device="cuda", **gi.BIG)
+    steps = [gi.make_inputs(31, [1] * len(lens), io="bf16", sub=500 + s, device="cuda", **gi.BIG) for s in range(70)]
+    say(f"decode under a grid cap of {cap}")
+    runs = []
+    for c in (0, cap):
+        pool = cpr.StatePool(policy_of(prompts), len(lens), boundary=True)
+        cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
+        pool.set_max_workgroups(c)
+        outs = [cpr.gdn_decode_step(pool, s.q, s.k, s.v, s.a, s.b) for s in steps]
+        torch.cuda.synchronize()
+        runs.append((sha(torch.stack(outs)), sha(pool.state), pool.pos.tolist(), sha(pool.boundary),
+                     pool.boundary_pos.tolist()))
+    assert runs[0] == runs[1]
+
+
 def test_long_sequence_decoded_65536_steps(long_x):
     x, so, sS, _ = long_x
     say("long: 65536 decode steps")

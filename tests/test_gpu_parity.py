@@ -219,6 +219,30 @@ def test_fused_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
 
 
+@pytest.mark.parametrize("dim", [16, 32, 64, 128])
+def test_prefill_under_a_grid_cap_matches_the_natural_launch(dim):
+    """A ragged batch (empty, one-token and multi-chunk sequences) with every capped kernel limited
+    to 1, 3 and 64 workgroups: two-pass with and without the c stash, one-pass and overlapped --
+    o, final states, positions and chunk-start rows as in the natural launch, bit for bit."""
+    cpr = lib()
+    x = gi.make_inputs(29, LENS, h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io="bf16")
+    n = int(cpr.gdn_chunk_rows(x.cu_seqlens, 32)[-1])
+    o0, pool0, cs0 = prefill(x)
+    ref = (sha(o0), sha(pool0.state), pool0.pos.tolist(), sha(cs0[:n]))
+    for cap in (1, 3, 64):
+        say(f"grid cap {cap} dim={dim}")
+        for stash in (True, False):
+            pool = cpr.StatePool(policy_of(x), x.num_seqs)
+            pool.set_max_workgroups(cap)
+            o, pool, cs = prefill(x, pool=pool, c_stash=stash)
+            assert (sha(o), sha(pool.state), pool.pos.tolist(), sha(cs[:n])) == ref, (cap, stash)
+        for overlapped in (False, True):
+            pool = cpr.StatePool(policy_of(x), x.num_seqs)
+            pool.set_max_workgroups(cap)
+            o, pool, cs = _fused(x, pool=pool, overlapped=overlapped)
+            assert (sha(o), sha(pool.state), pool.pos.tolist(), sha(cs[:n])) == ref, (cap, overlapped)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("dim", [16, 32, 64, 128])
 def test_c_stash_changes_no_bit(dim, io):
