@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 METRIC = "CPR-GDN prefill tok/s (5×2048) + decode µs/step (256×1), % HBM peak"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 FLOP/clk/CU)
-FP32_UNPACKED_PEAK_TFLOPS = 78.6  # the same without packed fp32 (disabled in this build)
+FP32_UNPACKED_PEAK_TFLOPS = 78.6  # the same without packed fp32 (the kernels are compiled without it)
 FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
 
 

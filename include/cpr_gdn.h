@@ -132,7 +132,8 @@ int gdn_sha256(const void* data, size_t n, uint8_t out[32]);
  * then refuse to run, as the execution contract prescribes).  Host-only. */
 int gdn_policy_check(const uint8_t mine[32], const uint8_t theirs[32]);
 
-/* Validate a policy against this build: GDN_OK, GDN_EINVAL or GDN_EUNSUPPORTED.  Host-only. */
+/* Validate a policy against what the library was compiled with: GDN_OK, GDN_EINVAL or
+ * GDN_EUNSUPPORTED.  Host-only. */
 int gdn_policy_validate(const gdn_policy* policy);
 
 /* Bytes of a state array for num_slots slots: num_slots * h_v * dv * dk * 4 (0 on bad input). */

@@ -189,7 +189,7 @@ def test_long_sequence_matches_oracle(long_x):
         check_close("bf16", o[:, h].float().cpu().numpy(), ref_o, f"o head {h}")
 
 
-@pytest.mark.parametrize("batch", [2, 8, 64])
+@pytest.mark.parametrize("batch", [2, 4, 8, 16, 32, 64])
 def test_long_sequence_invariant_to_neighbours(long_x, batch):
     x, so, sS, _ = long_x
     y, pos = gi.long_in_batch(x, batch, sub=batch)
