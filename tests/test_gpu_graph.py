@@ -67,11 +67,13 @@ def test_decode_step_graph_replays_match_eager(boundary):
     assert graphed.boundary_pos.tolist() == eager.boundary_pos.tolist()
 
 
-def test_continuation_prefill_graph_replays_match_eager():
+@pytest.mark.parametrize("entry", ["gdn_prefill", "gdn_prefill_fused", "gdn_prefill_overlapped"])
+def test_continuation_prefill_graph_replays_match_eager(entry):
     cpr = lib()
+    run = getattr(cpr, entry)
     n, reps = 3, 4
     x = gi.make_inputs(93, [40] * n * reps, h_k=2, h_v=4, dk=64, dv=64, chunk=32, io="bf16").to("cuda")
-    say("graph: continuation prefill")
+    say(f"graph: continuation prefill ({entry})")
     eager, graphed = _pools(x, n, boundary=False)
     ids = torch.arange(n, dtype=torch.int32, device="cuda")
     cu = torch.tensor([0, 40, 80, 120], dtype=torch.int32, device="cuda")
@@ -85,12 +87,12 @@ def test_continuation_prefill_graph_replays_match_eager():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        cpr.gdn_prefill(scratch, cu, sq, sk, sv, sa, sb, slot_ids=ids, from_state=True, o=so, chunk_states=cs)
+        run(scratch, cu, sq, sk, sv, sa, sb, slot_ids=ids, from_state=True, o=so, chunk_states=cs)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        cpr.gdn_prefill(graphed, cu, sq, sk, sv, sa, sb, slot_ids=ids, from_state=True, o=so, chunk_states=cs)
+        run(graphed, cu, sq, sk, sv, sa, sb, slot_ids=ids, from_state=True, o=so, chunk_states=cs)
     torch.cuda.synchronize()
     for r in range(reps):
         sq.copy_(x.q[part(r)]); sk.copy_(x.k[part(r)]); sv.copy_(x.v[part(r)])
