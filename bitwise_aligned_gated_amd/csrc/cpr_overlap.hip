@@ -147,8 +147,8 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
     }
     if (A.round_boundary && m.p0 % C == 0) resync_round(s);   // the first token is a chunk start
     if (act) store_f32x8(&L.hs[0][cw][g * kLeaf], s);
-    int nb = static_cast<int>(C - m.p0 % C);                   // tokens until the next chunk start
-    int left = nb < m.len ? nb : m.len;                        // tokens of this chunk still to run
+    const int first = static_cast<int>(C - m.p0 % C);          // tokens until the next chunk start
+    int left = first < m.len ? first : m.len;                  // tokens of this chunk still to run
     int c = 0;                                                 // chunk being run
     int cbuf = 0, pos = static_cast<int>(m.p0 % C);            // its hand-off buffer; token position
     float pc = 0.0f;                                           // c of the previous token, not yet in LDS

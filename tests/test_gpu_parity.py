@@ -219,6 +219,28 @@ def test_fused_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
 
 
+@pytest.mark.parametrize("dim,io", [(16, "f32"), (128, "bf16")])
+def test_column_permutation_permutes_outputs_bitwise(dim, io):
+    """Permuting the d_v columns of v and of the initial state permutes the columns of o and of the
+    final state bit for bit: every column runs the same arithmetic on its own data, whichever lanes
+    and workgroups hold it."""
+    import dataclasses
+    cpr = lib()
+    x = gi.make_inputs(35, [70, 1, 130], h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io=io)
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(dim))
+    s0 = torch.randn((x.num_seqs, x.h_v, dim, dim), generator=torch.Generator().manual_seed(5)) * 0.1
+    say(f"column permutation dim={dim} io={io}")
+    pool1 = cpr.StatePool(policy_of(x), x.num_seqs)
+    pool1.state.copy_(s0.cuda())
+    o1, pool1, _ = prefill(x, pool=pool1, from_state=True)
+    xp = dataclasses.replace(x, v=x.v[:, :, perm].contiguous())
+    pool2 = cpr.StatePool(policy_of(x), x.num_seqs)
+    pool2.state.copy_(s0[:, :, perm, :].contiguous().cuda())      # state [slot][H_v][d_v][d_k]
+    o2, pool2, _ = prefill(xp, pool=pool2, from_state=True)
+    assert sha(o2) == sha(o1[:, :, perm.cuda()].contiguous())
+    assert sha(pool2.state) == sha(pool1.state[:, :, perm.cuda(), :].contiguous())
+
+
 @pytest.mark.parametrize("dim", [16, 32, 64, 128])
 def test_prefill_under_a_grid_cap_matches_the_natural_launch(dim):
     """A ragged batch (empty, one-token and multi-chunk sequences) with every capped kernel limited
