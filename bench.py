@@ -150,6 +150,32 @@ def decode_bytes(batch, h_k, h_v, dk, dv, io_bytes=2):
     return state + tokens
 
 
+def host_environment():
+    """Host-side facts for the record, gathered before anything touches the GPU: the CPU model,
+    the numpy version and the GPU clocks rocm-smi reports before the run, i.e. at idle (None where
+    a tool is missing)."""
+    import subprocess
+    env = {"cpu_model": None, "host_cpus": os.cpu_count(), "numpy": None, "gpu_clocks_idle": None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            env["cpu_model"] = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        import numpy
+        env["numpy"] = numpy.__version__
+    except ImportError:
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        if r.returncode == 0:
+            card = next(iter(json.loads(r.stdout).values()), {})
+            env["gpu_clocks_idle"] = {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk", "socclk"))} or card
+    except (OSError, ValueError, subprocess.SubprocessError, StopIteration, AttributeError):
+        pass
+    return env
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +198,7 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         sys.exit("--steps must be >= 1 and --warmup >= 0")
 
+    host_env = host_environment()
     pool = None if args.no_cpu_baseline else _start_pool(args.cpu_workers)
 
     import numpy as np
@@ -498,7 +525,8 @@ def main():
                "sample": f"the whole prefill workload ({B}x{x.lengths[0]} tokens, {P.h_v} value heads): "
                          f"{len(items)} (sequence, head) recurrences over a {args.cpu_workers}-process pool, "
                          f"{cpu_wall:.1f} s wall",
-               "parity_vs_gpu": {"max_normwise_o": worst_o, "max_normwise_S": worst_S, "tolerance": 3e-3}}
+               "parity_vs_gpu": {"max_normwise_o": worst_o, "max_normwise_S": worst_S, "tolerance": 3e-3},
+               "cpu_model": host_env["cpu_model"], "numpy": host_env["numpy"]}
 
     out = {
         "metric": METRIC, "value": round(N / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
@@ -518,6 +546,9 @@ def main():
         "decode": decode,
         "trainer": trainer,
         "cpu_baseline": cpu,
+        "environment": {"gpu": torch.cuda.get_device_name(0),
+                        "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+                        "hip": torch.version.hip, "torch": torch.__version__, **host_env},
         "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "prefill_5x2048_native": 0.844,
                                           "decode_256x1_cpr": 0.0846, "decode_256x1_native": 0.0612,
                                           "trainer_fwd_bwd_10240_cpr": 7.386, "trainer_fwd_bwd_10240_native": 5.177},
