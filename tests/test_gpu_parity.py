@@ -219,6 +219,34 @@ def test_fused_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
 
 
+def test_many_sequences_beyond_one_scan_block():
+    """700 ragged sequences (0..40 tokens, empty ones included) are more than a workgroup has
+    threads, so the device-side varlen planners scan cu_seqlens in several blocks: the two-pass
+    prefill with and without the c stash, the one-pass kernel and the overlapped kernel (under a
+    cap that lets it run) agree bit for bit, and sampled sequences match the oracle."""
+    cpr = lib()
+    lens = [(37 * i) % 41 for i in range(700)]
+    x = gi.make_inputs(36, lens, h_k=1, h_v=2, dk=16, dv=16, chunk=16, io="f32")
+    say("700 ragged sequences")
+    n = int(cpr.gdn_chunk_rows(x.cu_seqlens, 16)[-1])
+    o0, pool0, cs0 = prefill(x)
+    ref = (sha(o0), sha(pool0.state), pool0.pos.tolist(), sha(cs0[:n]))
+    o1, pool1, cs1 = prefill(x, c_stash=False)
+    assert (sha(o1), sha(pool1.state), pool1.pos.tolist(), sha(cs1[:n])) == ref
+    o2, pool2, cs2 = _fused(x)
+    assert (sha(o2), sha(pool2.state), pool2.pos.tolist(), sha(cs2[:n])) == ref
+    pool3 = cpr.StatePool(policy_of(x), x.num_seqs)
+    pool3.set_max_workgroups(200)
+    o3, pool3, cs3 = _fused(x, pool=pool3, overlapped=True)
+    assert (sha(o3), sha(pool3.state), pool3.pos.tolist(), sha(cs3[:n])) == ref
+    for i in (3, 350, 699):
+        for h in range(x.h_v):
+            ref_o, ref_S, _ = oracle_seq_head(x, i, h)
+            t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+            check_close("f32", o0[t0:t1, h].float().cpu().numpy(), ref_o, f"o seq {i} head {h}")
+            check_close("f32", gpu_state_math(pool0, i, h), ref_S, f"S seq {i} head {h}")
+
+
 @pytest.mark.parametrize("dim,io", [(16, "f32"), (128, "bf16")])
 def test_column_permutation_permutes_outputs_bitwise(dim, io):
     """Permuting the d_v columns of v and of the initial state permutes the columns of o and of the
