@@ -432,7 +432,7 @@ __device__ __forceinline__ double block_sum_f64(double x, double* red) {
 // Stage rows [j0, j0 + HR) of a D x D fp32 matrix in [dv][dk] layout into S.u.p.mat (row r at
 // mrow(r)), and the same
 // rows of C^T (C [t][j] of this chunk, zero past its n tokens) into S.u.p.ct.
-template <int D, bool DIRECT>
+template <int D, bool DIRECT, bool CT = true>
 __device__ __forceinline__ void stage_part(MLds<D>& S, const float* mat, const float* cc, int64_t tok, int n,
                                            int h_v, int h, int j0) {
   using M = MCfg<D>;
@@ -453,7 +453,7 @@ __device__ __forceinline__ void stage_part(MLds<D>& S, const float* mat, const f
           reinterpret_cast<const float4*>(mat + static_cast<int64_t>(j0 + r) * D)[c4];
     }
   }
-  for (int e = threadIdx.x; e < M::L * M::HR / 4; e += 256) {
+  for (int e = threadIdx.x; CT && e < M::L * M::HR / 4; e += 256) {
     const int t = e / (M::HR / 4), c4 = e % (M::HR / 4);
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (t < n) x = *reinterpret_cast<const float4*>(cc + ((tok + t) * h_v + h) * D + j0 + 4 * c4);
@@ -577,14 +577,9 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
           }
         }
       }
-    }
-    const double h0 = block_sum_f64(hp, S.red);
-    // dk += (Gam_L / Gam_t) C G_end^T
-#pragma unroll 1
-    for (int part = 0; part < NH; ++part) {
-      const int j0 = part * HR;
+      // dk += (Gam_L / Gam_t) C G_end^T over the same columns, while their C^T is staged
       __syncthreads();
-      stage_part<D, DS>(S, ge, A.cc, tok, L, A.h_v, h, j0);
+      stage_part<D, DS, false>(S, ge, A.cc, tok, L, A.h_v, h, j0);   // C^T of this part stays
       __syncthreads();
 #pragma unroll 1
       for (int p = 0; p < HR / 16; ++p) {
@@ -599,6 +594,7 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
         }
       }
     }
+    const double h0 = block_sum_f64(hp, S.red);
     __syncthreads();                                         // C^T and G_end reads done
     // A1, A2 -> LDS; K rows -> LDS
 #pragma unroll
