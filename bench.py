@@ -281,6 +281,13 @@ def main():
     o_host = o.float().cpu().numpy()
     S_host = spool.state.cpu().numpy()
     digest_two_pass = hashlib.sha256(o.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
+    # SHA-256 identity digests of the timed call (the execution contract's admission check):
+    # inputs (q, k, v, a, b bytes in that order), o, and the final states
+    hin = hashlib.sha256()
+    for t in (x.q, x.k, x.v, x.a, x.b):
+        hin.update(t.contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    identity = {"inputs": hin.hexdigest(), "o": digest_two_pass,
+                "final_state": hashlib.sha256(spool.state.view(torch.uint8).cpu().numpy().tobytes()).hexdigest()}
 
     # the same call without the c stash (pass 2 predicts every c again): context, same bits
     npool = cpr.StatePool(P, B, device=dev)
@@ -540,6 +547,7 @@ def main():
                     "cpr_bytes": int(cpr_bytes), "hbm_frac": round(prefill_gbs / HBM_PEAK_GBS, 4),
                     "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                 for k, v in kernels.items()},
+                    "sha256": identity,
                     "without_c_stash": no_stash, "one_pass_variant": fused, "chunked_matrix_core": chunked,
                     "long_sequence": long_seq},
         "roofline": roofline,

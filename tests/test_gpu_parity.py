@@ -187,6 +187,19 @@ def test_repeat_runs_are_identical():
         assert [sha(prefill(x)[0])] == first
 
 
+@pytest.mark.parametrize("chunk", [1, 16])
+def test_overlapped_repeat_runs_are_identical(chunk):
+    """The overlapped kernel's waves meet through LDS counters; a missing or misplaced wait would
+    show up as run-to-run differences.  Chunk 1 hands over a chunk at every token.  Five runs,
+    each equal to gdn_prefill bit for bit."""
+    x = gi.make_inputs(18, [700, 45, 1], h_k=2, h_v=4, dk=128, dv=128, chunk=chunk, io="bf16")
+    say(f"overlapped repeat runs, chunk {chunk}")
+    o_ref, pool_ref, _ = prefill(x, chunk=chunk)
+    for _ in range(5):
+        o, pool, _ = _fused(x, chunk=chunk, overlapped=True)
+        assert sha(o) == sha(o_ref) and sha(pool.state) == sha(pool_ref.state)
+
+
 def _fused(x, chunk=None, pool=None, from_state=False, stash=True, overlapped=False):
     cpr = lib()
     xd = x.to("cuda")
