@@ -150,6 +150,13 @@ def decode_bytes(batch, h_k, h_v, dk, dv, io_bytes=2):
     return state + tokens
 
 
+def _bf16_order(bits):
+    """bf16 bit patterns as integers in value order (so that |a - b| counts ulps; +0 and -0 meet)."""
+    import numpy as np
+    u = bits.astype(np.int64)
+    return np.where(u & 0x8000, -(u & 0x7FFF), u)
+
+
 def host_environment():
     """Host-side facts for the record, gathered before anything touches the GPU: the CPU model,
     the numpy version and the GPU clocks rocm-smi reports before the run, i.e. at idle (None where
@@ -279,6 +286,7 @@ def main():
 
     # parity of the timed prefill output against the oracle (computed in the CPU leg below)
     o_host = o.float().cpu().numpy()
+    o_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
     S_host = spool.state.cpu().numpy()
     digest_two_pass = hashlib.sha256(o.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
     # SHA-256 identity digests of the timed call (the execution contract's admission check):
@@ -523,16 +531,23 @@ def main():
         pool.close()
         pool.join()
         worst_o = worst_S = 0.0
+        ulps = np.zeros(4, dtype=np.int64)          # o elements 0, 1, 2 and more bf16 ulps from the oracle
         for (i, h, s0, s1), (ro, rS, _) in zip(keys, res):
             d = np.linalg.norm(ro)
             worst_o = max(worst_o, float(np.linalg.norm(o_host[s0:s1, h] - ro) / (d if d else 1.0)))
             dS = np.linalg.norm(rS)
             worst_S = max(worst_S, float(np.linalg.norm(S_host[i, h].T - rS) / (dS if dS else 1.0)))
+            dist = np.abs(_bf16_order(o_bits[s0:s1, h]) - _bf16_order(gi.f32_to_bf16_bits(ro.astype(np.float32))))
+            ulps += np.bincount(np.minimum(dist, 3).ravel(), minlength=4)
         cpu = {"value": round(N / cpu_wall, 1), "unit": "tok/s", "cores": args.cpu_workers, "kind": "oracle",
                "sample": f"the whole prefill workload ({B}x{x.lengths[0]} tokens, {P.h_v} value heads): "
                          f"{len(items)} (sequence, head) recurrences over a {args.cpu_workers}-process pool, "
                          f"{cpu_wall:.1f} s wall",
-               "parity_vs_gpu": {"max_normwise_o": worst_o, "max_normwise_S": worst_S, "tolerance": 3e-3},
+               "parity_vs_gpu": {"max_normwise_o": worst_o, "max_normwise_S": worst_S, "tolerance": 3e-3,
+                                 "o_bf16_ulps": {"0": int(ulps[0]), "1": int(ulps[1]), "2": int(ulps[2]),
+                                                 "more": int(ulps[3])},
+                                 "o_bf16_ulps_note": "distance of each bf16 output from the oracle's value "
+                                                     "rounded to fp32 and then to bf16"},
                "cpu_model": host_env["cpu_model"], "numpy": host_env["numpy"]}
 
     out = {
