@@ -521,8 +521,6 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
                  size_t workspace_bytes, void* stream, void* const* events) {
   if (int rc = gdn_policy_validate(policy); rc != GDN_OK) return rc;
   const gdn_policy& P = *policy;
-  if (P.state_dtype != GDN_F32)
-    return fail(GDN_EUNSUPPORTED, "gdn_backward: only the fp32 boundary dtype has a backward");
   if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "gdn_backward: chunk %d > 64", P.chunk);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_backward: negative sizes");
   if (total_tokens >= (int64_t(1) << 31))

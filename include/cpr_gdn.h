@@ -337,9 +337,12 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
 /* Gradients of a trainer forward (gdn_trainer_forward, gdn_prefill or gdn_prefill_fused over the
  * same packed batch, every sequence starting at position 0: from_state 0, or 1 from slots at
  * position 0).
- *   policy        the forward's policy; the fp32 boundary dtype and chunk <= 64 are supported
- *                 (GDN_EUNSUPPORTED otherwise).  Every gate a_t must be positive (da_t is
- *                 obtained by dividing by a_t); the gate form exp(-softplus(x)) always is.
+ *   policy        the forward's policy; chunk <= 64 is supported (GDN_EUNSUPPORTED otherwise).
+ *                 With the bf16 boundary dtype the rounding at chunk starts is read as the
+ *                 identity (straight-through): the gradients are those of the trajectory the
+ *                 forward took (from its rounded chunk-start states), with dL/dS passed through
+ *                 each rounding unchanged.  Every gate a_t must be positive (da_t is obtained by
+ *                 dividing by a_t); the gate form exp(-softplus(x)) always is.
  *   cu_seqlens, total_tokens, q, k, v, a, b   the forward's inputs (device, layouts above).
  *   chunk_states  the forward's stash, chunk_state_rows >= total_tokens / C + num_seqs (any
  *                 forward stash qualifies): row 0 of a sequence is its initial state S_0.

@@ -22,32 +22,52 @@ for a loss L with upstream gradients dO_t = dL/do_t and dS_T = dL/dS_T.  With G_
     G_{t-1} = a_t Ghat_t + k_t du_t^T
 
 and dS_0 = G_0.  Key heads receive the sum of their value heads' dq and dk.
+
+Boundary dtype.  With bf16 boundaries the forward rounds S to bf16 just before each token at a
+chunk-start position (the forward oracle's resynchronisation).  Rounding has a zero derivative
+almost everywhere, so the backward reads it as the identity (straight-through): every formula above
+uses the state the token actually read, and G passes through the rounding unchanged.  A caller
+may instead hand in the chunk-start states a forward used (`starts`), so that the gradients follow
+exactly that trajectory.
 """
 from __future__ import annotations
 
 import numpy as np
 
+from .gdn_oracle import round_to_bf16
+
 __all__ = ["recurrence_backward", "gdn_varlen_backward"]
 
 
-def recurrence_backward(q, k, v, a, b, dO, S0=None, dS_T=None):
-    """Gradients for one (sequence, value head), in fp64.
+def recurrence_backward(q, k, v, a, b, dO, S0=None, dS_T=None, chunk: int = 64, boundary: str = "f32",
+                        starts=None):
+    """Gradients for one (sequence, value head), in fp64, for a forward that starts at position 0.
 
     q, k: [T, d_k]; v: [T, d_v]; a, b: [T]; dO: [T, d_v]; S0, dS_T: [d_k, d_v] or None (zero).
+    boundary "bf16": S is rounded to bf16 before every token at a multiple of `chunk` (straight-
+    through in the backward).  starts: optional {t: [d_k, d_v]} states that replace S just before
+    token t (the chunk-start states a forward used).
     Returns (dq [T, d_k], dk [T, d_k], dv [T, d_v], da [T], db [T], dS0 [d_k, d_v])."""
     q, k, v, a, b, dO = (np.asarray(x, np.float64) for x in (q, k, v, a, b, dO))
+    if boundary not in ("f32", "bf16"):
+        raise ValueError("boundary must be 'f32' or 'bf16'")
     T, dk_ = k.shape
     dv_ = v.shape[1]
     S = np.zeros((dk_, dv_)) if S0 is None else np.array(S0, dtype=np.float64, copy=True)
-    # forward, keeping every state and the per-token intermediates
-    states = [S]
+    # forward, keeping the state each token read, the state it left and its intermediates
+    prev, after = [], []
     us, ws, cs = [], [], []
     for t in range(T):
+        if starts is not None and t in starts:
+            S = np.array(starts[t], dtype=np.float64, copy=True)
+        elif boundary == "bf16" and t % chunk == 0:
+            S = round_to_bf16(S)
+        prev.append(S)
         u = S.T @ k[t]
         w = v[t] - a[t] * u
         c = b[t] * w
         S = a[t] * S + np.outer(k[t], c)
-        states.append(S)
+        after.append(S)
         us.append(u)
         ws.append(w)
         cs.append(c)
@@ -58,7 +78,7 @@ def recurrence_backward(q, k, v, a, b, dO, S0=None, dS_T=None):
     da = np.zeros(T)
     db = np.zeros(T)
     for t in range(T - 1, -1, -1):
-        S_prev, S_t = states[t], states[t + 1]
+        S_prev, S_t = prev[t], after[t]
         Gh = G + np.outer(q[t], dO[t])
         dq[t] = S_t @ dO[t]
         dc = Gh.T @ k[t]
@@ -74,10 +94,13 @@ def recurrence_backward(q, k, v, a, b, dO, S0=None, dS_T=None):
     return dq, dkk, dv, da, db, G
 
 
-def gdn_varlen_backward(q, k, v, a, b, dO, cu_seqlens, h_k: int, h_v: int, S0=None, dS_T=None):
+def gdn_varlen_backward(q, k, v, a, b, dO, cu_seqlens, h_k: int, h_v: int, S0=None, dS_T=None,
+                        chunk: int = 64, boundary: str = "f32", chunk_states=None, row0=None):
     """Gradients over a packed batch.  q, k: [N, H_k, d_k]; v, dO: [N, H_v, d_v]; a, b: [N, H_v];
-    S0, dS_T: [B, H_v, d_k, d_v] or None.  Returns (dq, dk [N, H_k, d_k], dv [N, H_v, d_v],
-    da, db [N, H_v], dS0 [B, H_v, d_k, d_v]); dq and dk of a key head sum its value heads."""
+    S0, dS_T: [B, H_v, d_k, d_v] or None.  chunk_states [rows, H_v, d_k, d_v] with row0[i] the
+    first row of sequence i: the chunk-start states a forward used (chunk c of sequence i starts
+    from row row0[i] + c).  Returns (dq, dk [N, H_k, d_k], dv [N, H_v, d_v], da, db [N, H_v],
+    dS0 [B, H_v, d_k, d_v]); dq and dk of a key head sum its value heads."""
     group = h_v // h_k
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     B, N = len(cu) - 1, int(cu[-1])
@@ -92,9 +115,13 @@ def gdn_varlen_backward(q, k, v, a, b, dO, cu_seqlens, h_k: int, h_v: int, S0=No
         t0, t1 = int(cu[i]), int(cu[i + 1])
         for h in range(h_v):
             g = h // group
+            starts = None
+            if chunk_states is not None:
+                starts = {c * chunk: chunk_states[int(row0[i]) + c, h] for c in range((t1 - t0 + chunk - 1) // chunk)}
             r = recurrence_backward(q[t0:t1, g], k[t0:t1, g], v[t0:t1, h], a[t0:t1, h], b[t0:t1, h],
                                     dO[t0:t1, h], None if S0 is None else S0[i, h],
-                                    None if dS_T is None else dS_T[i, h])
+                                    None if dS_T is None else dS_T[i, h], chunk=chunk, boundary=boundary,
+                                    starts=starts)
             dq[t0:t1, g] += r[0]
             dkk[t0:t1, g] += r[1]
             dv[t0:t1, h] = r[2]

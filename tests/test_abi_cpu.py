@@ -227,8 +227,9 @@ def test_backward_argument_errors_before_launch():
                                 rows, None, d_o, None, fake, fake, fake, fake, fake, None, ws, ws_bytes, None, None)
 
     f32 = cpr.Policy(2, 4, 16, 16, chunk=64, io="f32")
-    assert call(cpr.Policy(2, 4, 16, 16, chunk=64, io="f32", boundary="bf16")) == 2
-    assert b"boundary" in lib.gdn_last_error()
+    # the bf16 boundary dtype has a backward (straight-through) and meets the same checks
+    assert call(cpr.Policy(2, 4, 16, 16, chunk=64, io="f32", boundary="bf16"), rows=2) == 1
+    assert b"chunk_state_rows" in lib.gdn_last_error()
     assert call(cpr.Policy(2, 4, 16, 16, chunk=128, io="f32")) == 2
     assert call(cpr.Policy(2, 3, 16, 16, chunk=64, io="f32")) == 1            # H_v not a multiple of H_k
     assert call(f32, rows=2) == 1 and b"chunk_state_rows" in lib.gdn_last_error()   # needs 100/64 + 2 = 3

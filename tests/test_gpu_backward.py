@@ -35,11 +35,11 @@ def _close(got, ref, what):
     assert normwise(got, ref) <= NORMWISE, f"{what}: normwise {normwise(got, ref):.3e}"
 
 
-def _forward(x, s0=None, fused=False):
+def _forward(x, s0=None, fused=False, policy=None):
     """Trainer forward on the GPU; returns the chunk-state stash."""
     cpr = lib()
     xd = x.to("cuda")
-    pool = cpr.StatePool(policy_of(x), max(x.num_seqs, 1))
+    pool = cpr.StatePool(policy or policy_of(x), max(x.num_seqs, 1))
     if s0 is not None:
         pool.state[: x.num_seqs].copy_(s0)
     fn = cpr.gdn_prefill_fused if fused else cpr.gdn_prefill
@@ -49,23 +49,29 @@ def _forward(x, s0=None, fused=False):
     return cs
 
 
-def _backward(x, ct, cs, want_d_state0=True):
+def _backward(x, ct, cs, want_d_state0=True, policy=None):
     cpr = lib()
     xd = x.to("cuda")
     d_state = None if ct["d_state"] is None else ct["d_state"].to("cuda")
-    g = cpr.gdn_backward(policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs, ct["d_o"].to("cuda"),
+    g = cpr.gdn_backward(policy or policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs, ct["d_o"].to("cuda"),
                          d_state=d_state, want_d_state0=want_d_state0)
     torch.cuda.synchronize()
     return g
 
 
-def _oracle(x, ct):
+def _oracle(x, ct, starts=None):
+    """The adjoint oracle; `starts` (the forward's stash) pins it to the trajectory the GPU forward
+    took from its chunk-start states."""
     cpu = x.to("cpu")
     dO = ct["d_o"].cpu().double().numpy()
     dS = None if ct["d_state"] is None else ct["d_state"].cpu().double().numpy().transpose(0, 1, 3, 2)
     S0 = None if ct["s0"] is None else ct["s0"].cpu().double().numpy().transpose(0, 1, 3, 2)
+    kw = {}
+    if starts is not None:
+        kw = dict(chunk=x.chunk, chunk_states=starts.cpu().double().numpy().transpose(0, 1, 3, 2),
+                  row0=lib().gdn_chunk_rows(x.cu_seqlens, x.chunk).numpy())
     return gdn_varlen_backward(cpu.widen("q"), cpu.widen("k"), cpu.widen("v"), cpu.widen("a"), cpu.widen("b"),
-                               dO, x.cu_seqlens, x.h_k, x.h_v, S0=S0, dS_T=dS)
+                               dO, x.cu_seqlens, x.h_k, x.h_v, S0=S0, dS_T=dS, **kw)
 
 
 def _compare_all(x, g, ref):
@@ -101,6 +107,25 @@ def test_backward_matches_oracle(dim, io, chunk, with_ds, with_s0):
     cs = _forward(x, None if ct["s0"] is None else ct["s0"].to("cuda"))
     g = _backward(x, ct, cs)
     _compare_all(x, g, _oracle(x, ct))
+
+
+@pytest.mark.parametrize("dim,io,chunk", [(16, "f32", 8), (128, "bf16", 64)])
+def test_backward_bf16_boundaries_straight_through(dim, io, chunk):
+    """bf16 boundary dtype: the forward rounds the state at every chunk start and the backward
+    reads the rounding as the identity.  Against the adjoint oracle run on the GPU forward's own
+    chunk-start states (the trajectory the forward took), at the fp32 tolerances; the stash rows
+    are bf16 values, so the rounding did happen."""
+    lens = [1, 64, 65, 200, 0, 33]
+    x = gi.make_inputs(65, lens, h_k=2, h_v=4, dk=dim, dv=dim, chunk=chunk, io=io)
+    ct = gi.make_cotangents(x, 66, with_d_state=True, with_s0=True)
+    pol = lib().Policy(x.h_k, x.h_v, x.dk, x.dv, chunk, io, boundary="bf16")
+    say(f"backward, bf16 boundaries, dim={dim} io={io} C={chunk}")
+    cs = _forward(x, ct["s0"].to("cuda"), policy=pol)
+    n = int(lib().gdn_chunk_rows(x.cu_seqlens, chunk)[-1])
+    rows = cs[:n].cpu()
+    assert torch.equal(rows, rows.to(torch.bfloat16).to(torch.float32))
+    g = _backward(x, ct, cs, policy=pol)
+    _compare_all(x, g, _oracle(x, ct, starts=cs[:n]))
 
 
 def test_backward_gqa_ratio_four():

@@ -59,6 +59,53 @@ def test_backward_matches_torch_autograd():
         assert np.allclose(g, t.grad.numpy(), rtol=1e-11, atol=1e-12)
 
 
+def test_bf16_boundaries_match_torch_straight_through_autograd():
+    """With bf16 boundaries the oracle's gradients are those of the rounded forward with the
+    rounding read as the identity: torch fp64 autograd of a separately written forward in which each
+    chunk start does S = S + (bf16(S) - S).detach() gives the same gradients."""
+    q, k, v, a, b, S0, dO, dST = _case(4, T=19, dk=8, dv=6)
+    C = 4
+    T_ = lambda x: torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    tq, tk, tv, ta, tb, tS = T_(q), T_(k), T_(v), T_(a), T_(b), T_(S0)
+    S = tS
+    outs = []
+    for t in range(q.shape[0]):
+        if t % C == 0:
+            r = S.detach().to(torch.float32).to(torch.bfloat16).to(torch.float64)
+            S = S + (r - S).detach()
+        kt = tk[t]
+        corr = tv[t] - ta[t] * (kt @ S)
+        S = ta[t] * S + tb[t] * torch.outer(kt, corr)
+        outs.append(tq[t] @ S)
+    loss = (torch.stack(outs) * torch.tensor(dO)).sum() + (S * torch.tensor(dST)).sum()
+    loss.backward()
+    ours = recurrence_backward(q, k, v, a, b, dO, S0=S0, dS_T=dST, chunk=C, boundary="bf16")
+    for g, t in zip(ours, (tq, tk, tv, ta, tb, tS)):
+        assert np.allclose(g, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+    # the rounding is real: the f32-boundary gradients differ
+    plain = recurrence_backward(q, k, v, a, b, dO, S0=S0, dS_T=dST)
+    assert not np.allclose(plain[3], ours[3], rtol=1e-6, atol=0)
+
+
+def test_given_chunk_starts_reproduce_the_trajectory():
+    """Handing the backward the chunk-start states its own bf16-boundary forward used gives the
+    same gradients as letting it round; with f32 boundaries the f32 forward's own starts change
+    nothing."""
+    q, k, v, a, b, S0, dO, dST = _case(5, T=13, dk=8, dv=4)
+    C = 4
+    _, _, rows = recurrence(q, k, v, a, b, S0=S0, chunk=C, boundary="bf16")
+    starts = {c * C: rows[c] for c in range(len(rows))}
+    ref = recurrence_backward(q, k, v, a, b, dO, S0=S0, dS_T=dST, chunk=C, boundary="bf16")
+    got = recurrence_backward(q, k, v, a, b, dO, S0=S0, dS_T=dST, chunk=C, starts=starts)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+    _, _, rows32 = recurrence(q, k, v, a, b, S0=S0, chunk=C)
+    got32 = recurrence_backward(q, k, v, a, b, dO, S0=S0, dS_T=dST, chunk=C,
+                                starts={c * C: rows32[c] for c in range(len(rows32))})
+    for g, r in zip(got32, recurrence_backward(q, k, v, a, b, dO, S0=S0, dS_T=dST)):
+        assert np.allclose(g, r, rtol=1e-12, atol=1e-13)
+
+
 def test_varlen_backward_sums_value_heads_into_key_heads():
     r = np.random.default_rng(4)
     lens, hk, hv, dk, dv = [5, 0, 9], 1, 2, 4, 3
