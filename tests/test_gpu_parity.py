@@ -232,6 +232,33 @@ def test_fused_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
 
 
+@pytest.mark.parametrize("dim,io", [(16, "f32"), (128, "bf16")])
+def test_degenerate_gates(dim, io):
+    """The method's degenerate cases on the GPU.  a = 1, b = 0: the update writes nothing, so the
+    final state is the initial one bit for bit (fma(k, 0, 1 * S) = S) and o_t = S_0^T q_t.  a = 0:
+    the state forgets everything each token, S_t = b_t k_t v_t^T and o_t = b_t (k_t . q_t) v_t.
+    Outputs against the oracle at the usual tolerances."""
+    import dataclasses
+    cpr = lib()
+    x = gi.make_inputs(37, [50, 1, 77], h_k=2, h_v=4, dk=dim, dv=dim, chunk=32, io=io)
+    s0 = torch.randn((x.num_seqs, x.h_v, dim, dim), generator=torch.Generator().manual_seed(7)) * 0.1
+    for case, (av, bv) in {"keep": (1.0, 0.0), "forget": (0.0, None)}.items():
+        say(f"degenerate gates {case} dim={dim} io={io}")
+        xa = dataclasses.replace(x, a=torch.full_like(x.a, av), b=x.b if bv is None else torch.full_like(x.b, bv))
+        pool = cpr.StatePool(policy_of(xa), xa.num_seqs)
+        pool.state.copy_(s0.cuda())
+        o, pool, _ = prefill(xa, pool=pool, from_state=True)
+        if case == "keep":
+            assert torch.equal(pool.state.cpu(), s0)
+        for i in range(xa.num_seqs):
+            t0, t1 = int(xa.cu_seqlens[i]), int(xa.cu_seqlens[i + 1])
+            for h in (0, 3):
+                S0_math = s0[i, h].double().numpy().T
+                ref_o, ref_S, _ = oracle_seq_head(xa, i, h, S0=S0_math)
+                check_close(io, o[t0:t1, h].float().cpu().numpy(), ref_o, f"{case} o seq {i} head {h}")
+                check_close(io, gpu_state_math(pool, i, h), ref_S, f"{case} S seq {i} head {h}")
+
+
 def test_many_sequences_beyond_one_scan_block():
     """700 ragged sequences (0..40 tokens, empty ones included) are more than a workgroup has
     threads, so the device-side varlen planners scan cu_seqlens in several blocks: the two-pass
