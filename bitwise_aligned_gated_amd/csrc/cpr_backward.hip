@@ -724,6 +724,26 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
   }
 }
 
+// One block per sequence: where its rows start in the caller's stash (chunk A.chunk), as a slot
+// id over that stash, with a zero position there, so that pass 1 at the gradient tile's chunk
+// starts every sequence from the state it began with.
+__global__ void __launch_bounds__(256) rechunk_setup_kernel(BackwardArgs A, int32_t* slot_ids, int64_t* pos) {
+  __shared__ int64_t red[(256 + 63) / 64 + 2];
+  const int j = blockIdx.x;
+  const int64_t r0 = plan_row_offset(A, j, red);
+  if (threadIdx.x == 0) {
+    slot_ids[j] = static_cast<int32_t>(r0 < A.rows_cap ? r0 : A.rows_cap);
+    if (r0 < A.rows_cap) pos[r0] = 0;
+  }
+}
+
+hipError_t launch_rechunk_setup(const BackwardArgs& A, int32_t* slot_ids, int64_t* pos, hipStream_t stream) {
+  if (A.num_seqs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rechunk_setup_kernel, dim3(static_cast<unsigned>(A.num_seqs)), dim3(256), 0, stream, A,
+                     slot_ids, pos);
+  return hipGetLastError();
+}
+
 template <int DK, int DV, int IO>
 static hipError_t launch_backward_t(const BackwardArgs& A, hipStream_t stream) {
   using Cfg = ColCfg<DK, DV>;

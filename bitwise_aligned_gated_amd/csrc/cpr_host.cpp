@@ -499,6 +499,20 @@ static int64_t backward_rows(int64_t total_tokens, int32_t num_seqs, int32_t chu
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// The chunk-gradient kernel's tile is 64 tokens.  A forward at a larger chunk (fp32 boundaries)
+// is differentiated on a 64-token stash that pass 1 recomputes from each sequence's first row:
+// under fp32 boundaries those rows are the bits a 64-token forward would have stored.
+constexpr int32_t kGradTile = 64;
+
+// Workspace beyond the gradient passes' own when the forward's chunk exceeds the tile: the
+// 64-token stash, a slot id per sequence and a position per row of the forward's stash.
+static int64_t rechunk_bytes(const gdn_policy& P, int64_t total_tokens, int32_t num_seqs) {
+  if (P.chunk <= kGradTile) return 0;
+  const int64_t plane = int64_t(P.dk) * P.dv;
+  return align256(backward_rows(total_tokens, num_seqs, kGradTile) * P.h_v * plane * 4) +
+         align256(int64_t(num_seqs) * 4) + align256(backward_rows(total_tokens, num_seqs, P.chunk) * 8);
+}
+
 int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs) {
   if (gdn_policy_validate(policy) != GDN_OK) return -1;
   if (total_tokens < 0 || num_seqs < 0) {
@@ -507,10 +521,11 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
   }
   const gdn_policy& P = *policy;
   const int64_t plane = int64_t(P.dk) * P.dv;
-  const int64_t adj = (backward_rows(total_tokens, num_seqs, P.chunk) + num_seqs) * P.h_v * plane * 4;
+  const int32_t chunk = P.chunk < kGradTile ? P.chunk : kGradTile;   // the gradient passes' chunk
+  const int64_t adj = (backward_rows(total_tokens, num_seqs, chunk) + num_seqs) * P.h_v * plane * 4;
   const int64_t per_token = total_tokens * P.h_v * int64_t(P.dv) * 4;
   ok();
-  return align256(adj) + 3 * align256(per_token);
+  return align256(adj) + 3 * align256(per_token) + rechunk_bytes(P, total_tokens, num_seqs);
 }
 
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -521,7 +536,8 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
                  size_t workspace_bytes, void* stream, void* const* events) {
   if (int rc = gdn_policy_validate(policy); rc != GDN_OK) return rc;
   const gdn_policy& P = *policy;
-  if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "gdn_backward: chunk %d > 64", P.chunk);
+  if (P.chunk > kGradTile && P.state_dtype != GDN_F32)
+    return fail(GDN_EUNSUPPORTED, "gdn_backward: chunk %d > %d with bf16 boundaries", P.chunk, kGradTile);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_backward: negative sizes");
   if (total_tokens >= (int64_t(1) << 31))
     return fail(GDN_EINVAL, "gdn_backward: total_tokens must fit int32 cu_seqlens");
@@ -544,15 +560,54 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return fail(GDN_EINVAL, "gdn_backward: workspace must be 16-byte aligned");
   const int64_t plane = int64_t(P.dk) * P.dv;
-  const int64_t adj_bytes = align256((rows + num_seqs) * P.h_v * plane * 4);
+  const int32_t chunk = P.chunk < kGradTile ? P.chunk : kGradTile;   // the gradient passes' chunk
+  const int64_t rows_g = backward_rows(total_tokens, num_seqs, chunk);
+  if (rows_g * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_backward: too many chunks for one launch");
+  const int64_t adj_bytes = align256((rows_g + num_seqs) * P.h_v * plane * 4);
   const int64_t tok_bytes = align256(total_tokens * P.h_v * int64_t(P.dv) * 4);
   char* ws = static_cast<char*>(workspace);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const float* stash = chunk_states;
+  if (P.chunk > kGradTile && num_seqs > 0) {
+    // the 64-token stash: pass 1 from each sequence's first row of the caller's stash
+    char* xs = ws + adj_bytes + 3 * tok_bytes;
+    float* fine = reinterpret_cast<float*>(xs);
+    int32_t* ids = reinterpret_cast<int32_t*>(xs + align256(rows_g * P.h_v * plane * 4));
+    int64_t* pos = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(ids) + align256(int64_t(num_seqs) * 4));
+    cpr::BackwardArgs R{};
+    R.cu = cu_seqlens;
+    R.total_tokens = total_tokens;
+    R.num_seqs = num_seqs;
+    R.chunk = P.chunk;
+    R.rows_cap = rows;
+    hipError_t e = cpr::launch_rechunk_setup(R, ids, pos, hs);
+    if (e != hipSuccess) return hip_fail(e, "gdn_backward re-chunk setup");
+    cpr::PrefillArgs F{};
+    F.cu = cu_seqlens;
+    F.slot_ids = ids;
+    F.pos = pos;
+    F.pos_out = pos;
+    F.q = q; F.k = k; F.v = v; F.a = a; F.b = b;
+    F.o = nullptr;
+    F.state = const_cast<float*>(chunk_states);    // read only: every sequence continues from its row 0
+    F.chunk_states = fine;
+    F.total_tokens = total_tokens;
+    F.rows_cap = rows_g;
+    F.num_seqs = num_seqs;
+    F.num_slots = static_cast<int32_t>(rows);
+    F.from_state = 1;
+    F.h_k = P.h_k; F.h_v = P.h_v; F.chunk = kGradTile;
+    F.round_boundary = 0;
+    e = cpr::launch_boundary_pass(P.dk, P.dv, P.io_dtype, F, hs);
+    if (e != hipSuccess) return hip_fail(e, "gdn_backward re-chunk pass");
+    stash = fine;
+  }
   cpr::BackwardArgs A;
   A.cu = cu_seqlens;
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b;
   A.d_o = d_o;
   A.d_state = d_state;
-  A.chunk_states = chunk_states;
+  A.chunk_states = stash;
   A.adjoint = reinterpret_cast<float*>(ws);
   A.dc = reinterpret_cast<float*>(ws + adj_bytes);
   A.cc = reinterpret_cast<float*>(ws + adj_bytes + tok_bytes);
@@ -565,12 +620,12 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   A.dq = dq; A.dk = dk; A.dv = dv; A.da = da; A.db = db;
   A.d_state0 = d_state0;
   A.total_tokens = total_tokens;
-  A.rows_cap = rows;
-  A.adj_rows = rows + num_seqs;
+  A.rows_cap = rows_g;
+  A.adj_rows = rows_g + num_seqs;
   A.num_seqs = num_seqs;
-  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = chunk;
   A.events = events;
-  const hipError_t e = cpr::launch_backward(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  const hipError_t e = cpr::launch_backward(P.dk, P.dv, P.io_dtype, A, hs);
   if (e != hipSuccess) return hip_fail(e, "gdn_backward launch");
   return ok();
 }

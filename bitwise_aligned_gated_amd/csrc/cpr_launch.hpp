@@ -24,6 +24,11 @@ hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStr
 // started from chunk states already stored.
 hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream);
 hipError_t launch_output_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+// Pass 1 alone (chunk-start states up to each sequence's last chunk start, no c, no finish).
+hipError_t launch_boundary_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+// For a backward at a chunk above the chunk-gradient tile: slot_ids[j] = the first row of sequence
+// j in a stash at chunk A.chunk, and a zero position at each such row.
+hipError_t launch_rechunk_setup(const BackwardArgs& A, int32_t* slot_ids, int64_t* pos, hipStream_t stream);
 // Chunkwise evaluation on matrix cores: mode 0 native outputs, mode 1 chunk-form boundary states
 // followed by the CPR output pass.  ws holds chunked_workspace_floats(d) floats per chunk row and
 // value head.

@@ -600,6 +600,26 @@ static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream)
   return launch_prefill_finish(A, stream);
 }
 
+template <int DK, int DV, int IO>
+static hipError_t launch_boundary_pass_t(const PrefillArgs& A, hipStream_t stream) {
+  using C1 = PassCfg<DK, DV, kBoundary>;
+  if (A.num_seqs <= 0) return hipSuccess;
+  const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
+  return launch_items(boundary_pass_kernel<DK, DV, IO, kBoundary>, boundary_pass_strided_kernel<DK, DV, IO, kBoundary>,
+                      g1, C1::THREADS, stream, A);
+}
+
+hipError_t launch_boundary_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
+#define CPR_CASE(D, IOV) \
+  if (dk == D && dv == D && io == IOV) return launch_boundary_pass_t<D, D, IOV>(A, stream);
+  CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
+  CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
+  CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)
+  CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
+#undef CPR_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_output_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
 #define CPR_CASE(D, IOV) \
   if (dk == D && dv == D && io == IOV) return launch_output_pass_t<D, D, IOV>(A, stream);

@@ -330,14 +330,22 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
  * fixed order, so the gradients are bitwise reproducible for any batch composition or packing. */
 
 /* Workspace bytes gdn_backward needs for total_tokens tokens in num_seqs sequences (-1 on bad
- * input): dL/dS at every chunk boundary (total_tokens / C + 2 num_seqs states) and three fp32
- * per-token arrays of N * H_v * d_v (dc, c, w), each part padded to 256 bytes. */
+ * input): dL/dS at every boundary of 64-token (or C-token, C < 64) chunks (total_tokens / C' +
+ * 2 num_seqs states, C' = min(C, 64)) and three fp32 per-token arrays of N * H_v * d_v (dc, c,
+ * w); for C > 64 also a 64-token stash (total_tokens / 64 + num_seqs states), one int32 per
+ * sequence and one int64 per row of the forward's stash.  Each part is padded to 256 bytes. */
 int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
 
 /* Gradients of a trainer forward (gdn_trainer_forward, gdn_prefill or gdn_prefill_fused over the
  * same packed batch, every sequence starting at position 0: from_state 0, or 1 from slots at
  * position 0).
- *   policy        the forward's policy; chunk <= 64 is supported (GDN_EUNSUPPORTED otherwise).
+ *   policy        the forward's policy.  The chunk-gradient kernel's tile is 64 tokens: for a
+ *                 chunk C > 64 a fourth kernel first rebuilds the 64-token stash with the
+ *                 boundary pass, from each sequence's row 0 of `chunk_states`.  Under fp32
+ *                 boundaries a chunk-start state does not depend on C, so that stash holds the
+ *                 bits a 64-token forward would have stored and the gradients equal those for
+ *                 C = 64 bit for bit.  A bf16 boundary dtype with C > 64 is GDN_EUNSUPPORTED
+ *                 (its chunk starts differ).
  *                 With the bf16 boundary dtype the rounding at chunk starts is read as the
  *                 identity (straight-through): the gradients are those of the trajectory the
  *                 forward took (from its rounded chunk-start states), with dL/dS passed through
@@ -355,7 +363,8 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
  *                 continued from slots).
  *   workspace     device, 16-byte aligned, workspace_bytes >= gdn_backward_workspace_bytes().
  * Outputs are fully overwritten for every token of every well-formed sequence.  Three kernels on
- * `stream`; events: NULL, or 4 hipEvent_t recorded before, between and after them. */
+ * `stream` (after the stash rebuild when C > 64); events: NULL, or 4 hipEvent_t recorded
+ * before, between and after those three. */
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                  const void* q, const void* k, const void* v, const float* a, const float* b,
                  const float* chunk_states, int64_t chunk_state_rows, const float* cw, const void* d_o,

@@ -213,6 +213,14 @@ def test_backward_workspace_bytes():
     p = cpr.Policy(1, 2, 16, 16, chunk=8, io="f32")
     adj, tok = (100 // 8 + 3 + 3) * 2 * 16 * 16 * 4, 100 * 2 * 16 * 4
     assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == pad(adj) + 3 * pad(tok)
+    # a chunk above 64 tokens is differentiated on a 64-token stash: the gradient parts are those of
+    # chunk 64, then the 64-token stash ((N/64 + B) states), an int32 slot id per sequence and an
+    # int64 position per row of the forward's (N/C + B)-row stash
+    p = cpr.Policy(2, 4, 32, 32, chunk=200, io="f32")
+    plane = 4 * 32 * 32 * 4
+    adj, tok = (1000 // 64 + 5 + 5) * plane, 1000 * 4 * 32 * 4
+    extra = pad((1000 // 64 + 5) * plane) + pad(5 * 4) + pad((1000 // 200 + 5) * 8)
+    assert cpr.gdn_backward_workspace_bytes(p, 1000, 5) == pad(adj) + 3 * pad(tok) + extra
     with pytest.raises(cpr.GdnError):
         cpr.gdn_backward_workspace_bytes(p, -1, 3)
 
@@ -230,7 +238,12 @@ def test_backward_argument_errors_before_launch():
     # the bf16 boundary dtype has a backward (straight-through) and meets the same checks
     assert call(cpr.Policy(2, 4, 16, 16, chunk=64, io="f32", boundary="bf16"), rows=2) == 1
     assert b"chunk_state_rows" in lib.gdn_last_error()
-    assert call(cpr.Policy(2, 4, 16, 16, chunk=128, io="f32")) == 2
+    # chunks above 64 tokens: fp32 boundaries meet the usual checks (rows >= 100/128 + 2 = 2),
+    # bf16 boundaries are unsupported there
+    assert call(cpr.Policy(2, 4, 16, 16, chunk=128, io="f32"), rows=1) == 1
+    assert b"chunk_state_rows" in lib.gdn_last_error()
+    assert call(cpr.Policy(2, 4, 16, 16, chunk=128, io="f32"), ws_bytes=16) == 1
+    assert call(cpr.Policy(2, 4, 16, 16, chunk=128, io="f32", boundary="bf16")) == 2
     assert call(cpr.Policy(2, 3, 16, 16, chunk=64, io="f32")) == 1            # H_v not a multiple of H_k
     assert call(f32, rows=2) == 1 and b"chunk_state_rows" in lib.gdn_last_error()   # needs 100/64 + 2 = 3
     assert call(f32, ws_bytes=16) == 1 and b"workspace" in lib.gdn_last_error()

@@ -9,6 +9,8 @@ per gradient tensor of a sequence (dq, dk per key head; dv, da, db, dS_0 per val
 autograd of the same recurrence on the CPU lands at ~2e-7 normwise and ~1.5e-7 of the scale at
 these sizes, so both bounds leave a wide margin while still catching any wrong term.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -126,6 +128,36 @@ def test_backward_bf16_boundaries_straight_through(dim, io, chunk):
     assert torch.equal(rows, rows.to(torch.bfloat16).to(torch.float32))
     g = _backward(x, ct, cs, policy=pol)
     _compare_all(x, g, _oracle(x, ct, starts=cs[:n]))
+
+
+@pytest.mark.parametrize("dim,io,chunk", [(16, "f32", 100), (32, "f32", 128), (128, "bf16", 256)])
+def test_backward_chunk_above_64_equals_chunk_64(dim, io, chunk):
+    """A chunk above the gradient kernel's 64-token tile: the backward first rebuilds a 64-token
+    stash from each sequence's row 0 of the forward's stash.  With fp32 boundaries that is the
+    stash a 64-token forward keeps, so the gradients match the oracle and equal the chunk-64
+    backward bit for bit; with the trainer forward's c and w they are the same bits again."""
+    cpr = lib()
+    lens = [0, 1, 64, 65, 200, 0, 33, 300, 0]
+    x = gi.make_inputs(72, lens, h_k=2, h_v=4, dk=dim, dv=dim, chunk=chunk, io=io)
+    x64 = dataclasses.replace(x, chunk=64)
+    ct = gi.make_cotangents(x, 73, with_d_state=True, with_s0=True)
+    say(f"backward, chunk {chunk} > 64, dim={dim} io={io}")
+    s0 = ct["s0"].to("cuda")
+    g = _backward(x, ct, _forward(x, s0))
+    _compare_all(x, g, _oracle(x, ct))
+    g64 = _backward(x64, ct, _forward(x64, s0))
+    for n in GRADS + ("d_state0",):
+        assert sha(g[n]) == sha(g64[n]), n
+    # from zero states, with the kept c and w of the trainer forward at this chunk
+    xd = x.to("cuda")
+    pool = cpr.StatePool(policy_of(x), x.num_seqs)
+    _, cs, cw = cpr.gdn_trainer_forward(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    d_state = ct["d_state"].to("cuda")
+    g1 = cpr.gdn_backward(policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs, ct["d_o"].to("cuda"),
+                          d_state=d_state, want_d_state0=True, cw=cw)
+    g2 = _backward(x64, ct, _forward(x64))
+    for n in GRADS + ("d_state0",):
+        assert sha(g1[n]) == sha(g2[n]), n
 
 
 def test_backward_gqa_ratio_four():
