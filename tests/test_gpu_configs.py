@@ -246,25 +246,59 @@ def test_long_sequence_one_pass_and_overlapped_under_a_grid_cap(long_x, cap):
         assert sha(o) == so and sha(pool.state) == sS
 
 
+@pytest.mark.parametrize("record", [True, False])
 @pytest.mark.parametrize("cap", [1, 7, 64])
-def test_decode_under_a_grid_cap(cap):
+def test_decode_under_a_grid_cap(cap, record):
     """Ragged prompts, then 70 decode steps that cross chunk starts, with the decode step capped
     at `cap` workgroups: every output, state, position and boundary record as in the natural
-    launch."""
+    launch.  With a boundary record the step counts finished workgroups per slot; without one
+    (fp32 boundaries) it takes the uncounted launch shape.  The sequences live in a permuted
+    subset of a larger pool, so three slots are never listed and must stay untouched."""
     cpr = lib()
     lens = [(53 * i) % 190 + 1 for i in range(16)]
     prompts = gi.make_inputs(31, lens, io="bf16", device="cuda", **gi.BIG)
     steps = [gi.make_inputs(31, [1] * len(lens), io="bf16", sub=500 + s, device="cuda", **gi.BIG) for s in range(70)]
-    say(f"decode under a grid cap of {cap}")
+    n_slots = len(lens) + 3
+    ids = torch.tensor([(7 * i + 5) % n_slots for i in range(len(lens))], dtype=torch.int32, device="cuda")
+    assert len(set(ids.tolist())) == len(lens)
+    say(f"decode under a grid cap of {cap}, boundary record {record}")
     runs = []
     for c in (0, cap):
-        pool = cpr.StatePool(policy_of(prompts), len(lens), boundary=True)
-        cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
+        pool = cpr.StatePool(policy_of(prompts), n_slots, boundary=record)
+        cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b,
+                        slot_ids=ids)
         pool.set_max_workgroups(c)
+        outs = [cpr.gdn_decode_step(pool, s.q, s.k, s.v, s.a, s.b, slot_ids=ids) for s in steps]
+        torch.cuda.synchronize()
+        pos = pool.pos.tolist()
+        assert [pos[i] for i in ids.tolist()] == [L + len(steps) for L in lens]
+        unlisted = sorted(set(range(n_slots)) - set(ids.tolist()))
+        assert [pos[i] for i in unlisted] == [0] * 3
+        assert not pool.state[unlisted].any()
+        runs.append((sha(torch.stack(outs)), sha(pool.state), pos,
+                     sha(pool.boundary) if record else None, pool.boundary_pos.tolist() if record else None))
+    assert runs[0] == runs[1]
+
+
+def test_decode_counted_and_uncounted_shapes_agree():
+    """The same prompts and 70 decode steps through a pool with a boundary record (the counted
+    launch shape) and one without (the uncounted shape): outputs, states and positions are equal
+    bit for bit, and the record holds each slot's last chunk-start state."""
+    cpr = lib()
+    lens = [(71 * i) % 300 + 1 for i in range(24)]
+    prompts = gi.make_inputs(33, lens, io="bf16", device="cuda", **gi.BIG)
+    steps = [gi.make_inputs(33, [1] * len(lens), io="bf16", sub=700 + s, device="cuda", **gi.BIG) for s in range(70)]
+    say("decode: counted and uncounted launch shapes")
+    runs = []
+    for record in (True, False):
+        pool = cpr.StatePool(policy_of(prompts), len(lens), boundary=record)
+        cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
         outs = [cpr.gdn_decode_step(pool, s.q, s.k, s.v, s.a, s.b) for s in steps]
         torch.cuda.synchronize()
-        runs.append((sha(torch.stack(outs)), sha(pool.state), pool.pos.tolist(), sha(pool.boundary),
-                     pool.boundary_pos.tolist()))
+        runs.append((sha(torch.stack(outs)), sha(pool.state), pool.pos.tolist()))
+        if record:
+            bpos = pool.boundary_pos.tolist()
+            assert bpos == [(L + len(steps) - 1) // 64 * 64 for L in lens]
     assert runs[0] == runs[1]
 
 

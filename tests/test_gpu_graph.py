@@ -21,17 +21,19 @@ def _pools(x, n_slots, boundary):
     return cpr.StatePool(pol, n_slots, boundary=boundary), cpr.StatePool(pol, n_slots, boundary=boundary)
 
 
-@pytest.mark.parametrize("boundary", ["f32", "bf16"])
-def test_decode_step_graph_replays_match_eager(boundary):
+@pytest.mark.parametrize("boundary,record", [("f32", True), ("bf16", True), ("f32", False)])
+def test_decode_step_graph_replays_match_eager(boundary, record):
+    """One decode step captured and replayed 70 times against eager steps.  fp32 boundaries with
+    no boundary record take the uncounted launch shape; the other cases count workgroups."""
     cpr = lib()
     B, steps = 8, 70
     prompts = gi.make_inputs(91, [5, 60, 63, 64, 1, 100, 127, 33], h_k=2, h_v=4, dk=128, dv=128, chunk=64,
                              io="bf16")
     toks = gi.make_inputs(92, [steps] * B, h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16").to("cuda")
-    say(f"graph: decode, boundary={boundary}")
+    say(f"graph: decode, boundary={boundary}, record={record}")
     pol = cpr.Policy(2, 4, 128, 128, 64, "bf16", boundary=boundary)
-    eager = cpr.StatePool(pol, B, boundary=True)
-    graphed = cpr.StatePool(pol, B, boundary=True)
+    eager = cpr.StatePool(pol, B, boundary=record)
+    graphed = cpr.StatePool(pol, B, boundary=record)
     pd = prompts.to("cuda")
     for pool in (eager, graphed):
         cpr.gdn_prefill(pool, prompts.cu_seqlens, pd.q, pd.k, pd.v, pd.a, pd.b)
@@ -43,7 +45,7 @@ def test_decode_step_graph_replays_match_eager(boundary):
     so = torch.empty((B, 4, 128), dtype=torch.bfloat16, device="cuda")
     ids = torch.arange(B, dtype=torch.int32, device="cuda")
     # warm up the capture stream on a throwaway pool, then capture one step on the graphed pool
-    scratch = cpr.StatePool(pol, B, boundary=True)
+    scratch = cpr.StatePool(pol, B, boundary=record)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -63,8 +65,9 @@ def test_decode_step_graph_replays_match_eager(boundary):
         torch.cuda.synchronize()
         assert sha(so) == sha(oe), t
         assert sha(graphed.state) == sha(eager.state) and graphed.pos.tolist() == eager.pos.tolist(), t
-    assert sha(graphed.boundary) == sha(eager.boundary)
-    assert graphed.boundary_pos.tolist() == eager.boundary_pos.tolist()
+    if record:
+        assert sha(graphed.boundary) == sha(eager.boundary)
+        assert graphed.boundary_pos.tolist() == eager.boundary_pos.tolist()
 
 
 @pytest.mark.parametrize("entry", ["gdn_prefill", "gdn_prefill_fused", "gdn_prefill_overlapped"])
