@@ -7,19 +7,17 @@
 // kernel is bound by those 2 x d_k x d_v x 4 bytes per (slot, value head).  Work mapping: G =
 // d_k/8 lanes per column with one 8-row leaf each (the boundary pass's mapping).
 //
-// Two launch shapes, chosen per call, with the same arithmetic per column:
-//  - uncounted (fp32 boundary dtype and no boundary record): the step never needs the slot's
-//    position, so no workgroup reads it and one workgroup per slot advances it.  Workgroups are
-//    small (one column per lane: 8 KiB of state at d = 128) and numbered in state order, so those
-//    in flight together stream through one compact window of the state pool;
-//  - counted (bf16 boundaries or a boundary record): every workgroup reads the position to find
-//    chunk starts, and the slot's last workgroup advances it through a completion count.  One
-//    workgroup per (slot, value head) with several columns per lane, numbered entries first so
-//    that the workgroups in flight together count on different slots.
+// Workgroups are small (one column per lane: 8 KiB of state at d = 128) and numbered in state
+// order, so the workgroups in flight together stream through one compact window of the pool.
+// The slot's position is needed only for chunk-start work (bf16 boundaries, a boundary record):
+//  - without such work no workgroup reads it, and one workgroup per slot advances it;
+//  - with it every workgroup reads it, and a second, one-thread-per-entry kernel advances it
+//    after the step, so no workgroup of the step ever sees a moved position.
 //
-// Resynchronisation: a slot whose position is a multiple of C holds a chunk-start state.  The
-// boundary dtype is fp32, so re-basing it on the boundary state is exact and leaves the values
-// as they are; the state is committed to the pool's boundary record when the pool has one.
+// Resynchronisation: a slot whose position is a multiple of C holds a chunk-start state.  With
+// the fp32 boundary dtype re-basing it on the boundary state is exact and leaves the values as
+// they are; with bf16 the state is rounded.  The state is then committed to the pool's boundary
+// record when the pool has one.
 #include <hip/hip_runtime.h>
 
 #include "cpr_common.hpp"
@@ -27,14 +25,11 @@
 
 namespace cpr {
 
-constexpr int kPosBits = 48;                               // positions below 2^48
-constexpr int64_t kPosMask = (int64_t(1) << kPosBits) - 1;
-
-#ifndef CPR_DECODE_MAX_NC
-#define CPR_DECODE_MAX_NC 8   // counted shape, columns per lane: 8 -> one workgroup per (slot, value head) at d = 128
+#ifndef CPR_DECODE_NC
+#define CPR_DECODE_NC 1         // step kernel, columns per lane
 #endif
-#ifndef CPR_DECODE_FAST_NC
-#define CPR_DECODE_FAST_NC 1  // uncounted shape, columns per lane
+#ifndef CPR_RESYNC_NC
+#define CPR_RESYNC_NC 8         // explicit resync, columns per lane (one workgroup per (slot, value head) at d = 128)
 #endif
 #ifndef CPR_DECODE_NT
 #define CPR_DECODE_NT 0       // streaming (non-temporal) state access: bit 0 loads, bit 1 stores
@@ -47,12 +42,11 @@ __device__ __forceinline__ void state_store(float* p, const float (&x)[8]) {
   if constexpr ((CPR_DECODE_NT & 2) != 0) store_f32x8_nt(p, x); else store_f32x8(p, x);
 }
 
-template <int DK, int DV, bool COUNTED>
+template <int DK, int DV, int NC_MAX>
 struct DecodeCfg {
   static constexpr int G = DK / kLeaf;                         // lanes per column, one leaf each
   static constexpr int SLOTS = (256 / G < DV) ? 256 / G : DV;  // column slots per workgroup
   static constexpr int NC_ALL = DV / SLOTS;
-  static constexpr int NC_MAX = COUNTED ? CPR_DECODE_MAX_NC : CPR_DECODE_FAST_NC;
   static constexpr int NC = NC_ALL < NC_MAX ? NC_ALL : NC_MAX;  // columns per lane
   static constexpr int WG_COLS = SLOTS * NC;                   // columns per workgroup
   static constexpr int THREADS = SLOTS * G;
@@ -63,28 +57,25 @@ struct DecodeCfg {
 // loads of all its NC columns (NC x 32 bytes of state), then runs the step on each column; lane
 // (slot, g) owns columns col0 + slot + SLOTS * c, so each load instruction of a wave covers whole
 // 512-byte columns.
-template <int DK, int DV, int IO, bool COUNTED>
+template <int DK, int DV>
+using StepCfg = DecodeCfg<DK, DV, CPR_DECODE_NC>;
+
+template <int DK, int DV, int IO>
 __device__ __forceinline__ void decode_step_item(const DecodeArgs& A, int64_t vb) {
-  using Cfg = DecodeCfg<DK, DV, COUNTED>;
+  using Cfg = StepCfg<DK, DV>;
   constexpr int G = Cfg::G, NC = Cfg::NC, SLOTS = Cfg::SLOTS, NCG = DV / Cfg::WG_COLS;
   __shared__ float o_lds[Cfg::WG_COLS];
   const int per_entry = A.h_v * NCG;
-  int e, h, z;
-  if constexpr (COUNTED) {   // entries fastest, then value heads, then column groups
-    e = static_cast<int>(vb % A.batch);
-    h = static_cast<int>(vb / A.batch % A.h_v);
-    z = static_cast<int>(vb / A.batch / A.h_v);
-  } else {                   // state order: column groups fastest, then value heads, then entries
-    z = static_cast<int>(vb % NCG);
-    h = static_cast<int>(vb / NCG % A.h_v);
-    e = static_cast<int>(vb / per_entry);
-  }
+  // state order: column groups fastest, then value heads, then entries
+  const int z = static_cast<int>(vb % NCG), h = static_cast<int>(vb / NCG % A.h_v);
+  const int e = static_cast<int>(vb / per_entry);
   const int col0 = z * Cfg::WG_COLS;
   const int32_t slot = A.slot_ids[e];
   if (slot < 0 || slot >= A.num_slots) return;                  // uniform across the block
-  // Counted: the low 48 bits are the position; the high bits count this step's finished
-  // workgroups.  Uncounted: the position is not needed (no chunk-start work) and not read here.
-  const int64_t p = COUNTED ? (A.pos[slot] & kPosMask) : 0;
+  // With chunk-start work the position is read here and advanced by decode_advance_kernel after
+  // this launch; without it the position is not read, and one workgroup advances it below.
+  const bool chunk_work = A.boundary != nullptr || A.round_boundary != 0;
+  const int64_t p = chunk_work ? A.pos[slot] : 0;
   const int tid = threadIdx.x, cs = tid / G, g = tid % G;
   const int64_t head = (static_cast<int64_t>(slot) * A.h_v + h) * DV * DK;
   const int kh = h / (A.h_v / A.h_k);
@@ -103,7 +94,7 @@ __device__ __forceinline__ void decode_step_item(const DecodeArgs& A, int64_t vb
   const float a = A.a[static_cast<int64_t>(e) * A.h_v + h];
   const float b = A.b[static_cast<int64_t>(e) * A.h_v + h];
 
-  const bool at_chunk_start = COUNTED && p % A.chunk == 0;
+  const bool at_chunk_start = chunk_work && p % A.chunk == 0;
   if (A.round_boundary && at_chunk_start) {                      // resynchronise: re-base on bf16
 #pragma unroll
     for (int c = 0; c < NC; ++c) resync_round(s[c]);
@@ -129,38 +120,37 @@ __device__ __forceinline__ void decode_step_item(const DecodeArgs& A, int64_t vb
     for (int i = 0; i < 8; ++i) x[i] = o_lds[tid * 8 + i];
     store8<IO>(A.o, vo + tid * 8, x);
   }
-  if constexpr (COUNTED) {
-    if (tid == 0) {
-      // Every work item of this slot read pos above, before its own increment here, so the last
-      // one to finish can advance the position and clear the counter without racing a reader.
-      const unsigned long long done = static_cast<unsigned long long>(per_entry);
-      const unsigned long long old =
-          atomicAdd(reinterpret_cast<unsigned long long*>(A.pos + slot), 1ull << kPosBits);
-      if ((old >> kPosBits) == done - 1) A.pos[slot] = static_cast<int64_t>(old & kPosMask) + 1;
-    }
-  } else {
-    // Slot ids are distinct and no other work item of this launch touches pos[slot].
-    if (h == 0 && z == 0 && tid == 0) A.pos[slot] = (A.pos[slot] & kPosMask) + 1;
-  }
+  // Slot ids are distinct and, without chunk-start work, no other work item touches pos[slot].
+  if (!chunk_work && h == 0 && z == 0 && tid == 0) A.pos[slot] += 1;
 }
 
-template <int DK, int DV, int IO, bool COUNTED>
-__global__ void __launch_bounds__((DecodeCfg<DK, DV, COUNTED>::THREADS)) decode_step_kernel(DecodeArgs A) {
-  decode_step_item<DK, DV, IO, COUNTED>(A, blockIdx.x);
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((StepCfg<DK, DV>::THREADS)) decode_step_kernel(DecodeArgs A) {
+  decode_step_item<DK, DV, IO>(A, blockIdx.x);
 }
 
 // The same items under a capped grid: each workgroup takes items b, b + gridDim.x, ...
-template <int DK, int DV, int IO, bool COUNTED>
-__global__ void __launch_bounds__((DecodeCfg<DK, DV, COUNTED>::THREADS)) decode_step_strided_kernel(DecodeArgs A) {
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((StepCfg<DK, DV>::THREADS)) decode_step_strided_kernel(DecodeArgs A) {
   for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
     if (vb != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
-    decode_step_item<DK, DV, IO, COUNTED>(A, vb);
+    decode_step_item<DK, DV, IO>(A, vb);
+  }
+}
+
+// pos[slot] += 1 for every listed slot, after a step with chunk-start work (entries taken in turn
+// when the grid is capped).
+__global__ void __launch_bounds__(256) decode_advance_kernel(DecodeArgs A) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < A.batch;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int32_t slot = A.slot_ids[e];
+    if (slot >= 0 && slot < A.num_slots) A.pos[slot] += 1;
   }
 }
 
 template <int DK, int DV>
-__global__ void __launch_bounds__((DecodeCfg<DK, DV, true>::THREADS)) resync_kernel(DecodeArgs A) {
-  using Cfg = DecodeCfg<DK, DV, true>;
+__global__ void __launch_bounds__((DecodeCfg<DK, DV, CPR_RESYNC_NC>::THREADS)) resync_kernel(DecodeArgs A) {
+  using Cfg = DecodeCfg<DK, DV, CPR_RESYNC_NC>;
   const int e = blockIdx.x, h = blockIdx.y;
   const int32_t slot = A.slot_ids[e];
   if (slot < 0 || slot >= A.num_slots) return;
@@ -184,29 +174,30 @@ __global__ void __launch_bounds__((DecodeCfg<DK, DV, true>::THREADS)) resync_ker
   if (A.boundary != nullptr && h == 0 && blockIdx.z == 0 && tid == 0) A.boundary_pos[slot] = p;
 }
 
-template <int DK, int DV, int IO, bool COUNTED>
-static hipError_t launch_step_t(const DecodeArgs& A, hipStream_t stream) {
-  using Cfg = DecodeCfg<DK, DV, COUNTED>;
-  const int64_t items = static_cast<int64_t>(A.batch) * A.h_v * (DV / Cfg::WG_COLS);
-  return launch_items(decode_step_kernel<DK, DV, IO, COUNTED>, decode_step_strided_kernel<DK, DV, IO, COUNTED>, items,
-                      Cfg::THREADS, stream, A);
-}
-
 template <int DK, int DV, int IO>
 static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
+  using Cfg = StepCfg<DK, DV>;
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.batch > 0) {
-    const bool counted = A.boundary != nullptr || A.round_boundary != 0;
-    e = counted ? launch_step_t<DK, DV, IO, true>(A, stream) : launch_step_t<DK, DV, IO, false>(A, stream);
+    const int64_t items = static_cast<int64_t>(A.batch) * A.h_v * (DV / Cfg::WG_COLS);
+    e = launch_items(decode_step_kernel<DK, DV, IO>, decode_step_strided_kernel<DK, DV, IO>, items, Cfg::THREADS,
+                     stream, A);
     if (e != hipSuccess) return e;
+    if (A.boundary != nullptr || A.round_boundary != 0) {
+      int64_t wgs = (static_cast<int64_t>(A.batch) + 255) / 256;
+      if (A.max_wgs > 0 && A.max_wgs < wgs) wgs = A.max_wgs;
+      hipLaunchKernelGGL(decode_advance_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, A);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return record_event(A.events, 1, stream);
 }
 
 template <int DK, int DV>
 static hipError_t launch_resync_t(const DecodeArgs& A, hipStream_t stream) {
-  using Cfg = DecodeCfg<DK, DV, true>;
+  using Cfg = DecodeCfg<DK, DV, CPR_RESYNC_NC>;
   if (A.batch == 0 || (A.boundary == nullptr && !A.round_boundary)) return hipSuccess;
   hipLaunchKernelGGL((resync_kernel<DK, DV>), dim3(A.batch, A.h_v, DV / Cfg::WG_COLS), dim3(Cfg::THREADS), 0, stream, A);
   return hipGetLastError();

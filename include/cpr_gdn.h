@@ -266,10 +266,9 @@ int gdn_prefill_overlapped(gdn_state* st, const int32_t* cu_seqlens, int32_t num
  *   a, b [batch][H_v].
  * For a slot whose position is a multiple of C the incoming state is a chunk-start state: it is
  * resynchronised first (see gdn_state_resync) and then the token is applied with the same pinned
- * step as prefill.  Afterwards pos[slot] += 1, inside the step kernel: with the fp32 boundary
- * dtype and no boundary record the step needs no position, and one workgroup per slot advances
- * it; otherwise the slot's last workgroup does, keeping a completion count in bits 48..63 of pos
- * while the kernel runs.  Positions must stay below 2^48.  batch may be 0.  One kernel launch.
+ * step as prefill.  Afterwards pos[slot] += 1.  With the fp32 boundary dtype and no boundary
+ * record the step needs no position and advances it itself (one kernel launch); otherwise a
+ * second kernel advances it after the step (two launches).  batch may be 0.
  * events: NULL, or 2 hipEvent_t (as void*) recorded on `stream` before and after the step kernel. */
 int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
                     const void* q, const void* k, const void* v, const float* a, const float* b,
