@@ -427,6 +427,7 @@ def main():
             t = toks[s % len(toks)]
             cpr.gdn_decode_step(wpool, t.q, t.k, t.v, t.a, t.b, slot_ids=dids, o=od)
         del wpool
+        snap_state, snap_pos = dpool.state.clone(), dpool.pos.clone()   # for the boundary-record run
         torch.cuda.synchronize()
         devs = [[hip.event() for _ in range(3)] for _ in range(args.decode_steps)]
         t0 = time.perf_counter()
@@ -453,6 +454,25 @@ def main():
                          "frac": round(dbytes / (k_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": traffic.get("decode_step"), "bytes_per_step": dbytes},
         }
+        # The same steps through a pool with a boundary record: every chunk start is committed to
+        # the record and a second kernel advances the positions.  Same bits as the steps above.
+        rpool = cpr.StatePool(P, nb, device=dev, boundary=True)
+        rpool.state.copy_(snap_state)
+        rpool.pos.copy_(snap_pos)
+        del snap_state, snap_pos
+        od_r = torch.empty_like(od)
+        revs = [[hip.event() for _ in range(2)] for _ in range(args.decode_steps)]
+        for s in range(args.decode_steps):
+            t = toks[s]
+            cpr.gdn_decode_step(rpool, t.q, t.k, t.v, t.a, t.b, slot_ids=dids, o=od_r, events=revs[s])
+        torch.cuda.synchronize()
+        r_us = statistics.median(hip.ms(e[0], e[1]) * 1e3 for e in revs)
+        decode["with_boundary_record"] = {
+            "us_per_step_median": round(r_us, 2),
+            "bitwise_equal": bool(torch.equal(rpool.state, dpool.state) and torch.equal(rpool.pos, dpool.pos)
+                                  and torch.equal(od_r.view(torch.int16), od.view(torch.int16))),
+        }
+        del rpool, od_r
 
     # ---------------------------------------------------------------- trainer forward + backward
     trainer = None
