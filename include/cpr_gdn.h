@@ -269,7 +269,8 @@ int gdn_prefill_overlapped(gdn_state* st, const int32_t* cu_seqlens, int32_t num
  * step as prefill.  Afterwards pos[slot] += 1.  With the fp32 boundary dtype and no boundary
  * record the step needs no position and advances it itself (one kernel launch); otherwise a
  * second kernel advances it after the step (two launches).  batch may be 0.
- * events: NULL, or 2 hipEvent_t (as void*) recorded on `stream` before and after the step kernel. */
+ * events: NULL, or 2 hipEvent_t (as void*) recorded on `stream` before the step and after its last
+ * launch. */
 int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch,
                     const void* q, const void* k, const void* v, const float* a, const float* b,
                     void* o, void* stream, void* const* events);
