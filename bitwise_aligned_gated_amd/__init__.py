@@ -8,6 +8,7 @@ The function names mirror the C entry points declared in ``include/cpr_gdn.h``.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -17,7 +18,8 @@ __all__ = [
     "LIB_PATH", "GdnError", "Policy", "StatePool", "gdn_policy_digest", "gdn_policy_check",
     "gdn_semantic_digest", "gdn_deployment_digest",
     "gdn_sha256", "gdn_chunk_rows", "gdn_chunk_rows_bound", "gdn_check_cu_seqlens", "gdn_prefill",
-    "gdn_prefill_fused", "gdn_prefill_overlapped", "gdn_decode_step", "gdn_state_resync", "gdn_backward", "gdn_backward_workspace_bytes",
+    "gdn_prefill_fused", "gdn_prefill_overlapped", "gdn_decode_step", "gdn_state_resync", "gdn_device_status",
+    "gdn_backward", "gdn_backward_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_chunked_workspace_bytes", "GDN_CHUNKED_NATIVE", "GDN_CHUNKED_R2",
     "gdn_trainer_forward",
     "EXPORTS",
@@ -64,6 +66,8 @@ _SIGS = {
     "gdn_state_data": (_P, [_P]),
     "gdn_state_positions": (_P, [_P]),
     "gdn_state_set_max_workgroups": (ctypes.c_int, [_P, _i64]),
+    "gdn_state_set_wait_limit": (ctypes.c_int, [_P, ctypes.c_uint32]),
+    "gdn_device_status": (ctypes.c_int, [_P]),
     "gdn_check_cu_seqlens": (ctypes.c_int, [_P, _i32, _i64]),
     "gdn_chunk_rows_bound": (_i64, [_i64, _i32, _i32]),
     "gdn_chunk_rows": (ctypes.c_int, [_P, _P, _i32, _i32, _P]),
@@ -197,6 +201,20 @@ def _stream_ptr(stream) -> int:
     return s.cuda_stream
 
 
+def _on_stream(fn):
+    """Run a binding with the caller's `stream` (a torch.cuda.Stream) as torch's current stream, so
+    that every tensor it allocates (outputs, scratch, device copies of host arguments) belongs to the
+    stream the kernels run on and the caching allocator cannot hand that memory to other streams'
+    work while the kernels still use it."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return run
+
+
 def _dev(t: torch.Tensor, name: str, dtype, shape, device, align: int = 16) -> torch.Tensor:
     """Check a device tensor argument; vector-loaded tensors need 16-byte alignment, scalars 4."""
     if not isinstance(t, torch.Tensor):
@@ -251,6 +269,11 @@ class StatePool:
         0 restores one workgroup per work item.  Results are bitwise the same either way."""
         _check(_lib.gdn_state_set_max_workgroups(self._h, int(n)))
 
+    def set_wait_limit(self, polls: int) -> None:
+        """Bound of each wait in the overlapped prefill's later calls (C gdn_state_set_wait_limit);
+        0 restores the default.  A tiny bound makes waits give up, reported by gdn_device_status."""
+        _check(_lib.gdn_state_set_wait_limit(self._h, int(polls)))
+
     def close(self):
         if getattr(self, "_h", None):
             _lib.gdn_state_free(self._h)
@@ -261,6 +284,12 @@ class StatePool:
             self.close()
         except Exception:
             pass
+
+
+def gdn_device_status(stream=None) -> None:
+    """Synchronise the stream and raise GdnError (GDN_EHIP) if a wait of an overlapped prefill on
+    the current device gave up since the last check (C gdn_device_status); the check clears it."""
+    _check(_lib.gdn_device_status(_stream_ptr(stream)))
 
 
 def _ids(ids, n: int, device) -> torch.Tensor:
@@ -294,6 +323,7 @@ def _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o):
     return N, B, cu_d, ids, o
 
 
+@_on_stream
 def gdn_prefill_fused(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
                       o=None, chunk_states=None, stream=None, events=None):
     """One-pass prefill (C gdn_prefill_fused); bitwise equal to gdn_prefill.  chunk_states None:
@@ -311,6 +341,7 @@ def gdn_prefill_fused(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None,
     return o, chunk_states
 
 
+@_on_stream
 def gdn_prefill_overlapped(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
                            o=None, chunk_states=None, stream=None, events=None):
     """Overlapped prefill (C gdn_prefill_overlapped): pass 1 and the chunk outputs in one launch;
@@ -329,14 +360,18 @@ def gdn_prefill_overlapped(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=
     return o, chunk_states
 
 
+@_on_stream
 def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
                 o=None, chunk_states=None, c_stash=True, stream=None, events=None):
     """Prefill / trainer forward over a packed batch (C gdn_prefill).
 
     cu_seqlens: host sequence (checked on the host, then copied) or a device int32 tensor.
     c_stash: True allocates the [N][H_v][dv] fp32 scratch in which pass 1 keeps every token's c for
-    pass 2; a tensor is used as that scratch; None or False passes NULL (pass 2 predicts c again).
-    The bits of every result are the same either way.
+    pass 2 (168 MB for 10240 tokens at 32 heads of 128: callers that cannot allocate per call, such
+    as code under graph capture, pass a tensor they own); a tensor is used as that scratch; None or
+    False passes NULL (pass 2 predicts c again).  The bits of every result are the same either way.
+    stream: a torch.cuda.Stream (default: the current stream); every tensor the call allocates is
+    allocated on it.
     Returns (o, chunk_states); chunk_states is allocated with the bound's row count when None."""
     P, dev = pool.policy, pool.device
     N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
@@ -356,6 +391,7 @@ def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_
     return o, chunk_states
 
 
+@_on_stream
 def gdn_trainer_forward(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
                         o=None, chunk_states=None, cw=None, stream=None, events=None):
     """Trainer forward (C gdn_trainer_forward): gdn_prefill that also keeps every token's c and w
@@ -376,6 +412,7 @@ def gdn_trainer_forward(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=Non
     return o, chunk_states, cw
 
 
+@_on_stream
 def gdn_decode_step(pool: StatePool, q, k, v, a, b, slot_ids=None, o=None, stream=None, events=None):
     """One token for each listed slot (C gdn_decode_step).  Returns o [batch, H_v, dv]."""
     P, dev = pool.policy, pool.device
@@ -397,6 +434,7 @@ def gdn_decode_step(pool: StatePool, q, k, v, a, b, slot_ids=None, o=None, strea
     return o
 
 
+@_on_stream
 def gdn_state_resync(pool: StatePool, slot_ids, stream=None):
     """Resynchronise listed slots at chunk starts (C gdn_state_resync)."""
     dev = pool.device
@@ -411,6 +449,7 @@ def gdn_backward_workspace_bytes(policy: Policy, total_tokens: int, num_seqs: in
     return int(r)
 
 
+@_on_stream
 def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state=None,
                  want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None, cw=None):
     """Gradients of a trainer forward (C gdn_backward) from its inputs and chunk-state stash.
@@ -470,6 +509,7 @@ def gdn_prefill_chunked_workspace_bytes(policy: Policy, total_tokens: int, num_s
     return int(r)
 
 
+@_on_stream
 def gdn_prefill_chunked(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
                         outputs: int = GDN_CHUNKED_NATIVE, o=None, chunk_states=None, workspace=None, stream=None,
                         events=None):

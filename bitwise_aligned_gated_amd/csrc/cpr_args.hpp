@@ -32,6 +32,8 @@ struct PrefillArgs {
   void* const* events;        // nullable: hipEvent_t recorded around the kernels
   int64_t grid_items;         // set per launch: the kernel's work items (one per natural workgroup)
   int64_t max_wgs;            // 0: one workgroup per item; else at most this many, taking items in turn
+  uint32_t* status;           // overlapped kernel: device word a bounded wait that gives up ORs a flag into
+  uint32_t wait_limit;        // overlapped kernel: polls per bounded wait (0: the default)
 };
 
 struct DecodeArgs {

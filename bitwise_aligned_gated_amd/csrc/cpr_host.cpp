@@ -22,6 +22,7 @@ struct gdn_state {
   int64_t* boundary_pos;
   bool owns;
   int64_t max_wgs;   // launch-shape cap of the compute kernels (0: one workgroup per work item)
+  uint32_t wait_limit;   // polls per bounded wait of the overlapped kernel (0: the default)
 };
 
 namespace {
@@ -258,6 +259,7 @@ int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, i
   st->boundary_pos = boundary_pos;
   st->owns = self;
   st->max_wgs = 0;
+  st->wait_limit = 0;
   *out = st;
   return ok();
 }
@@ -278,6 +280,35 @@ int gdn_state_set_max_workgroups(gdn_state* st, int64_t max_workgroups) {
     return fail(GDN_EINVAL, "gdn_state_set_max_workgroups: %lld is outside [0, 2^31)", (long long)max_workgroups);
   st->max_wgs = max_workgroups;
   return ok();
+}
+
+int gdn_state_set_wait_limit(gdn_state* st, uint32_t polls) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_state_set_wait_limit: state handle is NULL");
+  st->wait_limit = polls;
+  return ok();
+}
+
+int gdn_device_status(void* stream) {
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  uint32_t* word = nullptr;
+  hipError_t e = cpr::wait_status_word(&word);
+  if (e != hipSuccess) return hip_fail(e, "gdn_device_status: status word");
+  uint32_t flags = 0;
+  static const uint32_t zero = 0;
+  e = hipMemcpyAsync(&flags, word, sizeof flags, hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e, "gdn_device_status: reading the status word");
+  if (flags == 0) return ok();
+  e = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(e, "gdn_device_status: clearing the status word");
+  return fail(GDN_EHIP,
+              "an overlapped prefill gave up a bounded wait (flags 0x%x:%s%s%s%s); its outputs and states are "
+              "not valid",
+              flags, (flags & 1u) ? " pass 1 waiting for staged inputs" : "",
+              (flags & 2u) ? " pass 1 waiting for a free hand-off buffer" : "",
+              (flags & 4u) ? " pass 2 waiting for a hand-off" : "",
+              (flags & 8u) ? " staging waiting for a free tile buffer" : "");
 }
 
 float* gdn_state_data(gdn_state* st) { return st ? st->state : nullptr; }
@@ -420,6 +451,7 @@ static int onepass_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.c_stash = nullptr;
   A.w_stash = nullptr;
   A.events = events;
+  A.wait_limit = st->wait_limit;
   const bool overlapped = overlap && P.chunk <= cpr::overlap_max_chunk() && cpr::overlap_fits(P.dk, P.dv, A);
   const hipError_t e = overlapped
                            ? cpr::launch_prefill_overlap(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream))
@@ -478,7 +510,6 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
   const gdn_policy& P = st->policy;
   cpr::DecodeArgs A{};
   A.max_wgs = st->max_wgs;
-  std::memset(&A, 0, sizeof A);
   A.slot_ids = slot_ids;
   A.pos = st->pos;
   A.state = st->state;
@@ -499,15 +530,25 @@ static int64_t backward_rows(int64_t total_tokens, int32_t num_seqs, int32_t chu
 
 static int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// The chunk-gradient kernel's tile is 64 tokens.  A forward at a larger chunk (fp32 boundaries)
-// is differentiated on a 64-token stash that pass 1 recomputes from each sequence's first row:
-// under fp32 boundaries those rows are the bits a 64-token forward would have stored.
+// The chunk-gradient kernel's tile is 64 tokens.  Under fp32 boundaries the gradients are always
+// taken at chunk 64: a forward at any other chunk is differentiated on a 64-token stash that pass 1
+// recomputes from each sequence's first row.  A chunk-start state does not depend on C there, so
+// those rows are the bits a 64-token forward would have stored, and the gradients are the same bits
+// whatever C the forward ran at (C is a deployment setting, as the policy digest says).  Under
+// bf16 boundaries C is numerical policy and the gradients run at min(C, 64) on the forward's own
+// (rounded) rows.
 constexpr int32_t kGradTile = 64;
 
-// Workspace beyond the gradient passes' own when the forward's chunk exceeds the tile: the
-// 64-token stash, a slot id per sequence and a position per row of the forward's stash.
+static bool rebuilds_stash(const gdn_policy& P) { return P.state_dtype == GDN_F32 && P.chunk != kGradTile; }
+
+static int32_t grad_chunk_of(const gdn_policy& P) {
+  return P.state_dtype == GDN_F32 ? kGradTile : (P.chunk < kGradTile ? P.chunk : kGradTile);
+}
+
+// Workspace beyond the gradient passes' own when the stash is rebuilt: the 64-token stash, a slot
+// id per sequence and a position per row of the forward's stash.
 static int64_t rechunk_bytes(const gdn_policy& P, int64_t total_tokens, int32_t num_seqs) {
-  if (P.chunk <= kGradTile) return 0;
+  if (!rebuilds_stash(P)) return 0;
   const int64_t plane = int64_t(P.dk) * P.dv;
   return align256(backward_rows(total_tokens, num_seqs, kGradTile) * P.h_v * plane * 4) +
          align256(int64_t(num_seqs) * 4) + align256(backward_rows(total_tokens, num_seqs, P.chunk) * 8);
@@ -521,7 +562,7 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
   }
   const gdn_policy& P = *policy;
   const int64_t plane = int64_t(P.dk) * P.dv;
-  const int32_t chunk = P.chunk < kGradTile ? P.chunk : kGradTile;   // the gradient passes' chunk
+  const int32_t chunk = grad_chunk_of(P);   // the gradient passes' chunk
   const int64_t adj = (backward_rows(total_tokens, num_seqs, chunk) + num_seqs) * P.h_v * plane * 4;
   const int64_t per_token = total_tokens * P.h_v * int64_t(P.dv) * 4;
   ok();
@@ -560,7 +601,7 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return fail(GDN_EINVAL, "gdn_backward: workspace must be 16-byte aligned");
   const int64_t plane = int64_t(P.dk) * P.dv;
-  const int32_t chunk = P.chunk < kGradTile ? P.chunk : kGradTile;   // the gradient passes' chunk
+  const int32_t chunk = grad_chunk_of(P);   // the gradient passes' chunk
   const int64_t rows_g = backward_rows(total_tokens, num_seqs, chunk);
   if (rows_g * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_backward: too many chunks for one launch");
   const int64_t adj_bytes = align256((rows_g + num_seqs) * P.h_v * plane * 4);
@@ -568,7 +609,7 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   char* ws = static_cast<char*>(workspace);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const float* stash = chunk_states;
-  if (P.chunk > kGradTile && num_seqs > 0) {
+  if (rebuilds_stash(P) && num_seqs > 0) {
     // the 64-token stash: pass 1 from each sequence's first row of the caller's stash
     char* xs = ws + adj_bytes + 3 * tok_bytes;
     float* fine = reinterpret_cast<float*>(xs);

@@ -15,6 +15,8 @@ hipError_t launch_prefill_fused(int dk, int dv, int io, const PrefillArgs& A, hi
 // Pass 1 and the chunk outputs in one workgroup per column group (chunks up to overlap_max_chunk()).
 hipError_t launch_prefill_overlap(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
 int overlap_max_chunk();
+// The current device's status word of the overlapped kernel's bounded waits (device address).
+hipError_t wait_status_word(uint32_t** out);
 // Whether every workgroup of the overlapped kernel is resident at once (one per CU).
 bool overlap_fits(int dk, int dv, const PrefillArgs& A);
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);

@@ -19,7 +19,10 @@
 // The waves meet only through LDS counters (chunks handed over, chunks released, tiles staged,
 // tiles consumed), on the same CU, so no data crosses XCDs or L2s; NH + 1 hand-off buffers let
 // pass 1 run up to NH chunks ahead.  Every wait is bounded, so a wave that is never signalled
-// still finishes.
+// still finishes.  A wave whose wait gives up touches no shared buffer afterwards: it ORs a flag
+// into the device's status word (read back by gdn_device_status, which then reports GDN_EHIP) and
+// leaves the item, so the call's results are refused rather than silently wrong (section "The
+// execution contract": refuse to run rather than run mismatched numerics).
 #include <hip/hip_runtime.h>
 
 #include "cpr_common.hpp"
@@ -77,13 +80,31 @@ struct alignas(16) OvLds {
 
 constexpr uint32_t kSpinLimit = 1u << 22;   // ~0.2 s of s_sleep polls: far beyond any real wait
 
-// Wait until *cnt >= target (workgroup-scope acquire); false if the bound ran out.
-__device__ __forceinline__ bool wait_count(const int* cnt, int target) {
-  for (uint32_t it = 0; it < kSpinLimit; ++it) {
-    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return true;
+// Which wait gave up, as bits of the status word.
+enum : uint32_t {
+  kGaveUpTile = 1u,       // a pass-1 wave waiting for its staged input tile
+  kGaveUpBuffer = 2u,     // a pass-1 wave waiting for a free hand-off buffer
+  kGaveUpHandOff = 4u,    // a pass-2 wave waiting for a handed-over chunk
+  kGaveUpStaging = 8u,    // the staging wave waiting for a free tile buffer
+};
+
+// The device's status word: flags of bounded waits that gave up since the host last read it.
+__device__ uint32_t g_wait_status;
+
+// Wait until *cnt >= target (workgroup-scope acquire), polling at most `limit` times; false if
+// the bound ran out.  The result is the same in every lane of the wave.
+__device__ __forceinline__ bool wait_count(const int* cnt, int target, uint32_t limit) {
+  for (uint32_t it = 0; it < limit; ++it) {
+    const int seen = __builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (seen >= target) return true;
     __builtin_amdgcn_s_sleep(2);
   }
   return false;
+}
+
+// Record that a wait of this wave gave up (one lane's vector atomic).
+__device__ __forceinline__ void gave_up(const PrefillArgs& A, uint32_t what) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(A.status, what, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // A pass-1 token's inputs for one lane: its 8 rows of k, its column's v, the gates.
@@ -130,6 +151,7 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
   __syncthreads();                      // the last block-wide barrier: the waves now meet only in LDS
   const int nchunks = static_cast<int>(m.nrows);
   const bool rows_on = A.chunk_states != nullptr;
+  const uint32_t limit = A.wait_limit != 0 ? A.wait_limit : kSpinLimit;
 
   if (wave < P) {
     // ---------------------------------------------------------------- pass 1
@@ -153,12 +175,14 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
     int cbuf = 0, pos = static_cast<int>(m.p0 % C);            // its hand-off buffer; token position
     float pc = 0.0f;                                           // c of the previous token, not yet in LDS
     int pslot = -1;
+    bool stop = false;                                         // a wait gave up: no further token runs
     auto read_in = [&](const OvTile<DK, DV>& T, int tt, OvIn& x) {
       lds_read_kq<G, kLeaf>(&T.k[tt][0], g, x.k);
       x.v = T.v[tt][act ? cw : 0];
       x.ab = T.ab[tt];
     };
     auto run_token = [&](int t, const OvIn& x) {
+      if (stop) return;                                        // uniform across the wave
       // the previous token's c goes to LDS first, so the lane-masked write does not split this
       // token's arithmetic
       if (pslot >= 0 && g == 0 && act) L.hc[cbuf][pslot][cw] = pc;
@@ -172,8 +196,13 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
         if (!last) {
           if (A.round_boundary) resync_round(s);               // a chunk start with a token to follow
           // chunk c + 1 goes to the buffer chunk c + 1 - NB = c - NH used: wait until its pass-2
-          // wave (c mod NH) is done with it, i.e. has released c / NH chunks
-          if (c >= O::NH) wait_count(&L.released[c % O::NH], c / O::NH);
+          // wave (c mod NH) is done with it, i.e. has released c / NH chunks.  If that wait gives
+          // up the buffer may still be in use: chunk c is not handed over and the wave stops.
+          if (c >= O::NH && !wait_count(&L.released[c % O::NH], c / O::NH, limit)) {
+            gave_up(A, kGaveUpBuffer);
+            stop = true;
+            return;
+          }
           cbuf = cbuf + 1 == O::NB ? 0 : cbuf + 1;
           if (act) store_f32x8(&L.hs[cbuf][cw][g * kLeaf], s);
           pos = 0;
@@ -185,8 +214,12 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
     };
     // tile by tile as the staging wave provides them; within a tile the next token's inputs are
     // read from LDS while the current one runs
-    for (int it = 0, t0 = 0; t0 < m.len; ++it, t0 += TT) {
-      if (!wait_count(&L.loaded, it + 1)) break;
+    for (int it = 0, t0 = 0; t0 < m.len && !stop; ++it, t0 += TT) {
+      if (!wait_count(&L.loaded, it + 1, limit)) {
+        gave_up(A, kGaveUpTile);
+        stop = true;
+        break;
+      }
       const OvTile<DK, DV>& T = L.tile[it % O::NT];
       const int n = m.len - t0 < TT ? m.len - t0 : TT;
       OvIn nx;
@@ -205,10 +238,10 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
           run_token(t0 + tt, cur);
         }
       }
-      if (lane == 0)                                           // the tile's buffer may be refilled
+      if (lane == 0 && !stop)                                  // the tile's buffer may be refilled
         __hip_atomic_store(&L.consumed[wave], it + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    if (act) store_f32x8(slot_state, s);
+    if (act && !stop) store_f32x8(slot_state, s);
   } else if (wave < P + O::NH) {
     // ---------------------------------------------------------------- pass 2
     // Wave P + w takes chunks w, w + NH, ... with G2 lanes per column and R2 rows per lane.  Its
@@ -259,8 +292,11 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
     for (int c = w; c < nchunks; c += O::NH) {
       bool ready = true;                                       // every pass-1 wave is past chunk c
 #pragma unroll
-      for (int p = 0; p < P; ++p) ready = ready && wait_count(&L.handed[p], c + 1);
-      if (!ready) break;
+      for (int p = 0; p < P; ++p) ready = ready && wait_count(&L.handed[p], c + 1, limit);
+      if (!ready) {
+        gave_up(A, kGaveUpHandOff);
+        break;
+      }
       const int off = c == 0 ? static_cast<int>(p0 % C) : 0;  // position of token tb in the chunk
       float s[R2];
 #pragma unroll
@@ -317,9 +353,12 @@ __device__ __forceinline__ void overlap_item(const PrefillArgs& A, int64_t vb) {
       bool free_ = true;
       if (it >= O::NT) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) free_ = free_ && wait_count(&L.consumed[p], it - O::NT + 1);
+        for (int p = 0; p < P; ++p) free_ = free_ && wait_count(&L.consumed[p], it - O::NT + 1, limit);
       }
-      if (!free_) break;
+      if (!free_) {
+        gave_up(A, kGaveUpStaging);
+        break;
+      }
       OvTile<DK, DV>& T = L.tile[it % O::NT];
       const int n = m.len - t0 < TT ? m.len - t0 : TT;
       Raw8<IO> rk[O::KU], rv[O::VU];
@@ -381,10 +420,12 @@ __global__ void __launch_bounds__((OvCfg<DK, DV>::THREADS)) overlap_strided_kern
 }
 
 template <int DK, int DV, int IO>
-static hipError_t launch_overlap_t(const PrefillArgs& A, hipStream_t stream) {
+static hipError_t launch_overlap_t(const PrefillArgs& A0, hipStream_t stream) {
   using O = OvCfg<DK, DV>;
-  hipError_t e = record_event(A.events, 0, stream);
+  PrefillArgs A = A0;
+  hipError_t e = wait_status_word(&A.status);
   if (e != hipSuccess) return e;
+  if ((e = record_event(A.events, 0, stream)) != hipSuccess) return e;
   if (A.num_seqs > 0) {
     const int64_t grid = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * O::NCG);
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -396,6 +437,27 @@ static hipError_t launch_overlap_t(const PrefillArgs& A, hipStream_t stream) {
 }
 
 int overlap_max_chunk() { return OvCfg<128, 128>::CMAX; }
+
+// The status word of the current device, found once per device by symbol (its host-side name is
+// no device address).
+hipError_t wait_status_word(uint32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static uint32_t* words[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t* w = __atomic_load_n(&words[dev], __ATOMIC_ACQUIRE);
+  if (w == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_wait_status));
+    if (e != hipSuccess) return e;
+    w = static_cast<uint32_t*>(p);
+    __atomic_store_n(&words[dev], w, __ATOMIC_RELEASE);
+  }
+  *out = w;
+  return hipSuccess;
+}
 
 // The kernel's LDS holds one workgroup per CU, so a grid larger than the CU count would run in
 // rounds, each as long as the longest sequence; the one-pass kernel is faster there.

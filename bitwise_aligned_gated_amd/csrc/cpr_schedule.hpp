@@ -6,8 +6,10 @@ namespace cpr {
 constexpr int kSchedule = 1;  // schedule version (see cpr_step.hpp)
 constexpr int kLeaf = 8;      // rows per leaf of the pinned dot product
 // Version of the kernels' work mapping (lanes per column, columns per lane, tile sizes, workgroup
-// order).  The schedule fixes leaves and tree, so the mapping never moves a bit; it enters only
-// the deployment digest.
-constexpr int kMappingVersion = 3;
+// order, which kernels a call launches).  The schedule fixes leaves and tree, so the mapping never
+// moves a bit; it enters only the deployment digest.  Raised with every change of a kernel's work
+// mapping (4: one-column-per-lane decode in state order with a separate position update, the
+// overlapped prefill, and the chunk-64 backward under fp32 boundaries).
+constexpr int kMappingVersion = 4;
 
 }  // namespace cpr

@@ -136,10 +136,14 @@ int gdn_policy_check(const uint8_t mine[32], const uint8_t theirs[32]);
  * GDN_EUNSUPPORTED.  Host-only. */
 int gdn_policy_validate(const gdn_policy* policy);
 
-/* Bytes of a state array for num_slots slots: num_slots * h_v * dv * dk * 4 (0 on bad input). */
+/* Bytes of a state array for num_slots slots: num_slots * h_v * dv * dk * 4 (0 on bad input).
+ * The state is the fp32 matrix the recurrence carries per (sequence, value head) (section "Solving
+ * the linear-attention headache": decode keeps it between tokens and re-bases it every chunk). */
 size_t gdn_state_bytes(const gdn_policy* policy, int32_t num_slots);
 
-/* Create a state pool handle for num_slots slots.
+/* Create a state pool handle for num_slots slots: the recurrent states decode carries from token
+ * to token and prefill starts from or leaves behind (section "Solving the linear-attention
+ * headache"), with the policy that pins their arithmetic (section "The execution contract").
  *   state, pos:     caller-owned device arrays (layouts above; state_bytes must equal
  *                   gdn_state_bytes).  The caller initialises them (normally to zero).  If both
  *                   are NULL the library allocates and zero-fills them itself (hipMalloc,
@@ -152,7 +156,8 @@ int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, i
                     size_t state_bytes, float* boundary, int64_t* boundary_pos,
                     gdn_state** out);
 
-/* Release a handle (and the device arrays if the library allocated them).  NULL is a no-op. */
+/* Release a handle made by gdn_state_alloc (and the device arrays if the library allocated them);
+ * caller-owned arrays are left untouched.  NULL is a no-op. */
 int gdn_state_free(gdn_state* st);
 
 /* Device pointers of a pool (for callers that let the library allocate).  Host-only. */
@@ -168,6 +173,25 @@ int64_t* gdn_state_positions(gdn_state* st);
  * chunkwise and backward kernels keep their natural shapes.  GDN_EINVAL for a NULL handle, a
  * negative value or one of 2^31 or more.  Host-only. */
 int gdn_state_set_max_workgroups(gdn_state* st, int64_t max_workgroups);
+
+/* Bound of each wait in the overlapped prefill's later calls on this pool: the number of polls
+ * (about 50 ns each) after which a wave stops waiting for another wave of its workgroup.
+ * 0, the default, is 2^22 polls (about 0.2 s), far beyond any wait of a working kernel.  A small
+ * value makes waits give up, which is reported by gdn_device_status; it exists so that the error
+ * path can be exercised with every kernel still ending normally.  GDN_EINVAL for a NULL handle.
+ * Host-only. */
+int gdn_state_set_wait_limit(gdn_state* st, uint32_t polls);
+
+/* Outcome of the overlapped prefills run on the current device since the last call (section "The
+ * execution contract": refuse to run, rather than run mismatched numerics).  Each wave of the
+ * overlapped kernel waits for others of its workgroup only for a bounded time; a wave whose wait
+ * gives up touches no shared buffer afterwards, leaves its work item and sets a flag in a
+ * per-device status word.  This call synchronises `stream`, reads that word and clears it:
+ * GDN_OK when no wait gave up, GDN_EHIP otherwise (gdn_last_error names which waits), in which
+ * case the outputs, final states, positions and chunk-start rows of those calls are not valid.
+ * Unlike every other call it synchronises the host (with `stream`).  The word is shared by every
+ * pool on the device: any give-up since the last check is reported. */
+int gdn_device_status(void* stream);
 
 /* Host-side check of a cu_seqlens array (host copy): GDN_OK if cu[0] == 0, non-decreasing and
  * cu[num_seqs] == total_tokens; GDN_EINVAL otherwise. */
@@ -215,7 +239,9 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
                 void* o, float* chunk_states, int64_t chunk_state_rows, float* c_stash, void* stream,
                 void* const* events);
 
-/* The trainer forward ([A]'s "trainer_fwd" case): gdn_prefill, bit for bit in o, final states
+/* The trainer forward (the "trainer_fwd" case of section "The execution contract", whose per-layer
+ * table in section "Solving the linear-attention headache" times CPR for the trainer's forward and
+ * backward): gdn_prefill, bit for bit in o, final states
  * and chunk states, that also keeps what the backward would otherwise recompute:
  *   cw  device fp32 [2][N][H_v][d_v]: every token's c_t = b_t w_t (block 0) and
  *       w_t = v_t - a_t S_{t-1}^T k_t (block 1), as the pinned step computed them.  Block 0
@@ -331,22 +357,26 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
  * fixed order, so the gradients are bitwise reproducible for any batch composition or packing. */
 
 /* Workspace bytes gdn_backward needs for total_tokens tokens in num_seqs sequences (-1 on bad
- * input): dL/dS at every boundary of 64-token (or C-token, C < 64) chunks (total_tokens / C' +
- * 2 num_seqs states, C' = min(C, 64)) and three fp32 per-token arrays of N * H_v * d_v (dc, c,
- * w); for C > 64 also a 64-token stash (total_tokens / 64 + num_seqs states), one int32 per
- * sequence and one int64 per row of the forward's stash.  Each part is padded to 256 bytes. */
+ * input): dL/dS at every boundary of the gradient chunks (total_tokens / C' + 2 num_seqs states;
+ * C' = 64 with fp32 boundaries, min(C, 64) with bf16 boundaries) and three fp32 per-token arrays
+ * of N * H_v * d_v (dc, c, w); with fp32 boundaries and C != 64 also a rebuilt 64-token stash
+ * (total_tokens / 64 + num_seqs states), one int32 per sequence and one int64 per row of the
+ * forward's stash.  Each part is padded to 256 bytes. */
 int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
 
 /* Gradients of a trainer forward (gdn_trainer_forward, gdn_prefill or gdn_prefill_fused over the
  * same packed batch, every sequence starting at position 0: from_state 0, or 1 from slots at
  * position 0).
- *   policy        the forward's policy.  The chunk-gradient kernel's tile is 64 tokens: for a
- *                 chunk C > 64 a fourth kernel first rebuilds the 64-token stash with the
- *                 boundary pass, from each sequence's row 0 of `chunk_states`.  Under fp32
- *                 boundaries a chunk-start state does not depend on C, so that stash holds the
- *                 bits a 64-token forward would have stored and the gradients equal those for
- *                 C = 64 bit for bit.  A bf16 boundary dtype with C > 64 is GDN_EUNSUPPORTED
- *                 (its chunk starts differ).
+ *   policy        the forward's policy.  The chunk-gradient kernel's tile is 64 tokens.  With fp32
+ *                 boundaries the gradients are always taken at chunk 64: for a forward at any
+ *                 other chunk C a fourth kernel first rebuilds the 64-token stash with the
+ *                 boundary pass, from each sequence's row 0 of `chunk_states`.  A chunk-start
+ *                 state does not depend on C there, so that stash holds the bits a 64-token
+ *                 forward would have stored, and the gradients are the same bits for every C
+ *                 (C is a deployment setting, as the policy digest says; section "The execution
+ *                 contract": equal policy digests, equal bits).  With bf16 boundaries C is part of
+ *                 the policy: the gradients run at chunk C on the forward's own rounded rows, and
+ *                 C > 64 is GDN_EUNSUPPORTED.
  *                 With the bf16 boundary dtype the rounding at chunk starts is read as the
  *                 identity (straight-through): the gradients are those of the trajectory the
  *                 forward took (from its rounded chunk-start states), with dL/dS passed through

@@ -101,3 +101,56 @@ def check_close(io: str, got: np.ndarray, ref: np.ndarray, what: str):
         err = normwise(got, ref)
         assert err <= BF16_NORMWISE, f"{what}: normwise {err:.3e} > {BF16_NORMWISE}"
     return err
+
+
+def _raw(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a tensor's exact bytes: bf16 as uint16 bit patterns, fp32 as float32."""
+    t = t.detach().to("cpu").contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def oracle_items(x: gi.GdnInputs, o: torch.Tensor, state: torch.Tensor, pairs=None, slots=None,
+                 chunk_states=None, S0=None, pos0=None, with_state=True):
+    """Work items for tests.oracle_pool.check_pair, one per (sequence, value head) of `pairs`
+    (default: every pair): the exact input bytes of x, the GPU's outputs o, its final states
+    (state[slots[i], h], stored transposed), and, when chunk_states is given, the sequence's
+    chunk-start rows (row offsets from gdn_chunk_rows).  S0 [B, H_v, d_v, d_k] (stored
+    orientation) and pos0 [B] describe a continuation."""
+    cpr = lib()
+    q, k, v, a, b = (_raw(getattr(x, n)) for n in ("q", "k", "v", "a", "b"))
+    go = _raw(o)
+    st = state.detach().to("cpu").numpy() if with_state else None
+    s0 = None if S0 is None else S0.detach().to("cpu").numpy()
+    p0 = [0] * x.num_seqs if pos0 is None else [int(p) for p in pos0]
+    cs = rows = None
+    if chunk_states is not None:
+        cs = chunk_states.detach().to("cpu").numpy()
+        rows = cpr.gdn_chunk_rows(x.cu_seqlens, x.chunk, pos0=None if pos0 is None else p0).numpy()
+    if pairs is None:
+        pairs = [(i, h) for i in range(x.num_seqs) for h in range(x.h_v)]
+    ratio = x.h_v // x.h_k
+    items = []
+    for i, h in pairs:
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        g = h // ratio
+        slot = i if slots is None else int(slots[i])
+        items.append(dict(
+            label=f"{x.name} seq {i} head {h}", io=x.io, q=q[t0:t1, g], k=k[t0:t1, g], v=v[t0:t1, h],
+            a=a[t0:t1, h], b=b[t0:t1, h], pos0=p0[i], chunk=x.chunk,
+            S0=None if s0 is None else s0[i, h].T.astype(np.float64),
+            got_o=go[t0:t1, h], got_S=None if st is None else st[slot, h].T.astype(np.float64),
+            got_rows=None if cs is None else cs[rows[i]:rows[i + 1], h].transpose(0, 2, 1).astype(np.float64)))
+    return items
+
+
+def run_oracle_checks(items, what: str) -> dict:
+    """Run tests.oracle_pool.check_pair over the items; fail with the first messages if any failed.
+    Returns the totals of the elementwise counts."""
+    from tests import oracle_pool
+    say(f"{what}: {len(items)} oracle checks ({oracle_pool.WORKERS or 'no'} pool workers)")
+    res = oracle_pool.run(items, progress=lambda n: say(f"{what}: {n}/{len(items)} checked"))
+    bad = [r["msg"] for r in res if not r["ok"]]
+    assert not bad, f"{len(bad)} failing pairs: {bad[:4]}"
+    tot = oracle_pool.summarize(res)
+    say(f"{what}: {tot}")
+    return tot

@@ -79,7 +79,10 @@ def test_semantic_and_deployment_digests():
         assert cpr.gdn_semantic_digest(other) == cpr.gdn_semantic_digest(p)
     assert cpr.gdn_semantic_digest(cpr.Policy(16, 32, 64, 64)) != cpr.gdn_semantic_digest(p)
     dep = cpr.gdn_deployment_digest(p)
-    assert dep[:0] == b"" and len(dep) == 32
+    # canonical bytes: the tag, chunk (fp32 boundaries) and the kernels' work-mapping version (4)
+    assert dep == hashlib.sha256(b"cpr-gdn-deploy-v1" + struct.pack("<2i", 64, 4)).digest()
+    assert cpr.gdn_deployment_digest(cpr.Policy(16, 32, 128, 128, chunk=64, boundary="bf16")) == \
+        hashlib.sha256(b"cpr-gdn-deploy-v1" + struct.pack("<2i", 0, 4)).digest()
     # fp32 boundaries: chunk is a deployment setting (deployment digest moves, policy digest not)
     p16 = cpr.Policy(16, 32, 128, 128, chunk=16)
     assert cpr.gdn_deployment_digest(p16) != dep and cpr.gdn_policy_digest(p16) == cpr.gdn_policy_digest(p)
@@ -196,6 +199,10 @@ def test_prefill_argument_errors_before_launch():
         for n in (-1, 1 << 31):
             assert lib.gdn_state_set_max_workgroups(h, n) == 1 and b"max_workgroups" in lib.gdn_last_error()
         assert lib.gdn_state_set_max_workgroups(None, 4) == 1 and b"state handle" in lib.gdn_last_error()
+        # the overlapped kernel's wait bound: any value is accepted, a NULL handle is not
+        for n in (0, 1, 0xFFFFFFFF):
+            assert lib.gdn_state_set_wait_limit(h, n) == 0
+        assert lib.gdn_state_set_wait_limit(None, 1) == 1 and b"state handle" in lib.gdn_last_error()
     finally:
         assert lib.gdn_state_free(h) == 0
     assert lib.gdn_state_free(None) == 0
@@ -210,17 +217,19 @@ def test_backward_workspace_bytes():
     adj = (10240 // 64 + 4 + 4) * 32 * 128 * 128 * 4
     tok = 10240 * 32 * 128 * 4
     assert cpr.gdn_backward_workspace_bytes(p, 10240, 4) == pad(adj) + 3 * pad(tok)
-    p = cpr.Policy(1, 2, 16, 16, chunk=8, io="f32")
+    # bf16 boundaries below 64 tokens: the gradient passes run at the forward's chunk
+    p = cpr.Policy(1, 2, 16, 16, chunk=8, io="f32", boundary="bf16")
     adj, tok = (100 // 8 + 3 + 3) * 2 * 16 * 16 * 4, 100 * 2 * 16 * 4
     assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == pad(adj) + 3 * pad(tok)
-    # a chunk above 64 tokens is differentiated on a 64-token stash: the gradient parts are those of
-    # chunk 64, then the 64-token stash ((N/64 + B) states), an int32 slot id per sequence and an
-    # int64 position per row of the forward's (N/C + B)-row stash
-    p = cpr.Policy(2, 4, 32, 32, chunk=200, io="f32")
-    plane = 4 * 32 * 32 * 4
-    adj, tok = (1000 // 64 + 5 + 5) * plane, 1000 * 4 * 32 * 4
-    extra = pad((1000 // 64 + 5) * plane) + pad(5 * 4) + pad((1000 // 200 + 5) * 8)
-    assert cpr.gdn_backward_workspace_bytes(p, 1000, 5) == pad(adj) + 3 * pad(tok) + extra
+    # fp32 boundaries at any chunk but 64 are differentiated on a rebuilt 64-token stash: the
+    # gradient parts are those of chunk 64, then the 64-token stash ((N/64 + B) states), an int32
+    # slot id per sequence and an int64 position per row of the forward's (N/C + B)-row stash
+    for C in (8, 20, 200):
+        p = cpr.Policy(2, 4, 32, 32, chunk=C, io="f32")
+        plane = 4 * 32 * 32 * 4
+        adj, tok = (1000 // 64 + 5 + 5) * plane, 1000 * 4 * 32 * 4
+        extra = pad((1000 // 64 + 5) * plane) + pad(5 * 4) + pad((1000 // C + 5) * 8)
+        assert cpr.gdn_backward_workspace_bytes(p, 1000, 5) == pad(adj) + 3 * pad(tok) + extra, C
     with pytest.raises(cpr.GdnError):
         cpr.gdn_backward_workspace_bytes(p, -1, 3)
 

@@ -190,20 +190,53 @@ def test_backward_deterministic_and_packing_invariant():
         assert sha(gi_["d_state0"][0]) == sha(g1["d_state0"][i]), i
 
 
-def test_backward_chunk_size_changes_no_forward_bits_but_gradients_stay_close():
-    """The forward's bits do not depend on the chunk size (fp32 boundaries); the backward's
-    chunk-parallel sums do, within the fp32 tolerance, and each chunk size is reproducible."""
-    x = gi.make_inputs(67, [257], h_k=1, h_v=2, dk=32, dv=32, chunk=64, io="f32")
-    ct = gi.make_cotangents(x, 68)
-    say("backward across chunk sizes")
+@pytest.mark.parametrize("dim,io", [(32, "f32"), (128, "bf16")])
+def test_backward_bits_do_not_depend_on_the_chunk(dim, io):
+    """With fp32 boundaries the chunk size is a deployment setting (it is left out of the policy
+    digest): the forward's bits do not depend on it, and neither do the gradients', because the
+    backward always differentiates at chunk 64 on a 64-token stash rebuilt from each sequence's
+    first row.  Every gradient is the same bits for C in {8, 20, 32, 64, 100}, from the forward's
+    stash and from the trainer forward's kept c and w, and matches the oracle."""
+    cpr = lib()
+    x = gi.make_inputs(67, [257, 0, 64, 1, 130], h_k=2, h_v=4, dk=dim, dv=dim, chunk=64, io=io)
+    ct = gi.make_cotangents(x, 68, with_s0=True)
+    s0 = ct["s0"].to("cuda")
     ref = _oracle(x, ct)
-    for C in (8, 32, 64):
-        xc = gi.GdnInputs(x.name, x.h_k, x.h_v, x.dk, x.dv, C, x.io, x.cu_seqlens, x.q, x.k, x.v, x.a, x.b,
-                          x.meta)
-        g = _backward(xc, ct, _forward(xc))
+    digests = []
+    for C in (8, 20, 32, 64, 100):
+        say(f"backward bits at chunk {C} dim={dim} io={io}")
+        xc = dataclasses.replace(x, chunk=C)
+        pol = policy_of(xc)
+        assert cpr.gdn_policy_digest(pol) == cpr.gdn_policy_digest(policy_of(x))
+        g = _backward(xc, ct, _forward(xc, s0))
         _compare_all(xc, g, ref)
-        g2 = _backward(xc, ct, _forward(xc))
-        assert all(sha(g[n]) == sha(g2[n]) for n in GRADS)
+        digests.append(tuple(sha(g[n]) for n in GRADS + ("d_state0",)))
+        # the trainer forward's c and w at this chunk, from zero states
+        xd = xc.to("cuda")
+        pool = cpr.StatePool(pol, xc.num_seqs)
+        _, cs, cw = cpr.gdn_trainer_forward(pool, xc.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+        g1 = cpr.gdn_backward(pol, xc.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs, ct["d_o"].to("cuda"),
+                              d_state=ct["d_state"].to("cuda"), cw=cw)
+        torch.cuda.synchronize()
+        digests.append(tuple(sha(g1[n]) for n in GRADS) + ("zero-start",))
+    assert len(set(d for d in digests if d[-1] != "zero-start")) == 1
+    assert len(set(d for d in digests if d[-1] == "zero-start")) == 1
+
+
+def test_backward_bf16_boundaries_depend_on_the_chunk():
+    """With bf16 boundaries the chunk is numerical policy: the rounded trajectory moves with C, so
+    do the gradients, and the policy digests differ."""
+    cpr = lib()
+    x = gi.make_inputs(75, [200, 77], h_k=1, h_v=2, dk=32, dv=32, chunk=32, io="f32")
+    ct = gi.make_cotangents(x, 76)
+    say("backward, bf16 boundaries at chunks 16 and 32")
+    out = []
+    for C in (16, 32):
+        xc = dataclasses.replace(x, chunk=C)
+        pol = cpr.Policy(x.h_k, x.h_v, x.dk, x.dv, C, "f32", boundary="bf16")
+        g = _backward(xc, ct, _forward(xc, policy=pol), policy=pol)
+        out.append((cpr.gdn_policy_digest(pol), sha(g["dk"])))
+    assert out[0][0] != out[1][0] and out[0][1] != out[1][1]
 
 
 def test_backward_trainer_10240_varlen():

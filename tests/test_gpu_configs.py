@@ -1,5 +1,7 @@
 """GPU parity and identity at the workloads' full sizes, in the launch configuration the
-benchmark times.  The oracle checks sampled (sequence, value head) pairs one by one; identity is
+benchmark times.  The oracle checks every (sequence, value head) pair of the prefill, decode,
+trainer and long workloads (in a host process pool), element by element against a forward error
+bound of the fp32 arithmetic (tests/bf16_check.py) besides the normwise tolerance; identity is
 checked on every output byte with SHA-256.
 
   prefill   5 x 2048 tokens, 32 value heads over 16 key heads, d = 128, chunk 64, bf16
@@ -12,7 +14,8 @@ import pytest
 import torch
 
 import gdn_inputs as gi
-from tests.gpu_util import (check_close, gpu_state_math, lib, oracle_seq_head, policy_of, prefill, say, sha)
+from tests.gpu_util import (check_close, gpu_state_math, lib, oracle_items, oracle_seq_head, policy_of, prefill,
+                            run_oracle_checks, say, sha)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,15 +41,11 @@ def test_prefill_5x2048():
     say("prefill 5x2048: packed run")
     o, pool, cs = prefill(x)
     rows = cpr.gdn_chunk_rows(x.cu_seqlens, 64).numpy()
-    o_np = o.float().cpu().numpy()
-    for (i, h) in [(0, 0), (1, 7), (2, 16), (3, 25), (4, 31)]:
-        say(f"prefill 5x2048: oracle seq {i} head {h}")
-        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
-        ref_o, ref_S, ref_R = oracle_seq_head(x, i, h)
-        check_close("bf16", o_np[t0:t1, h], ref_o, f"o seq {i} head {h}")
-        check_close("bf16", gpu_state_math(pool, i, h), ref_S, f"S seq {i} head {h}")
-        for r in (0, 1, 17, len(ref_R) - 1):
-            check_close("bf16", cs[rows[i] + r, h].cpu().double().numpy().T, ref_R[r], f"row {r}")
+    # every (sequence, value head): o element by element, the final state column by column, and
+    # every chunk-start row
+    tot = run_oracle_checks(oracle_items(x, o, pool.state, chunk_states=cs), "prefill 5x2048")
+    assert tot["elements"] == x.total_tokens * x.h_v * x.dv
+    assert tot["ulp0"] >= 0.999 * tot["elements"]       # round to nearest even: nearly all outputs exact
     say("prefill 5x2048: sequence 2 alone")
     o2, pool2, _ = prefill(x.select([2]))
     assert sha(o2) == sha(o[int(x.cu_seqlens[2]):int(x.cu_seqlens[3])])
@@ -106,6 +105,7 @@ def test_decode_256x1_128_steps_equals_one_prefill():
     P = policy_of(prompts)
     pool = cpr.StatePool(P, n, boundary=True)
     cpr.gdn_prefill(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b)
+    start_state = pool.state.clone()
     steps = [gi.decode_tokens(s, n, device="cuda") for s in range(128)]
     say("decode: 128 steps")
     outs = []
@@ -132,10 +132,18 @@ def test_decode_256x1_128_steps_equals_one_prefill():
         if bp[i] >= 0:
             assert sha(pool.boundary[i]) == sha(cs_full[rows[i] + bp[i] // 64]), f"boundary {i}"
     for (i, h) in [(int(np.argmin(L)), 3), (int(np.argmax(L)), 30)]:
-        say(f"decode: oracle slot {i} head {h}")
+        say(f"decode: oracle slot {i} head {h} over prompt and generated tokens")
         ref_o, ref_S, _ = oracle_seq_head(full, i, h)
         check_close("bf16", dec_o[i, :, h].float().cpu().numpy(), ref_o[-128:], f"decode o slot {i}")
         check_close("bf16", gpu_state_math(pool, i, h), ref_S, f"decode S slot {i}")
+    # every (slot, value head): the oracle continues from the state the prefill left in the slot
+    # (fp32, exact in fp64) over the 128 generated tokens, against every decode output
+    gen = gi.GdnInputs("decode", P.h_k, P.h_v, P.dk, P.dv, 64, "bf16", gi.cu_from_lengths([128] * n),
+                       *(torch.stack([getattr(s, f) for s in steps], dim=1).reshape(
+                           (n * 128,) + tuple(getattr(steps[0], f).shape[1:])) for f in ("q", "k", "v", "a", "b")))
+    tot = run_oracle_checks(oracle_items(gen, dec_o.reshape(n * 128, P.h_v, P.dv), pool.state, S0=start_state,
+                                         pos0=L.tolist()), "decode 256x128")
+    assert tot["elements"] == n * 128 * P.h_v * P.dv
 
 
 def test_trainer_forward_10240_varlen_with_stash():
@@ -147,15 +155,8 @@ def test_trainer_forward_10240_varlen_with_stash():
                         dtype=torch.float32, device="cuda")
     o, pool, cs = prefill(x, chunk_states=stash)
     assert cs is stash
-    for (i, h) in [(0, 1), (int(np.argmax(x.lengths)), 22)]:
-        say(f"trainer: oracle seq {i} head {h}")
-        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
-        ref_o, ref_S, ref_R = oracle_seq_head(x, i, h)
-        check_close("bf16", o[t0:t1, h].float().cpu().numpy(), ref_o, f"o seq {i}")
-        check_close("bf16", gpu_state_math(pool, i, h), ref_S, f"S seq {i}")
-        assert len(ref_R) == rows[i + 1] - rows[i]
-        for r in range(0, len(ref_R), 7):
-            check_close("bf16", stash[rows[i] + r, h].cpu().double().numpy().T, ref_R[r], f"stash row {r}")
+    tot = run_oracle_checks(oracle_items(x, o, pool.state, chunk_states=stash), "trainer 10240")
+    assert tot["elements"] == x.total_tokens * x.h_v * x.dv
     for i in range(x.num_seqs):
         say(f"trainer: sequence {i} alone")
         oi, pi, ci = prefill(x.select([i]))
@@ -182,11 +183,32 @@ def long_x():
 
 
 def test_long_sequence_matches_oracle(long_x):
+    """Every value head of the 65536-token sequence against the oracle, element by element."""
     x, _, _, o = long_x
-    for h in (0, 19):
-        say(f"long: oracle head {h}")
-        ref_o, _, _ = oracle_seq_head(x, 0, h)
-        check_close("bf16", o[:, h].float().cpu().numpy(), ref_o, f"o head {h}")
+    pool = lib().StatePool(policy_of(x), 1)
+    o2, pool, _ = prefill(x, pool=pool)
+    assert sha(o2) == sha(o)
+    tot = run_oracle_checks(oracle_items(x, o, pool.state), "long 65536")
+    assert tot["elements"] == x.total_tokens * x.h_v * x.dv
+
+
+@pytest.mark.parametrize("cap", [1, 7, 64, 4096])
+def test_long_sequence_among_neighbours_under_a_grid_cap(long_x, cap):
+    """X packed among 7 random neighbours with every compute kernel capped at `cap` workgroups
+    ("Making kernels parallelism-invariant": identical bits however the work is split and whatever
+    shares the launch): X's o and final state equal those of X alone, bit for bit, and the
+    neighbours' equal their uncapped run."""
+    x, so, sS, _ = long_x
+    y, pos = gi.long_in_batch(x, 8, sub=100 + cap)
+    say(f"long: X among 7 neighbours at position {pos} under a grid cap of {cap}")
+    ref_o, ref_pool, _ = prefill(y)
+    pool = lib().StatePool(policy_of(y), y.num_seqs)
+    pool.set_max_workgroups(cap)
+    o, pool, _ = prefill(y, pool=pool)
+    t0 = int(y.cu_seqlens[pos])
+    assert sha(o[t0:t0 + x.total_tokens]) == so
+    assert sha(pool.state[pos:pos + 1]) == sS
+    assert sha(o) == sha(ref_o) and sha(pool.state) == sha(ref_pool.state)
 
 
 @pytest.mark.parametrize("batch", [2, 4, 8, 16, 32, 64])
@@ -251,9 +273,10 @@ def test_long_sequence_one_pass_and_overlapped_under_a_grid_cap(long_x, cap):
 def test_decode_under_a_grid_cap(cap, record):
     """Ragged prompts, then 70 decode steps that cross chunk starts, with the decode step capped
     at `cap` workgroups: every output, state, position and boundary record as in the natural
-    launch.  With a boundary record the step counts finished workgroups per slot; without one
-    (fp32 boundaries) it takes the uncounted launch shape.  The sequences live in a permuted
-    subset of a larger pool, so three slots are never listed and must stay untouched."""
+    launch.  With a boundary record every workgroup reads the slot's position and a second kernel
+    advances it after the step; without one (fp32 boundaries) no workgroup reads the position and
+    one workgroup per slot advances it.  The sequences live in a permuted subset of a larger pool,
+    so three slots are never listed and must stay untouched."""
     cpr = lib()
     lens = [(53 * i) % 190 + 1 for i in range(16)]
     prompts = gi.make_inputs(31, lens, io="bf16", device="cuda", **gi.BIG)
@@ -281,9 +304,10 @@ def test_decode_under_a_grid_cap(cap, record):
 
 
 def test_decode_counted_and_uncounted_shapes_agree():
-    """The same prompts and 70 decode steps through a pool with a boundary record (the counted
-    launch shape) and one without (the uncounted shape): outputs, states and positions are equal
-    bit for bit, and the record holds each slot's last chunk-start state."""
+    """The same prompts and 70 decode steps through a pool with a boundary record (every workgroup
+    reads the position; a second kernel advances it) and one without (no position read; one
+    workgroup per slot advances it): outputs, states and positions are equal bit for bit, and the
+    record holds each slot's last chunk-start state."""
     cpr = lib()
     lens = [(71 * i) % 300 + 1 for i in range(24)]
     prompts = gi.make_inputs(33, lens, io="bf16", device="cuda", **gi.BIG)

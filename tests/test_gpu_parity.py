@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import gdn_inputs as gi
-from tests.gpu_util import (check_close, decode_all, gpu_state_math, lib, oracle_all, oracle_seq_head,
-                            policy_of, prefill, say, sha)
+from tests.gpu_util import (check_close, decode_all, gpu_state_math, lib, oracle_all, oracle_items,
+                            oracle_seq_head, policy_of, prefill, run_oracle_checks, say, sha)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,59 @@ def test_exact_vector_is_bitwise_equal_to_oracle(dk):
     pool_d = lib().StatePool(policy_of(x), 1)
     o_d = decode_all(x, pool_d)
     assert np.array_equal(o_d.cpu().double().numpy(), ref_o)
+
+
+def _tie_inputs(T=300, dk=16, hv=2, seed=5):
+    """bf16 io with a = b = 1 and one-hot keys: the write makes row pi(t) of S equal v_t exactly,
+    and with dyadic values (multiples of 2^-13 below 2) and queries in {-1, 0, 1} every fp32
+    operation of the step and of the output dot is exact.  Many outputs then fall exactly halfway
+    between two bf16 values (1 + 2^-8, for one), where round-to-nearest-even keeps the even one."""
+    r = np.random.default_rng(seed)
+    perm = r.integers(0, dk, (T, 1))
+    k = np.eye(dk, dtype=np.float32)[perm]
+    q = r.integers(-1, 2, (T, 1, dk)).astype(np.float32)
+    vals = np.array([0.0, 1.0, -1.0, 2.0 ** -8, -(2.0 ** -8), 3 * 2.0 ** -8, -3 * 2.0 ** -8, 2.0 ** -7, 1.5,
+                     -1.5, 2.0 ** -13, 0.5], np.float32)
+    v = vals[r.integers(0, len(vals), (T, hv, dk))]
+    ones = np.ones((T, hv), np.float32)
+    t = lambda z: torch.from_numpy(np.ascontiguousarray(z))
+    bf = lambda z: t(z).to(torch.bfloat16)
+    x = gi.GdnInputs("ties", 1, hv, dk, dk, 64, "bf16", gi.cu_from_lengths([T]), bf(q), bf(k), bf(v), t(ones),
+                     t(ones.copy()))
+    assert torch.equal(x.v.float(), t(v)) and torch.equal(x.q.float(), t(q))      # exact in bf16
+    return x
+
+
+@pytest.mark.parametrize("dk", [16, 128])
+def test_bf16_rounding_is_nearest_even_bit_for_bit(dk):
+    """Exact fp32 outputs rounded to bf16 by every output path (pass 2, one-pass, overlapped,
+    decode) equal the oracle's exact values rounded to nearest even, bit for bit, ties included."""
+    from tests.bf16_check import bf16_bits_to_f64, rne_bf16_bits
+    cpr = lib()
+    x = _tie_inputs(dk=dk)
+    ref_o, ref_S, _ = oracle_all(x)
+    f32 = ref_o.astype(np.float32)
+    assert np.array_equal(f32.astype(np.float64), ref_o)                # the outputs are exact in fp32
+    u = f32.view(np.uint32)
+    ties = int(((u & 0xFFFF) == 0x8000).sum())
+    assert ties >= 0.03 * u.size                                         # many exact ties
+    # compared as values, so that the sign of an exact zero (which the dot's order decides) is free
+    want = bf16_bits_to_f64(rne_bf16_bits(ref_o))
+    bits = lambda o: bf16_bits_to_f64(o.view(torch.int16).cpu().numpy().view(np.uint16))
+    say(f"bf16 ties dk={dk}: two-pass ({ties} ties of {u.size})")
+    o, pool, _ = prefill(x)
+    assert np.array_equal(bits(o), want)
+    for h in range(x.h_v):
+        assert np.array_equal(gpu_state_math(pool, 0, h), ref_S[0, h])
+    o_np, _, _ = prefill(x, c_stash=None)
+    assert np.array_equal(bits(o_np), want)
+    for overlapped in (False, True):
+        say(f"bf16 ties dk={dk}: {'overlapped' if overlapped else 'one-pass'}")
+        o1, _, _ = _fused(x, overlapped=overlapped)
+        assert np.array_equal(bits(o1), want)
+    say(f"bf16 ties dk={dk}: decode")
+    o_d = decode_all(x, cpr.StatePool(policy_of(x), 1))
+    assert np.array_equal(bits(o_d), want)
 
 
 LENS = [1, 5, 64, 65, 130, 33, 0, 97]
@@ -230,6 +283,8 @@ def test_fused_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert bool(torch.isnan(cs1[n:]).all())              # nothing written past the last row
     o3, pool3, _ = _fused(x, stash=False)
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
+    # and directly against the oracle: o, final states and chunk-start rows of every pair
+    run_oracle_checks(oracle_items(x, o1, pool1.state, chunk_states=cs1), f"fused dim={dim} io={io}")
 
 
 @pytest.mark.parametrize("dim,io", [(16, "f32"), (128, "bf16")])
@@ -413,6 +468,69 @@ def test_overlapped_prefill_is_bitwise_equal_to_two_pass(dim, io):
     assert bool(torch.isnan(cs1[n:]).all())
     o3, pool3, _ = _fused(x, stash=False, overlapped=True)
     assert sha(o3) == sha(o2) and sha(pool3.state) == sha(pool2.state)
+    lib().gdn_device_status()                               # no wait gave up
+    run_oracle_checks(oracle_items(x, o1, pool1.state, chunk_states=cs1), f"overlapped dim={dim} io={io}")
+
+
+def test_overlapped_wait_give_up_is_reported():
+    """With the overlapped kernel's wait bound set to one poll from the host, its waves give up
+    waiting for each other (the staging wave cannot be a tile ahead, pass 2 cannot see a chunk
+    handed over); every wave still leaves its work item normally, and gdn_device_status reports
+    GDN_EHIP.  The status is cleared by the check: the same call with the default bound then
+    reports nothing and gives gdn_prefill's bits."""
+    cpr = lib()
+    x = gi.make_inputs(29, [1000], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    xd = x.to("cuda")
+    say("overlapped prefill with a one-poll wait bound")
+    cpr.gdn_device_status()
+    pool = cpr.StatePool(policy_of(x), 1)
+    pool.set_wait_limit(1)
+    cpr.gdn_prefill_overlapped(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    with pytest.raises(cpr.GdnError) as e:
+        cpr.gdn_device_status()
+    assert e.value.code == 3 and "gave up" in str(e.value)
+    cpr.gdn_device_status()                                 # cleared by the check above
+    say("overlapped prefill with the default wait bound")
+    o_ref, pool_ref, _ = prefill(x)
+    pool2 = cpr.StatePool(policy_of(x), 1)
+    pool2.set_wait_limit(0)
+    o, _ = cpr.gdn_prefill_overlapped(pool2, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    cpr.gdn_device_status()
+    assert sha(o) == sha(o_ref) and sha(pool2.state) == sha(pool_ref.state)
+
+
+def test_side_stream_calls_match_the_current_stream():
+    """Prefill (with the c stash the binding allocates), decode, the overlapped prefill and the
+    backward called with a non-current stream: every tensor the binding allocates is allocated on
+    that stream, and the results equal those of the same calls on the current stream bit for bit.
+    Allocations on the current stream are made meanwhile, so memory the binding freed early would
+    be reused under the kernels."""
+    cpr = lib()
+    x = gi.make_inputs(30, [300, 5, 129], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16", device="cuda")
+    steps = [gi.make_inputs(30, [1] * 3, h_k=2, h_v=4, dk=128, dv=128, io="bf16", sub=900 + s, device="cuda")
+             for s in range(5)]
+    ct = gi.make_cotangents(x, 31, device="cuda")
+
+    def run(stream):
+        pool = cpr.StatePool(policy_of(x), 3)
+        o, cs = cpr.gdn_prefill(pool, x.cu_seqlens, x.q, x.k, x.v, x.a, x.b, stream=stream)
+        junk = [torch.randn(1 << 20, device="cuda") for _ in range(4)]     # current-stream allocations
+        outs = [cpr.gdn_decode_step(pool, s.q, s.k, s.v, s.a, s.b, stream=stream) for s in steps]
+        g = cpr.gdn_backward(policy_of(x), x.cu_seqlens, x.q, x.k, x.v, x.a, x.b, cs, ct["d_o"],
+                             d_state=ct["d_state"], stream=stream)
+        p2 = cpr.StatePool(policy_of(x), 3)
+        o2, _ = cpr.gdn_prefill_overlapped(p2, x.cu_seqlens, x.q, x.k, x.v, x.a, x.b, stream=stream)
+        if stream is not None:
+            stream.synchronize()
+        torch.cuda.synchronize()
+        del junk
+        return [sha(o), sha(pool.state), sha(torch.stack(outs)), sha(o2)] + [sha(g[n]) for n in ("dq", "dk", "dv", "da", "db")]
+
+    say("calls on the current stream")
+    ref = run(None)
+    say("the same calls on a side stream")
+    side = torch.cuda.Stream()
+    assert run(side) == ref
 
 
 def test_overlapped_prefill_beyond_one_workgroup_per_cu():
