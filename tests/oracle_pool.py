@@ -16,19 +16,29 @@ POOL = None
 WORKERS = 0
 
 
-def _init_worker():
-    os.environ["OMP_NUM_THREADS"] = "1"
-    os.environ["OPENBLAS_NUM_THREADS"] = "1"
-    os.environ["MKL_NUM_THREADS"] = "1"
+_ONE_THREAD = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
 
 
 def start(workers: int | None = None) -> None:
+    """Start the pool.  Each worker's BLAS runs one thread: the variables are set in the environment
+    the workers inherit (numpy reads them when a worker imports it) and restored afterwards, so the
+    test process itself keeps its own settings."""
     global POOL, WORKERS
     if POOL is not None:
         return
     import multiprocessing as mp
     WORKERS = workers or max(1, min(16, os.cpu_count() or 1))
-    POOL = mp.get_context("spawn").Pool(WORKERS, initializer=_init_worker)
+    saved = {k: os.environ.get(k) for k in _ONE_THREAD}
+    try:
+        for k in _ONE_THREAD:
+            os.environ[k] = "1"
+        POOL = mp.get_context("spawn").Pool(WORKERS)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def stop() -> None:
@@ -42,7 +52,8 @@ def stop() -> None:
 def run(items, progress=None):
     """check_pair over every item, in the pool when there is one; returns the results in order."""
     out = []
-    it = POOL.imap(check_pair, items, chunksize=1) if POOL is not None else map(check_pair, items)
+    chunk = max(1, len(items) // (8 * max(WORKERS, 1)))
+    it = POOL.imap(check_pair, items, chunksize=chunk) if POOL is not None else map(check_pair, items)
     for n, r in enumerate(it, 1):
         out.append(r)
         if progress is not None and (n % 32 == 0 or n == len(items)):
