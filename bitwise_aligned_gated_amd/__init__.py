@@ -21,7 +21,7 @@ __all__ = [
     "gdn_prefill_fused", "gdn_prefill_overlapped", "gdn_decode_step", "gdn_state_resync", "gdn_device_status",
     "gdn_backward", "gdn_backward_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_chunked_workspace_bytes", "GDN_CHUNKED_NATIVE", "GDN_CHUNKED_R2",
-    "gdn_trainer_forward",
+    "gdn_trainer_forward", "gdn_prefill_static", "GDN_STATIC_SCRATCH_BYTES",
     "EXPORTS",
 ]
 
@@ -34,6 +34,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP, GDN_EPOLICY = 0, 1, 2, 3, 4
 GDN_F32, GDN_BF16 = 0, 1
 GDN_CHUNKED_NATIVE, GDN_CHUNKED_R2 = 0, 1
+GDN_STATIC_SCRATCH_BYTES = 256 << 20
 _CODES = {1: "GDN_EINVAL", 2: "GDN_EUNSUPPORTED", 3: "GDN_EHIP", 4: "GDN_EPOLICY"}
 
 
@@ -84,6 +85,7 @@ _SIGS = {
                                     _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P, _P]),
     "gdn_trainer_forward": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P,
                                            _P]),
+    "gdn_prefill_static": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
@@ -389,6 +391,31 @@ def gdn_prefill(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_
                             o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0], stash_ptr,
                             _stream_ptr(stream), _events(events, 3)))
     return o, chunk_states
+
+
+def gdn_prefill_static(pool: StatePool, cu_seqlens: torch.Tensor, q, k, v, a, b, slot_ids: torch.Tensor,
+                       o: torch.Tensor, from_state: bool = False, stream=None, events=None):
+    """gdn_prefill that allocates nothing (C gdn_prefill_static): its scratch is a library-owned
+    static device buffer of GDN_STATIC_SCRATCH_BYTES.  Every argument is a caller-owned device
+    tensor (cu_seqlens and slot_ids int32 on the pool's device, o preallocated), so that neither the
+    library nor this binding allocates; the results are gdn_prefill's bits.  Calls that overlap on
+    one device race on the buffer.  Returns o."""
+    P, dev = pool.policy, pool.device
+    N = q.shape[0]
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens.shape, dev, align=4)
+    B = cu_seqlens.numel() - 1
+    _dev(slot_ids, "slot_ids", torch.int32, (B,), dev, align=4)
+    io = P.torch_io
+    _dev(q, "q", io, (N, P.h_k, P.dk), dev)
+    _dev(k, "k", io, (N, P.h_k, P.dk), dev)
+    _dev(v, "v", io, (N, P.h_v, P.dv), dev)
+    _dev(a, "a", torch.float32, (N, P.h_v), dev, align=4)
+    _dev(b, "b", torch.float32, (N, P.h_v), dev, align=4)
+    _dev(o, "o", io, (N, P.h_v, P.dv), dev)
+    _check(_lib.gdn_prefill_static(pool.handle, cu_seqlens.data_ptr(), B, N, slot_ids.data_ptr(),
+                                   int(bool(from_state)), q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(),
+                                   b.data_ptr(), o.data_ptr(), _stream_ptr(stream), _events(events, 3)))
+    return o
 
 
 @_on_stream

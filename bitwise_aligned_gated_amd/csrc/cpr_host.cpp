@@ -401,6 +401,35 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
                       chunk_state_rows, c_stash, nullptr, stream, events, "gdn_prefill");
 }
 
+int gdn_prefill_static(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                       const float* a, const float* b, void* o, void* stream, void* const* events) {
+  static const char* who = "gdn_prefill_static";
+  if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", who);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", who);
+  const gdn_policy& P = st->policy;
+  const int64_t rows = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
+  const int64_t plane = int64_t(P.h_v) * P.dv * P.dk * 4;
+  const int64_t rows_bytes = (rows * plane + 255) / 256 * 256;
+  const int64_t stash_bytes = total_tokens * P.h_v * int64_t(P.dv) * 4;
+  const int64_t cap = int64_t(cpr::kStaticScratchBytes);
+  if (rows < 0 || rows_bytes > cap)
+    return fail(GDN_EINVAL,
+                "%s: %lld chunk-state rows of %lld bytes need %lld bytes of scratch, above the library's static "
+                "%lld; split the batch or use gdn_prefill with caller-owned chunk states",
+                who, (long long)rows, (long long)plane, (long long)rows_bytes, (long long)cap);
+  void* scratch = nullptr;
+  const hipError_t e = cpr::static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "gdn_prefill_static: static scratch");
+  // the chunk-start rows first; the c stash after them when it fits too (the same bits either way)
+  float* rows_ptr = static_cast<float*>(scratch);
+  float* stash = total_tokens > 0 && rows_bytes + stash_bytes <= cap
+                     ? reinterpret_cast<float*>(static_cast<char*>(scratch) + rows_bytes)
+                     : nullptr;
+  return prefill_impl(st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v, a, b, o, rows_ptr,
+                      rows, stash, nullptr, stream, events, who);
+}
+
 int gdn_trainer_forward(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                         const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
                         const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,

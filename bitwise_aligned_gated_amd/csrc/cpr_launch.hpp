@@ -17,6 +17,10 @@ hipError_t launch_prefill_overlap(int dk, int dv, int io, const PrefillArgs& A, 
 int overlap_max_chunk();
 // The current device's status word of the overlapped kernel's bounded waits (device address).
 hipError_t wait_status_word(uint32_t** out);
+// The library-owned scratch of gdn_prefill_static on the current device (its device address, taken
+// once per device), kStaticScratchBytes long and 256-byte aligned.
+constexpr size_t kStaticScratchBytes = size_t(256) << 20;
+hipError_t static_scratch(void** out);
 // Whether every workgroup of the overlapped kernel is resident at once (one per CU).
 bool overlap_fits(int dk, int dv, const PrefillArgs& A);
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);

@@ -239,6 +239,30 @@ int gdn_prefill(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int6
                 void* o, float* chunk_states, int64_t chunk_state_rows, float* c_stash, void* stream,
                 void* const* events);
 
+/* gdn_prefill without any device memory from the caller or the allocator, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The chunk-start states the two passes hand over, and the c stash when it fits as well, live in a
+ * library-owned static device buffer of GDN_STATIC_SCRATCH_BYTES (256 MiB), which every device the
+ * library runs on holds from its first use of this call until the process ends.  The call itself
+ * allocates nothing and frees nothing.
+ *   Arguments as gdn_prefill, without chunk_states and c_stash.  The results (o, final states,
+ *   positions) are gdn_prefill's bits.
+ *   Limit: gdn_chunk_rows_bound(total_tokens, num_seqs, chunk) * h_v * dv * dk * 4 bytes (rounded
+ *   up to 256) must fit the buffer -- 128 rows at 32 value heads of 128 x 128, e.g. 7,680 tokens in
+ *   4 sequences at chunk 64; larger batches return GDN_EINVAL with a message naming the sizes
+ *   (split them, or use gdn_prefill).  The c stash is used when the rows and N * h_v * dv * 4 bytes
+ *   both fit; otherwise the output pass recomputes c (the same bits).
+ *   Nothing in the buffer needs clearing: every row or c a call reads was written earlier in the
+ *   same call.  The buffer is shared by every call on the device and keeps the last call's
+ *   contents: calls that overlap on one device (on different streams, or from different host
+ *   threads) race on it and must be ordered by the caller.
+ * events: as gdn_prefill. */
+#define GDN_STATIC_SCRATCH_BYTES (256u << 20)
+int gdn_prefill_static(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                       const int32_t* slot_ids, int32_t from_state,
+                       const void* q, const void* k, const void* v, const float* a, const float* b,
+                       void* o, void* stream, void* const* events);
+
 /* The trainer forward (the "trainer_fwd" case of section "The execution contract", whose per-layer
  * table in section "Solving the linear-attention headache" times CPR for the trainer's forward and
  * backward): gdn_prefill, bit for bit in o, final states

@@ -199,6 +199,12 @@ def test_prefill_argument_errors_before_launch():
         for n in (-1, 1 << 31):
             assert lib.gdn_state_set_max_workgroups(h, n) == 1 and b"max_workgroups" in lib.gdn_last_error()
         assert lib.gdn_state_set_max_workgroups(None, 4) == 1 and b"state handle" in lib.gdn_last_error()
+        # the prefill with static scratch refuses, before touching the GPU, a batch whose chunk-start
+        # rows exceed its buffer: 5,000,000 tokens at chunk 64 need 78,127 rows of 4 KiB (305 MiB)
+        rc = lib.gdn_prefill_static(h, fake, 2, 5_000_000, fake, 0, fake, fake, fake, fake, fake, fake, None, None)
+        assert rc == 1 and b"static" in lib.gdn_last_error()
+        assert lib.gdn_prefill_static(None, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, None, None) == 1
+        assert cpr.GDN_STATIC_SCRATCH_BYTES == 256 << 20
         # the overlapped kernel's wait bound: any value is accepted, a NULL handle is not
         for n in (0, 1, 0xFFFFFFFF):
             assert lib.gdn_state_set_wait_limit(h, n) == 0
