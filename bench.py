@@ -469,6 +469,7 @@ def main():
         del wpool
         snap_state, snap_pos = dpool.state.clone(), dpool.pos.clone()   # for the boundary-record run
         dec_lens = [int(p) for p in snap_pos.tolist()]
+        start_host = snap_state.cpu().numpy() if pool is not None else None   # for the oracle leg
         torch.cuda.synchronize()
         devs = [[hip.event() for _ in range(3)] for _ in range(args.decode_steps)]
         t0 = time.perf_counter()
@@ -520,7 +521,7 @@ def main():
             # host copies for the oracle leg: the states the prompts left (fp32, exact in fp64), the
             # 128 tokens of every slot and every decode output of the timed steps
             u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            dec_host = {"S0": snap_state.cpu().numpy(), "final": dpool.state.cpu().numpy(), "lens": dec_lens,
+            dec_host = {"S0": start_host, "final": dpool.state.cpu().numpy(), "lens": dec_lens,
                         "q": np.stack([u16(t.q) for t in toks], 1), "k": np.stack([u16(t.k) for t in toks], 1),
                         "v": np.stack([u16(t.v) for t in toks], 1),
                         "a": np.stack([t.a.cpu().numpy() for t in toks], 1),
