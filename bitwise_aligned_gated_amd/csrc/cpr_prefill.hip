@@ -38,24 +38,36 @@ namespace cpr {
 // With a stash, pass 1 runs every token and also keeps each token's write value c (and w when
 // asked), and pass 2 applies the kept c instead of predicting it again: the same values enter
 // the same update, so the bits do not change, and pass 2 skips the prediction's dot product.
-enum : int { kBoundary = 0, kOutput = 1, kFused = 2, kOutputC = 3, kBoundaryC = 4 };
+// Pass 1 comes in two lane mappings: one 8-row leaf per lane (kBoundary, kBoundaryC) or two
+// (kBoundary2, kBoundaryC2).  Two leaves per lane halve the tree levels and the per-column work
+// (w, c) per state element, so a column costs ~11% fewer instructions per token, but a column
+// chain then occupies half as many lanes: the launcher picks the mapping that loads the busiest
+// SIMD least (launch_pass1 below).  The schedule fixes leaves and tree, not lanes, so both give the
+// same bits.
+enum : int { kBoundary = 0, kOutput = 1, kFused = 2, kOutputC = 3, kBoundaryC = 4, kBoundary2 = 5, kBoundaryC2 = 6 };
 constexpr bool has_out(int mode) { return mode == kOutput || mode == kFused || mode == kOutputC; }
-constexpr bool has_rows(int mode) { return mode == kBoundary || mode == kFused || mode == kBoundaryC; }
+constexpr bool is_pass1(int mode) {
+  return mode == kBoundary || mode == kBoundaryC || mode == kBoundary2 || mode == kBoundaryC2;
+}
+constexpr bool two_leaves(int mode) { return mode == kBoundary2 || mode == kBoundaryC2; }
+constexpr bool has_rows(int mode) { return is_pass1(mode) || mode == kFused; }
 constexpr bool is_wide(int mode) { return mode == kOutput || mode == kOutputC; }
 constexpr bool reads_c(int mode) { return mode == kOutputC; }      // c from the stash instead of v, b
-constexpr bool keeps_c(int mode) { return mode == kBoundaryC; }    // writes the stash
+constexpr bool keeps_c(int mode) { return mode == kBoundaryC || mode == kBoundaryC2; }    // writes the stash
+constexpr bool stops_at_last_start(int mode) { return mode == kBoundary || mode == kBoundary2; }
 
 template <int DK, int DV, int MODE>
 struct PassCfg {
   static constexpr bool WIDE = is_wide(MODE);     // parallel over chunks: fewer, longer lanes
-  static constexpr int G = WIDE ? (DK / kLeaf < 4 ? DK / kLeaf : 4) : DK / kLeaf;  // lanes per column
+  static constexpr int G = WIDE ? (DK / kLeaf < 4 ? DK / kLeaf : 4)
+                                : (two_leaves(MODE) && DK >= 2 * kLeaf ? DK / (2 * kLeaf) : DK / kLeaf);  // lanes per column
   static constexpr int NL = DK / (kLeaf * G);                                  // leaves per lane
   static constexpr int R = NL * kLeaf;                                         // rows per lane
   static constexpr int NC = WIDE ? 2 : 1;                                      // columns per lane
   static constexpr int WG_MAX_COLS = 256 / G * NC;                             // 4 waves
   static constexpr int WG_COLS = WG_MAX_COLS < DV ? WG_MAX_COLS : DV;
   static constexpr int THREADS = WG_COLS / NC * G;
-  static constexpr int TT = (MODE == kBoundary || MODE == kBoundaryC) ? 32 : 16;  // tokens per tile
+  static constexpr int TT = is_pass1(MODE) ? 32 : 16;  // tokens per tile
   static constexpr int K_UNITS = TT * DK / 8;          // 8-element units of a k (or q) tile
   static constexpr int V_UNITS = TT * WG_COLS / 8;
   static constexpr int K_PER_T = (K_UNITS + THREADS - 1) / THREADS;
@@ -241,7 +253,7 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
       if constexpr (MODE == kOutputC) {                    // vv holds the stashed c
 #pragma unroll
         for (int c = 0; c < NC; ++c) o[c] = cpr_step_given_c<NL, G>(s[c], kr, qr, ab.x, vv[c]);
-      } else if constexpr (MODE == kBoundaryC) {
+      } else if constexpr (keeps_c(MODE)) {
         float u;
         cpr_update<NL, G>(s[0], kr, vv[0], ab.x, ab.y, u, pw, pc);
         ptt = tt;
@@ -267,22 +279,24 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
         if (--nb == 0) {                                   // the new state enters a chunk start
           nb = A.chunk;
           // resynchronise where a token at this position follows (pass 2 applies it after pass 1)
-          if (A.round_boundary && (MODE == kBoundary || t0 + tt + 1 < te)) {
+          if (A.round_boundary && (stops_at_last_start(MODE) || t0 + tt + 1 < te)) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) resync_round(s[c]);
           }
           if (rows_on && row < row_end && row < A.rows_cap) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-              store_f32x8(A.chunk_states + (row * A.h_v + h) * plane +
-                              static_cast<int64_t>(col0 + cp * NC + c) * DK + g * R,
-                          *reinterpret_cast<float(*)[8]>(&s[c][0]));
+#pragma unroll
+              for (int r = 0; r < R; r += 8)
+                store_f32x8(A.chunk_states + (row * A.h_v + h) * plane +
+                                static_cast<int64_t>(col0 + cp * NC + c) * DK + g * R + r,
+                            *reinterpret_cast<float(*)[8]>(&s[c][r]));
           }
           ++row;
         }
       }
     };
-    if constexpr (MODE == kBoundary || MODE == kBoundaryC) {
+    if constexpr (is_pass1(MODE)) {
       In nx;
       read_in(0, nx);
       if (n == Cfg::TT) {                      // full tile: unrolled, immediate offsets
@@ -339,12 +353,12 @@ __device__ __forceinline__ void run_tokens(const PrefillArgs& A, TileLds<DK, DV,
   }
 }
 
-// MODE kBoundary: tokens up to the last chunk start; kBoundaryC: every token, keeping c (and w).
+// MODE kBoundary(2): tokens up to the last chunk start; kBoundaryC(2): every token, keeping c (and w).
 template <int DK, int DV, int IO, int MODE>
 __device__ __forceinline__ void boundary_pass_item(const PrefillArgs& A, int64_t vb) {
   using Cfg = PassCfg<DK, DV, MODE>;
-  static_assert(Cfg::R == kLeaf && Cfg::NC == 1, "pass 1 holds one leaf of one column per lane");
-  static_assert(MODE == kBoundary || MODE == kBoundaryC, "pass 1 modes");
+  static_assert(Cfg::R % kLeaf == 0 && Cfg::NC == 1, "pass 1 holds whole leaves of one column per lane");
+  static_assert(is_pass1(MODE), "pass 1 modes");
   __shared__ TileLds<DK, DV, MODE> L;
   __shared__ int64_t red[(Cfg::THREADS + 63) / 64 + 2];
   // group = (sequence, key head); members = its value heads x column groups
@@ -359,26 +373,32 @@ __device__ __forceinline__ void boundary_pass_item(const PrefillArgs& A, int64_t
   const int64_t plane = static_cast<int64_t>(DV) * DK;
   const int64_t col_off = static_cast<int64_t>(cg * Cfg::WG_COLS + lc) * DK + g * Cfg::R;
   float s[1][Cfg::R];
+  auto store_s = [&](float* p) {
+#pragma unroll
+    for (int r = 0; r < Cfg::R; r += 8) store_f32x8(p + r, *reinterpret_cast<float(*)[8]>(&s[0][r]));
+  };
   if (m.slot >= 0 && m.len == 0 && !A.from_state) {          // an empty sequence from zero: zero slot
 #pragma unroll
     for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
-    store_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s[0]);
+    store_s(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off);
   }
   if (m.nrows == 0 || row0 >= A.rows_cap) return;            // uniform across the block
   if (A.from_state) {
-    load_f32x8(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off, s[0]);
+    const float* src = A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane + col_off;
+#pragma unroll
+    for (int r = 0; r < Cfg::R; r += 8) load_f32x8(src + r, *reinterpret_cast<float(*)[8]>(&s[0][r]));
   } else {
 #pragma unroll
     for (int r = 0; r < Cfg::R; ++r) s[0][r] = 0.0f;
   }
   if (A.round_boundary && m.p0 % A.chunk == 0) resync_round(s[0]);   // the first token is a chunk start
-  store_f32x8(A.chunk_states + (row0 * A.h_v + h) * plane + col_off, s[0]);
-  if (MODE == kBoundary && m.nrows < 2) return;
+  store_s(A.chunk_states + (row0 * A.h_v + h) * plane + col_off);
+  if (stops_at_last_start(MODE) && m.nrows < 2) return;
   // tokens up to the last recorded chunk start (or all of them); the first chunk start is
   // C - p0 % C tokens in
   const int64_t C = A.chunk;
   const int first_nb = static_cast<int>(C - m.p0 % C);
-  const int last = MODE == kBoundaryC ? m.len : static_cast<int>((m.p0 / C + m.nrows - 1) * C - m.p0);
+  const int last = keeps_c(MODE) ? m.len : static_cast<int>((m.p0 / C + m.nrows - 1) * C - m.p0);
   run_tokens<DK, DV, IO, MODE>(A, L, s, static_cast<int>(m.tok0), 0, last, h, cg, row0, row0 + m.nrows, first_nb);
 }
 
@@ -514,21 +534,53 @@ __global__ void prefill_finish_kernel(PrefillArgs A) {
   A.pos_out[m.slot] = m.p0 + m.len;
 }
 
+template <int DK, int DV, int IO, int MODE>
+static hipError_t launch_pass1_mode(const PrefillArgs& A, hipStream_t stream) {
+  using C1 = PassCfg<DK, DV, MODE>;
+  const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
+  if (g1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  return launch_items(boundary_pass_kernel<DK, DV, IO, MODE>, boundary_pass_strided_kernel<DK, DV, IO, MODE>, g1,
+                      C1::THREADS, stream, A);
+}
+
+// Pass 1's lane mapping for a launch.  Two leaves per lane issue fewer instructions per state
+// element, but a column's chain then runs on half as many lanes, so each wave carries twice the
+// columns and the per-token dependent chain (two leaves, the in-lane add, three DPP levels, w, c,
+// the update) is exposed unless many waves share each SIMD -- and the two-leaf kernel's 138 VGPRs
+// leave room for only three resident waves per SIMD.  Measured at d_k = 128 (pass 1 with the c
+// stash, ms, one leaf / two leaves): 5 x 2048 tokens 0.562 / 0.568; the 10240-token trainer batch
+// 0.592 / 0.623; 8 x 2048 0.860 / 0.917; 16 x 2048 1.667 / 1.614; 256 prompts of 1..2048 tokens
+// 13.08 / 12.09.  Two leaves are taken from 8 waves per SIMD on (16 or more sequences of
+// 32 x 128 columns) on; other head dims, and launches under a workgroup cap, keep one leaf per lane.
+bool pass1_two_leaves(int dk, const PrefillArgs& A) {
+  if (dk != 128 || A.num_seqs <= 0 || A.max_wgs > 0) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0)
+    return false;
+  const int64_t simds = 4 * static_cast<int64_t>(cus);
+  const int64_t waves2 = static_cast<int64_t>(A.num_seqs) * A.h_v * 128 * 8 / 64;   // columns x 8 lanes
+  return waves2 >= 8 * simds;
+}
+
+template <int DK, int DV, int IO>
+static hipError_t launch_pass1(const PrefillArgs& A, hipStream_t stream) {
+  if constexpr (DK == 128) {
+    if (pass1_two_leaves(DK, A))
+      return A.c_stash != nullptr ? launch_pass1_mode<DK, DV, IO, kBoundaryC2>(A, stream)
+                                  : launch_pass1_mode<DK, DV, IO, kBoundary2>(A, stream);
+  }
+  return A.c_stash != nullptr ? launch_pass1_mode<DK, DV, IO, kBoundaryC>(A, stream)
+                              : launch_pass1_mode<DK, DV, IO, kBoundary>(A, stream);
+}
+
 template <int DK, int DV, int IO>
 static hipError_t launch_prefill_t(const PrefillArgs& A, hipStream_t stream) {
-  using C1 = PassCfg<DK, DV, kBoundary>;
   using C2 = PassCfg<DK, DV, kOutput>;
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess) return e;
   if (A.num_seqs > 0) {
-    const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
-    if (g1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    if (A.c_stash != nullptr)
-      e = launch_items(boundary_pass_kernel<DK, DV, IO, kBoundaryC>, boundary_pass_strided_kernel<DK, DV, IO, kBoundaryC>,
-                       g1, C1::THREADS, stream, A);
-    else
-      e = launch_items(boundary_pass_kernel<DK, DV, IO, kBoundary>, boundary_pass_strided_kernel<DK, DV, IO, kBoundary>,
-                       g1, C1::THREADS, stream, A);
+    e = launch_pass1<DK, DV, IO>(A, stream);
     if (e != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 1, stream)) != hipSuccess) return e;
@@ -602,11 +654,8 @@ static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream)
 
 template <int DK, int DV, int IO>
 static hipError_t launch_boundary_pass_t(const PrefillArgs& A, hipStream_t stream) {
-  using C1 = PassCfg<DK, DV, kBoundary>;
   if (A.num_seqs <= 0) return hipSuccess;
-  const int64_t g1 = xcd_grid(static_cast<int64_t>(A.num_seqs) * A.h_k, A.h_v / A.h_k * (DV / C1::WG_COLS));
-  return launch_items(boundary_pass_kernel<DK, DV, IO, kBoundary>, boundary_pass_strided_kernel<DK, DV, IO, kBoundary>,
-                      g1, C1::THREADS, stream, A);
+  return launch_pass1<DK, DV, IO>(A, stream);
 }
 
 hipError_t launch_boundary_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
