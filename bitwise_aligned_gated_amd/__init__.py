@@ -86,6 +86,9 @@ _SIGS = {
     "gdn_trainer_forward": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64, _P, _P,
                                            _P]),
     "gdn_prefill_static": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "gdn_r2_ring_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i32]),
+    "gdn_r2_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i32]),
+    "gdn_state_attach_r2": (ctypes.c_int, [_P, _P, _sz, _P, _sz]),
 }
 EXPORTS = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
@@ -270,6 +273,27 @@ class StatePool:
         """Cap the compute kernels of later calls at n workgroups (C gdn_state_set_max_workgroups);
         0 restores one workgroup per work item.  Results are bitwise the same either way."""
         _check(_lib.gdn_state_set_max_workgroups(self._h, int(n)))
+
+    def attach_r2(self, ring=None, workspace=None) -> None:
+        """R2 resynchronisation in decode (C gdn_state_attach_r2): allocate the token ring and the
+        workspace (or use the given uint8 device tensors) and bind them; needs a boundary record.
+        attach_r2(False) detaches."""
+        if ring is False:
+            _check(_lib.gdn_state_attach_r2(self._h, None, 0, None, 0))
+            self.r2_ring = self.r2_workspace = None
+            return
+        c = ctypes.byref(self.policy.c())
+        rb = int(_lib.gdn_r2_ring_bytes(c, self.num_slots))
+        wb = int(_lib.gdn_r2_workspace_bytes(c, self.num_slots))
+        if rb < 0 or wb < 0:
+            _check(GDN_EUNSUPPORTED)
+        ring = torch.zeros(rb, dtype=torch.uint8, device=self.device) if ring is None else ring
+        workspace = torch.zeros(wb, dtype=torch.uint8, device=self.device) if workspace is None else workspace
+        _dev(ring, "ring", torch.uint8, (ring.numel(),), self.device)
+        _dev(workspace, "workspace", torch.uint8, (workspace.numel(),), self.device)
+        _check(_lib.gdn_state_attach_r2(self._h, ring.data_ptr(), ring.numel(), workspace.data_ptr(),
+                                        workspace.numel()))
+        self.r2_ring, self.r2_workspace = ring, workspace
 
     def set_wait_limit(self, polls: int) -> None:
         """Bound of each wait in the overlapped prefill's later calls (C gdn_state_set_wait_limit);

@@ -34,6 +34,12 @@ struct PrefillArgs {
   int64_t max_wgs;            // 0: one workgroup per item; else at most this many, taking items in turn
   uint32_t* status;           // overlapped kernel: device word a bounded wait that gives up ORs a flag into
   uint32_t wait_limit;        // overlapped kernel: polls per bounded wait (0: the default)
+  const int32_t* gate;        // chunk-form kernels, nullable: sequence j runs only where gate[j] != 0, and then
+                              //   as one chunk row (row j) of C tokens (the decode resynchronisation)
+  const float* state_in;      // chunk-form state pass, nullable: where continuing sequences start (else state)
+  void* r2_ring;              // chunked R2 prefill, nullable: the pool's decode ring to fill
+  float* r2_boundary;         //   and its boundary record (state and position) to set
+  int64_t* r2_boundary_pos;
 };
 
 struct DecodeArgs {

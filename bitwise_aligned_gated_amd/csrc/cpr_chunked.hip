@@ -159,7 +159,13 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* w
   if (w >= A.rows_cap) return;                                // uniform across the block
   int i;
   int64_t c;
-  if (!plan_find_row(A, w, &i, &c, red)) return;              // uniform across the block
+  if (A.gate != nullptr) {                                    // one row per sequence, run where gated in
+    i = static_cast<int>(w);
+    c = 0;
+    if (A.gate[i] == 0) return;                               // uniform across the block
+  } else if (!plan_find_row(A, w, &i, &c, red)) {
+    return;                                                   // uniform across the block
+  }
   const SeqMeta m = seq_meta(A, i);
   int t0, t1;
   chunk_range(m, c, A.chunk, &t0, &t1);
@@ -369,8 +375,9 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* 
   if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
   const int i = static_cast<int>(gs.group / A.h_k), kh = static_cast<int>(gs.group % A.h_k);
   const int h = kh * ratio + gs.member / NSL, sl = gs.member % NSL;
+  if (A.gate != nullptr && A.gate[i] == 0) return;            // uniform across the block
   const SeqMeta m = seq_meta(A, i);
-  const int64_t row0 = plan_row_offset(A, i, red);
+  const int64_t row0 = A.gate != nullptr ? i : plan_row_offset(A, i, red);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lg = lane >> 4;
   const int64_t plane = static_cast<int64_t>(D) * D;
   const int j0 = sl * NS;
@@ -379,11 +386,12 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* 
   const int64_t nrows = row0 + m.nrows <= A.rows_cap ? m.nrows : (A.rows_cap > row0 ? A.rows_cap - row0 : 0);
   StateRegs<D> R;
   if (nrows > 0) state_fetch<D>(A, ws, m, row0, 0, h, kh, j0, R);
-  // the entering state: the slot's (continuation) or zero
+  // the entering state: the slot's (continuation; from state_in when given) or zero
+  const float* sin = A.state_in != nullptr ? A.state_in : A.state;
   for (int e = tid; e < NS * D / 4; e += 256) {
     const int jj = e / (D / 4), c4 = e % (D / 4);
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (A.from_state) x = reinterpret_cast<const float4*>(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane +
+    if (A.from_state) x = reinterpret_cast<const float4*>(sin + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane +
                                                           static_cast<int64_t>(j0 + jj) * D)[c4];
     *reinterpret_cast<float4*>(&S.st[jj * SS + 4 * c4]) = x;
   }
@@ -393,8 +401,8 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* 
     int t0, t1;
     chunk_range(m, c, A.chunk, &t0, &t1);
     const int n = t1 - t0;
-    // the state entering this chunk -> its chunk-state row
-    for (int e = tid; e < NS * D / 4; e += 256) {
+    // the state entering this chunk -> its chunk-state row (when rows are kept)
+    for (int e = tid; A.chunk_states != nullptr && e < NS * D / 4; e += 256) {
       const int jj = e / (D / 4), c4 = e % (D / 4);
       reinterpret_cast<float4*>(A.chunk_states + (w * A.h_v + h) * plane + static_cast<int64_t>(j0 + jj) * D)[c4] =
           *reinterpret_cast<const float4*>(&S.st[jj * SS + 4 * c4]);
@@ -557,6 +565,224 @@ __global__ void __launch_bounds__(256) chunk_output_kernel(PrefillArgs A, const 
   }
 }
 
+// ---- R2 resynchronisation in decode -----------------------------------------------------------
+// Under the R2 reading a chunk-start state is the chunk form's state, computed from the previous
+// chunk-start state over the chunk's tokens, and the tokens in between run the pinned per-token
+// step from it.  A decode step keeps, per slot, the chunk-start state of the chunk its last token
+// fell in (the pool's boundary record) and that chunk's tokens so far (the ring, indexed by
+// position mod C).  When a slot reaches the next chunk start, the chunk form over the ring's C
+// tokens from the recorded state gives the new chunk-start state: the same chunk_prep and
+// chunk_state kernels as the chunked prefill, run over the ring as a batch of one-chunk sequences
+// (one per slot, gated to the slots at a chunk start), so the state has the bits a chunked R2
+// prefill over the same tokens computes.  The decode step then applies the token from it and
+// records it, and the token is appended to the ring.
+
+// Ring layout (num_slots x C token positions): q, k [S C][H_k][D] bf16, v [S C][H_v][D] bf16,
+// a, b [S C][H_v] fp32, each part 256-byte aligned.
+struct RingParts {
+  __bf16* q;
+  __bf16* k;
+  __bf16* v;
+  float* a;
+  float* b;
+};
+
+static int64_t pad256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t r2_ring_bytes(int h_k, int h_v, int d, int chunk, int num_slots) {
+  const int64_t n = static_cast<int64_t>(num_slots) * chunk;
+  return 2 * pad256(n * h_k * d * 2) + pad256(n * h_v * d * 2) + 2 * pad256(n * h_v * 4);
+}
+
+static RingParts ring_parts(void* ring, int h_k, int h_v, int d, int chunk, int num_slots) {
+  const int64_t n = static_cast<int64_t>(num_slots) * chunk;
+  char* p = static_cast<char*>(ring);
+  RingParts r;
+  r.q = reinterpret_cast<__bf16*>(p);
+  p += pad256(n * h_k * d * 2);
+  r.k = reinterpret_cast<__bf16*>(p);
+  p += pad256(n * h_k * d * 2);
+  r.v = reinterpret_cast<__bf16*>(p);
+  p += pad256(n * h_v * d * 2);
+  r.a = reinterpret_cast<float*>(p);
+  p += pad256(n * h_v * 4);
+  r.b = reinterpret_cast<float*>(p);
+  return r;
+}
+
+// Workspace: the one-chunk batch's cu_seqlens [S + 1], slot ids [S], gate [S] (int32), positions
+// [S] (int64, zero), then the chunk-form workspace of S rows.
+struct R2Work {
+  int32_t* cu;
+  int32_t* ids;
+  int32_t* gate;
+  int64_t* vpos;
+  float* ws;
+};
+
+int64_t r2_workspace_bytes(int h_v, int d, int num_slots) {
+  const int64_t S = num_slots;
+  return pad256((S + 1) * 4) + 2 * pad256(S * 4) + pad256(S * 8) + S * h_v * chunked_workspace_floats(d) * 4;
+}
+
+static R2Work r2_work(void* work, int num_slots) {
+  const int64_t S = num_slots;
+  char* p = static_cast<char*>(work);
+  R2Work w;
+  w.cu = reinterpret_cast<int32_t*>(p);
+  p += pad256((S + 1) * 4);
+  w.ids = reinterpret_cast<int32_t*>(p);
+  p += pad256(S * 4);
+  w.gate = reinterpret_cast<int32_t*>(p);
+  p += pad256(S * 4);
+  w.vpos = reinterpret_cast<int64_t*>(p);
+  p += pad256(S * 8);
+  w.ws = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// The one-chunk batch over every slot, nobody gated in yet.
+__global__ void r2_batch_kernel(R2Work W, int num_slots, int chunk) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s > num_slots) return;
+  W.cu[s] = s * chunk;
+  if (s == num_slots) return;
+  W.ids[s] = s;
+  W.gate[s] = 0;
+  W.vpos[s] = 0;
+}
+
+// Gate in the listed slots that stand at a chunk start with a chunk behind them.
+__global__ void r2_gate_kernel(R2Work W, const int32_t* slot_ids, int batch, const int64_t* pos, int num_slots,
+                               int chunk) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= batch) return;
+  const int32_t s = slot_ids[j];
+  if (s < 0 || s >= num_slots) return;
+  const int64_t p = pos[s];
+  if (p > 0 && p % chunk == 0) W.gate[s] = 1;
+}
+
+// After the step (positions already advanced): each listed slot's token to ring position
+// (pos - 1) mod C.  One workgroup per batch entry.
+template <int D>
+__global__ void __launch_bounds__(256) r2_ring_append_kernel(DecodeArgs A, RingParts R) {
+  const int j = blockIdx.x;
+  const int32_t s = A.slot_ids[j];
+  if (s < 0 || s >= A.num_slots) return;
+  const int64_t p = A.pos[s] - 1;
+  if (p < 0) return;
+  const int64_t dst = static_cast<int64_t>(s) * A.chunk + p % A.chunk;
+  const uint4* q = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.q) + static_cast<int64_t>(j) * A.h_k * D);
+  const uint4* k = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.k) + static_cast<int64_t>(j) * A.h_k * D);
+  const uint4* v = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.v) + static_cast<int64_t>(j) * A.h_v * D);
+  uint4* rq = reinterpret_cast<uint4*>(R.q + dst * A.h_k * D);
+  uint4* rk = reinterpret_cast<uint4*>(R.k + dst * A.h_k * D);
+  uint4* rv = reinterpret_cast<uint4*>(R.v + dst * A.h_v * D);
+  for (int e = threadIdx.x; e < A.h_k * D / 8; e += 256) {
+    rq[e] = q[e];
+    rk[e] = k[e];
+  }
+  for (int e = threadIdx.x; e < A.h_v * D / 8; e += 256) rv[e] = v[e];
+  for (int e = threadIdx.x; e < A.h_v; e += 256) {
+    R.a[dst * A.h_v + e] = A.a[static_cast<int64_t>(j) * A.h_v + e];
+    R.b[dst * A.h_v + e] = A.b[static_cast<int64_t>(j) * A.h_v + e];
+  }
+}
+
+// After a chunked R2 prefill (before its position update): each sequence's tokens from the start
+// of its last chunk on go to the ring, and the state entering that chunk (its last chunk-state
+// row) to the boundary record.  One workgroup per sequence.
+template <int D>
+__global__ void __launch_bounds__(256) r2_ring_fill_kernel(PrefillArgs A, RingParts R, float* boundary,
+                                                           int64_t* boundary_pos) {
+  __shared__ int64_t red[6];
+  const int i = blockIdx.x;
+  const SeqMeta m = seq_meta(A, i);
+  const int64_t row0 = plan_row_offset(A, i, red);
+  if (m.slot < 0 || m.len == 0) return;                      // uniform across the block
+  const int64_t C = A.chunk, p_end = m.p0 + m.len;
+  const int64_t bpos = (p_end - 1) / C * C, first = bpos > m.p0 ? bpos : m.p0;
+  for (int64_t p = first; p < p_end; ++p) {
+    const int64_t src = m.tok0 + (p - m.p0), dst = static_cast<int64_t>(m.slot) * C + p % C;
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.q) + src * A.h_k * D);
+    const uint4* k = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.k) + src * A.h_k * D);
+    const uint4* v = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.v) + src * A.h_v * D);
+    uint4* rq = reinterpret_cast<uint4*>(R.q + dst * A.h_k * D);
+    uint4* rk = reinterpret_cast<uint4*>(R.k + dst * A.h_k * D);
+    uint4* rv = reinterpret_cast<uint4*>(R.v + dst * A.h_v * D);
+    for (int e = threadIdx.x; e < A.h_k * D / 8; e += 256) {
+      rq[e] = q[e];
+      rk[e] = k[e];
+    }
+    for (int e = threadIdx.x; e < A.h_v * D / 8; e += 256) rv[e] = v[e];
+    for (int e = threadIdx.x; e < A.h_v; e += 256) {
+      R.a[dst * A.h_v + e] = A.a[src * A.h_v + e];
+      R.b[dst * A.h_v + e] = A.b[src * A.h_v + e];
+    }
+  }
+  const int64_t row = row0 + m.nrows - 1;
+  if (row >= A.rows_cap) return;
+  const int64_t plane = static_cast<int64_t>(A.h_v) * D * D;
+  const float4* srow = reinterpret_cast<const float4*>(A.chunk_states + row * plane);
+  float4* brow = reinterpret_cast<float4*>(boundary + static_cast<int64_t>(m.slot) * plane);
+  for (int64_t e = threadIdx.x; e < plane / 4; e += 256) brow[e] = srow[e];
+  if (threadIdx.x == 0) boundary_pos[m.slot] = bpos;
+}
+
+template <int D>
+static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work, hipStream_t stream) {
+  using M = ChunkCfg<D>;
+  const int S = A.num_slots, ratio = A.h_v / A.h_k;
+  const RingParts R = ring_parts(ring, A.h_k, A.h_v, D, A.chunk, S);
+  const R2Work W = r2_work(work, S);
+  hipError_t e = record_event(A.events, 0, stream);
+  if (e != hipSuccess || A.batch == 0) return e != hipSuccess ? e : record_event(A.events, 1, stream);
+  hipLaunchKernelGGL(r2_batch_kernel, dim3((S + 1 + 255) / 256), dim3(256), 0, stream, W, S, A.chunk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(r2_gate_kernel, dim3((A.batch + 255) / 256), dim3(256), 0, stream, W, A.slot_ids, A.batch, A.pos,
+                     S, A.chunk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the chunk form over every gated slot's ring: recorded chunk-start state in, new one into the slot
+  PrefillArgs F{};
+  F.cu = W.cu;
+  F.slot_ids = W.ids;
+  F.pos = W.vpos;
+  F.pos_out = W.vpos;
+  F.q = R.q; F.k = R.k; F.v = R.v; F.a = R.a; F.b = R.b;
+  F.o = nullptr;
+  F.state = A.state;
+  F.state_in = A.boundary;
+  F.chunk_states = nullptr;
+  F.total_tokens = static_cast<int64_t>(S) * A.chunk;
+  F.rows_cap = S;
+  F.num_seqs = S;
+  F.num_slots = S;
+  F.from_state = 1;
+  F.h_k = A.h_k; F.h_v = A.h_v; F.chunk = A.chunk;
+  F.gate = W.gate;
+  const int64_t gp = xcd_grid(static_cast<int64_t>(S) * A.h_k, ratio);
+  hipLaunchKernelGGL((chunk_prep_kernel<D>), dim3(static_cast<unsigned>(gp)), dim3(256), 0, stream, F, W.ws);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t gs = xcd_grid(static_cast<int64_t>(S) * A.h_k, ratio * (D / M::NS));
+  hipLaunchKernelGGL((chunk_state_kernel<D>), dim3(static_cast<unsigned>(gs)), dim3(256), 0, stream, F, W.ws, 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the token from that state (recorded at the chunk start), positions advanced, then the ring
+  DecodeArgs B = A;
+  B.events = nullptr;
+  if ((e = launch_decode(D, D, IO_BF16, B, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL((r2_ring_append_kernel<D>), dim3(static_cast<unsigned>(A.batch)), dim3(256), 0, stream, A, R);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return record_event(A.events, 1, stream);
+}
+
+hipError_t launch_decode_r2(int d, const DecodeArgs& A, void* ring, void* work, hipStream_t stream) {
+  if (d == 32) return launch_decode_r2_t<32>(A, ring, work, stream);
+  if (d == 64) return launch_decode_r2_t<64>(A, ring, work, stream);
+  if (d == 128) return launch_decode_r2_t<128>(A, ring, work, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int D>
 static hipError_t launch_chunked_t(const PrefillArgs& A, float* ws, int mode, hipStream_t stream) {
   using M = ChunkCfg<D>;
@@ -587,8 +813,21 @@ static hipError_t launch_chunked_t(const PrefillArgs& A, float* ws, int mode, hi
     }
     if ((e = launch_prefill_finish(A, stream)) != hipSuccess) return e;
   } else {
-    // R2: the CPR output pass (pinned per-token step) from the chunk-form states just stored
-    if ((e = launch_output_pass(D, D, IO_BF16, A, stream)) != hipSuccess) return e;
+    // R2: the CPR output pass (pinned per-token step) from the chunk-form states just stored; with a
+    // decode ring attached, each sequence's last chunk goes to the ring and its entering state to
+    // the boundary record before the positions move
+    if (A.r2_ring == nullptr) {
+      if ((e = launch_output_pass(D, D, IO_BF16, A, stream)) != hipSuccess) return e;
+    } else {
+      if ((e = launch_output_pass_only(D, D, IO_BF16, A, stream)) != hipSuccess) return e;
+      const RingParts R = ring_parts(A.r2_ring, A.h_k, A.h_v, D, A.chunk, A.num_slots);
+      if (A.num_seqs > 0) {
+        hipLaunchKernelGGL((r2_ring_fill_kernel<D>), dim3(static_cast<unsigned>(A.num_seqs)), dim3(256), 0, stream, A,
+                           R, A.r2_boundary, A.r2_boundary_pos);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      if ((e = launch_prefill_finish(A, stream)) != hipSuccess) return e;
+    }
   }
   return record_event(A.events, 3, stream);
 }

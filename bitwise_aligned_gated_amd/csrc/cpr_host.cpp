@@ -23,6 +23,8 @@ struct gdn_state {
   bool owns;
   int64_t max_wgs;   // launch-shape cap of the compute kernels (0: one workgroup per work item)
   uint32_t wait_limit;   // polls per bounded wait of the overlapped kernel (0: the default)
+  void* r2_ring;         // R2 resynchronisation in decode (gdn_state_attach_r2): token ring and workspace
+  void* r2_work;
 };
 
 namespace {
@@ -260,6 +262,8 @@ int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, i
   st->owns = self;
   st->max_wgs = 0;
   st->wait_limit = 0;
+  st->r2_ring = nullptr;
+  st->r2_work = nullptr;
   *out = st;
   return ok();
 }
@@ -311,6 +315,60 @@ int gdn_device_status(void* stream) {
               (flags & 8u) ? " staging waiting for a free tile buffer" : "");
 }
 
+// R2 resynchronisation needs the chunk form: bf16 io, fp32 boundaries, chunks of at most 64 tokens,
+// dk = dv in {32, 64, 128}.
+static int r2_policy(const gdn_policy* p, const char* who) {
+  if (int rc = validate_policy(p); rc != GDN_OK) return rc;
+  if (p->io_dtype != GDN_BF16 || p->state_dtype != GDN_F32 || p->chunk > 64 || p->dk != p->dv ||
+      (p->dk != 32 && p->dk != 64 && p->dk != 128))
+    return fail(GDN_EUNSUPPORTED, "%s: R2 needs bf16 io, fp32 boundaries, chunk <= 64 and dk = dv in {32, 64, 128}",
+                who);
+  return GDN_OK;
+}
+
+int64_t gdn_r2_ring_bytes(const gdn_policy* policy, int32_t num_slots) {
+  if (r2_policy(policy, "gdn_r2_ring_bytes") != GDN_OK) return -1;
+  if (num_slots <= 0) {
+    fail(GDN_EINVAL, "gdn_r2_ring_bytes: num_slots must be positive");
+    return -1;
+  }
+  ok();
+  return cpr::r2_ring_bytes(policy->h_k, policy->h_v, policy->dk, policy->chunk, num_slots);
+}
+
+int64_t gdn_r2_workspace_bytes(const gdn_policy* policy, int32_t num_slots) {
+  if (r2_policy(policy, "gdn_r2_workspace_bytes") != GDN_OK) return -1;
+  if (num_slots <= 0) {
+    fail(GDN_EINVAL, "gdn_r2_workspace_bytes: num_slots must be positive");
+    return -1;
+  }
+  ok();
+  return cpr::r2_workspace_bytes(policy->h_v, policy->dk, num_slots);
+}
+
+int gdn_state_attach_r2(gdn_state* st, void* ring, size_t ring_bytes, void* workspace, size_t workspace_bytes) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_state_attach_r2: state handle is NULL");
+  if (ring == nullptr && workspace == nullptr) {
+    st->r2_ring = st->r2_work = nullptr;
+    return ok();
+  }
+  if (ring == nullptr || workspace == nullptr)
+    return fail(GDN_EINVAL, "gdn_state_attach_r2: ring and workspace must both be set (or both NULL)");
+  if (int rc = r2_policy(&st->policy, "gdn_state_attach_r2"); rc != GDN_OK) return rc;
+  if (st->boundary == nullptr)
+    return fail(GDN_EINVAL, "gdn_state_attach_r2: the pool needs a boundary record (the chunk-start states)");
+  const int64_t rb = cpr::r2_ring_bytes(st->policy.h_k, st->policy.h_v, st->policy.dk, st->policy.chunk, st->num_slots);
+  const int64_t wb = cpr::r2_workspace_bytes(st->policy.h_v, st->policy.dk, st->num_slots);
+  if (int64_t(ring_bytes) < rb || int64_t(workspace_bytes) < wb)
+    return fail(GDN_EINVAL, "gdn_state_attach_r2: ring %zu < %lld or workspace %zu < %lld bytes", ring_bytes,
+                (long long)rb, workspace_bytes, (long long)wb);
+  if ((reinterpret_cast<uintptr_t>(ring) | reinterpret_cast<uintptr_t>(workspace)) % 16 != 0)
+    return fail(GDN_EINVAL, "gdn_state_attach_r2: ring and workspace must be 16-byte aligned");
+  st->r2_ring = ring;
+  st->r2_work = workspace;
+  return ok();
+}
+
 float* gdn_state_data(gdn_state* st) { return st ? st->state : nullptr; }
 int64_t* gdn_state_positions(gdn_state* st) { return st ? st->pos : nullptr; }
 
@@ -354,6 +412,9 @@ static int prefill_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
                         const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
                         float* c_stash, float* w_stash, void* stream, void* const* events, const char* who) {
   if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", who);
+  if (st->r2_ring != nullptr)
+    return fail(GDN_EINVAL, "%s: the pool resynchronises under R2 (gdn_state_attach_r2); prefill it with "
+                            "gdn_prefill_chunked(GDN_CHUNKED_R2)", who);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", who);
   if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", who);
   if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
@@ -448,6 +509,9 @@ static int onepass_impl(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
                         const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
                         void* stream, void* const* events, bool overlap, const char* who) {
   if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", who);
+  if (st->r2_ring != nullptr)
+    return fail(GDN_EINVAL, "%s: the pool resynchronises under R2 (gdn_state_attach_r2); prefill it with "
+                            "gdn_prefill_chunked(GDN_CHUNKED_R2)", who);
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", who);
   if (total_tokens >= (int64_t(1) << 31))
     return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", who);
@@ -527,13 +591,17 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const
   A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
   A.round_boundary = P.state_dtype == GDN_BF16;
   A.events = events;
-  const hipError_t e = cpr::launch_decode(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
+  const hipError_t e = st->r2_ring != nullptr
+                           ? cpr::launch_decode_r2(P.dk, A, st->r2_ring, st->r2_work, static_cast<hipStream_t>(stream))
+                           : cpr::launch_decode(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
   return ok();
 }
 
 int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* stream) {
   if (st == nullptr) return fail(GDN_EINVAL, "gdn_state_resync: state handle is NULL");
+  if (st->r2_ring != nullptr)
+    return fail(GDN_EINVAL, "gdn_state_resync: the pool resynchronises under R2 inside gdn_decode_step");
   if (n < 0) return fail(GDN_EINVAL, "gdn_state_resync: negative count");
   if (n > 0 && slot_ids == nullptr) return fail(GDN_EINVAL, "gdn_state_resync: slot_ids is NULL");
   const gdn_policy& P = st->policy;
@@ -726,6 +794,9 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: chunk %d > 64", P.chunk);
   if (outputs != GDN_CHUNKED_NATIVE && outputs != GDN_CHUNKED_R2)
     return fail(GDN_EINVAL, "gdn_prefill_chunked: outputs must be GDN_CHUNKED_NATIVE or GDN_CHUNKED_R2");
+  if (outputs == GDN_CHUNKED_NATIVE && st->r2_ring != nullptr)
+    return fail(GDN_EINVAL, "gdn_prefill_chunked: the pool resynchronises under R2; native outputs would leave its "
+                            "ring behind");
   if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill_chunked: negative sizes");
   if (total_tokens >= (int64_t(1) << 31))
     return fail(GDN_EINVAL, "gdn_prefill_chunked: total_tokens must fit int32 cu_seqlens");
@@ -766,6 +837,11 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.c_stash = nullptr;
   A.w_stash = nullptr;
   A.events = events;
+  if (outputs == GDN_CHUNKED_R2 && st->r2_ring != nullptr) {
+    A.r2_ring = st->r2_ring;
+    A.r2_boundary = st->boundary;
+    A.r2_boundary_pos = st->boundary_pos;
+  }
   const hipError_t e = cpr::launch_prefill_chunked(P.dk, P.dv, 1, A, workspace, outputs,
                                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");

@@ -30,6 +30,8 @@ hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStr
 // started from chunk states already stored.
 hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream);
 hipError_t launch_output_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
+// The CPR output pass alone, without the position update.
+hipError_t launch_output_pass_only(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
 // Pass 1 alone (chunk-start states up to each sequence's last chunk start, no c, no finish).
 hipError_t launch_boundary_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream);
 // For a backward at a chunk above the chunk-gradient tile: slot_ids[j] = the first row of sequence
@@ -41,5 +43,10 @@ hipError_t launch_rechunk_setup(const BackwardArgs& A, int32_t* slot_ids, int64_
 hipError_t launch_prefill_chunked(int dk, int dv, int io, const PrefillArgs& A, void* ws, int mode,
                                   hipStream_t stream);
 int64_t chunked_workspace_floats(int d);
+// R2 resynchronisation in decode: ring and workspace sizes, and the step (the chunk form over the
+// ring for slots at a chunk start, then the pinned step, then the ring append).
+int64_t r2_ring_bytes(int h_k, int h_v, int d, int chunk, int num_slots);
+int64_t r2_workspace_bytes(int h_v, int d, int num_slots);
+hipError_t launch_decode_r2(int d, const DecodeArgs& A, void* ring, void* work, hipStream_t stream);
 
 }  // namespace cpr

@@ -640,15 +640,21 @@ hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream) {
 }
 
 template <int DK, int DV, int IO>
-static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream) {
+static hipError_t launch_output_pass_only_t(const PrefillArgs& A, hipStream_t stream) {
   using C2 = PassCfg<DK, DV, kOutput>;
   if (A.num_seqs > 0 && A.rows_cap > 0) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, A.h_v / A.h_k * (DV / C2::WG_COLS));
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const hipError_t e = launch_items(output_pass_kernel<DK, DV, IO, kOutput>,
-                                      output_pass_strided_kernel<DK, DV, IO, kOutput>, g2, C2::THREADS, stream, A);
-    if (e != hipSuccess) return e;
+    return launch_items(output_pass_kernel<DK, DV, IO, kOutput>, output_pass_strided_kernel<DK, DV, IO, kOutput>, g2,
+                        C2::THREADS, stream, A);
   }
+  return hipSuccess;
+}
+
+template <int DK, int DV, int IO>
+static hipError_t launch_output_pass_t(const PrefillArgs& A, hipStream_t stream) {
+  const hipError_t e = launch_output_pass_only_t<DK, DV, IO>(A, stream);
+  if (e != hipSuccess) return e;
   return launch_prefill_finish(A, stream);
 }
 
@@ -661,6 +667,17 @@ static hipError_t launch_boundary_pass_t(const PrefillArgs& A, hipStream_t strea
 hipError_t launch_boundary_pass(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
 #define CPR_CASE(D, IOV) \
   if (dk == D && dv == D && io == IOV) return launch_boundary_pass_t<D, D, IOV>(A, stream);
+  CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
+  CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
+  CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)
+  CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
+#undef CPR_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_output_pass_only(int dk, int dv, int io, const PrefillArgs& A, hipStream_t stream) {
+#define CPR_CASE(D, IOV) \
+  if (dk == D && dv == D && io == IOV) return launch_output_pass_only_t<D, D, IOV>(A, stream);
   CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
   CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
   CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)

@@ -357,6 +357,34 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
  * events: NULL, or 4 hipEvent_t recorded before and between the three stages and at the end. */
 #define GDN_CHUNKED_NATIVE 0
 #define GDN_CHUNKED_R2 1
+
+/* ---- R2 resynchronisation in decode ---------------------------------------------------------
+ * Under the R2 reading of CPR's first pass (GDN_CHUNKED_R2 above), the state at every chunk start
+ * is the chunk form's, and decode "resynchronizes the hidden state every chunk-size tokens" (section
+ * "Solving the linear-attention headache") by recomputing it with the chunk form.  A pool with R2
+ * attached keeps, per slot, the chunk-start state of the chunk its last token fell in (in its
+ * boundary record, with that chunk start as boundary_pos) and the chunk's tokens so far (a
+ * caller-owned ring, indexed by position mod C).  Then:
+ *   gdn_prefill_chunked(GDN_CHUNKED_R2) also fills each sequence's ring with the tokens from the
+ *     start of its last chunk on, and its boundary record with the state entering that chunk;
+ *   gdn_decode_step, for each listed slot whose position is a chunk start p > 0, first replaces
+ *     the slot's state by the chunk form's state at p, computed from the recorded state over the
+ *     ring's C tokens by the same kernels as gdn_prefill_chunked (so with its bits), then applies
+ *     the token with the pinned step (recording the new chunk-start state) and appends it to the
+ *     ring.
+ * Decoding a prompt's continuation this way gives the bits of one gdn_prefill_chunked(R2) over
+ * prompt and generated tokens, when each R2 prefill of the slot started at a chunk start (such as
+ * position 0).  R2 pools refuse the R1 prefills, gdn_state_resync and native chunked outputs, which
+ * would leave the ring behind.
+ * Requirements: as gdn_prefill_chunked, and a pool with a boundary record.
+ *   gdn_r2_ring_bytes       num_slots * C token positions of q, k (bf16 [H_k][dk]), v (bf16
+ *                           [H_v][dv]), a and b (fp32 [H_v]); -1 on bad input.
+ *   gdn_r2_workspace_bytes  the chunk form's workspace for one chunk per slot plus small tables.
+ *   gdn_state_attach_r2     binds caller-owned device memory (16-byte aligned, at least those
+ *                           sizes); both NULL detaches.  Host-only, no device work. */
+int64_t gdn_r2_ring_bytes(const gdn_policy* policy, int32_t num_slots);
+int64_t gdn_r2_workspace_bytes(const gdn_policy* policy, int32_t num_slots);
+int gdn_state_attach_r2(gdn_state* st, void* ring, size_t ring_bytes, void* workspace, size_t workspace_bytes);
 int64_t gdn_prefill_chunked_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
 int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                         const int32_t* slot_ids, int32_t from_state,

@@ -205,6 +205,9 @@ def test_prefill_argument_errors_before_launch():
         assert rc == 1 and b"static" in lib.gdn_last_error()
         assert lib.gdn_prefill_static(None, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, None, None) == 1
         assert cpr.GDN_STATIC_SCRATCH_BYTES == 256 << 20
+        # R2 resynchronisation: this pool has fp32 io and no boundary record
+        assert lib.gdn_state_attach_r2(h, fake, 1 << 30, fake, 1 << 30) == 2
+        assert lib.gdn_r2_ring_bytes(ctypes.byref(pol), 3) == -1
         # the overlapped kernel's wait bound: any value is accepted, a NULL handle is not
         for n in (0, 1, 0xFFFFFFFF):
             assert lib.gdn_state_set_wait_limit(h, n) == 0
@@ -300,3 +303,48 @@ def test_chunked_workspace_and_argument_errors():
     assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), ws_bytes=64) == 1 and b"workspace" in msgs[-1]
     assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), ws=fake + 8) == 1
     assert call(cpr.Policy(2, 4, 64, 64, io="bf16"), rows=2) == 1
+
+
+def test_r2_sizes_and_attach_errors():
+    """R2 ring and workspace sizes, attach checks, and the refusal of R1 calls on an R2 pool (no
+    GPU: host checks only, fake addresses never dereferenced)."""
+    lib = cpr._lib
+    pad = lambda x: -(-x // 256) * 256
+    p = cpr.Policy(16, 32, 128, 128, chunk=64, io="bf16")
+    n = 256 * 64
+    ring = 2 * pad(n * 16 * 128 * 2) + pad(n * 32 * 128 * 2) + 2 * pad(n * 32 * 4)
+    assert lib.gdn_r2_ring_bytes(ctypes.byref(p.c()), 256) == ring
+    ws = pad(257 * 4) + 2 * pad(256 * 4) + pad(256 * 8) + 256 * 32 * (3 * 64 * 128 + 2 * 72) * 4
+    assert lib.gdn_r2_workspace_bytes(ctypes.byref(p.c()), 256) == ws
+    assert lib.gdn_r2_ring_bytes(ctypes.byref(cpr.Policy(16, 32, 128, 128, chunk=100).c()), 4) == -1
+    assert lib.gdn_r2_ring_bytes(ctypes.byref(cpr.Policy(16, 32, 16, 16).c()), 4) == -1
+    fake = 0x10000
+    small = cpr.Policy(2, 4, 32, 32, chunk=16, io="bf16")
+    nb = lib.gdn_state_bytes(ctypes.byref(small.c()), 3)
+    rb, wb = lib.gdn_r2_ring_bytes(ctypes.byref(small.c()), 3), lib.gdn_r2_workspace_bytes(ctypes.byref(small.c()), 3)
+    h = ctypes.c_void_p()
+    assert lib.gdn_state_alloc(ctypes.byref(small.c()), 3, fake, fake, nb, None, None, ctypes.byref(h)) == 0
+    try:
+        assert lib.gdn_state_attach_r2(h, fake, rb, fake, wb) == 1 and b"boundary record" in lib.gdn_last_error()
+    finally:
+        lib.gdn_state_free(h)
+    assert lib.gdn_state_alloc(ctypes.byref(small.c()), 3, fake, fake, nb, fake, fake, ctypes.byref(h)) == 0
+    try:
+        assert lib.gdn_state_attach_r2(h, fake, rb - 1, fake, wb) == 1
+        assert lib.gdn_state_attach_r2(h, fake + 4, rb, fake, wb) == 1
+        assert lib.gdn_state_attach_r2(h, fake, rb, None, wb) == 1
+        assert lib.gdn_state_attach_r2(h, fake, rb, fake, wb) == 0
+        # R1 calls would leave the ring behind: refused before any launch
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, None, None, None)
+        assert rc == 1 and b"R2" in lib.gdn_last_error()
+        rc = lib.gdn_prefill_fused(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, None, 0, None, None)
+        assert rc == 1 and b"R2" in lib.gdn_last_error()
+        assert lib.gdn_state_resync(h, fake, 2, None) == 1
+        rc = lib.gdn_prefill_chunked(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99, 0, fake,
+                                     1 << 40, None, None)
+        assert rc == 1 and b"R2" in lib.gdn_last_error()
+        assert lib.gdn_state_attach_r2(h, None, 0, None, 0) == 0          # detached: R1 checks as usual
+        rc = lib.gdn_prefill(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 4, None, None, None)
+        assert rc == 1 and b"chunk_state_rows" in lib.gdn_last_error()
+    finally:
+        lib.gdn_state_free(h)

@@ -163,3 +163,80 @@ def test_chunked_rejects_unsupported_policies():
     with pytest.raises(cpr.GdnError) as e:
         cpr.gdn_prefill_chunked(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
     assert e.value.code == cpr.GDN_EUNSUPPORTED
+
+
+def _prompt_plus_generated(prompts: gi.GdnInputs, steps, order):
+    """Each sequence's prompt followed by its generated tokens; steps[s] holds the token of slot
+    order[s][j] in row j."""
+    n, T = prompts.num_seqs, len(steps)
+    L = prompts.lengths
+    cu = gi.cu_from_lengths(L + T)
+    parts = {}
+    for name in ("q", "k", "v", "a", "b"):
+        p = getattr(prompts, name)
+        out = torch.empty((int(cu[-1]),) + tuple(p.shape[1:]), dtype=p.dtype, device=p.device)
+        for i in range(n):
+            o0, p0 = int(cu[i]), int(prompts.cu_seqlens[i])
+            out[o0:o0 + L[i]] = p[p0:p0 + L[i]]
+        for s, st in enumerate(steps):
+            rows = getattr(st, name)
+            for j, i in enumerate(order[s]):
+                out[int(cu[i]) + L[i] + s] = rows[j]
+        parts[name] = out
+    return gi.GdnInputs("prompt+generated", prompts.h_k, prompts.h_v, prompts.dk, prompts.dv, prompts.chunk,
+                        prompts.io, cu, *(parts[nm] for nm in ("q", "k", "v", "a", "b")))
+
+
+@pytest.mark.parametrize("dim,chunk", [(32, 16), (128, 64)])
+def test_r2_decode_equals_one_chunked_r2_prefill(dim, chunk):
+    """R2 inside gdn_decode_step: prompts prefilled with gdn_prefill_chunked(R2) into a pool with R2
+    attached, then decode steps that cross several chunk starts (slots listed in a different order
+    every step): every decode output and the final states equal, bit for bit, one chunked R2
+    prefill over prompt and generated tokens; the boundary record holds R2's last chunk-start state.
+    The resynchronisation changes values (an R1 decode of the same tokens differs), and the
+    outputs stay within the bf16 tolerance of the oracle."""
+    cpr = lib()
+    lens = [chunk, 1, 100, 2 * chunk, 37, 3 * chunk + 5]
+    T = 2 * chunk + 11
+    prompts = gi.make_inputs(41, lens, h_k=2, h_v=4, dk=dim, dv=dim, chunk=chunk, io="bf16", device="cuda")
+    steps = [gi.make_inputs(41, [1] * len(lens), h_k=2, h_v=4, dk=dim, dv=dim, chunk=chunk, io="bf16",
+                            sub=300 + s, device="cuda") for s in range(T)]
+    rng = np.random.default_rng(41)
+    order = [rng.permutation(len(lens)).tolist() for _ in range(T)]
+    P = policy_of(prompts)
+    say(f"R2 decode dim={dim} C={chunk}: prompts {lens}, {T} steps")
+    pool = cpr.StatePool(P, len(lens), boundary=True)
+    pool.attach_r2()
+    cpr.gdn_prefill_chunked(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b,
+                            outputs=cpr.GDN_CHUNKED_R2)
+    r1 = cpr.StatePool(P, len(lens), boundary=True)
+    cpr.gdn_prefill_chunked(r1, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b,
+                            outputs=cpr.GDN_CHUNKED_R2)
+    outs = torch.empty((len(lens), T, P.h_v, P.dv), dtype=torch.bfloat16, device="cuda")
+    outs_r1 = torch.empty_like(outs)
+    for s, st in enumerate(steps):
+        ids = torch.tensor(order[s], dtype=torch.int32, device="cuda")
+        o = cpr.gdn_decode_step(pool, st.q, st.k, st.v, st.a, st.b, slot_ids=ids)
+        o1 = cpr.gdn_decode_step(r1, st.q, st.k, st.v, st.a, st.b, slot_ids=ids)
+        outs[ids.long(), s] = o
+        outs_r1[ids.long(), s] = o1
+    torch.cuda.synchronize()
+    assert pool.pos.tolist() == [L + T for L in lens]
+    say(f"R2 decode dim={dim} C={chunk}: one chunked R2 prefill over prompt and generated tokens")
+    full = _prompt_plus_generated(prompts, steps, order)
+    ref = cpr.StatePool(P, len(lens))
+    o_full, _ = cpr.gdn_prefill_chunked(ref, full.cu_seqlens, full.q, full.k, full.v, full.a, full.b,
+                                        outputs=cpr.GDN_CHUNKED_R2)
+    torch.cuda.synchronize()
+    for i in range(len(lens)):
+        t1 = int(full.cu_seqlens[i + 1])
+        assert sha(outs[i]) == sha(o_full[t1 - T:t1]), f"slot {i}"
+    assert sha(pool.state) == sha(ref.state)
+    bpos = pool.boundary_pos.tolist()
+    assert bpos == [(L + T - 1) // chunk * chunk for L in lens]
+    assert sha(outs_r1) != sha(outs)                    # R1's per-token chunk starts differ from R2's
+    for i in (0, 5):
+        for h in (0, 3):
+            ref_o, ref_S, _ = oracle_seq_head(full, i, h)
+            assert normwise(outs[i, :, h].float().cpu().double().numpy(), ref_o[-T:]) <= TOL
+            assert normwise(gpu_state_math(pool, i, h), ref_S) <= TOL
