@@ -568,6 +568,8 @@ def main():
         rep_ms = avg([(b[1], b[2]) for _, b in tev])
         grad_ms = avg([(b[2], b[3]) for _, b in tev])
         fa, _, fg = backward_flops([int(l) for l in xt.lengths], P.h_v, P.dk, P.dv, P.chunk)
+        # the per-token gradient kernel reads dc, w (fp32) and v (bf16) and writes dv (fp32)
+        tok_bytes = Nt * P.h_v * P.dv * (4 + 4 + 2 + 4)
         trainer = {
             "workload": f"trainer forward+backward, {Nt} tokens packed varlen {xt.lengths.tolist()} (H_k=16, "
                         "H_v=32, dk=dv=128, chunk=64, bf16 io); the forward keeps its chunk states and every "
@@ -576,8 +578,11 @@ def main():
             "backward_ms": round(adj_ms + rep_ms + grad_ms, 4),
             "kernels": {"adjoint": {"avg_ms": round(adj_ms, 4), "tflops": round(fa / (adj_ms * 1e-3) / 1e12, 3),
                                     "bound": "alu", "peak_unpacked": FP32_UNPACKED_PEAK_TFLOPS},
-                        "replay": {"avg_ms": round(rep_ms, 4),
-                                   "note": "not launched: the trainer forward kept every token's c and w"},
+                        "token_grads": {"avg_ms": round(rep_ms, 4), "bound": "hbm",
+                                        "bytes": int(tok_bytes), "gbs": round(tok_bytes / (rep_ms * 1e-3) / 1e9, 1),
+                                        "note": "dv = b dc, db = dc . w and v . dv per token-head (the replay "
+                                                "would run here too, but the trainer forward kept every token's "
+                                                "c and w)"},
                         "grad_chunk": {"avg_ms": round(grad_ms, 4), "tflops": round(fg / (grad_ms * 1e-3) / 1e12, 3),
                                        "bound": "mfma", "peak": FP32_MFMA_PEAK_TFLOPS,
                                        "frac": round(fg / (grad_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)}},

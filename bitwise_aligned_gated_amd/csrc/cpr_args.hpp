@@ -80,6 +80,8 @@ struct BackwardArgs {
   float* dc;                  // workspace [N][H_v][dv]: (G_t + q_t dO_t^T)^T k_t
   float* cc;                  // workspace [N][H_v][dv]: c_t of the forward
   float* ww;                  // workspace [N][H_v][dv]: w_t of the forward
+  double* hpart;              // workspace [adj_rows][H_v][partials]: <G, S> at each chunk start, in parts
+  float* xv;                  // workspace [N][H_v]: v_t . dv_t
   float* dq;                  // [N][H_k][dk]
   float* dk;                  // [N][H_k][dk]
   float* dv;                  // [N][H_v][dv]

@@ -27,6 +27,9 @@
 //     remaining gradients are per token: dv_t = b_t dc_t, db_t = dc_t . w_t, and
 //     a_t da_t = <G_{t-1}, S_{t-1}> =: h_{t-1}, where h_0 = <G at the chunk start, S_0> and
 //     h_t = h_{t-1} - q_t . dq_t + v_t . (b_t dc_t) (the per-value-head dq), accumulated in fp64.
+//     h_0 is formed by the adjoint pass, which holds G at the chunk start anyway: each wave adds its
+//     lanes' part of <G, S_0> (S_0 prefetched from the stash a chunk ahead) and stores it, and the
+//     chunk-gradient pass adds the parts in a fixed order.
 //     dq and dk of a key head add its value heads' totals in head order inside the workgroup.
 // Every sum has a fixed order, so the gradients are bitwise reproducible for any batch
 // composition or packing.
@@ -46,8 +49,25 @@ struct ColCfg {
   static constexpr int THREADS = WG_COLS * G;
   static constexpr int NCG = DV / WG_COLS;                     // column groups per value head
   static constexpr int TT = 16;                                // tokens per staged tile
+  static constexpr int WAVES = (THREADS + 63) / 64;
+  static constexpr int PARTS = NCG * WAVES;                    // parts of <G, S_0> per chunk and head
   static_assert(DV % WG_COLS == 0 && WG_COLS % 8 == 0, "shape");
 };
+
+template <int D>
+__host__ __device__ constexpr int adjoint_parts_of() {
+  return ColCfg<D, D>::PARTS;
+}
+
+int adjoint_parts(int d) {
+  switch (d) {
+    case 16: return ColCfg<16, 16>::PARTS;
+    case 32: return ColCfg<32, 32>::PARTS;
+    case 64: return ColCfg<64, 64>::PARTS;
+    case 128: return ColCfg<128, 128>::PARTS;
+    default: return 0;
+  }
+}
 
 template <int DK, int DV>
 struct alignas(16) ColLds {
@@ -236,6 +256,10 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
     adj_fetch<DK, DV, IO>(A, Rg, m.tok0 + t0, m.len - t0, kh, h, col0);
     adj_commit<DK, DV, IO>(Rg, L);
   }
+  // the stash row of the chunk start the walk reaches next (the last chunk's first), a chunk ahead
+  const int64_t srow0 = brow0 - i;                           // chunk c of sequence i: stash row srow0 + c
+  float sb[R];
+  if (m.len > 0) load_f32x8(A.chunk_states + ((srow0 + (m.len - 1) / C) * A.h_v + h) * plane + off, sb);
   __syncthreads();
   for (int t1 = m.len; t1 > 0; t1 -= Cfg::TT) {
     const int t0 = t1 - Cfg::TT > 0 ? t1 - Cfg::TT : 0;
@@ -268,7 +292,19 @@ __global__ void __launch_bounds__((ColCfg<DK, DV>::THREADS)) adjoint_kernel(Back
       pdc = dc;
       ptt = tt;
       if (rem == 0) {                                        // G is now dL/dS at a chunk boundary
-        if (brow < A.adj_rows) store_f32x8(A.adjoint + (brow * A.h_v + h) * plane + off, Gs);
+        if (brow < A.adj_rows) {
+          store_f32x8(A.adjoint + (brow * A.h_v + h) * plane + off, Gs);
+          // this wave's part of <G, S> at the chunk start: rows in order, then a lane butterfly
+          double hp = 0.0;
+#pragma unroll
+          for (int r = 0; r < R; ++r) hp = __builtin_fma(static_cast<double>(Gs[r]), static_cast<double>(sb[r]), hp);
+#pragma unroll
+          for (int o = (Cfg::THREADS < 64 ? Cfg::THREADS : 64) / 2; o >= 1; o >>= 1) hp += __shfl_xor(hp, o, 64);
+          if ((tid & 63) == 0)
+            A.hpart[(brow * A.h_v + h) * Cfg::PARTS + cg * Cfg::WAVES + (tid >> 6)] = hp;
+          if (brow > brow0)                                  // the next chunk start's row, a chunk ahead
+            load_f32x8(A.chunk_states + ((brow - 1 - i) * A.h_v + h) * plane + off, sb);
+        }
         rem = C;
         --brow;
       }
@@ -400,8 +436,6 @@ struct alignas(16) MLds {
   double lgd[M::L + 1];             // sum of log a over the chunk's tokens before token t
   float2 ab[M::L];
   float xq[M::L];                   // q_t . dq_t of the current value head
-  float xv[M::L];                   // v_t . dW_t
-  double red[8];
 };
 
 template <int IO>
@@ -415,18 +449,41 @@ __device__ __forceinline__ float4 load4(const void* base, int64_t elem) {
   }
 }
 
-__device__ __forceinline__ float comp(const float4& v, int e) {
-  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+// Four consecutive io-typed values kept as raw bits until used, and their exact widening.
+template <int IO>
+struct Raw4;
+template <>
+struct Raw4<IO_F32> {
+  float4 x;
+};
+template <>
+struct Raw4<IO_BF16> {
+  uint2 x;
+};
+
+template <int IO>
+__device__ __forceinline__ Raw4<IO> load_raw4(const void* base, int64_t elem) {
+  Raw4<IO> r;
+  if constexpr (IO == IO_F32)
+    r.x = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+  else
+    r.x = *reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(base) + elem);
+  return r;
 }
 
-// Sum of one double per thread over a 256-thread block in a fixed order; every thread gets it.
-__device__ __forceinline__ double block_sum_f64(double x, double* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+template <int IO>
+__device__ __forceinline__ float4 widen4(const Raw4<IO>& r) {
+  if constexpr (IO == IO_F32) {
+    return r.x;
+  } else {
+    const uint2 u = r.x;
+    return make_float4(__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xFFFF0000u),
+                       __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xFFFF0000u));
+  }
+}
+
+__device__ __forceinline__ float comp(const float4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
 // Stage rows [j0, j0 + HR) of a D x D fp32 matrix in [dv][dk] layout into S.u.p.mat (row r at
@@ -474,6 +531,59 @@ __device__ __forceinline__ void stage_kq(MLds<D>& S, const void* src, int64_t to
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     if (t < n) x = load4<IO>(src, ((tok + t) * h_k + kh) * D + 4 * c4);
     *reinterpret_cast<float4*>(&S.u.m.kq[t * M::SB + 4 * c4]) = x;
+  }
+}
+
+// The per-token gradients that need no chunk form, over every (token, value head): dv_t = b_t dc_t,
+// db_t = dc_t . w_t, and v_t . dv_t for the chunk pass's h recurrence.  D/8 lanes per token-head,
+// eight columns each, summed in column order per lane and then by the DPP tree over the lanes; each
+// lane group takes two token-heads, their loads issued together.
+template <int D, int IO>
+__global__ void __launch_bounds__(256) token_grads_kernel(BackwardArgs A) {
+  constexpr int LPT = D / 8;                                    // lanes per token-head
+  constexpr int PER_BLOCK = 2 * 256 / LPT;                      // token-heads per workgroup
+  const int64_t n = A.total_tokens * A.h_v;
+  const int c8 = threadIdx.x % LPT;
+  int64_t th[2];
+  float4 dc[2][2], w[2][2], v[2][2];
+  float bt[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    th[u] = static_cast<int64_t>(blockIdx.x) * PER_BLOCK + u * (256 / LPT) + threadIdx.x / LPT;
+    const int64_t base = (th[u] < n ? th[u] : 0) * D + 8 * c8;   // [t][h][D] with th = t H_v + h
+    dc[u][0] = reinterpret_cast<const float4*>(A.dc + base)[0];
+    dc[u][1] = reinterpret_cast<const float4*>(A.dc + base)[1];
+    w[u][0] = reinterpret_cast<const float4*>(A.ww + base)[0];
+    w[u][1] = reinterpret_cast<const float4*>(A.ww + base)[1];
+    v[u][0] = load4<IO>(A.v, base);
+    v[u][1] = load4<IO>(A.v, base + 4);
+    bt[u] = A.b[th[u] < n ? th[u] : 0];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const float x[8] = {dc[u][0].x, dc[u][0].y, dc[u][0].z, dc[u][0].w, dc[u][1].x, dc[u][1].y, dc[u][1].z, dc[u][1].w};
+    const float y[8] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w, w[u][1].x, w[u][1].y, w[u][1].z, w[u][1].w};
+    const float z[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+    float dv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dv[e] = bt[u] * x[e];
+    float sv = z[0] * dv[0], sd = x[0] * y[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      sv = __builtin_fmaf(z[e], dv[e], sv);
+      sd = __builtin_fmaf(x[e], y[e], sd);
+    }
+    sv = lane_tree<LPT>(sv);
+    sd = lane_tree<LPT>(sd);
+    if (th[u] < n) {
+      float* dst = A.dv + th[u] * D + 8 * c8;
+      reinterpret_cast<float4*>(dst)[0] = make_float4(dv[0], dv[1], dv[2], dv[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(dv[4], dv[5], dv[6], dv[7]);
+      if (c8 == 0) {
+        A.db[th[u]] = sd;
+        A.xv[th[u]] = sv;
+      }
+    }
   }
 }
 
@@ -526,7 +636,6 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
     const float fc = rv ? __expf(static_cast<float>(S.lgd[L] - lr1)) : 0.f;     // Gam_L / Gam_row
     const float su = -abr.x * abr.y;                                              // dU = su * dc
     const float* s0 = A.chunk_states + (w * A.h_v + h) * plane;
-    const float* g0 = A.adjoint + (gstart * A.h_v + h) * plane;
     const float* ge = A.adjoint + ((gstart + 1) * A.h_v + h) * plane;
 
     // dq += Gam_t dO S0^T; dk += Gam_{t-1} dU S0^T; A1 = dO C^T; A2 = dU C^T; h_0 = <G_start, S0>
@@ -535,29 +644,28 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
     for (int n = 0; n < NT; ++n) acc_dq[n] = acc_dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < 4; ++n) a1[n] = a2[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    double hp = 0.0;
 #pragma unroll 1
     for (int part = 0; part < NH; ++part) {
       const int j0 = part * HR;
       __syncthreads();
       stage_part<D, DS>(S, s0, A.cc, tok, L, A.h_v, h, j0);
       __syncthreads();
-      for (int e = tid; e < HR * D / 4; e += 256) {
-        const int r = e / (D / 4), c4 = e % (D / 4);
-        const float4 gv = reinterpret_cast<const float4*>(g0 + static_cast<int64_t>(j0 + r) * D)[c4];
-        const float4 sv = *reinterpret_cast<const float4*>(&S.u.p.mat[mrow<D, DS>(r) + 4 * c4]);
-        hp += static_cast<double>(gv.x) * sv.x + static_cast<double>(gv.y) * sv.y +
-              static_cast<double>(gv.z) * sv.z + static_cast<double>(gv.w) * sv.w;
-      }
+      // this lane's dO and dc elements of panel p are fetched while panel p - 1 runs: raw bits, a
+      // row past the chunk reading row 0 (its values are then replaced by zeros at use)
+      const int64_t arow = ((tok + (rv ? row : 0)) * A.h_v + h) * D + j0 + 4 * lgp;
+      Raw4<IO> o_next = load_raw4<IO>(A.d_o, arow);
+      float4 c_next = *reinterpret_cast<const float4*>(A.dc + arow);
 #pragma unroll 1
       for (int p = 0; p < HR / 16; ++p) {
         const int kl = 16 * p + 4 * lgp;                     // k within the part
         const int mk = mrow<D, DS>(kl);
-        float4 o4 = make_float4(0.f, 0.f, 0.f, 0.f), c4 = o4;
-        if (rv) {
-          o4 = load4<IO>(A.d_o, ((tok + row) * A.h_v + h) * D + j0 + kl);
-          c4 = *reinterpret_cast<const float4*>(A.dc + ((tok + row) * A.h_v + h) * D + j0 + kl);
-        }
+        const Raw4<IO> o_raw = o_next;
+        const float4 c_cur = c_next;
+        const int pn = p + 1 < HR / 16 ? p + 1 : p;          // the last panel fetches itself again
+        o_next = load_raw4<IO>(A.d_o, arow + 16 * pn);
+        c_next = *reinterpret_cast<const float4*>(A.dc + arow + 16 * pn);
+        const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 o4 = rv ? widen4<IO>(o_raw) : zero, c4 = rv ? c_cur : zero;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k = kl + e;
@@ -594,7 +702,6 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
         }
       }
     }
-    const double h0 = block_sum_f64(hp, S.red);
     __syncthreads();                                         // C^T and G_end reads done
     // A1, A2 -> LDS; K rows -> LDS
 #pragma unroll
@@ -676,41 +783,12 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
           }
         }
       }
-      // dv = b dc; v . dv; db = dc . w: four threads per token, D/4 columns each
-      const int t = tid >> 2, part = tid & 3;
-      float sv = 0.f, sd = 0.f;
-      if (t < L) {
-        const int64_t base = ((tok + t) * A.h_v + h) * D;
-        const float bt = S.ab[t].y;
-        for (int j4 = part * (D / 16); j4 < (part + 1) * (D / 16); ++j4) {
-          const float4 dc4 = reinterpret_cast<const float4*>(A.dc + base)[j4];
-          const float4 w4 = reinterpret_cast<const float4*>(A.ww + base)[j4];
-          const float4 v4 = load4<IO>(A.v, base + 4 * j4);
-          const float4 dv4 = make_float4(bt * dc4.x, bt * dc4.y, bt * dc4.z, bt * dc4.w);
-          reinterpret_cast<float4*>(A.dv + base)[j4] = dv4;
-          sv = __builtin_fmaf(v4.x, dv4.x, sv);
-          sv = __builtin_fmaf(v4.y, dv4.y, sv);
-          sv = __builtin_fmaf(v4.z, dv4.z, sv);
-          sv = __builtin_fmaf(v4.w, dv4.w, sv);
-          sd = __builtin_fmaf(dc4.x, w4.x, sd);
-          sd = __builtin_fmaf(dc4.y, w4.y, sd);
-          sd = __builtin_fmaf(dc4.z, w4.z, sd);
-          sd = __builtin_fmaf(dc4.w, w4.w, sd);
-        }
-      }
-      sv = dpp_pair_add<0xB1>(sv);
-      sv = dpp_pair_add<0x4E>(sv);
-      sd = dpp_pair_add<0xB1>(sd);
-      sd = dpp_pair_add<0x4E>(sd);
-      if (part == 0 && t < L) {
-        S.xv[t] = sv;
-        A.db[(tok + t) * A.h_v + h] = sd;
-      }
     }
     __syncthreads();
     // h_{t-1} = h_0 - sum_{s<t} (q_s . dq_s - v_s . dv_s); da_t = h_{t-1} / a_t
     if (tid < LT) {
-      const double x = tid < L ? static_cast<double>(S.xq[tid]) - static_cast<double>(S.xv[tid]) : 0.0;
+      const double x = tid < L ? static_cast<double>(S.xq[tid]) - static_cast<double>(A.xv[(tok + tid) * A.h_v + h])
+                               : 0.0;
       double incl = x;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -719,6 +797,11 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
       }
       double excl = __shfl_up(incl, 1, 64);
       if (lane == 0) excl = 0.0;
+      // h_0 = <G_start, S_0>: the adjoint pass's parts, added in order
+      const double* hpp = A.hpart + (gstart * A.h_v + h) * adjoint_parts_of<D>();
+      double h0 = 0.0;
+#pragma unroll 1
+      for (int p = 0; p < adjoint_parts_of<D>(); ++p) h0 += hpp[p];
       if (tid < L) A.da[(tok + tid) * A.h_v + h] = static_cast<float>((h0 - excl) / static_cast<double>(S.ab[tid].x));
     }
   }
@@ -762,6 +845,13 @@ static hipError_t launch_backward_t(const BackwardArgs& A, hipStream_t stream) {
     const int64_t g2 = xcd_grid(A.rows_cap * A.h_k, ratio * Cfg::NCG);
     if (g2 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((replay_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(Cfg::THREADS), 0, stream, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (A.total_tokens > 0) {
+    const int64_t per_block = 2 * 256 / (DK / 8);
+    const int64_t g = (A.total_tokens * A.h_v + per_block - 1) / per_block;
+    if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((token_grads_kernel<DK, IO>), dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;

@@ -660,10 +660,14 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
   const gdn_policy& P = *policy;
   const int64_t plane = int64_t(P.dk) * P.dv;
   const int32_t chunk = grad_chunk_of(P);   // the gradient passes' chunk
-  const int64_t adj = (backward_rows(total_tokens, num_seqs, chunk) + num_seqs) * P.h_v * plane * 4;
+  const int64_t adj_rows = backward_rows(total_tokens, num_seqs, chunk) + num_seqs;
+  const int64_t adj = adj_rows * P.h_v * plane * 4;
   const int64_t per_token = total_tokens * P.h_v * int64_t(P.dv) * 4;
+  const int64_t parts = adj_rows * P.h_v * cpr::adjoint_parts(P.dk) * 8;
+  const int64_t xv = total_tokens * P.h_v * 4;
   ok();
-  return align256(adj) + 3 * align256(per_token) + rechunk_bytes(P, total_tokens, num_seqs);
+  return align256(adj) + 3 * align256(per_token) + align256(parts) + align256(xv) +
+         rechunk_bytes(P, total_tokens, num_seqs);
 }
 
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -703,12 +707,14 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   if (rows_g * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_backward: too many chunks for one launch");
   const int64_t adj_bytes = align256((rows_g + num_seqs) * P.h_v * plane * 4);
   const int64_t tok_bytes = align256(total_tokens * P.h_v * int64_t(P.dv) * 4);
+  const int64_t part_bytes = align256((rows_g + num_seqs) * P.h_v * cpr::adjoint_parts(P.dk) * 8) +
+                             align256(total_tokens * P.h_v * 4);   // and v_t . dv_t per token-head
   char* ws = static_cast<char*>(workspace);
   const hipStream_t hs = static_cast<hipStream_t>(stream);
   const float* stash = chunk_states;
   if (rebuilds_stash(P) && num_seqs > 0) {
     // the 64-token stash: pass 1 from each sequence's first row of the caller's stash
-    char* xs = ws + adj_bytes + 3 * tok_bytes;
+    char* xs = ws + adj_bytes + 3 * tok_bytes + part_bytes;
     float* fine = reinterpret_cast<float*>(xs);
     int32_t* ids = reinterpret_cast<int32_t*>(xs + align256(rows_g * P.h_v * plane * 4));
     int64_t* pos = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(ids) + align256(int64_t(num_seqs) * 4));
@@ -750,6 +756,9 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   A.dc = reinterpret_cast<float*>(ws + adj_bytes);
   A.cc = reinterpret_cast<float*>(ws + adj_bytes + tok_bytes);
   A.ww = reinterpret_cast<float*>(ws + adj_bytes + 2 * tok_bytes);
+  A.hpart = reinterpret_cast<double*>(ws + adj_bytes + 3 * tok_bytes);
+  A.xv = reinterpret_cast<float*>(ws + adj_bytes + 3 * tok_bytes +
+                                  align256((rows_g + num_seqs) * P.h_v * cpr::adjoint_parts(P.dk) * 8));
   A.have_cw = cw != nullptr;
   if (cw != nullptr) {                       // the trainer forward's c and w: no replay needed
     A.cc = const_cast<float*>(cw);

@@ -26,6 +26,8 @@ bool overlap_fits(int dk, int dv, const PrefillArgs& A);
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream);
+// Parts of <G, S_0> the adjoint pass stores per chunk start and value head (head dim d).
+int adjoint_parts(int d);
 // The position update that ends every prefill, and the CPR output pass (with that update) alone,
 // started from chunk states already stored.
 hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream);

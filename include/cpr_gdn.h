@@ -410,8 +410,10 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
 
 /* Workspace bytes gdn_backward needs for total_tokens tokens in num_seqs sequences (-1 on bad
  * input): dL/dS at every boundary of the gradient chunks (total_tokens / C' + 2 num_seqs states;
- * C' = 64 with fp32 boundaries, min(C, 64) with bf16 boundaries) and three fp32 per-token arrays
- * of N * H_v * d_v (dc, c, w); with fp32 boundaries and C != 64 also a rebuilt 64-token stash
+ * C' = 64 with fp32 boundaries, min(C, 64) with bf16 boundaries), three fp32 per-token arrays
+ * of N * H_v * d_v (dc, c, w), per boundary and value head the parts of <dL/dS, S> (fp64:
+ * 32 at d = 128, 8 at 64, 2 at 32, 1 at 16), and one fp32 v_t . dv_t per token and value head;
+ * with fp32 boundaries and C != 64 also a rebuilt 64-token stash
  * (total_tokens / 64 + num_seqs states), one int32 per sequence and one int64 per row of the
  * forward's stash.  Each part is padded to 256 bytes. */
 int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);

@@ -222,14 +222,18 @@ def test_backward_workspace_bytes():
     # each H_v * dk * dv * 4 bytes; then three per-token arrays (dc, c, w) of N * H_v * dv * 4
     # bytes; each part padded to 256 bytes
     pad = lambda x: -(-x // 256) * 256
+    # then the parts of <dL/dS, S> at every boundary: 32 fp64 per value head at d = 128, 1 at d = 16
     p = cpr.Policy(16, 32, 128, 128, chunk=64)
     adj = (10240 // 64 + 4 + 4) * 32 * 128 * 128 * 4
     tok = 10240 * 32 * 128 * 4
-    assert cpr.gdn_backward_workspace_bytes(p, 10240, 4) == pad(adj) + 3 * pad(tok)
+    parts = (10240 // 64 + 4 + 4) * 32 * 32 * 8
+    xv = 10240 * 32 * 4                                                  # v_t . dv_t per token-head
+    assert cpr.gdn_backward_workspace_bytes(p, 10240, 4) == pad(adj) + 3 * pad(tok) + pad(parts) + pad(xv)
     # bf16 boundaries below 64 tokens: the gradient passes run at the forward's chunk
     p = cpr.Policy(1, 2, 16, 16, chunk=8, io="f32", boundary="bf16")
     adj, tok = (100 // 8 + 3 + 3) * 2 * 16 * 16 * 4, 100 * 2 * 16 * 4
-    assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == pad(adj) + 3 * pad(tok)
+    assert cpr.gdn_backward_workspace_bytes(p, 100, 3) == pad(adj) + 3 * pad(tok) + pad((100 // 8 + 3 + 3) * 2 * 8) + \
+        pad(100 * 2 * 4)
     # fp32 boundaries at any chunk but 64 are differentiated on a rebuilt 64-token stash: the
     # gradient parts are those of chunk 64, then the 64-token stash ((N/64 + B) states), an int32
     # slot id per sequence and an int64 position per row of the forward's (N/C + B)-row stash
@@ -237,8 +241,10 @@ def test_backward_workspace_bytes():
         p = cpr.Policy(2, 4, 32, 32, chunk=C, io="f32")
         plane = 4 * 32 * 32 * 4
         adj, tok = (1000 // 64 + 5 + 5) * plane, 1000 * 4 * 32 * 4
+        parts = (1000 // 64 + 5 + 5) * 4 * 2 * 8                        # 2 parts per value head at d = 32
         extra = pad((1000 // 64 + 5) * plane) + pad(5 * 4) + pad((1000 // C + 5) * 8)
-        assert cpr.gdn_backward_workspace_bytes(p, 1000, 5) == pad(adj) + 3 * pad(tok) + extra, C
+        assert cpr.gdn_backward_workspace_bytes(p, 1000, 5) == pad(adj) + 3 * pad(tok) + pad(parts) + \
+            pad(1000 * 4 * 4) + extra, C
     with pytest.raises(cpr.GdnError):
         cpr.gdn_backward_workspace_bytes(p, -1, 3)
 
