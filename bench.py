@@ -219,8 +219,9 @@ def host_environment():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # 20 warm-up calls: the first ~20 prefill calls of a process run ~12% slower than the steady
-    # state (0.98 ms against 1.10 ms per 5x2048 call at 3 warm-up calls), so fewer would time a ramp
+    # 20 warm-up calls: the first ~20 prefill calls of a process run up to ~30% slower than the steady
+    # state, because the GPU lowers its clocks while idle (here while the first call loads the code
+    # object) and raises them over ~20 ms of load; fewer warm-up calls time part of that ramp
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=128)
@@ -278,10 +279,9 @@ def main():
         cpr.gdn_prefill(pool, cu, x.q, x.k, x.v, x.a, x.b, slot_ids=ids, o=out, chunk_states=cs, c_stash=c_stash,
                         events=events)
 
+    evs = [[hip.event() for _ in range(3)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -527,6 +527,31 @@ def main():
                         "a": np.stack([t.a.cpu().numpy() for t in toks], 1),
                         "b": np.stack([t.b.cpu().numpy() for t in toks], 1),
                         "o": np.stack([u16(o_) for o_ in dec_outs], 1)}
+        # the same workload under the R2 reading: prompts prefilled by the chunk form (GDN_CHUNKED_R2),
+        # decode resynchronising with the chunk form at every chunk start (context; other values)
+        prompts = gi.decode_prompts(device=dev)
+        r2pool = cpr.StatePool(P, nb, device=dev, boundary=True)
+        r2pool.attach_r2()
+        cpr.gdn_prefill_chunked(r2pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b,
+                                outputs=cpr.GDN_CHUNKED_R2)
+        del prompts
+        torch.cuda.synchronize()
+        r2evs = [[hip.event() for _ in range(2)] for _ in range(args.decode_steps)]
+        od2 = torch.empty_like(od)
+        for s in range(args.decode_steps):
+            t = toks[s]
+            cpr.gdn_decode_step(r2pool, t.q, t.k, t.v, t.a, t.b, slot_ids=dids, o=od2, events=r2evs[s])
+        torch.cuda.synchronize()
+        r2_us = sorted(hip.ms(e[0], e[1]) * 1e3 for e in r2evs)
+        starts = sum(1 for s in range(args.decode_steps) for L in dec_lens if (L + s) % P.chunk == 0)
+        decode["r2_reading"] = {
+            "us_per_step_median": round(statistics.median(r2_us), 2),
+            "us_per_step_max": round(r2_us[-1], 2),
+            "resyncs": starts,
+            "note": "prompts by gdn_prefill_chunked(R2); each step runs the chunk form over the token ring of "
+                    "the slots at a chunk start (gated), then the pinned step; ring and workspace "
+                    f"{(r2pool.r2_ring.numel() + r2pool.r2_workspace.numel()) / 2**20:.0f} MiB"}
+        del r2pool, od2
 
     # ---------------------------------------------------------------- trainer forward + backward
     trainer = None
