@@ -207,6 +207,14 @@ def host_environment():
     except ImportError:
         pass
     try:
+        # under a profiler that loads its tool library into this process, the GPU is initialised
+        # before main() runs, and a child started from here may not replace itself by exec
+        with open("/proc/self/maps") as fh:
+            if "rocprofiler" in fh.read():
+                return env
+    except OSError:
+        pass
+    try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         if r.returncode == 0:
             card = next(iter(json.loads(r.stdout).values()), {})
