@@ -182,6 +182,14 @@ def backward_flops(lengths, h_v, dk, dv, chunk):
     return n * h_v * 7 * dk * dv, n * h_v * 5 * dk * dv, mfma
 
 
+def normwise_t(got, ref) -> float:
+    """||got - ref|| / ||ref|| of two device tensors, in fp64."""
+    import torch
+    g, r = got.double(), ref.double()
+    den = float(torch.linalg.vector_norm(r))
+    return float(torch.linalg.vector_norm(g - r)) / den if den > 0 else float(torch.linalg.vector_norm(g))
+
+
 def decode_bytes(batch, h_k, h_v, dk, dv, io_bytes=2):
     """Algorithmic HBM bytes of one decode step: the state read and written once, the token's
     q, k (per key head), v, a, b read and o written."""
@@ -622,6 +630,44 @@ def main():
             "workspace_bytes": int(ws.numel()),
             "h100_fwd_bwd_ms": 7.386,
         }
+
+        # the native trainer: chunkwise forward on matrix cores and the chunk form of its backward
+        npool = cpr.StatePool(P, Bt, device=dev)
+        ncs = torch.empty_like(tcs)
+        no = torch.empty_like(to)
+        nstash = torch.empty(cpr.gdn_trainer_forward_chunked_stash_bytes(P, Nt, Bt), dtype=torch.uint8, device=dev)
+        nws = torch.empty(cpr.gdn_backward_chunked_workspace_bytes(P, Nt, Bt), dtype=torch.uint8, device=dev)
+        ngrads = {k: torch.empty_like(v) for k, v in grads.items()}
+
+        def native_step(fe=None, be=None):
+            cpr.gdn_trainer_forward_chunked(npool, tcu, xt.q, xt.k, xt.v, xt.a, xt.b, slot_ids=tids, o=no,
+                                            chunk_states=ncs, stash=nstash, events=fe)
+            cpr.gdn_backward_chunked(P, tcu, xt.q, xt.k, xt.v, xt.a, xt.b, ncs, nstash, ct["d_o"],
+                                     d_state=ct["d_state"], workspace=nws, out=ngrads, events=be)
+
+        for _ in range(args.warmup):
+            native_step()
+        nev = [([hip.event() for _ in range(4)], [hip.event() for _ in range(4)]) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            native_step(*nev[i])
+        torch.cuda.synchronize()
+        n_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        nf_ms = avg([(f[0], f[3]) for f, _ in nev])
+        nb = [avg([(b[j], b[j + 1]) for _, b in nev]) for j in range(3)]
+        trainer["native_chunked"] = {
+            "ms_per_step": round(n_ms, 4), "forward_ms": round(nf_ms, 4), "backward_ms": round(sum(nb), 4),
+            "backward_stages_ms": {"chunk_form_adjoint": round(nb[0], 4), "token_grads": round(nb[1], 4),
+                                   "grad_chunk": round(nb[2], 4)},
+            "normwise_vs_cpr": {k: round(float(normwise_t(ngrads[k], grads[k])), 8) for k in grads},
+            "cpr_over_native": round(t_ms / n_ms, 3),
+            "h100_fwd_bwd_ms": 5.177,
+            "note": "gdn_trainer_forward_chunked (prep, state, output on bf16 matrix cores, keeping T^T, W^T and "
+                    "c) and gdn_backward_chunked (w and the intra-chunk part of dC, the chunk chain of the "
+                    "adjoint last chunk first, then the same per-token and chunk-gradient kernels as CPR)",
+        }
+        del npool, ncs, no, nstash, nws, ngrads
         del tpool, tcs, tcw, to, ws, grads, xt, ct
 
     # ---------------------------------------------------------------- CPU baseline (oracle)

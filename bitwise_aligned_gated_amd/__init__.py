@@ -22,6 +22,8 @@ __all__ = [
     "gdn_backward", "gdn_backward_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_chunked_workspace_bytes", "GDN_CHUNKED_NATIVE", "GDN_CHUNKED_R2",
     "gdn_trainer_forward", "gdn_prefill_static", "GDN_STATIC_SCRATCH_BYTES",
+    "gdn_trainer_forward_chunked", "gdn_trainer_forward_chunked_stash_bytes", "gdn_backward_chunked",
+    "gdn_backward_chunked_workspace_bytes",
     "EXPORTS",
 ]
 
@@ -89,6 +91,12 @@ _SIGS = {
     "gdn_r2_ring_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i32]),
     "gdn_r2_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i32]),
     "gdn_state_attach_r2": (ctypes.c_int, [_P, _P, _sz, _P, _sz]),
+    "gdn_trainer_forward_chunked_stash_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i64, _i32]),
+    "gdn_trainer_forward_chunked": (ctypes.c_int, [_P, _P, _i32, _i64, _P, _i32, _P, _P, _P, _P, _P, _P, _P, _i64,
+                                                   _P, _sz, _P, _P]),
+    "gdn_backward_chunked_workspace_bytes": (_i64, [ctypes.POINTER(_CPolicy), _i64, _i32]),
+    "gdn_backward_chunked": (ctypes.c_int, [ctypes.POINTER(_CPolicy), _P, _i32, _i64, _P, _P, _P, _P, _P, _P, _i64,
+                                            _P, _sz, _P, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P, _P]),
 }
 EXPORTS = tuple(_SIGS)
 for _name, (_res, _args) in _SIGS.items():
@@ -500,14 +508,8 @@ def gdn_backward_workspace_bytes(policy: Policy, total_tokens: int, num_seqs: in
     return int(r)
 
 
-@_on_stream
-def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state=None,
-                 want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None, cw=None):
-    """Gradients of a trainer forward (C gdn_backward) from its inputs and chunk-state stash.
-
-    Returns a dict of fp32 device tensors dq, dk [N, H_k, d_k], dv [N, H_v, d_v], da, db [N, H_v]
-    and, when want_d_state0, d_state0 [num_seqs, H_v, d_v, d_k].  `out` may supply any of them."""
-    P = policy
+def _backward_args(P, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state, want_d_state0, out):
+    """Checks of a backward call's inputs; the gradient outputs (allocated where `out` has none)."""
     dev = q.device
     N = q.shape[0]
     if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device.type == "cuda":
@@ -525,8 +527,6 @@ def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d
     _dev(b, "b", torch.float32, (N, P.h_v), dev, align=4)
     _dev(d_o, "d_o", io, (N, P.h_v, P.dv), dev)
     _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
-    if cw is not None:
-        _dev(cw, "cw", torch.float32, (2, N, P.h_v, P.dv), dev)
     if d_state is not None:
         _dev(d_state, "d_state", torch.float32, (B, P.h_v, P.dv, P.dk), dev)
     out = dict(out or {})
@@ -538,6 +538,21 @@ def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d
         if out.get(name) is None:
             out[name] = torch.empty(shape, dtype=torch.float32, device=dev)
         _dev(out[name], name, torch.float32, shape, dev)
+    return dev, N, B, cu_d, out
+
+
+@_on_stream
+def gdn_backward(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state=None,
+                 want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None, cw=None):
+    """Gradients of a trainer forward (C gdn_backward) from its inputs and chunk-state stash.
+
+    Returns a dict of fp32 device tensors dq, dk [N, H_k, d_k], dv [N, H_v, d_v], da, db [N, H_v]
+    and, when want_d_state0, d_state0 [num_seqs, H_v, d_v, d_k].  `out` may supply any of them."""
+    P = policy
+    dev, N, B, cu_d, out = _backward_args(P, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state, want_d_state0,
+                                          out)
+    if cw is not None:
+        _dev(cw, "cw", torch.float32, (2, N, P.h_v, P.dv), dev)
     need = gdn_backward_workspace_bytes(P, N, B)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
@@ -582,3 +597,67 @@ def gdn_prefill_chunked(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=Non
                                     workspace.data_ptr(), workspace.numel(), _stream_ptr(stream),
                                     _events(events, 4)))
     return o, chunk_states
+
+
+def gdn_trainer_forward_chunked_stash_bytes(policy: Policy, total_tokens: int, num_seqs: int) -> int:
+    r = _lib.gdn_trainer_forward_chunked_stash_bytes(ctypes.byref(policy.c()), total_tokens, num_seqs)
+    if r < 0:
+        _check(GDN_EUNSUPPORTED if policy.dk not in (32, 64, 128) else GDN_EINVAL)
+    return int(r)
+
+
+@_on_stream
+def gdn_trainer_forward_chunked(pool: StatePool, cu_seqlens, q, k, v, a, b, slot_ids=None, from_state: bool = False,
+                                o=None, chunk_states=None, stash=None, stream=None, events=None):
+    """Chunkwise trainer forward on matrix cores (C gdn_trainer_forward_chunked): the native
+    chunked prefill that also keeps the stash gdn_backward_chunked reads.  Returns
+    (o, chunk_states, stash)."""
+    P, dev = pool.policy, pool.device
+    N, B, cu_d, ids, o = _prefill_args(pool, cu_seqlens, q, k, v, a, b, slot_ids, o)
+    bound = gdn_chunk_rows_bound(N, B, P.chunk)
+    if chunk_states is None:
+        chunk_states = torch.empty((max(bound, 1), P.h_v, P.dv, P.dk), dtype=torch.float32, device=dev)
+    _dev(chunk_states, "chunk_states", torch.float32, (chunk_states.shape[0], P.h_v, P.dv, P.dk), dev)
+    need = gdn_trainer_forward_chunked_stash_bytes(P, N, B)
+    if stash is None:
+        stash = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev(stash, "stash", torch.uint8, (stash.numel(),), dev)
+    _check(_lib.gdn_trainer_forward_chunked(pool.handle, cu_d.data_ptr(), B, N, ids.data_ptr(), int(bool(from_state)),
+                                            q.data_ptr(), k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(),
+                                            o.data_ptr(), chunk_states.data_ptr(), chunk_states.shape[0],
+                                            stash.data_ptr(), stash.numel(), _stream_ptr(stream),
+                                            _events(events, 4)))
+    return o, chunk_states, stash
+
+
+def gdn_backward_chunked_workspace_bytes(policy: Policy, total_tokens: int, num_seqs: int) -> int:
+    r = _lib.gdn_backward_chunked_workspace_bytes(ctypes.byref(policy.c()), total_tokens, num_seqs)
+    if r < 0:
+        _check(GDN_EUNSUPPORTED if policy.dk not in (32, 64, 128) else GDN_EINVAL)
+    return int(r)
+
+
+@_on_stream
+def gdn_backward_chunked(policy: Policy, cu_seqlens, q, k, v, a, b, chunk_states, stash, d_o, d_state=None,
+                         want_d_state0: bool = False, workspace=None, out=None, stream=None, events=None):
+    """Gradients of a chunkwise trainer forward (C gdn_backward_chunked) from its inputs, chunk
+    states and stash.  Returns the dict gdn_backward returns."""
+    P = policy
+    dev, N, B, cu_d, out = _backward_args(P, cu_seqlens, q, k, v, a, b, chunk_states, d_o, d_state, want_d_state0,
+                                          out)
+    _dev(stash, "stash", torch.uint8, (stash.numel(),), dev)
+    need = gdn_backward_chunked_workspace_bytes(P, N, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+    d0 = out.get("d_state0")
+    _check(_lib.gdn_backward_chunked(ctypes.byref(P.c()), cu_d.data_ptr(), B, N, q.data_ptr(), k.data_ptr(),
+                                     v.data_ptr(), a.data_ptr(), b.data_ptr(), chunk_states.data_ptr(),
+                                     chunk_states.shape[0], stash.data_ptr(), stash.numel(), d_o.data_ptr(),
+                                     None if d_state is None else d_state.data_ptr(),
+                                     out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(),
+                                     out["da"].data_ptr(), out["db"].data_ptr(),
+                                     None if d0 is None else d0.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream_ptr(stream),
+                                     _events(events, 4)))
+    return out

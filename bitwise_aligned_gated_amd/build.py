@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "libcpr_gdn.so")
 BUILD_DIR = os.environ.get("CPR_BUILD_DIR", os.path.join(ROOT, "_build"))
 
 SOURCES = ["cpr_prefill.hip", "cpr_overlap.hip", "cpr_decode.hip", "cpr_backward.hip", "cpr_chunked.hip",
+           "cpr_chunked_bwd.hip",
            "cpr_static.hip", "cpr_host.cpp"]
 EXTRA_FLAGS = os.environ.get("CPR_EXTRA_HIPCC_FLAGS", "").split()
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -40,6 +40,8 @@ struct PrefillArgs {
   void* r2_ring;              // chunked R2 prefill, nullable: the pool's decode ring to fill
   float* r2_boundary;         //   and its boundary record (state and position) to set
   int64_t* r2_boundary_pos;
+  float* chunk_bwd;           // chunk-form prep, nullable: T^T and W^T per (chunk row, value head) for the
+                              //   chunk-form backward (the chunk-form state pass then also writes c_stash)
 };
 
 struct DecodeArgs {
@@ -96,7 +98,10 @@ struct BackwardArgs {
   int32_t h_v;
   int32_t chunk;
   int32_t have_cw;            // 1: cc and ww came from the trainer forward (no replay needed)
+  int32_t hparts;             // parts of <G, S> per chunk start and value head in hpart
   void* const* events;        // nullable: 4 hipEvent_t around the three kernels
+  const float* fws;           // chunk-form backward: the forward's per-chunk workspace (W, U, C^T, log gates)
+  const float* fbw;           //   and what its prep kept for the backward (T^T, W^T)
 };
 
 }  // namespace cpr

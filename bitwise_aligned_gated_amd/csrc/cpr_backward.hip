@@ -797,11 +797,11 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
       }
       double excl = __shfl_up(incl, 1, 64);
       if (lane == 0) excl = 0.0;
-      // h_0 = <G_start, S_0>: the adjoint pass's parts, added in order
-      const double* hpp = A.hpart + (gstart * A.h_v + h) * adjoint_parts_of<D>();
+      // h_0 = <G_start, S_0>: the parts the adjoint pass stored, added in order
+      const double* hpp = A.hpart + (gstart * A.h_v + h) * A.hparts;
       double h0 = 0.0;
 #pragma unroll 1
-      for (int p = 0; p < adjoint_parts_of<D>(); ++p) h0 += hpp[p];
+      for (int p = 0; p < A.hparts; ++p) h0 += hpp[p];
       if (tid < L) A.da[(tok + tid) * A.h_v + h] = static_cast<float>((h0 - excl) / static_cast<double>(S.ab[tid].x));
     }
   }
@@ -827,6 +827,39 @@ hipError_t launch_rechunk_setup(const BackwardArgs& A, int32_t* slot_ids, int64_
   return hipGetLastError();
 }
 
+// The per-token gradients (after which event 2 is recorded) and the chunk gradients (event 3),
+// from dc, G at every chunk boundary, the <G, S> parts, c and w.
+template <int D, int IO>
+static hipError_t launch_gradient_passes_t(const BackwardArgs& A, hipStream_t stream) {
+  hipError_t e;
+  if (A.total_tokens > 0) {
+    const int64_t per_block = 2 * 256 / (D / 8);
+    const int64_t g = (A.total_tokens * A.h_v + per_block - 1) / per_block;
+    if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((token_grads_kernel<D, IO>), dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
+  if (A.num_seqs > 0 && A.rows_cap > 0) {
+    const int64_t g3 = A.rows_cap * A.h_k;
+    if (g3 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((grad_chunk_kernel<D, IO>), dim3(static_cast<unsigned>(g3)), dim3(256), 0, stream, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return record_event(A.events, 3, stream);
+}
+
+hipError_t launch_gradient_passes(int d, int io, const BackwardArgs& A, hipStream_t stream) {
+#define CPR_CASE(D, IOV) \
+  if (d == D && io == IOV) return launch_gradient_passes_t<D, IOV>(A, stream);
+  CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
+  CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
+  CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)
+  CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
+#undef CPR_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int DK, int DV, int IO>
 static hipError_t launch_backward_t(const BackwardArgs& A, hipStream_t stream) {
   using Cfg = ColCfg<DK, DV>;
@@ -847,21 +880,7 @@ static hipError_t launch_backward_t(const BackwardArgs& A, hipStream_t stream) {
     hipLaunchKernelGGL((replay_kernel<DK, DV, IO>), dim3(static_cast<unsigned>(g2)), dim3(Cfg::THREADS), 0, stream, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (A.total_tokens > 0) {
-    const int64_t per_block = 2 * 256 / (DK / 8);
-    const int64_t g = (A.total_tokens * A.h_v + per_block - 1) / per_block;
-    if (g > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((token_grads_kernel<DK, IO>), dim3(static_cast<unsigned>(g)), dim3(256), 0, stream, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if ((e = record_event(A.events, 2, stream)) != hipSuccess) return e;
-  if (A.num_seqs > 0 && A.rows_cap > 0) {
-    const int64_t g3 = A.rows_cap * A.h_k;
-    if (g3 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((grad_chunk_kernel<DK, IO>), dim3(static_cast<unsigned>(g3)), dim3(256), 0, stream, A);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return record_event(A.events, 3, stream);
+  return launch_gradient_passes_t<DK, IO>(A, stream);
 }
 
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream) {

@@ -746,7 +746,7 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
     if (e != hipSuccess) return hip_fail(e, "gdn_backward re-chunk pass");
     stash = fine;
   }
-  cpr::BackwardArgs A;
+  cpr::BackwardArgs A{};
   A.cu = cu_seqlens;
   A.q = q; A.k = k; A.v = v; A.a = a; A.b = b;
   A.d_o = d_o;
@@ -760,6 +760,7 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
   A.xv = reinterpret_cast<float*>(ws + adj_bytes + 3 * tok_bytes +
                                   align256((rows_g + num_seqs) * P.h_v * cpr::adjoint_parts(P.dk) * 8));
   A.have_cw = cw != nullptr;
+  A.hparts = cpr::adjoint_parts(P.dk);
   if (cw != nullptr) {                       // the trainer forward's c and w: no replay needed
     A.cc = const_cast<float*>(cw);
     A.ww = const_cast<float*>(cw) + total_tokens * P.h_v * int64_t(P.dv);
@@ -792,41 +793,41 @@ int64_t gdn_prefill_chunked_workspace_bytes(const gdn_policy* policy, int64_t to
   return gdn_chunk_rows_bound(total_tokens, num_seqs, policy->chunk) * policy->h_v * per * 4;
 }
 
-int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                        const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
-                        const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
-                        int32_t outputs, void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
-  if (st == nullptr) return fail(GDN_EINVAL, "gdn_prefill_chunked: state handle is NULL");
+// The chunkwise evaluation behind gdn_prefill_chunked and gdn_trainer_forward_chunked; `bwd`
+// (nullable) is the trainer forward's stash past the workspace: T^T and W^T per chunk row and value
+// head, then every token's c.
+static int chunked_call(const char* fn, gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, const int32_t* slot_ids, int32_t from_state, const void* q,
+                        const void* k, const void* v, const float* a, const float* b, void* o, float* chunk_states,
+                        int64_t chunk_state_rows, int32_t outputs, void* workspace, size_t workspace_bytes,
+                        float* bwd, void* stream, void* const* events) {
+  if (st == nullptr) return fail(GDN_EINVAL, "%s: state handle is NULL", fn);
   const gdn_policy& P = st->policy;
-  if (P.io_dtype != GDN_BF16) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: bf16 io only");
-  if (P.state_dtype != GDN_F32) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: fp32 boundary dtype only");
-  if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: chunk %d > 64", P.chunk);
+  if (P.io_dtype != GDN_BF16) return fail(GDN_EUNSUPPORTED, "%s: bf16 io only", fn);
+  if (P.state_dtype != GDN_F32) return fail(GDN_EUNSUPPORTED, "%s: fp32 boundary dtype only", fn);
+  if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "%s: chunk %d > 64", fn, P.chunk);
   if (outputs != GDN_CHUNKED_NATIVE && outputs != GDN_CHUNKED_R2)
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: outputs must be GDN_CHUNKED_NATIVE or GDN_CHUNKED_R2");
+    return fail(GDN_EINVAL, "%s: outputs must be GDN_CHUNKED_NATIVE or GDN_CHUNKED_R2", fn);
   if (outputs == GDN_CHUNKED_NATIVE && st->r2_ring != nullptr)
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: the pool resynchronises under R2; native outputs would leave its "
-                            "ring behind");
-  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "gdn_prefill_chunked: negative sizes");
-  if (total_tokens >= (int64_t(1) << 31))
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: total_tokens must fit int32 cu_seqlens");
+    return fail(GDN_EINVAL, "%s: the pool resynchronises under R2; native outputs would leave its ring behind", fn);
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", fn);
+  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", fn);
   if (num_seqs > 0 && (cu_seqlens == nullptr || slot_ids == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: cu_seqlens/slot_ids NULL");
-  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "gdn_prefill_chunked: from_state must be 0 or 1");
+    return fail(GDN_EINVAL, "%s: cu_seqlens/slot_ids NULL", fn);
+  if (from_state != 0 && from_state != 1) return fail(GDN_EINVAL, "%s: from_state must be 0 or 1", fn);
   if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr || o == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: token tensor NULL");
+    return fail(GDN_EINVAL, "%s: token tensor NULL", fn);
   const int64_t bound = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
-  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "gdn_prefill_chunked: chunk_states is NULL");
+  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "%s: chunk_states is NULL", fn);
   if (chunk_state_rows < bound)
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: chunk_state_rows %lld < bound %lld", (long long)chunk_state_rows,
+    return fail(GDN_EINVAL, "%s: chunk_state_rows %lld < bound %lld", fn, (long long)chunk_state_rows,
                 (long long)bound);
-  if (bound * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "gdn_prefill_chunked: too many chunks for one launch");
+  if (bound * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "%s: too many chunks for one launch", fn);
   const int64_t need = gdn_prefill_chunked_workspace_bytes(&P, total_tokens, num_seqs);
   if (need < 0) return GDN_EUNSUPPORTED;
   if (int64_t(workspace_bytes) < need || (need > 0 && workspace == nullptr))
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: workspace of %lld bytes < %lld", (long long)workspace_bytes,
-                (long long)need);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
-    return fail(GDN_EINVAL, "gdn_prefill_chunked: workspace must be 16-byte aligned");
+    return fail(GDN_EINVAL, "%s: workspace of %lld bytes < %lld", fn, (long long)workspace_bytes, (long long)need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return fail(GDN_EINVAL, "%s: workspace must be 16-byte aligned", fn);
   cpr::PrefillArgs A{};
   A.max_wgs = st->max_wgs;
   A.cu = cu_seqlens;
@@ -846,6 +847,10 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   A.c_stash = nullptr;
   A.w_stash = nullptr;
   A.events = events;
+  if (bwd != nullptr) {
+    A.chunk_bwd = bwd;
+    A.c_stash = bwd + bound * P.h_v * cpr::chunked_bwd_floats(P.dk);
+  }
   if (outputs == GDN_CHUNKED_R2 && st->r2_ring != nullptr) {
     A.r2_ring = st->r2_ring;
     A.r2_boundary = st->boundary;
@@ -853,7 +858,137 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
   }
   const hipError_t e = cpr::launch_prefill_chunked(P.dk, P.dv, 1, A, workspace, outputs,
                                                    static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "gdn_prefill_chunked launch");
+  if (e != hipSuccess) return hip_fail(e, (std::string(fn) + " launch").c_str());
+  return ok();
+}
+
+int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const int32_t* slot_ids, int32_t from_state, const void* q, const void* k, const void* v,
+                        const float* a, const float* b, void* o, float* chunk_states, int64_t chunk_state_rows,
+                        int32_t outputs, void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  return chunked_call("gdn_prefill_chunked", st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q, k, v,
+                      a, b, o, chunk_states, chunk_state_rows, outputs, workspace, workspace_bytes, nullptr, stream,
+                      events);
+}
+
+// The chunkwise trainer forward keeps, in one stash: the chunk form's workspace, then T^T and W^T
+// per chunk row and value head, then every token's c.
+static int64_t chunked_stash_parts(const gdn_policy& P, int64_t total_tokens, int32_t num_seqs, int64_t* ws_bytes,
+                                   int64_t* bwd_bytes) {
+  const int64_t rows = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
+  *ws_bytes = align256(rows * P.h_v * cpr::chunked_workspace_floats(P.dk) * 4);
+  *bwd_bytes = rows * P.h_v * cpr::chunked_bwd_floats(P.dk) * 4 + total_tokens * P.h_v * int64_t(P.dv) * 4;
+  return *ws_bytes + align256(*bwd_bytes);
+}
+
+int64_t gdn_trainer_forward_chunked_stash_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs) {
+  if (gdn_prefill_chunked_workspace_bytes(policy, total_tokens, num_seqs) < 0) return -1;
+  int64_t ws, bw;
+  const int64_t n = chunked_stash_parts(*policy, total_tokens, num_seqs, &ws, &bw);
+  ok();
+  return n;
+}
+
+int gdn_trainer_forward_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                const int32_t* slot_ids, int32_t from_state, const void* q, const void* k,
+                                const void* v, const float* a, const float* b, void* o, float* chunk_states,
+                                int64_t chunk_state_rows, void* stash, size_t stash_bytes, void* stream,
+                                void* const* events) {
+  if (st == nullptr) return fail(GDN_EINVAL, "gdn_trainer_forward_chunked: state handle is NULL");
+  const int64_t need = gdn_trainer_forward_chunked_stash_bytes(&st->policy, total_tokens, num_seqs);
+  if (need < 0) return GDN_EUNSUPPORTED;
+  if (int64_t(stash_bytes) < need || (need > 0 && stash == nullptr))
+    return fail(GDN_EINVAL, "gdn_trainer_forward_chunked: stash of %lld bytes < %lld", (long long)stash_bytes,
+                (long long)need);
+  int64_t ws, bw;
+  chunked_stash_parts(st->policy, total_tokens, num_seqs, &ws, &bw);
+  float* bwd = reinterpret_cast<float*>(static_cast<char*>(stash) + ws);
+  return chunked_call("gdn_trainer_forward_chunked", st, cu_seqlens, num_seqs, total_tokens, slot_ids, from_state, q,
+                      k, v, a, b, o, chunk_states, chunk_state_rows, GDN_CHUNKED_NATIVE, stash, size_t(ws), bwd,
+                      stream, events);
+}
+
+int64_t gdn_backward_chunked_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs) {
+  if (gdn_prefill_chunked_workspace_bytes(policy, total_tokens, num_seqs) < 0) return -1;
+  const gdn_policy& P = *policy;
+  const int64_t plane = int64_t(P.dk) * P.dv;
+  const int64_t adj_rows = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk) + num_seqs;
+  const int64_t per_token = total_tokens * P.h_v * int64_t(P.dv) * 4;
+  ok();
+  return align256(adj_rows * P.h_v * plane * 4) + 2 * align256(per_token) +
+         align256(adj_rows * P.h_v * cpr::backward_chunked_parts(P.dk) * 8) + align256(total_tokens * P.h_v * 4);
+}
+
+int gdn_backward_chunked(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         const void* q, const void* k, const void* v, const float* a, const float* b,
+                         const float* chunk_states, int64_t chunk_state_rows, const void* stash, size_t stash_bytes,
+                         const void* d_o, const float* d_state, float* dq, float* dk, float* dv, float* da, float* db,
+                         float* d_state0, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* events) {
+  const char* fn = "gdn_backward_chunked";
+  if (int rc = gdn_policy_validate(policy); rc != GDN_OK) return rc;
+  const gdn_policy& P = *policy;
+  if (P.io_dtype != GDN_BF16) return fail(GDN_EUNSUPPORTED, "%s: bf16 io only", fn);
+  if (P.state_dtype != GDN_F32) return fail(GDN_EUNSUPPORTED, "%s: fp32 boundary dtype only", fn);
+  if (P.chunk > 64) return fail(GDN_EUNSUPPORTED, "%s: chunk %d > 64", fn, P.chunk);
+  const int64_t need_stash = gdn_trainer_forward_chunked_stash_bytes(policy, total_tokens, num_seqs);
+  const int64_t need = gdn_backward_chunked_workspace_bytes(policy, total_tokens, num_seqs);
+  if (need_stash < 0 || need < 0) return GDN_EUNSUPPORTED;
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_EINVAL, "%s: negative sizes", fn);
+  if (total_tokens >= (int64_t(1) << 31)) return fail(GDN_EINVAL, "%s: total_tokens must fit int32 cu_seqlens", fn);
+  if (num_seqs > 0 && cu_seqlens == nullptr) return fail(GDN_EINVAL, "%s: cu_seqlens is NULL", fn);
+  if (total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || a == nullptr || b == nullptr ||
+                           d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || da == nullptr ||
+                           db == nullptr))
+    return fail(GDN_EINVAL, "%s: token tensor NULL", fn);
+  const int64_t rows = gdn_chunk_rows_bound(total_tokens, num_seqs, P.chunk);
+  if (num_seqs > 0 && chunk_states == nullptr) return fail(GDN_EINVAL, "%s: chunk_states is NULL", fn);
+  if (num_seqs > 0 && chunk_state_rows < rows)
+    return fail(GDN_EINVAL, "%s: chunk_state_rows %lld < %lld", fn, (long long)chunk_state_rows, (long long)rows);
+  if (rows * P.h_k > 0x7FFFFFFF) return fail(GDN_EUNSUPPORTED, "%s: too many chunks for one launch", fn);
+  if (int64_t(stash_bytes) < need_stash || (need_stash > 0 && stash == nullptr))
+    return fail(GDN_EINVAL, "%s: stash of %lld bytes < %lld", fn, (long long)stash_bytes, (long long)need_stash);
+  if (int64_t(workspace_bytes) < need || (need > 0 && workspace == nullptr))
+    return fail(GDN_EINVAL, "%s: workspace of %lld bytes < %lld", fn, (long long)workspace_bytes, (long long)need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0 || (reinterpret_cast<uintptr_t>(stash) & 15) != 0)
+    return fail(GDN_EINVAL, "%s: workspace and stash must be 16-byte aligned", fn);
+  const int64_t plane = int64_t(P.dk) * P.dv;
+  const int64_t adj_bytes = align256((rows + num_seqs) * P.h_v * plane * 4);
+  const int64_t tok_bytes = align256(total_tokens * P.h_v * int64_t(P.dv) * 4);
+  const int parts = cpr::backward_chunked_parts(P.dk);
+  int64_t ws_bytes, bw_bytes;
+  chunked_stash_parts(P, total_tokens, num_seqs, &ws_bytes, &bw_bytes);
+  const char* st = static_cast<const char*>(stash);
+  char* ws = static_cast<char*>(workspace);
+  cpr::BackwardArgs A{};
+  A.cu = cu_seqlens;
+  A.q = q; A.k = k; A.v = v; A.a = a; A.b = b;
+  A.d_o = d_o;
+  A.d_state = d_state;
+  A.chunk_states = chunk_states;
+  A.fws = reinterpret_cast<const float*>(st);
+  A.fbw = reinterpret_cast<const float*>(st + ws_bytes);
+  A.cc = const_cast<float*>(A.fbw + rows * P.h_v * cpr::chunked_bwd_floats(P.dk));
+  A.adjoint = reinterpret_cast<float*>(ws);
+  A.dc = reinterpret_cast<float*>(ws + adj_bytes);
+  A.ww = reinterpret_cast<float*>(ws + adj_bytes + tok_bytes);
+  A.hpart = reinterpret_cast<double*>(ws + adj_bytes + 2 * tok_bytes);
+  A.xv = reinterpret_cast<float*>(ws + adj_bytes + 2 * tok_bytes + align256((rows + num_seqs) * P.h_v * parts * 8));
+  A.have_cw = 1;
+  A.hparts = parts;
+  A.dq = dq; A.dk = dk; A.dv = dv; A.da = da; A.db = db;
+  A.d_state0 = d_state0;
+  A.total_tokens = total_tokens;
+  A.rows_cap = rows;
+  A.adj_rows = rows + num_seqs;
+  A.num_seqs = num_seqs;
+  A.h_k = P.h_k; A.h_v = P.h_v; A.chunk = P.chunk;
+  A.events = events;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = cpr::launch_backward_chunked(P.dk, A, hs);
+  if (e != hipSuccess) return hip_fail(e, (std::string(fn) + " launch").c_str());
+  e = cpr::launch_gradient_passes(P.dk, P.io_dtype, A, hs);
+  if (e != hipSuccess) return hip_fail(e, (std::string(fn) + " gradient passes").c_str());
   return ok();
 }
 

@@ -28,6 +28,15 @@ hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream);
 // Parts of <G, S_0> the adjoint pass stores per chunk start and value head (head dim d).
 int adjoint_parts(int d);
+// The backward's per-token and chunk gradient kernels alone (events 2 and 3), given dc, the
+// adjoint rows, the <G, S> parts, c and w.
+hipError_t launch_gradient_passes(int d, int io, const BackwardArgs& A, hipStream_t stream);
+// The chunk-form backward's own passes (events 0 and 1): w and the intra-chunk part of dC, then
+// the reverse chunk chain (G at every chunk boundary, dc, the <G, S> parts), from what the
+// chunk-form trainer forward kept.  Head dims 32, 64 and 128, bf16 io.
+hipError_t launch_backward_chunked(int d, const BackwardArgs& A, hipStream_t stream);
+int backward_chunked_parts(int d);
+int64_t chunked_bwd_floats(int d);
 // The position update that ends every prefill, and the CPR output pass (with that update) alone,
 // started from chunk states already stored.
 hipError_t launch_prefill_finish(const PrefillArgs& A, hipStream_t stream);

@@ -360,8 +360,9 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
 
 /* ---- R2 resynchronisation in decode ---------------------------------------------------------
  * Under the R2 reading of CPR's first pass (GDN_CHUNKED_R2 above), the state at every chunk start
- * is the chunk form's, and decode "resynchronizes the hidden state every chunk-size tokens" (section
- * "Solving the linear-attention headache") by recomputing it with the chunk form.  A pool with R2
+ * is the chunk form's, and decode, which the section "Solving the linear-attention headache" has
+ * bring its state back in line once every chunk of tokens, does so by recomputing it with the chunk
+ * form.  A pool with R2
  * attached keeps, per slot, the chunk-start state of the chunk its last token fell in (in its
  * boundary record, with that chunk start as boundary_pos) and the chunk's tokens so far (a
  * caller-owned ring, indexed by position mod C).  Then:
@@ -456,6 +457,46 @@ int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t nu
                  const float* d_state,
                  float* dq, float* dk, float* dv, float* da, float* db, float* d_state0,
                  void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/* ---- chunkwise trainer: forward and backward on matrix cores ----------------------------------
+ * The "native" trainer column of the per-layer table in section "Solving the linear-attention
+ * headache": the chunkwise evaluation above for the forward, and the chunk form of the adjoint
+ * recurrence for the backward.  Per chunk (notation of the chunkwise block above), with J the
+ * gradient dL/dS at the chunk's end, the gradients reaching the write vectors solve the transposed
+ * system, dC = T^T R with R = (M . Q K^T)^T dO + diag(G_L/G) K J, and dL/dS at the chunk start is
+ * G_L J + Q^T diag(G) dO - W^T R; the forward's w = v - a S^T k is V - diag(G) K S_0 - (N . K K^T) C
+ * (N[t][s] = G_t/G_s, s < t).  A parallel pass forms w and the part of R without G_L, a pass per (sequence, value head,
+ * 32 columns) walks the chunks last to first, and dq, dk, dv, da and db then come from the same
+ * per-token and chunk-gradient kernels as gdn_backward.  The gradients agree with the recurrence's
+ * to the backward tolerance; they are deterministic (fixed summation orders) but not the bits of
+ * gdn_backward, and they depend on C, as the chunkwise forward does.
+ * Requirements: as gdn_prefill_chunked; every sequence starts at position 0 (from_state 0, or 1
+ * from slots at position 0).
+ *   gdn_trainer_forward_chunked_stash_bytes  bytes of the stash the forward keeps for the backward:
+ *       the chunk form's workspace, T^T and W^T per chunk row and value head (fp32), and every
+ *       token's c (fp32 [N][H_v][d_v]), each part padded to 256 bytes; -1 on bad input.
+ *   gdn_trainer_forward_chunked  gdn_prefill_chunked(GDN_CHUNKED_NATIVE) that also fills the
+ *       caller-owned stash (device, 16-byte aligned); chunk_states keeps the chunk-start states.
+ *       events: as gdn_prefill_chunked.
+ *   gdn_backward_chunked_workspace_bytes  dL/dS at every chunk boundary (total_tokens / C +
+ *       2 num_seqs states), dc and w (fp32 [N][H_v][d_v] each), 4 fp64 parts of <dL/dS, S> per
+ *       32 value columns per boundary and value head, and v . dv per token and value head.
+ *   gdn_backward_chunked  arguments as gdn_backward, with the forward's stash in place of cw;
+ *       d_state0 (nullable) receives dL/dS_0.  Events: NULL, or 4 hipEvent_t recorded before the
+ *       chunk-form passes, after them, after the per-token gradients and at the end. */
+int64_t gdn_trainer_forward_chunked_stash_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
+int gdn_trainer_forward_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                const int32_t* slot_ids, int32_t from_state,
+                                const void* q, const void* k, const void* v, const float* a, const float* b,
+                                void* o, float* chunk_states, int64_t chunk_state_rows,
+                                void* stash, size_t stash_bytes, void* stream, void* const* events);
+int64_t gdn_backward_chunked_workspace_bytes(const gdn_policy* policy, int64_t total_tokens, int32_t num_seqs);
+int gdn_backward_chunked(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         const void* q, const void* k, const void* v, const float* a, const float* b,
+                         const float* chunk_states, int64_t chunk_state_rows, const void* stash, size_t stash_bytes,
+                         const void* d_o, const float* d_state,
+                         float* dq, float* dk, float* dv, float* da, float* db, float* d_state0,
+                         void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
 #ifdef __cplusplus
 }

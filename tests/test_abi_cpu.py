@@ -354,3 +354,53 @@ def test_r2_sizes_and_attach_errors():
         assert rc == 1 and b"chunk_state_rows" in lib.gdn_last_error()
     finally:
         lib.gdn_state_free(h)
+
+
+def test_chunked_trainer_sizes_and_argument_errors():
+    """The chunkwise trainer's stash and backward workspace sizes, and the host checks of
+    gdn_trainer_forward_chunked and gdn_backward_chunked (no GPU: fake addresses are never
+    dereferenced)."""
+    lib = cpr._lib
+    pad = lambda x: -(-x // 256) * 256
+    N, B = 1000, 3
+    for d, parts in ((32, 4), (64, 8), (128, 16)):
+        p = cpr.Policy(2, 4, d, d, chunk=64, io="bf16")
+        rows = cpr.gdn_chunk_rows_bound(N, B, 64)
+        ws = cpr.gdn_prefill_chunked_workspace_bytes(p, N, B)
+        # the forward's workspace, then T^T (64 x 64) and W^T (d x 64) per chunk row and value head,
+        # then every token's c
+        stash = pad(ws) + pad(rows * 4 * (64 * 64 + 64 * d) * 4 + N * 4 * d * 4)
+        assert cpr.gdn_trainer_forward_chunked_stash_bytes(p, N, B) == stash
+        # G at every boundary, dc and w, the <G, S> parts (4 per 32 columns), v . dv
+        adj = (rows + B) * 4 * d * d * 4
+        wsb = pad(adj) + 2 * pad(N * 4 * d * 4) + pad((rows + B) * 4 * parts * 8) + pad(N * 4 * 4)
+        assert cpr.gdn_backward_chunked_workspace_bytes(p, N, B) == wsb
+    bad = cpr.Policy(2, 4, 16, 16, io="bf16")                                  # head dim not built
+    assert lib.gdn_trainer_forward_chunked_stash_bytes(ctypes.byref(bad.c()), 10, 1) == -1
+    assert lib.gdn_backward_chunked_workspace_bytes(ctypes.byref(bad.c()), 10, 1) == -1
+    fake = 0x10000
+    p = cpr.Policy(2, 4, 64, 64, chunk=64, io="bf16")
+    need = cpr.gdn_trainer_forward_chunked_stash_bytes(p, 100, 2)
+    h = ctypes.c_void_p()
+    nbytes = lib.gdn_state_bytes(ctypes.byref(p.c()), 3)
+    assert lib.gdn_state_alloc(ctypes.byref(p.c()), 3, fake, fake, nbytes, None, None, ctypes.byref(h)) == 0
+    try:
+        rc = lib.gdn_trainer_forward_chunked(h, fake, 2, 100, fake, 0, fake, fake, fake, fake, fake, fake, fake, 99,
+                                             fake, need - 1, None, None)
+        assert rc == 1 and b"stash" in lib.gdn_last_error()
+    finally:
+        lib.gdn_state_free(h)
+    wneed = cpr.gdn_backward_chunked_workspace_bytes(p, 100, 2)
+
+    def bwd(pol, stash_bytes=need, ws_bytes=wneed, ws=fake, rows=99):
+        return lib.gdn_backward_chunked(ctypes.byref(pol.c()), fake, 2, 100, fake, fake, fake, fake, fake, fake, rows,
+                                        fake, stash_bytes, fake, None, fake, fake, fake, fake, fake, None, ws, ws_bytes,
+                                        None, None)
+
+    assert bwd(cpr.Policy(2, 4, 64, 64, io="f32")) == 2
+    assert bwd(cpr.Policy(2, 4, 64, 64, io="bf16", boundary="bf16")) == 2
+    assert bwd(cpr.Policy(2, 4, 64, 64, chunk=100, io="bf16")) == 2
+    assert bwd(p, stash_bytes=need - 1) == 1 and b"stash" in lib.gdn_last_error()
+    assert bwd(p, ws_bytes=wneed - 1) == 1 and b"workspace" in lib.gdn_last_error()
+    assert bwd(p, ws=fake + 8) == 1
+    assert bwd(p, rows=2) == 1

@@ -1,0 +1,207 @@
+"""The chunkwise trainer on matrix cores (gdn_trainer_forward_chunked + gdn_backward_chunked): the
+native trainer column of the per-layer table in "Solving the linear-attention headache", against
+the fp64 oracle of the recurrence and its adjoint.
+
+Tolerance.  The chunk form runs its products on bf16 matrix cores with split operands: a value x
+is carried as hi + lo, hi = bf16(x) and lo = bf16(x - hi), which represents it to about 2^-18
+relative, and a product keeps hi*hi + hi*lo + lo*hi, dropping lo*lo (another 2^-18).  Every
+intermediate of the forward (C, the chunk-start states) and of the backward (R, dC, G) thus carries
+a relative error of a few 1e-6, against the per-token path's fp32 1e-7.  Measured on the cases
+below: dq, dk, dv, db and dS_0 within 1e-5 both normwise and in max-abs over their scale.  They are
+held to the per-token backward's max-abs bound, max |got - ref| <= 1e-4 * max(1, max |ref|), and to
+a normwise 5e-5 (the per-token backward's is 1e-5).  da is the exception: a_t da_t = <G_{t-1},
+S_{t-1}> sums d_k d_v products of two such matrices whose terms largely cancel, so its error scales
+with ||G|| ||S|| rather than with |da|; measured up to 1.0e-4 normwise and 2.7e-4 of its scale, it is
+held to 1e-3 for both.  The forward's o is held to the chunkwise forward's bf16 bound (normwise 3e-3
+per (sequence, value head)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+from oracle import gdn_varlen_backward, recurrence_backward
+from tests.gpu_util import lib, normwise, oracle_seq_head, policy_of, say, sha
+
+pytestmark = pytest.mark.gpu
+
+REL_MAX = {"da": 1e-3}                 # max-abs over max(1, max |ref|); 1e-4 for the others
+NORMWISE = {"da": 1e-3}                # normwise; 5e-5 for the others
+GRADS = ("dq", "dk", "dv", "da", "db")
+
+
+def _close(got, ref, what, stats=None):
+    """`what` ends with the gradient's name, which picks its bounds."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return
+    key = what.split()[-1]
+    err = float(np.max(np.abs(got - ref)))
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    nw = normwise(got, ref)
+    if stats is not None:
+        stats[key] = max(stats.get(key, (0.0, 0.0))[0], nw), max(stats.get(key, (0.0, 0.0))[1], err / scale)
+    rel_max, nw_max = REL_MAX.get(key, 1e-4), NORMWISE.get(key, 5e-5)
+    assert err <= rel_max * scale, f"{what}: max-abs {err:.3e} > {rel_max} * {scale:.3e}"
+    assert nw <= nw_max, f"{what}: normwise {nw:.3e} > {nw_max}"
+
+
+def _forward(x, s0=None):
+    """The chunkwise trainer forward; returns (o, pool, chunk_states, stash)."""
+    cpr = lib()
+    xd = x.to("cuda")
+    pool = cpr.StatePool(policy_of(x), max(x.num_seqs, 1))
+    if s0 is not None:
+        pool.state[: x.num_seqs].copy_(s0)
+    o, cs, stash = cpr.gdn_trainer_forward_chunked(pool, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b,
+                                                   from_state=s0 is not None)
+    torch.cuda.synchronize()
+    return o, pool, cs, stash
+
+
+def _backward(x, ct, cs, stash):
+    cpr = lib()
+    xd = x.to("cuda")
+    d_state = None if ct["d_state"] is None else ct["d_state"].to("cuda")
+    g = cpr.gdn_backward_chunked(policy_of(x), x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b, cs, stash,
+                                 ct["d_o"].to("cuda"), d_state=d_state, want_d_state0=True)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(x, ct):
+    cpu = x.to("cpu")
+    dO = ct["d_o"].cpu().double().numpy()
+    dS = None if ct["d_state"] is None else ct["d_state"].cpu().double().numpy().transpose(0, 1, 3, 2)
+    S0 = None if ct["s0"] is None else ct["s0"].cpu().double().numpy().transpose(0, 1, 3, 2)
+    return gdn_varlen_backward(cpu.widen("q"), cpu.widen("k"), cpu.widen("v"), cpu.widen("a"), cpu.widen("b"),
+                               dO, x.cu_seqlens, x.h_k, x.h_v, S0=S0, dS_T=dS)
+
+
+def _compare_all(x, g, ref, stats=None):
+    names = GRADS + ("dS0",)
+    for i in range(x.num_seqs):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        for n, r in zip(names, ref):
+            if n == "dS0":
+                _close(g["d_state0"][i].cpu().double().numpy().transpose(0, 2, 1), r[i], f"seq {i} dS0", stats)
+            else:
+                _close(g[n][t0:t1].cpu().double().numpy(), r[t0:t1], f"seq {i} {n}", stats)
+
+
+CASES = [
+    # dim, chunk, with d_state, with S0
+    (32, 64, True, True),
+    (32, 16, False, False),
+    (64, 32, True, False),
+    (128, 64, True, True),
+    (128, 20, False, True),
+]
+
+
+@pytest.mark.parametrize("dim,chunk,with_ds,with_s0", CASES)
+def test_chunked_trainer_matches_oracle(dim, chunk, with_ds, with_s0):
+    lens = [1, 64, 65, 200, 0, 33]
+    x = gi.make_inputs(71, lens, h_k=2, h_v=4, dk=dim, dv=dim, chunk=chunk, io="bf16")
+    ct = gi.make_cotangents(x, 72, with_d_state=with_ds, with_s0=with_s0)
+    say(f"chunked trainer vs oracle dim={dim} C={chunk} dS={with_ds} S0={with_s0}")
+    s0 = None if ct["s0"] is None else ct["s0"].to("cuda")
+    o, pool, cs, stash = _forward(x, s0)
+    o_np = o.float().cpu().double().numpy()
+    for i in range(x.num_seqs):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        for h in range(x.h_v):
+            ref_o, _, _ = oracle_seq_head(x, i, h, S0=None if ct["s0"] is None else ct["s0"][i, h].double().numpy().T)
+            if t1 > t0:
+                assert normwise(o_np[t0:t1, h], ref_o) <= 3e-3, (i, h, "o")
+    g = _backward(x, ct, cs, stash)
+    stats = {}
+    _compare_all(x, g, _oracle(x, ct), stats)
+    say("  worst normwise / max-abs over scale: " +
+        ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in sorted(stats.items())))
+
+
+def test_chunked_trainer_forward_is_the_chunked_prefill():
+    """The trainer forward computes what gdn_prefill_chunked(NATIVE) computes, bit for bit, and keeps
+    every token's c: the per-token step's c from the same inputs agrees with it to the chunk form's
+    rounding."""
+    cpr = lib()
+    x = gi.make_inputs(73, [130, 64, 1, 257], h_k=2, h_v=4, dk=128, dv=128, chunk=64, io="bf16")
+    o, pool, cs, stash = _forward(x)
+    xd = x.to("cuda")
+    p2 = cpr.StatePool(policy_of(x), x.num_seqs)
+    o2, cs2 = cpr.gdn_prefill_chunked(p2, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    torch.cuda.synchronize()
+    assert sha(o) == sha(o2) and sha(pool.state) == sha(p2.state)
+    used = int(cpr.gdn_chunk_rows(x.cu_seqlens, x.chunk)[-1])          # rows the plan fills
+    assert sha(cs[:used]) == sha(cs2[:used])
+    rows = cpr.gdn_chunk_rows_bound(x.total_tokens, x.num_seqs, x.chunk)
+    # c, the stash's last part (after the workspace and T^T, W^T per chunk row and value head),
+    # against the per-token trainer forward's c
+    N = x.total_tokens
+    ws = cpr.gdn_prefill_chunked_workspace_bytes(policy_of(x), N, x.num_seqs)
+    off = (ws + 255) // 256 * 256 + rows * x.h_v * (64 * 64 + 64 * x.dk) * 4
+    c_chunk = stash[off:off + N * x.h_v * x.dv * 4].view(torch.float32).view(N, x.h_v, x.dv)
+    p3 = cpr.StatePool(policy_of(x), x.num_seqs)
+    _, _, cw = cpr.gdn_trainer_forward(p3, x.cu_seqlens, xd.q, xd.k, xd.v, xd.a, xd.b)
+    torch.cuda.synchronize()
+    assert normwise(c_chunk.cpu().double().numpy(), cw[0].cpu().double().numpy()) <= 1e-4
+
+
+def test_chunked_backward_is_deterministic_and_packing_invariant():
+    """Two runs give the same bits, and every sequence's gradients are the bits it gets alone."""
+    cpr = lib()
+    lens = [300, 1, 64, 129]
+    x = gi.make_inputs(74, lens, h_k=2, h_v=4, dk=64, dv=64, chunk=64, io="bf16")
+    ct = gi.make_cotangents(x, 75, with_d_state=True, with_s0=False)
+    _, _, cs, stash = _forward(x)
+    g1 = _backward(x, ct, cs, stash)
+    g2 = _backward(x, ct, cs, stash)
+    for n in GRADS + ("d_state0",):
+        assert sha(g1[n]) == sha(g2[n]), n
+    for i in (0, 3):
+        y = x.select([i])
+        cty = {"d_o": ct["d_o"][int(x.cu_seqlens[i]):int(x.cu_seqlens[i + 1])].contiguous(),
+               "d_state": ct["d_state"][i:i + 1].contiguous(), "s0": None}
+        _, _, csy, stashy = _forward(y)
+        gy = _backward(y, cty, csy, stashy)
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        for n in GRADS:
+            assert sha(gy[n]) == sha(g1[n][t0:t1]), (i, n)
+        assert sha(gy["d_state0"]) == sha(g1["d_state0"][i:i + 1]), i
+    say(f"chunked backward: deterministic, packing invariant ({cpr.gdn_backward_chunked_workspace_bytes(policy_of(x), x.total_tokens, x.num_seqs)} workspace bytes)")
+
+
+def test_chunked_trainer_10240_matches_oracle():
+    """The trainer workload (10240 tokens packed varlen, d = 128, C = 64): every sequence's gradients
+    for key head 5 (value heads 10 and 11) against the oracle, finite gradients everywhere."""
+    x = gi.trainer_10240(device="cuda")
+    ct = gi.make_cotangents(x, 76, device="cuda")
+    say(f"chunked trainer 10240 lengths={x.lengths.tolist()}")
+    _, _, cs, stash = _forward(x)
+    g = _backward(x, ct, cs, stash)
+    for n in GRADS + ("d_state0",):
+        assert bool(torch.isfinite(g[n]).all()), n
+    cpu = x.to("cpu")
+    dO = ct["d_o"].cpu().double().numpy()
+    dS = ct["d_state"].cpu().double().numpy()
+    kh = 5
+    stats = {}
+    for i in range(x.num_seqs):
+        t0, t1 = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+        rows = slice(t0, t1)
+        dq = dk = 0
+        for h in (2 * kh, 2 * kh + 1):
+            r = recurrence_backward(cpu.widen("q", rows)[:, kh], cpu.widen("k", rows)[:, kh],
+                                    cpu.widen("v", rows)[:, h], cpu.widen("a", rows)[:, h],
+                                    cpu.widen("b", rows)[:, h], dO[t0:t1, h], None, dS[i, h].T)
+            dq, dk = dq + r[0], dk + r[1]
+            _close(g["dv"][t0:t1, h].cpu().double().numpy(), r[2], f"seq {i} h{h} dv", stats)
+            _close(g["da"][t0:t1, h].cpu().double().numpy(), r[3], f"seq {i} h{h} da", stats)
+            _close(g["db"][t0:t1, h].cpu().double().numpy(), r[4], f"seq {i} h{h} db", stats)
+            _close(g["d_state0"][i, h].cpu().double().numpy().T, r[5], f"seq {i} h{h} dS0", stats)
+        _close(g["dq"][t0:t1, kh].cpu().double().numpy(), dq, f"seq {i} dq", stats)
+        _close(g["dk"][t0:t1, kh].cpu().double().numpy(), dk, f"seq {i} dk", stats)
+    say("  worst normwise / max-abs over scale: " +
+        ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in sorted(stats.items())))
