@@ -30,7 +30,8 @@
 //     h_0 is formed by the adjoint pass, which holds G at the chunk start anyway: each wave adds its
 //     lanes' part of <G, S_0> (S_0 prefetched from the stash a chunk ahead) and stores it, and the
 //     chunk-gradient pass adds the parts in a fixed order.
-//     dq and dk of a key head add its value heads' totals in head order inside the workgroup.
+//     dq and dk of a key head accumulate its value heads in head order in the workgroup's
+//     matrix-core accumulators, and are stored once.
 // Every sum has a fixed order, so the gradients are bitwise reproducible for any batch
 // composition or packing.
 #include <hip/hip_runtime.h>
@@ -611,6 +612,12 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
   const int64_t plane = static_cast<int64_t>(D) * D;
   const int64_t gstart = w + i;                              // boundary rows around this chunk
 
+  // the key head's dq and dk: each value head's products accumulate onto the previous heads' in the
+  // matrix-core accumulators, heads in order; xprev holds q_t . dq_t of the heads before
+  f32x4 acc_dq[NT], acc_dk[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc_dq[n] = acc_dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float xprev[4] = {0.f, 0.f, 0.f, 0.f};
   for (int hh = 0; hh < ratio; ++hh) {
     const int h = kh * ratio + hh;
     __syncthreads();                                         // the previous head is done with LDS
@@ -639,9 +646,7 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
     const float* ge = A.adjoint + ((gstart + 1) * A.h_v + h) * plane;
 
     // dq += Gam_t dO S0^T; dk += Gam_{t-1} dU S0^T; A1 = dO C^T; A2 = dU C^T; h_0 = <G_start, S0>
-    f32x4 acc_dq[NT], acc_dk[NT], a1[4], a2[4];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc_dq[n] = acc_dk[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 a1[4], a2[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) a1[n] = a2[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
@@ -751,9 +756,9 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
         for (int n = 0; n < NT; ++n) acc_dk[n] = mfma4(ak1, S.u.m.kq[s * SB + 16 * n + lj], acc_dk[n]);
       }
     }
-    // per-token terms of this value head
+    // per-token terms of this value head: q_t . dq_t over this head's dq, the accumulated dq's dot
+    // less that of the heads before (rows 16 wave + 4 g + r, columns 16 n + j)
     {
-      // q_t . dq_t over this head's dq: rows 16 wave + 4 g + r, columns 16 n + j
       float xr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -761,27 +766,13 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
         float x = 0.f;
 #pragma unroll
         for (int n = 0; n < NT; ++n) x = __builtin_fmaf(acc_dq[n][r], S.u.m.kq[t * SB + 16 * n + lj], x);
-        xr[r] = lane_tree<16>(x);
+        const float xc = lane_tree<16>(x);
+        xr[r] = xc - xprev[r];
+        xprev[r] = xc;
       }
       if (lj == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) S.xq[16 * wave + 4 * lgp + r] = xr[r];
-      }
-      // this head's dq and dk added to the key head's, heads in order (the same thread owns the
-      // same elements for every head)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wave + 4 * lgp + r;
-        if (t < L) {
-          const int64_t base = ((tok + t) * A.h_k + kh) * D;
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            float* pq = A.dq + base + 16 * n + lj;
-            float* pk = A.dk + base + 16 * n + lj;
-            *pq = hh == 0 ? acc_dq[n][r] : *pq + acc_dq[n][r];
-            *pk = hh == 0 ? acc_dk[n][r] : *pk + acc_dk[n][r];
-          }
-        }
       }
     }
     __syncthreads();
@@ -803,6 +794,18 @@ __global__ void __launch_bounds__(256, 2) grad_chunk_kernel(BackwardArgs A) {
 #pragma unroll 1
       for (int p = 0; p < A.hparts; ++p) h0 += hpp[p];
       if (tid < L) A.da[(tok + tid) * A.h_v + h] = static_cast<float>((h0 - excl) / static_cast<double>(S.ab[tid].x));
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 16 * wave + 4 * lgp + r;
+    if (t < L) {
+      const int64_t base = ((tok + t) * A.h_k + kh) * D;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        A.dq[base + 16 * n + lj] = acc_dq[n][r];
+        A.dk[base + 16 * n + lj] = acc_dk[n][r];
+      }
     }
   }
 }
