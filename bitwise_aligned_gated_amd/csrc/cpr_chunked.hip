@@ -42,18 +42,13 @@ struct alignas(16) PrepLds {
   float bb[M::L];
 };
 
+// One (chunk row w, value head h) of the prep pass.  Uniform across the block; it returns early
+// for rows with no work.
 template <int D>
-__global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* ws) {
+__device__ __forceinline__ void prep_item(const PrefillArgs& A, float* ws, PrepLds<D>& S, int64_t* red, int64_t w,
+                                          int kh, int h) {
   using M = ChunkCfg<D>;
   constexpr int L = M::L, ST = M::ST, SF = M::SF, NT = D / 16;
-  __shared__ PrepLds<D> S;
-  __shared__ int64_t red[6];
-  const int ratio = A.h_v / A.h_k;
-  const GroupSlot gs = xcd_group(blockIdx.x, ratio);
-  const int64_t w = gs.group / A.h_k;
-  const int kh = static_cast<int>(gs.group % A.h_k);
-  const int h = kh * ratio + gs.member;
-  if (w >= A.rows_cap) return;                                // uniform across the block
   int i;
   int64_t c;
   if (A.gate != nullptr) {                                    // one row per sequence, run where gated in
@@ -215,6 +210,35 @@ __global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* w
   for (int e = tid; e <= L; e += 256) lgw[e] = S.lgd[e];
 }
 
+template <int D>
+__global__ void __launch_bounds__(256) chunk_prep_kernel(PrefillArgs A, float* ws) {
+  __shared__ PrepLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio);
+  const int64_t w = gs.group / A.h_k;
+  const int kh = static_cast<int>(gs.group % A.h_k);
+  if (w >= A.rows_cap) return;                                // uniform across the block
+  prep_item<D>(A, ws, S, red, w, kh, kh * ratio + gs.member);
+}
+
+// The prep pass over the rows of a listed set of sequences only (one row each, A.gate set): the
+// workgroups take (listed sequence, value head) items in turn, so the grid need not cover every
+// sequence.  list[0 .. *count) are sequence indices.
+template <int D>
+__global__ void __launch_bounds__(256) chunk_prep_list_kernel(PrefillArgs A, float* ws, const int32_t* list,
+                                                              const int32_t* count) {
+  __shared__ PrepLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const int64_t items = static_cast<int64_t>(*count) * A.h_v;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int h = static_cast<int>(it % A.h_v);
+    prep_item<D>(A, ws, S, red, list[it / A.h_v], h / ratio, h);
+    __syncthreads();                                          // LDS free for the next item
+  }
+}
+
 // ---- state: sequential over chunks per (sequence, value head, column slice) ---------------------
 template <int D>
 struct alignas(16) StateLds {
@@ -269,18 +293,13 @@ __device__ __forceinline__ void state_fetch(const PrefillArgs& A, const float* w
   R.lg = tid <= M::L ? reinterpret_cast<const double*>(wsb + 3 * M::WS_MAT)[tid] : 0.0;
 }
 
+// One (sequence i, value head h, column slice sl) of the state pass.  Uniform across the block;
+// it returns early for sequences with no work.
 template <int D>
-__global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* ws, int write_final) {
+__device__ __forceinline__ void state_item(const PrefillArgs& A, float* ws, int write_final, StateLds<D>& S,
+                                           int64_t* red, int i, int kh, int h, int sl) {
   using M = ChunkCfg<D>;
   constexpr int L = M::L, NS = M::NS, SS = M::SS, SF = M::SF, ST = M::ST;
-  constexpr int NSL = D / NS;                                  // column slices per value head
-  __shared__ StateLds<D> S;
-  __shared__ int64_t red[6];
-  const int ratio = A.h_v / A.h_k;
-  const GroupSlot gs = xcd_group(blockIdx.x, ratio * NSL);
-  if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
-  const int i = static_cast<int>(gs.group / A.h_k), kh = static_cast<int>(gs.group % A.h_k);
-  const int h = kh * ratio + gs.member / NSL, sl = gs.member % NSL;
   if (A.gate != nullptr && A.gate[i] == 0) return;            // uniform across the block
   const SeqMeta m = seq_meta(A, i);
   const int64_t row0 = A.gate != nullptr ? i : plan_row_offset(A, i, red);
@@ -383,6 +402,36 @@ __global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* 
       reinterpret_cast<float4*>(A.state + (static_cast<int64_t>(m.slot) * A.h_v + h) * plane +
                                 static_cast<int64_t>(j0 + jj) * D)[c4] = *reinterpret_cast<const float4*>(&S.st[jj * SS + 4 * c4]);
     }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) chunk_state_kernel(PrefillArgs A, float* ws, int write_final) {
+  constexpr int NSL = D / ChunkCfg<D>::NS;                     // column slices per value head
+  __shared__ StateLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const GroupSlot gs = xcd_group(blockIdx.x, ratio * NSL);
+  if (gs.group >= static_cast<int64_t>(A.num_seqs) * A.h_k) return;   // uniform across the block
+  const int i = static_cast<int>(gs.group / A.h_k), kh = static_cast<int>(gs.group % A.h_k);
+  state_item<D>(A, ws, write_final, S, red, i, kh, kh * ratio + gs.member / NSL, gs.member % NSL);
+}
+
+// The state pass over a listed set of sequences only (A.gate set): the workgroups take (listed
+// sequence, value head, column slice) items in turn.  list[0 .. *count) are sequence indices.
+template <int D>
+__global__ void __launch_bounds__(256) chunk_state_list_kernel(PrefillArgs A, float* ws, int write_final,
+                                                               const int32_t* list, const int32_t* count) {
+  constexpr int NSL = D / ChunkCfg<D>::NS;
+  __shared__ StateLds<D> S;
+  __shared__ int64_t red[6];
+  const int ratio = A.h_v / A.h_k;
+  const int64_t per = static_cast<int64_t>(A.h_v) * NSL;
+  const int64_t items = static_cast<int64_t>(*count) * per;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int r = static_cast<int>(it % per), h = r / NSL;
+    state_item<D>(A, ws, write_final, S, red, list[it / per], h / ratio, h, r % NSL);
+    __syncthreads();                                          // LDS free for the next item
   }
 }
 
@@ -526,12 +575,15 @@ struct R2Work {
   int32_t* ids;
   int32_t* gate;
   int64_t* vpos;
+  int32_t* list;     // the slots gated in this step, in any order
+  int32_t* count;    // how many
   float* ws;
 };
 
 int64_t r2_workspace_bytes(int h_v, int d, int num_slots) {
   const int64_t S = num_slots;
-  return pad256((S + 1) * 4) + 2 * pad256(S * 4) + pad256(S * 8) + S * h_v * chunked_workspace_floats(d) * 4;
+  return pad256((S + 1) * 4) + 2 * pad256(S * 4) + pad256(S * 8) + pad256(S * 4) + pad256(4) +
+         S * h_v * chunked_workspace_floats(d) * 4;
 }
 
 static R2Work r2_work(void* work, int num_slots) {
@@ -546,6 +598,10 @@ static R2Work r2_work(void* work, int num_slots) {
   p += pad256(S * 4);
   w.vpos = reinterpret_cast<int64_t*>(p);
   p += pad256(S * 8);
+  w.list = reinterpret_cast<int32_t*>(p);
+  p += pad256(S * 4);
+  w.count = reinterpret_cast<int32_t*>(p);
+  p += pad256(4);
   w.ws = reinterpret_cast<float*>(p);
   return w;
 }
@@ -553,6 +609,7 @@ static R2Work r2_work(void* work, int num_slots) {
 // The one-chunk batch over every slot, nobody gated in yet.
 __global__ void r2_batch_kernel(R2Work W, int num_slots, int chunk) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s == 0) *W.count = 0;
   if (s > num_slots) return;
   W.cu[s] = s * chunk;
   if (s == num_slots) return;
@@ -561,7 +618,8 @@ __global__ void r2_batch_kernel(R2Work W, int num_slots, int chunk) {
   W.vpos[s] = 0;
 }
 
-// Gate in the listed slots that stand at a chunk start with a chunk behind them.
+// Gate in the listed slots that stand at a chunk start with a chunk behind them, and list them (the
+// list's order depends on the atomics' order, which decides only which workgroup takes a slot).
 __global__ void r2_gate_kernel(R2Work W, const int32_t* slot_ids, int batch, const int64_t* pos, int num_slots,
                                int chunk) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
@@ -569,7 +627,10 @@ __global__ void r2_gate_kernel(R2Work W, const int32_t* slot_ids, int batch, con
   const int32_t s = slot_ids[j];
   if (s < 0 || s >= num_slots) return;
   const int64_t p = pos[s];
-  if (p > 0 && p % chunk == 0) W.gate[s] = 1;
+  if (p > 0 && p % chunk == 0) {
+    W.gate[s] = 1;
+    W.list[atomicAdd(W.count, 1)] = s;
+  }
 }
 
 // After the step (positions already advanced): each listed slot's token to ring position
@@ -639,10 +700,13 @@ __global__ void __launch_bounds__(256) r2_ring_fill_kernel(PrefillArgs A, RingPa
   if (threadIdx.x == 0) boundary_pos[m.slot] = bpos;
 }
 
+// Workgroups of the list-driven chunk-form kernels in an R2 decode step: 256 (one per CU).
+constexpr int64_t kR2ListGrid = 256;
+
 template <int D>
 static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work, hipStream_t stream) {
   using M = ChunkCfg<D>;
-  const int S = A.num_slots, ratio = A.h_v / A.h_k;
+  const int S = A.num_slots;
   const RingParts R = ring_parts(ring, A.h_k, A.h_v, D, A.chunk, S);
   const R2Work W = r2_work(work, S);
   hipError_t e = record_event(A.events, 0, stream);
@@ -670,11 +734,14 @@ static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work
   F.from_state = 1;
   F.h_k = A.h_k; F.h_v = A.h_v; F.chunk = A.chunk;
   F.gate = W.gate;
-  const int64_t gp = xcd_grid(static_cast<int64_t>(S) * A.h_k, ratio);
-  hipLaunchKernelGGL((chunk_prep_kernel<D>), dim3(static_cast<unsigned>(gp)), dim3(256), 0, stream, F, W.ws);
+  // grids sized for a few slots at a chunk start (the usual case); the workgroups take the listed
+  // slots' items in turn, so more slots only take more turns
+  const int64_t np = static_cast<int64_t>(S) * A.h_v, ns = np * (D / M::NS);
+  const unsigned gp = static_cast<unsigned>(np < kR2ListGrid ? np : kR2ListGrid);
+  const unsigned gs = static_cast<unsigned>(ns < kR2ListGrid ? ns : kR2ListGrid);
+  hipLaunchKernelGGL((chunk_prep_list_kernel<D>), dim3(gp), dim3(256), 0, stream, F, W.ws, W.list, W.count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t gs = xcd_grid(static_cast<int64_t>(S) * A.h_k, ratio * (D / M::NS));
-  hipLaunchKernelGGL((chunk_state_kernel<D>), dim3(static_cast<unsigned>(gs)), dim3(256), 0, stream, F, W.ws, 1);
+  hipLaunchKernelGGL((chunk_state_list_kernel<D>), dim3(gs), dim3(256), 0, stream, F, W.ws, 1, W.list, W.count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the token from that state (recorded at the chunk start), positions advanced, then the ring
   DecodeArgs B = A;
