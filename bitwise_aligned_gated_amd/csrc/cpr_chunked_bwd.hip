@@ -30,8 +30,12 @@ namespace cpr {
 template <int D>
 struct alignas(16) IntraLds {
   using M = ChunkCfg<D>;
+  static constexpr int KS = D + 8;                            // bf16 row stride of the K rows
   float pm[M::L * M::SF];       // (M . Q K^T)^T, then N . K K^T
-  __bf16 dt[D * M::ST];         // dO^T (zero past the chunk)
+  union {
+    __bf16 dt[D * M::ST];       // dO^T (zero past the chunk)
+    __bf16 kr[M::L * KS];       // then the K rows (zero past the chunk)
+  };
   double lgd[M::L + 1];
 };
 
@@ -138,26 +142,42 @@ __global__ void __launch_bounds__(256) nbwd_intra_kernel(BackwardArgs A) {
       }
   }
   __syncthreads();
-  // w = V - diag(Gam) K S_0 - (N . K K^T) C, one 16-column tile at a time
+  // w = V - diag(Gam) K S_0 - (N . K K^T) C.  Each wave takes whole 16-column tiles over all 64 rows,
+  // so the block reads S_0 and C^T once: the tile's S_0 and C^T fragments are split once and used for
+  // the four row blocks, whose K rows come from LDS.
+  constexpr int KS = IntraLds<D>::KS;
+  for (int e = tid; e < L * (D / 8); e += 256) {              // dO^T is no longer read
+    const int t = e / (D / 8), c8 = e % (D / 8);
+    bf16x8 x = {};
+    if (t < n) x = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+    *reinterpret_cast<bf16x8*>(&S.kr[t * KS + 8 * c8]) = x;
+  }
+  __syncthreads();
   const float* s0 = A.chunk_states + (w * A.h_v + h) * static_cast<int64_t>(D) * D;   // S^T [column][d]
   const float* ctw = wsb + 2 * M::WS_MAT;                                              // C^T [D][L]
 #pragma unroll 1
-  for (int nt = 0; nt < NT; ++nt) {
-    f32x4c acc = {};
+  for (int nt = wave; nt < NT; nt += 4) {
+    Split sf[D / 32], cf[L / 32];
 #pragma unroll
-    for (int p = 0; p < D / 32; ++p) acc = mma_split_b(kf[p], frag_f32(s0 + (16 * nt + lj) * D + 32 * p + 8 * lg), acc);
+    for (int p = 0; p < D / 32; ++p) sf[p] = frag_f32(s0 + (16 * nt + lj) * D + 32 * p + 8 * lg);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] *= __expf(static_cast<float>(S.lgd[16 * wave + 4 * lg + r + 1]));
+    for (int p = 0; p < L / 32; ++p) cf[p] = frag_f32(ctw + (16 * nt + lj) * L + 32 * p + 8 * lg);
+#pragma unroll 1
+    for (int rb = 0; rb < L / 16; ++rb) {
+      f32x4c acc = {};
 #pragma unroll
-    for (int p = 0; p < L / 32; ++p)
-      acc = mma_split(frag_f32(&S.pm[row * SF + 32 * p + 8 * lg]), frag_f32(ctw + (16 * nt + lj) * L + 32 * p + 8 * lg),
-                      acc);
+      for (int p = 0; p < D / 32; ++p) acc = mma_split_b(frag_bf16(&S.kr[(16 * rb + lj) * KS + 32 * p + 8 * lg]), sf[p], acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * lg + r;
-      if (t < n) {
-        const int64_t e = ((tok + t) * A.h_v + h) * D + 16 * nt + lj;
-        A.ww[e] = static_cast<float>(vin[e]) - acc[r];
+      for (int r = 0; r < 4; ++r) acc[r] *= __expf(static_cast<float>(S.lgd[16 * rb + 4 * lg + r + 1]));
+#pragma unroll
+      for (int p = 0; p < L / 32; ++p) acc = mma_split(frag_f32(&S.pm[(16 * rb + lj) * SF + 32 * p + 8 * lg]), cf[p], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * rb + 4 * lg + r;
+        if (t < n) {
+          const int64_t e = ((tok + t) * A.h_v + h) * D + 16 * nt + lj;
+          A.ww[e] = static_cast<float>(vin[e]) - acc[r];
+        }
       }
     }
   }
@@ -173,6 +193,61 @@ struct alignas(16) BwdStateLds {
   __bf16 qt[D * M::ST];         // Q^T of the chunk
   double lgd[M::L + 1];
 };
+
+// One chunk's inputs of the chain that do not depend on G, loaded a chunk ahead into registers.
+template <int D>
+struct BwdRegs {
+  using M = ChunkCfg<D>;
+  static constexpr int QU = ((M::L / 2) * (D / 8) + 255) / 256;   // token pairs of 8 Q columns per thread
+  bf16x8 q[2 * QU];
+  bf16x8 k[D / 32];                                            // this lane's K row, as A fragments
+  float ri[M::NS / 16][4];                                     // R's intra part at this lane's positions
+  float dov[M::NS / 16][4];                                    // dO there
+  double lg;                                                   // lgd[tid] (threads 0..L)
+};
+
+template <int D>
+__device__ __forceinline__ void bwd_fetch(const BackwardArgs& A, const SeqMeta& m, int64_t row0, int64_t c, int h,
+                                          int kh, int j0, BwdRegs<D>& R) {
+  using M = ChunkCfg<D>;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane & 15, lg = lane >> 4;
+  const int row = 16 * wave + lj;
+  int t0, t1;
+  chunk_range(m, c, A.chunk, &t0, &t1);
+  const int n = t1 - t0;
+  const int64_t tok = m.tok0 + t0;
+  const __bf16* qin = static_cast<const __bf16*>(A.q);
+  const __bf16* kin = static_cast<const __bf16*>(A.k);
+  const __bf16* din = static_cast<const __bf16*>(A.d_o);
+#pragma unroll
+  for (int x = 0; x < BwdRegs<D>::QU; ++x) {
+    const int e = tid + 256 * x, t = 2 * (e % (M::L / 2)), c8 = e / (M::L / 2);
+    R.q[2 * x] = R.q[2 * x + 1] = bf16x8{};
+    if (e < (M::L / 2) * (D / 8)) {
+      if (t < n) R.q[2 * x] = *reinterpret_cast<const bf16x8*>(qin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+      if (t + 1 < n) R.q[2 * x + 1] = *reinterpret_cast<const bf16x8*>(qin + ((tok + t + 1) * A.h_k + kh) * D + 8 * c8);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < D / 32; ++p) {
+    R.k[p] = bf16x8{};
+    if (row < n) R.k[p] = *reinterpret_cast<const bf16x8*>(kin + ((tok + row) * A.h_k + kh) * D + 32 * p + 8 * lg);
+  }
+#pragma unroll
+  for (int nt = 0; nt < M::NS / 16; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * lg + r;
+      R.ri[nt][r] = R.dov[nt][r] = 0.f;
+      if (t < n) {
+        const int64_t e = ((tok + t) * A.h_v + h) * D + j0 + 16 * nt + lj;
+        R.ri[nt][r] = A.dc[e];
+        R.dov[nt][r] = static_cast<float>(din[e]);
+      }
+    }
+  const float* wsb = A.fws + ((row0 + c) * A.h_v + h) * chunk_ws_floats<D>();
+  R.lg = tid <= M::L ? reinterpret_cast<const double*>(wsb + 3 * M::WS_MAT)[tid] : 0.0;
+}
 
 template <int D>
 __host__ __device__ constexpr int bwd_state_parts() {
@@ -198,9 +273,6 @@ __global__ void __launch_bounds__(256) nbwd_state_kernel(BackwardArgs A) {
   const int row = 16 * wave + lj;
   const int64_t plane = static_cast<int64_t>(D) * D;
   const int j0 = sl * NS;
-  const __bf16* qin = static_cast<const __bf16*>(A.q);
-  const __bf16* kin = static_cast<const __bf16*>(A.k);
-  const __bf16* din = static_cast<const __bf16*>(A.d_o);
   const int64_t nrows = row0 + m.nrows <= A.rows_cap ? m.nrows : (A.rows_cap > row0 ? A.rows_cap - row0 : 0);
   // G at the last token: dL/dS_T, or zero
   for (int e = tid; e < NS * D / 4; e += 256) {
@@ -221,28 +293,45 @@ __global__ void __launch_bounds__(256) nbwd_state_kernel(BackwardArgs A) {
     }
   };
   store_g(brow0 + nrows);
+  BwdRegs<D> R;
+  if (nrows > 0) bwd_fetch<D>(A, m, row0, nrows - 1, h, kh, j0, R);
   for (int64_t c = nrows - 1; c >= 0; --c) {
     const int64_t wr = row0 + c;
     int t0, t1;
     chunk_range(m, c, A.chunk, &t0, &t1);
     const int n = t1 - t0;
     const int64_t tok = m.tok0 + t0;
-    const float* wsb = A.fws + (wr * A.h_v + h) * chunk_ws_floats<D>();
     const float* bwb = A.fbw + (wr * A.h_v + h) * chunk_bwd_floats<D>();
-    if (tid <= L) S.lgd[tid] = reinterpret_cast<const double*>(wsb + 3 * M::WS_MAT)[tid];
-    stage_transposed<D, ST>(S.qt, qin + kh * D, tok, static_cast<int64_t>(A.h_k) * D, n);
+    // commit the fetched Q^T (two consecutive tokens per thread: 32-bit stores) and log products
+#pragma unroll
+    for (int x = 0; x < BwdRegs<D>::QU; ++x) {
+      const int e = tid + 256 * x, tp = e % (L / 2), c8 = e / (L / 2);
+      if (e < (L / 2) * (D / 8)) {
+#pragma unroll
+        for (int y = 0; y < 8; ++y) {
+          __bf16 pr[2] = {R.q[2 * x][y], R.q[2 * x + 1][y]};
+          *reinterpret_cast<unsigned*>(&S.qt[(8 * c8 + y) * ST + 2 * tp]) = __builtin_bit_cast(unsigned, pr);
+        }
+      }
+    }
+    if (tid <= L) S.lgd[tid] = R.lg;
+    // this chunk's T^T row fragments, in flight through the R step
+    float4 tt[L / 32][2];
+#pragma unroll
+    for (int p = 0; p < L / 32; ++p) {
+      const float4* src = reinterpret_cast<const float4*>(bwb + row * L + 32 * p + 8 * lg);
+      tt[p][0] = src[0];
+      tt[p][1] = src[1];
+    }
     __syncthreads();
-    // R = (the intra part, from the dc buffer) + diag(Gam_L / Gam) K G_L; R^T and (diag(Gam) dO)^T to LDS
+    // R = (the intra part) + diag(Gam_L / Gam) K G_L; R^T and (diag(Gam) dO)^T to LDS
     {
       f32x4c acc[NS / 16] = {};
 #pragma unroll
-      for (int p = 0; p < D / 32; ++p) {
-        bf16x8 kf = {};
-        if (row < n) kf = *reinterpret_cast<const bf16x8*>(kin + ((tok + row) * A.h_k + kh) * D + 32 * p + 8 * lg);
+      for (int p = 0; p < D / 32; ++p)
 #pragma unroll
         for (int nt = 0; nt < NS / 16; ++nt)
-          acc[nt] = mma_split_b(kf, frag_f32(&S.gt[(16 * nt + lj) * SS + 32 * p + 8 * lg]), acc[nt]);
-      }
+          acc[nt] = mma_split_b(R.k[p], frag_f32(&S.gt[(16 * nt + lj) * SS + 32 * p + 8 * lg]), acc[nt]);
       const double lgL = S.lgd[n];
 #pragma unroll
       for (int nt = 0; nt < NS / 16; ++nt)
@@ -251,21 +340,21 @@ __global__ void __launch_bounds__(256) nbwd_state_kernel(BackwardArgs A) {
           const int t = 16 * wave + 4 * lg + r, jj = 16 * nt + lj;
           float rv = 0.f, ov = 0.f;
           if (t < n) {
-            const int64_t e = ((tok + t) * A.h_v + h) * D + j0 + jj;
-            rv = A.dc[e] + __expf(static_cast<float>(lgL - S.lgd[t + 1])) * acc[nt][r];
-            ov = __expf(static_cast<float>(S.lgd[t + 1])) * static_cast<float>(din[e]);
+            rv = R.ri[nt][r] + __expf(static_cast<float>(lgL - S.lgd[t + 1])) * acc[nt][r];
+            ov = __expf(static_cast<float>(S.lgd[t + 1])) * R.dov[nt][r];
           }
           S.rt[jj * SF + t] = rv;
           S.ot[jj * SF + t] = ov;
         }
     }
     __syncthreads();
-    // dC = T^T R -> the dc buffer (the same elements this thread read above)
+    if (c > 0) bwd_fetch<D>(A, m, row0, c - 1, h, kh, j0, R);  // the next chunk's inputs, in flight
+    // dC = T^T R -> the dc buffer (the same elements this thread read as R's intra part)
     {
       f32x4c acc[NS / 16] = {};
 #pragma unroll
       for (int p = 0; p < L / 32; ++p) {
-        const Split af = frag_f32(bwb + row * L + 32 * p + 8 * lg);
+        const Split af = split8(tt[p][0], tt[p][1]);
 #pragma unroll
         for (int nt = 0; nt < NS / 16; ++nt)
           acc[nt] = mma_split(af, frag_f32(&S.rt[(16 * nt + lj) * SF + 32 * p + 8 * lg]), acc[nt]);
@@ -287,6 +376,9 @@ __global__ void __launch_bounds__(256) nbwd_state_kernel(BackwardArgs A) {
     for (int q = 0; q < TILES / 4; ++q) {
       const int tile = wave * (TILES / 4) + q;
       const int jt = tile / (D / 16), dt = tile % (D / 16);
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = s0[static_cast<int64_t>(j0 + 16 * jt + 4 * lg + r) * D + 16 * dt + lj];
       f32x4c u = {}, v = {};
 #pragma unroll
       for (int p = 0; p < L / 32; ++p) {
@@ -297,11 +389,10 @@ __global__ void __launch_bounds__(256) nbwd_state_kernel(BackwardArgs A) {
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int jj = 16 * jt + 4 * lg + r, d = 16 * dt + lj;
-        float& g = S.gt[jj * SS + d];
+        float& g = S.gt[(16 * jt + 4 * lg + r) * SS + 16 * dt + lj];
         const float ng = __builtin_fmaf(gL, g, u[r] - v[r]);
         g = ng;
-        hp = __builtin_fma(static_cast<double>(ng), static_cast<double>(s0[static_cast<int64_t>(j0 + jj) * D + d]), hp);
+        hp = __builtin_fma(static_cast<double>(ng), static_cast<double>(sv[r]), hp);
       }
     }
 #pragma unroll
