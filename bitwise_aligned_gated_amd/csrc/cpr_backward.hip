@@ -5,7 +5,7 @@
 // differentiation of the recurrence
 //     u_t = S_{t-1}^T k_t,  w_t = v_t - a_t u_t,  c_t = b_t w_t,  S_t = a_t S_{t-1} + k_t c_t^T,
 //     o_t = S_t^T q_t,
-// evaluated in three kernels over the forward's stash of chunk-start states.
+// evaluated in four kernels over the forward's stash of chunk-start states.
 //
 // adjoint (column-parallel, one token at a time, last token first)
 //     G = dL/dS satisfies G_{t-1} = a_t (I - b_t k_t k_t^T) Ghat_t with Ghat_t = G_t + q_t dO_t^T;
@@ -16,6 +16,8 @@
 //     the forward step of the shared pinned schedule from the stashed chunk-start state, writing
 //     c_t and w_t for every token: the same bits the forward computed.  Skipped when the trainer
 //     forward kept them.
+// per-token gradients (streaming, D/8 lanes per (token, value head))
+//     dv_t = b_t dc_t, db_t = dc_t . w_t and v_t . dv_t for the h recurrence below.
 // chunk gradients (matrix cores, one workgroup per (chunk, key head))
 //     Inside a chunk with gate products Gam_t = a_1 ... a_t, every state and adjoint is the
 //     chunk-start (or chunk-end) matrix plus rank-one terms, so with dU_t = -a_t b_t dc_t

@@ -401,13 +401,15 @@ int gdn_prefill_chunked(gdn_state* st, const int32_t* cu_seqlens, int32_t num_se
  *   dq_t = S_t dO_t,  dc = Gh^T k_t,  dw = b_t dc,  du = -a_t dw,  dv_t = dw,  db_t = <dc, w_t>,
  *   dk_t = Gh c_t + S_{t-1} du,  da_t = <Gh, S_{t-1}> - <dw, u_t>,  G <- a_t Gh + k_t du^T,
  * and dL/dS_0 is G after the first token; dq and dk of a key head sum its value heads'.
- * Three kernels evaluate it: an adjoint pass walks each sequence backward (G needs no forward
- * state) and keeps dc for every token and G at every chunk boundary; a replay pass re-runs the
- * pinned forward step of every chunk from the stash and keeps c and w; a chunk-gradient pass,
- * one workgroup per (chunk, key head), forms dq and dk on fp32 matrix cores from the chunk-form
- * expansion of S_t and G_t (chunk-start or chunk-end matrix plus decay-weighted rank-one terms),
- * and da from a_t da_t = <G_{t-1}, S_{t-1}>, carried along the chunk in fp64.  Every sum has a
- * fixed order, so the gradients are bitwise reproducible for any batch composition or packing. */
+ * Four kernels evaluate it: an adjoint pass walks each sequence backward (G needs no forward
+ * state) and keeps dc for every token, G at every chunk boundary and <G, S> at every chunk start;
+ * a replay pass re-runs the pinned forward step of every chunk from the stash and keeps c and w
+ * (skipped when the trainer forward kept them); a per-token pass forms dv and db; a
+ * chunk-gradient pass, one workgroup per (chunk, key head), forms dq and dk on fp32 matrix cores
+ * from the chunk-form expansion of S_t and G_t (chunk-start or chunk-end matrix plus
+ * decay-weighted rank-one terms), and da from a_t da_t = <G_{t-1}, S_{t-1}>, carried along the
+ * chunk in fp64.  Every sum has a fixed order, so the gradients are bitwise reproducible for any
+ * batch composition or packing. */
 
 /* Workspace bytes gdn_backward needs for total_tokens tokens in num_seqs sequences (-1 on bad
  * input): dL/dS at every boundary of the gradient chunks (total_tokens / C' + 2 num_seqs states;
@@ -448,9 +450,10 @@ int64_t gdn_backward_workspace_bytes(const gdn_policy* policy, int64_t total_tok
  *   d_state0      device fp32 [num_seqs][H_v][d_v][d_k] or NULL: dL/dS_0 (for a forward that
  *                 continued from slots).
  *   workspace     device, 16-byte aligned, workspace_bytes >= gdn_backward_workspace_bytes().
- * Outputs are fully overwritten for every token of every well-formed sequence.  Three kernels on
- * `stream` (after the stash rebuild when C > 64); events: NULL, or 4 hipEvent_t recorded
- * before, between and after those three. */
+ * Outputs are fully overwritten for every token of every well-formed sequence.  Up to four kernels
+ * on `stream` (after the stash rebuild when C != 64 with fp32 boundaries); events: NULL, or 4
+ * hipEvent_t recorded before the adjoint, after it, after the replay and per-token pass, and at
+ * the end. */
 int gdn_backward(const gdn_policy* policy, const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                  const void* q, const void* k, const void* v, const float* a, const float* b,
                  const float* chunk_states, int64_t chunk_state_rows, const float* cw, const void* d_o,
