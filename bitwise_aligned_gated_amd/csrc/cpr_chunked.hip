@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(256) chunk_prep_list_kernel(PrefillArgs A, flo
   __shared__ PrepLds<D> S;
   __shared__ int64_t red[6];
   const int ratio = A.h_v / A.h_k;
-  const int64_t items = static_cast<int64_t>(*count) * A.h_v;
+  const int64_t items = static_cast<int64_t>(*count < A.num_seqs ? *count : A.num_seqs) * A.h_v;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int h = static_cast<int>(it % A.h_v);
     prep_item<D>(A, ws, S, red, list[it / A.h_v], h / ratio, h);
@@ -427,7 +427,7 @@ __global__ void __launch_bounds__(256) chunk_state_list_kernel(PrefillArgs A, fl
   __shared__ int64_t red[6];
   const int ratio = A.h_v / A.h_k;
   const int64_t per = static_cast<int64_t>(A.h_v) * NSL;
-  const int64_t items = static_cast<int64_t>(*count) * per;
+  const int64_t items = static_cast<int64_t>(*count < A.num_seqs ? *count : A.num_seqs) * per;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int r = static_cast<int>(it % per), h = r / NSL;
     state_item<D>(A, ws, write_final, S, red, list[it / per], h / ratio, h, r % NSL);
@@ -629,7 +629,8 @@ __global__ void r2_gate_kernel(R2Work W, const int32_t* slot_ids, int batch, con
   const int64_t p = pos[s];
   if (p > 0 && p % chunk == 0) {
     W.gate[s] = 1;
-    W.list[atomicAdd(W.count, 1)] = s;
+    const int idx = atomicAdd(W.count, 1);
+    if (idx < num_slots) W.list[idx] = s;                     // a slot listed twice could overflow it
   }
 }
 
