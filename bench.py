@@ -190,6 +190,30 @@ def normwise_t(got, ref) -> float:
     return float(torch.linalg.vector_norm(g - r)) / den if den > 0 else float(torch.linalg.vector_norm(g))
 
 
+def prefill_bytes(lengths, h_k, h_v, dk, dv, chunk, io=2):
+    """HBM bytes of a two-pass prefill from zero states over sequences of the given lengths.
+    Returns (algorithmic, c stash one way, pass 1 as built, pass 2 as built):
+      algorithmic  the I/O (q, k per key head, v, a, b read; o and the final states written), pass
+                   1's second read of k, v, a, b for the tokens before each sequence's last chunk
+                   start, and every chunk-start state after a sequence's first written once and read
+                   once;
+      c stash      every token's c (fp32), written by pass 1 and read by pass 2 in this build;
+      pass 1 / 2   what each kernel moves as built: pass 1 reads k, v, a, b of every token and writes
+                   every chunk-start row and the c stash; pass 2 reads q, k, a, every row and the
+                   stash and writes o and the final states."""
+    n, B = sum(lengths), len(lengths)
+    n_rows = sum(0 if L == 0 else 1 + (L - 1) // chunk for L in lengths)
+    plane = h_v * dk * dv * 4
+    tok_kvab = h_k * dk * io + h_v * dv * io + 2 * h_v * 4
+    io_bytes = n * (2 * h_k * dk * io + 2 * h_v * dv * io + 2 * h_v * 4) + B * plane
+    p1_tokens = sum(max(0, ((L - 1) // chunk) * chunk) for L in lengths if L > 0)
+    alg = io_bytes + p1_tokens * tok_kvab + 2 * (n_rows - B) * plane
+    c_bytes = n * h_v * dv * 4
+    pass1 = n * tok_kvab + n_rows * plane + c_bytes
+    pass2 = n * (2 * h_k * dk * io + h_v * 4) + n_rows * plane + c_bytes + n * h_v * dv * io + B * plane
+    return alg, c_bytes, pass1, pass2
+
+
 def decode_bytes(batch, h_k, h_v, dk, dv, io_bytes=2):
     """Algorithmic HBM bytes of one decode step: the state read and written once, the token's
     q, k (per key head), v, a, b read and o written."""
@@ -325,19 +349,8 @@ def main():
     # sequence's last chunk start, and every chunk-start state after the first written once and read
     # once.  The c stash this build adds (each token's c written by pass 1 and read by pass 2) is a
     # trade of bytes for pass-2 arithmetic, not algorithmic traffic: its bytes are reported apart.
-    io = 2
-    lens = [int(l) for l in x.lengths]
-    n_rows = int(cpr.gdn_chunk_rows(x.cu_seqlens, P.chunk)[-1])
-    plane = P.h_v * P.dk * P.dv * 4
-    tok_kvab = P.h_k * P.dk * io + P.h_v * P.dv * io + 2 * P.h_v * 4
-    io_bytes = N * (2 * P.h_k * P.dk * io + 2 * P.h_v * P.dv * io + 2 * P.h_v * 4) + B * plane
-    p1_tokens = sum(max(0, ((L - 1) // P.chunk) * P.chunk) for L in lens if L > 0)
-    alg_bytes = io_bytes + p1_tokens * tok_kvab + 2 * (n_rows - B) * plane
-    c_bytes = N * P.h_v * P.dv * 4
-    # what this path moves per pass (its own count, with the stash and pass 1 over every token)
-    pass1_bytes = N * tok_kvab + n_rows * plane + c_bytes
-    pass2_bytes = N * (2 * P.h_k * P.dk * io + P.h_v * 4) + n_rows * plane + c_bytes + N * P.h_v * P.dv * io \
-        + B * plane
+    alg_bytes, c_bytes, pass1_bytes, pass2_bytes = prefill_bytes([int(l) for l in x.lengths], P.h_k, P.h_v,
+                                                                  P.dk, P.dv, P.chunk)
     kernels["boundary_pass"]["bytes"] = int(pass1_bytes)
     kernels["output_pass"]["bytes"] = int(pass2_bytes)
     prefill_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
