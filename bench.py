@@ -751,6 +751,32 @@ def main():
         pool.close()
         pool.join()
 
+    # The pages' per-layer table (native mixed / recurrent everywhere / CPR), measured here.
+    def _pick(d, *keys):
+        for key in keys:
+            d = d.get(key) if isinstance(d, dict) else None
+        return d
+
+    def _row(native, recurrent, cpr_, unit):
+        row = {"unit": unit, "native": native, "recurrent_everywhere": recurrent, "cpr": cpr_}
+        for name, val in (("recurrent_over_native", recurrent), ("cpr_over_native", cpr_)):
+            row[name] = round(val / native, 3) if native and val else None
+        return row
+
+    table = {
+        "rollout_prefill_5x2048": _row(_pick(chunked, "native", "ms_per_step"), _pick(fused, "ms_per_step"),
+                                       round(ms_step, 4), "ms"),
+        "rollout_decode_256x1": _row(_pick(decode, "us_per_step_median"), _pick(decode, "us_per_step_median"),
+                                     _pick(decode, "with_boundary_record", "us_per_step_median"), "us"),
+        "trainer_fwd_bwd_10240": _row(_pick(trainer, "native_chunked", "ms_per_step"), None,
+                                      _pick(trainer, "ms_per_step"), "ms"),
+        "note": "native = the chunk form on matrix cores (prefill, trainer) and the plain recurrent step "
+                "(decode); recurrent everywhere = the one-pass recurrent prefill (the same bits as CPR here) "
+                "and the same decode step; CPR decode = the step committing every chunk start to the "
+                "boundary record (reading R1; decode.r2_reading is R2's). No separate recurrent-everywhere "
+                "trainer is built: CPR's backward already runs the adjoint token by token.",
+    }
+
     out = {
         "metric": METRIC, "value": round(N / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -777,8 +803,11 @@ def main():
         "environment": {"gpu": torch.cuda.get_device_name(0),
                         "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
                         "hip": torch.version.hip, "torch": torch.__version__, **host_env},
-        "context": {"h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "prefill_5x2048_native": 0.844,
+        "context": {"table_mi355x": table,
+                    "h100_per_layer_ms": {"prefill_5x2048_cpr": 1.412, "prefill_5x2048_native": 0.844,
                                           "decode_256x1_cpr": 0.0846, "decode_256x1_native": 0.0612,
+                                          "decode_256x1_recurrent": 0.0612, "prefill_5x2048_recurrent": 3.639,
+                                          "trainer_fwd_bwd_10240_recurrent": 22.863,
                                           "trainer_fwd_bwd_10240_cpr": 7.386, "trainer_fwd_bwd_10240_native": 5.177},
                     "note": "pages' H100 figures; head layout not stated there"},
     }
