@@ -440,13 +440,24 @@ template <int D>
 struct alignas(16) OutLds {
   using M = ChunkCfg<D>;
   float qk[M::L * M::SF];       // M . Q K^T
+  __bf16 q[M::L * M::SB];       // Q rows (zero past the chunk)
+  __bf16 k[M::L * M::SB];       // K rows (zero past the chunk)
   double lgd[M::L + 1];
 };
 
+// One workgroup per (chunk row, value head).  Wave w first forms rows [16 w, 16 w + 16) of
+// M . Q K^T; then the 4 D/16 (row block, column tile) output tiles are dealt out so that each
+// wave owns whole column tiles (D >= 64) or half of one (D = 32): the S_0 and C^T fragments of a
+// column tile are read from memory by one wave only, once (the first tile's before anything
+// else, so that those loads overlap the staging and M . Q K^T), and Q, K and M . Q K^T come from
+// LDS.
+// Each output element's products run in one fixed order (Q S_0 over the D/32 blocks, the row's
+// Gam, then (M . Q K^T) C) whichever wave forms it, so the bits do not depend on the mapping.
 template <int D>
 __global__ void __launch_bounds__(256) chunk_output_kernel(PrefillArgs A, const float* ws) {
   using M = ChunkCfg<D>;
-  constexpr int L = M::L, SF = M::SF, NT = D / 16;
+  constexpr int L = M::L, SF = M::SF, SB = M::SB, NT = D / 16;
+  static_assert(NT % 2 == 0, "column tiles");
   __shared__ OutLds<D> S;
   __shared__ int64_t red[6];
   const int ratio = A.h_v / A.h_k;
@@ -468,28 +479,39 @@ __global__ void __launch_bounds__(256) chunk_output_kernel(PrefillArgs A, const 
   const __bf16* kin = static_cast<const __bf16*>(A.k);
   const float* wsb = ws + (w * A.h_v + h) * chunk_ws_floats<D>();
   const double* lgw = reinterpret_cast<const double*>(wsb + 3 * M::WS_MAT);
-  for (int e = tid; e <= L; e += 256) S.lgd[e] = lgw[e];
-  const int row = 16 * wave + lj;                              // this lane's A row
-  // Q fragments of this lane's row (exact bf16; zero past the chunk)
-  bf16x8 qf[D / 32];
+  const float* s0 = A.chunk_states + (w * A.h_v + h) * static_cast<int64_t>(D) * D;
+  const float* ctw = wsb + 2 * M::WS_MAT;                      // C^T [D][L]
+  Split sf[D / 32], cf[L / 32];                                // S_0 and C^T fragments of a column tile
+  auto fetch_tile = [&](int nt) {
 #pragma unroll
-  for (int p = 0; p < D / 32; ++p) {
-    qf[p] = bf16x8{};
-    if (row < n) qf[p] = *reinterpret_cast<const bf16x8*>(qin + ((tok + row) * A.h_k + kh) * D + 32 * p + 8 * lg);
+    for (int p = 0; p < D / 32; ++p) sf[p] = frag_f32(s0 + (16 * nt + lj) * D + 32 * p + 8 * lg);
+#pragma unroll
+    for (int p = 0; p < L / 32; ++p) cf[p] = frag_f32(ctw + (16 * nt + lj) * L + 32 * p + 8 * lg);
+  };
+  fetch_tile(wave * NT / 4);
+  for (int e = tid; e <= L; e += 256) S.lgd[e] = lgw[e];
+  // Q and K rows to LDS (exact bf16; zero past the chunk), 8 values per unit
+  for (int e = tid; e < L * (D / 8); e += 256) {
+    const int t = e / (D / 8), c8 = e % (D / 8);
+    bf16x8 x = {}, y = {};
+    if (t < n) {
+      x = *reinterpret_cast<const bf16x8*>(qin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+      y = *reinterpret_cast<const bf16x8*>(kin + ((tok + t) * A.h_k + kh) * D + 8 * c8);
+    }
+    *reinterpret_cast<bf16x8*>(&S.q[t * SB + 8 * c8]) = x;
+    *reinterpret_cast<bf16x8*>(&S.k[t * SB + 8 * c8]) = y;
   }
   __syncthreads();
-  // M . Q K^T -> LDS
+  // M . Q K^T -> LDS, rows of this wave's block
   {
+    const int row = 16 * wave + lj;
     f32x4c acc[4] = {};
 #pragma unroll
-    for (int p = 0; p < D / 32; ++p)
+    for (int p = 0; p < D / 32; ++p) {
+      const bf16x8 qf = frag_bf16(&S.q[row * SB + 32 * p + 8 * lg]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int s = 16 * nt + lj;
-        bf16x8 kf = {};
-        if (s < n) kf = *reinterpret_cast<const bf16x8*>(kin + ((tok + s) * A.h_k + kh) * D + 32 * p + 8 * lg);
-        acc[nt] = mma(qf[p], kf, acc[nt]);
-      }
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = mma(qf, frag_bf16(&S.k[(16 * nt + lj) * SB + 32 * p + 8 * lg]), acc[nt]);
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -501,23 +523,24 @@ __global__ void __launch_bounds__(256) chunk_output_kernel(PrefillArgs A, const 
       }
   }
   __syncthreads();
-  // O = diag(Gam) Q S_0 + (M . Q K^T) C
-  const float* s0 = A.chunk_states + (w * A.h_v + h) * static_cast<int64_t>(D) * D;
-  const float* ctw = wsb + 2 * M::WS_MAT;                      // C^T [D][L]
+  // O = diag(Gam) Q S_0 + (M . Q K^T) C: wave w takes tiles w NT .. w NT + NT - 1 of the 4 NT
+  // (column tile it / 4, row block it % 4)
   unsigned short* o = static_cast<unsigned short*>(A.o);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int k = 0; k < NT; ++k) {
+    const int it = wave * NT + k, nt = it / 4, rb = it % 4;
+    if (k > 0 && rb == 0) fetch_tile(nt);                      // this wave's next column tile
+    const int row = 16 * rb + lj;
     f32x4c acc = {};
 #pragma unroll
-    for (int p = 0; p < D / 32; ++p) acc = mma_split_b(qf[p], frag_f32(s0 + (16 * nt + lj) * D + 32 * p + 8 * lg), acc);
+    for (int p = 0; p < D / 32; ++p) acc = mma_split_b(frag_bf16(&S.q[row * SB + 32 * p + 8 * lg]), sf[p], acc);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] *= __expf(static_cast<float>(S.lgd[16 * wave + 4 * lg + r + 1]));
+    for (int r = 0; r < 4; ++r) acc[r] *= __expf(static_cast<float>(S.lgd[16 * rb + 4 * lg + r + 1]));
 #pragma unroll
-    for (int p = 0; p < L / 32; ++p)
-      acc = mma_split(frag_f32(&S.qk[row * SF + 32 * p + 8 * lg]), frag_f32(ctw + (16 * nt + lj) * L + 32 * p + 8 * lg), acc);
+    for (int p = 0; p < L / 32; ++p) acc = mma_split(frag_f32(&S.qk[row * SF + 32 * p + 8 * lg]), cf[p], acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * lg + r;
+      const int t = 16 * rb + 4 * lg + r;
       if (t < n) o[((tok + t) * A.h_v + h) * D + 16 * nt + lj] = f32_to_bf16_rne(acc[r]);
     }
   }
