@@ -112,6 +112,45 @@ __device__ __forceinline__ void stage_transposed(__bf16* dst, const __bf16* src,
   }
 }
 
+// stage_transposed in two steps: the loads into registers (issued early), then the transposed LDS
+// stores (once the destination is free).  Same threads, units and values.
+template <int D>
+struct TransposedRegs {
+  static constexpr int U = ((64 / 2) * (D / 8) + 255) / 256;   // units (two tokens of 8 columns) per thread
+  bf16x8 x[2 * U];
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_transposed(TransposedRegs<D>& R, const __bf16* src, int64_t tok, int64_t stride,
+                                                 int n) {
+  constexpr int L = 64;
+#pragma unroll
+  for (int u = 0; u < TransposedRegs<D>::U; ++u) {
+    const int e = threadIdx.x + 256 * u, tp = e % (L / 2), c8 = e / (L / 2), t = 2 * tp;
+    R.x[2 * u] = R.x[2 * u + 1] = bf16x8{};
+    if (e < (L / 2) * (D / 8)) {
+      if (t < n) R.x[2 * u] = *reinterpret_cast<const bf16x8*>(src + (tok + t) * stride + 8 * c8);
+      if (t + 1 < n) R.x[2 * u + 1] = *reinterpret_cast<const bf16x8*>(src + (tok + t + 1) * stride + 8 * c8);
+    }
+  }
+}
+
+template <int D, int ST>
+__device__ __forceinline__ void commit_transposed(__bf16* dst, const TransposedRegs<D>& R) {
+  constexpr int L = 64;
+#pragma unroll
+  for (int u = 0; u < TransposedRegs<D>::U; ++u) {
+    const int e = threadIdx.x + 256 * u, tp = e % (L / 2), c8 = e / (L / 2), t = 2 * tp;
+    if (e < (L / 2) * (D / 8)) {
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        __bf16 pr[2] = {R.x[2 * u][y], R.x[2 * u + 1][y]};
+        *reinterpret_cast<unsigned*>(&dst[(8 * c8 + y) * ST + t]) = __builtin_bit_cast(unsigned, pr);
+      }
+    }
+  }
+}
+
 // What the chunkwise forward keeps for its backward, per (chunk row, value head), after the
 // workspace above: T^T [L][L] (T^T[t][s] = T[s][t]) and W^T [D][L], fp32.
 template <int D>

@@ -31,11 +31,11 @@ namespace cpr {
 template <int D>
 struct alignas(16) PrepLds {
   using M = ChunkCfg<D>;
-  __bf16 kt[D * M::ST];         // K^T (zero past the chunk)
   float am[M::L * M::SF];       // A, then T
   float tp[M::L * M::SF];       // T, then T diag(b Gam), then T diag(b)
   union {
     float ty[M::L * M::SF];     // blocked-inverse scratch
+    __bf16 kt[D * M::ST];       // then K^T (zero past the chunk)
     __bf16 vt[D * M::ST];       // then V^T
   };
   double lgd[M::L + 1];
@@ -67,8 +67,11 @@ __device__ __forceinline__ void prep_item(const PrefillArgs& A, float* ws, PrepL
   const __bf16* kin = static_cast<const __bf16*>(A.k);
   const __bf16* vin = static_cast<const __bf16*>(A.v);
 
-  // K^T (zero past the chunk), gates and their log products
-  stage_transposed<D, ST>(S.kt, kin + kh * D, tok, static_cast<int64_t>(A.h_k) * D, n);
+  // K^T and V^T (zero past the chunk) into registers, committed to LDS once the inverse is done
+  // with its scratch; gates and their log products
+  TransposedRegs<D> kreg, vreg;
+  fetch_transposed<D>(kreg, kin + kh * D, tok, static_cast<int64_t>(A.h_k) * D, n);
+  fetch_transposed<D>(vreg, vin + static_cast<int64_t>(h) * D, tok, static_cast<int64_t>(A.h_v) * D, n);
   if (tid < L) {
     float a = 1.f, b = 0.f;
     if (tid < n) {
@@ -161,14 +164,14 @@ __device__ __forceinline__ void prep_item(const PrefillArgs& A, float* ws, PrepL
     }
     __syncthreads();
   }
-  // keep T in am; tp = T diag(b Gam); V^T into the scratch's space (zero past the chunk)
+  // keep T in am; tp = T diag(b Gam); K^T into the scratch's space
   for (int e = tid; e < L * L; e += 256) {
     const int t = e / L, s = e % L;
     const float tv = S.tp[t * SF + s];
     S.am[t * SF + s] = tv;
     S.tp[t * SF + s] = tv * (S.bb[s] * __expf(static_cast<float>(S.lgd[s + 1])));
   }
-  stage_transposed<D, ST>(S.vt, vin + static_cast<int64_t>(h) * D, tok, static_cast<int64_t>(A.h_v) * D, n);
+  commit_transposed<D, ST>(S.kt, kreg);
   __syncthreads();
   float* wsb = ws + (w * A.h_v + h) * chunk_ws_floats<D>();
   float* bwb = A.chunk_bwd != nullptr ? A.chunk_bwd + (w * A.h_v + h) * chunk_bwd_floats<D>() : nullptr;
@@ -198,11 +201,12 @@ __device__ __forceinline__ void prep_item(const PrefillArgs& A, float* ws, PrepL
             make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
     }
     if (which == 0) {
-      __syncthreads();
+      __syncthreads();                                         // K^T and tp reads done
       for (int e = tid; e < L * L; e += 256) {
         const int t = e / L, s = e % L;
         S.tp[t * SF + s] = S.am[t * SF + s] * S.bb[s];
       }
+      commit_transposed<D, ST>(S.vt, vreg);                    // V^T over K^T
       __syncthreads();
     }
   }
