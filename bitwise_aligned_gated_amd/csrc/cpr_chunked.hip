@@ -106,13 +106,23 @@ __device__ __forceinline__ void prep_item(const PrefillArgs& A, float* ws, PrepL
         acc[nt] = mma(af, bfr, acc[nt]);
       }
     }
+    // the log products of this lane's rows and columns, read before any use (unconditional reads
+    // issue together)
+    double lrow[4], lcol[4];
+    float brow[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      lrow[x] = S.lgd[16 * wave + 4 * lg + x + 1];
+      brow[x] = S.bb[16 * wave + 4 * lg + x];
+      lcol[x] = S.lgd[16 * x + lj + 1];
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * wave + 4 * lg + r, rr = 16 * nt + lj;
         float v = 0.f;
-        if (rr < s && s < n) v = S.bb[s] * __expf(static_cast<float>(S.lgd[s + 1] - S.lgd[rr + 1])) * acc[nt][r];
+        if (rr < s && s < n) v = brow[r] * __expf(static_cast<float>(lrow[r] - lcol[nt])) * acc[nt][r];
         S.am[s * SF + rr] = v;
       }
   }
@@ -516,13 +526,19 @@ __global__ void __launch_bounds__(256) chunk_output_kernel(PrefillArgs A, const 
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[nt] = mma(qf, frag_bf16(&S.k[(16 * nt + lj) * SB + 32 * p + 8 * lg]), acc[nt]);
     }
+    double lrow[4], lcol[4];                                   // read before any use
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      lrow[x] = S.lgd[16 * wave + 4 * lg + x + 1];
+      lcol[x] = S.lgd[16 * x + lj + 1];
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wave + 4 * lg + r, s = 16 * nt + lj;
         float v = 0.f;
-        if (s <= t && t < n) v = __expf(static_cast<float>(S.lgd[t + 1] - S.lgd[s + 1])) * acc[nt][r];
+        if (s <= t && t < n) v = __expf(static_cast<float>(lrow[r] - lcol[nt])) * acc[nt][r];
         S.qk[t * SF + s] = v;
       }
   }

@@ -89,13 +89,19 @@ __global__ void __launch_bounds__(256) nbwd_intra_kernel(BackwardArgs A) {
         if (s < n) qf = *reinterpret_cast<const bf16x8*>(qin + ((tok + s) * A.h_k + kh) * D + 32 * p + 8 * lg);
         acc[nt] = mma(kf[p], qf, acc[nt]);
       }
+    double lrow[4], lcol[4];                                   // read before any use
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      lrow[x] = S.lgd[16 * wave + 4 * lg + x + 1];
+      lcol[x] = S.lgd[16 * x + lj + 1];
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wave + 4 * lg + r, s = 16 * nt + lj;
         float x = 0.f;
-        if (t <= s && s < n) x = __expf(static_cast<float>(S.lgd[s + 1] - S.lgd[t + 1])) * acc[nt][r];
+        if (t <= s && s < n) x = __expf(static_cast<float>(lcol[nt] - lrow[r])) * acc[nt][r];
         S.pm[t * SF + s] = x;
       }
   }
@@ -131,13 +137,19 @@ __global__ void __launch_bounds__(256) nbwd_intra_kernel(BackwardArgs A) {
         if (s < n) kb = *reinterpret_cast<const bf16x8*>(kin + ((tok + s) * A.h_k + kh) * D + 32 * p + 8 * lg);
         acc[nt] = mma(kf[p], kb, acc[nt]);
       }
+    double lrow[4], lcol[4];                                   // read before any use
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      lrow[x] = S.lgd[16 * wave + 4 * lg + x + 1];
+      lcol[x] = S.lgd[16 * x + lj + 1];
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wave + 4 * lg + r, s = 16 * nt + lj;
         float x = 0.f;
-        if (s < t && t < n) x = __expf(static_cast<float>(S.lgd[t + 1] - S.lgd[s + 1])) * acc[nt][r];
+        if (s < t && t < n) x = __expf(static_cast<float>(lrow[r] - lcol[nt])) * acc[nt][r];
         S.pm[t * SF + s] = x;
       }
   }
