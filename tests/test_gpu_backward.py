@@ -306,3 +306,19 @@ def test_trainer_forward_stash_gives_the_same_gradients(dim, io):
     torch.cuda.synchronize()
     for name in GRADS + ("d_state0",):
         assert sha(g1[name]) == sha(g2[name]), name
+
+
+@pytest.mark.parametrize("lens,chunk", [([0, 3, 0], 16), ([0, 0], 16), ([0, 0], 100)])
+def test_backward_empty_sequences(lens, chunk):
+    """Empty sequences: a sequence with no token passes dL/dS_T through to dL/dS_0 unchanged and its
+    neighbours are unaffected; a batch of empty sequences alone (also where C > 64 makes the
+    backward rebuild a 64-token stash) gives just that."""
+    x = gi.make_inputs(79, lens, h_k=2, h_v=4, dk=16, dv=16, chunk=chunk, io="f32")
+    ct = gi.make_cotangents(x, 80, with_d_state=True, with_s0=True)
+    say(f"backward, empty sequences {lens} C={chunk}")
+    cs = _forward(x, ct["s0"].to("cuda"))
+    g = _backward(x, ct, cs)
+    _compare_all(x, g, _oracle(x, ct))
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert sha(g["d_state0"][i]) == sha(ct["d_state"][i].to("cuda")), i

@@ -205,3 +205,20 @@ def test_chunked_trainer_10240_matches_oracle():
         _close(g["dk"][t0:t1, kh].cpu().double().numpy(), dk, f"seq {i} dk", stats)
     say("  worst normwise / max-abs over scale: " +
         ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in sorted(stats.items())))
+
+
+@pytest.mark.parametrize("lens", [[0, 3, 0], [0, 0]])
+def test_chunked_trainer_empty_sequences(lens):
+    """Empty sequences in the chunkwise trainer: a sequence with no token passes dL/dS_T through to
+    dL/dS_0 unchanged, its neighbours are unaffected, and a batch of empty sequences alone launches
+    nothing that touches a token."""
+    x = gi.make_inputs(77, lens, h_k=2, h_v=4, dk=32, dv=32, chunk=16, io="bf16")
+    ct = gi.make_cotangents(x, 78, with_d_state=True, with_s0=True)
+    say(f"chunked trainer, empty sequences {lens}")
+    _, _, cs, stash = _forward(x, ct["s0"].to("cuda"))
+    g = _backward(x, ct, cs, stash)
+    ref = _oracle(x, ct)
+    _compare_all(x, g, ref)
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert sha(g["d_state0"][i]) == sha(ct["d_state"][i].to("cuda")), i
