@@ -65,6 +65,7 @@ struct DecodeArgs {
   void* const* events;        // nullable: 2 hipEvent_t recorded around the step kernel
   int64_t grid_items;         // set per launch: the kernel's work items
   int64_t max_wgs;            // 0: one workgroup per item; else at most this many, taking items in turn
+  int32_t skip_advance;       // 1: leave the positions to a later kernel (the R2 ring append)
 };
 
 // Gradients of a forward that started every sequence at position 0 (the trainer's case).

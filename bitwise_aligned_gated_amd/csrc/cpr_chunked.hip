@@ -649,59 +649,75 @@ static R2Work r2_work(void* work, int num_slots) {
   return w;
 }
 
-// The one-chunk batch over every slot, nobody gated in yet.
-__global__ void r2_batch_kernel(R2Work W, int num_slots, int chunk) {
-  const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s == 0) *W.count = 0;
-  if (s > num_slots) return;
-  W.cu[s] = s * chunk;
-  if (s == num_slots) return;
-  W.ids[s] = s;
-  W.gate[s] = 0;
-  W.vpos[s] = 0;
-}
+// The one-chunk batch over every slot, then the step's slots that stand at a chunk start with a
+// chunk behind them gated in and listed.  One workgroup: the list is built by a block scan in batch
+// order, so it needs no atomics.
+constexpr int kR2PrepareThreads = 1024;
 
-// Gate in the listed slots that stand at a chunk start with a chunk behind them, and list them (the
-// list's order depends on the atomics' order, which decides only which workgroup takes a slot).
-__global__ void r2_gate_kernel(R2Work W, const int32_t* slot_ids, int batch, const int64_t* pos, int num_slots,
-                               int chunk) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= batch) return;
-  const int32_t s = slot_ids[j];
-  if (s < 0 || s >= num_slots) return;
-  const int64_t p = pos[s];
-  if (p > 0 && p % chunk == 0) {
-    W.gate[s] = 1;
-    const int idx = atomicAdd(W.count, 1);
-    if (idx < num_slots) W.list[idx] = s;                     // a slot listed twice could overflow it
+__global__ void __launch_bounds__(kR2PrepareThreads) r2_prepare_kernel(R2Work W, const int32_t* slot_ids, int batch,
+                                                                      const int64_t* pos, int num_slots, int chunk) {
+  __shared__ int64_t red[kR2PrepareThreads / 64 + 2];
+  for (int s = threadIdx.x; s <= num_slots; s += kR2PrepareThreads) {
+    W.cu[s] = s * chunk;
+    if (s < num_slots) {
+      W.ids[s] = s;
+      W.gate[s] = 0;
+      W.vpos[s] = 0;
+    }
   }
+  __syncthreads();                                            // every gate cleared before any is set
+  int64_t listed = 0;
+  for (int base = 0; base < batch; base += kR2PrepareThreads) {   // uniform across the block
+    const int j = base + static_cast<int>(threadIdx.x);
+    int32_t s = -1;
+    if (j < batch) {
+      s = slot_ids[j];
+      if (s < 0 || s >= num_slots) {
+        s = -1;
+      } else {
+        const int64_t p = pos[s];
+        if (!(p > 0 && p % chunk == 0)) s = -1;
+      }
+    }
+    int64_t total;
+    const int64_t at = listed + block_excl_scan_i64(s >= 0 ? 1 : 0, red, &total);
+    if (s >= 0) {
+      W.gate[s] = 1;
+      if (at < num_slots) W.list[at] = s;                     // a slot listed twice could overflow it
+    }
+    listed += total;
+  }
+  if (threadIdx.x == 0) *W.count = static_cast<int32_t>(listed < num_slots ? listed : num_slots);
 }
 
-// After the step (positions already advanced): each listed slot's token to ring position
-// (pos - 1) mod C.  One workgroup per batch entry.
+// After the step, which leaves the positions alone here: each listed slot's token to ring position
+// pos mod C, then its position advanced.  One workgroup per batch entry.
 template <int D>
 __global__ void __launch_bounds__(256) r2_ring_append_kernel(DecodeArgs A, RingParts R) {
   const int j = blockIdx.x;
   const int32_t s = A.slot_ids[j];
-  if (s < 0 || s >= A.num_slots) return;
-  const int64_t p = A.pos[s] - 1;
-  if (p < 0) return;
-  const int64_t dst = static_cast<int64_t>(s) * A.chunk + p % A.chunk;
-  const uint4* q = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.q) + static_cast<int64_t>(j) * A.h_k * D);
-  const uint4* k = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.k) + static_cast<int64_t>(j) * A.h_k * D);
-  const uint4* v = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.v) + static_cast<int64_t>(j) * A.h_v * D);
-  uint4* rq = reinterpret_cast<uint4*>(R.q + dst * A.h_k * D);
-  uint4* rk = reinterpret_cast<uint4*>(R.k + dst * A.h_k * D);
-  uint4* rv = reinterpret_cast<uint4*>(R.v + dst * A.h_v * D);
-  for (int e = threadIdx.x; e < A.h_k * D / 8; e += 256) {
-    rq[e] = q[e];
-    rk[e] = k[e];
+  if (s < 0 || s >= A.num_slots) return;                      // uniform across the block
+  const int64_t p = A.pos[s];
+  if (p >= 0) {
+    const int64_t dst = static_cast<int64_t>(s) * A.chunk + p % A.chunk;
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.q) + static_cast<int64_t>(j) * A.h_k * D);
+    const uint4* k = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.k) + static_cast<int64_t>(j) * A.h_k * D);
+    const uint4* v = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(A.v) + static_cast<int64_t>(j) * A.h_v * D);
+    uint4* rq = reinterpret_cast<uint4*>(R.q + dst * A.h_k * D);
+    uint4* rk = reinterpret_cast<uint4*>(R.k + dst * A.h_k * D);
+    uint4* rv = reinterpret_cast<uint4*>(R.v + dst * A.h_v * D);
+    for (int e = threadIdx.x; e < A.h_k * D / 8; e += 256) {
+      rq[e] = q[e];
+      rk[e] = k[e];
+    }
+    for (int e = threadIdx.x; e < A.h_v * D / 8; e += 256) rv[e] = v[e];
+    for (int e = threadIdx.x; e < A.h_v; e += 256) {
+      R.a[dst * A.h_v + e] = A.a[static_cast<int64_t>(j) * A.h_v + e];
+      R.b[dst * A.h_v + e] = A.b[static_cast<int64_t>(j) * A.h_v + e];
+    }
   }
-  for (int e = threadIdx.x; e < A.h_v * D / 8; e += 256) rv[e] = v[e];
-  for (int e = threadIdx.x; e < A.h_v; e += 256) {
-    R.a[dst * A.h_v + e] = A.a[static_cast<int64_t>(j) * A.h_v + e];
-    R.b[dst * A.h_v + e] = A.b[static_cast<int64_t>(j) * A.h_v + e];
-  }
+  __syncthreads();                                            // every thread has read the position
+  if (threadIdx.x == 0) A.pos[s] = p + 1;
 }
 
 // After a chunked R2 prefill (before its position update): each sequence's tokens from the start
@@ -755,10 +771,8 @@ static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work
   const R2Work W = r2_work(work, S);
   hipError_t e = record_event(A.events, 0, stream);
   if (e != hipSuccess || A.batch == 0) return e != hipSuccess ? e : record_event(A.events, 1, stream);
-  hipLaunchKernelGGL(r2_batch_kernel, dim3((S + 1 + 255) / 256), dim3(256), 0, stream, W, S, A.chunk);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(r2_gate_kernel, dim3((A.batch + 255) / 256), dim3(256), 0, stream, W, A.slot_ids, A.batch, A.pos,
-                     S, A.chunk);
+  hipLaunchKernelGGL(r2_prepare_kernel, dim3(1), dim3(kR2PrepareThreads), 0, stream, W, A.slot_ids, A.batch, A.pos, S,
+                     A.chunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the chunk form over every gated slot's ring: recorded chunk-start state in, new one into the slot
   PrefillArgs F{};
@@ -787,9 +801,10 @@ static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((chunk_state_list_kernel<D>), dim3(gs), dim3(256), 0, stream, F, W.ws, 1, W.list, W.count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // the token from that state (recorded at the chunk start), positions advanced, then the ring
+  // the token from that state (recorded at the chunk start), then the ring and the positions
   DecodeArgs B = A;
   B.events = nullptr;
+  B.skip_advance = 1;
   if ((e = launch_decode(D, D, IO_BF16, B, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((r2_ring_append_kernel<D>), dim3(static_cast<unsigned>(A.batch)), dim3(256), 0, stream, A, R);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -184,7 +184,7 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
     e = launch_items(decode_step_kernel<DK, DV, IO>, decode_step_strided_kernel<DK, DV, IO>, items, Cfg::THREADS,
                      stream, A);
     if (e != hipSuccess) return e;
-    if (A.boundary != nullptr || A.round_boundary != 0) {
+    if ((A.boundary != nullptr || A.round_boundary != 0) && !A.skip_advance) {
       int64_t wgs = (static_cast<int64_t>(A.batch) + 255) / 256;
       if (A.max_wgs > 0 && A.max_wgs < wgs) wgs = A.max_wgs;
       hipLaunchKernelGGL(decode_advance_kernel, dim3(static_cast<unsigned>(wgs)), dim3(256), 0, stream, A);
