@@ -9,7 +9,8 @@ constexpr int kLeaf = 8;      // rows per leaf of the pinned dot product
 // order, which kernels a call launches).  The schedule fixes leaves and tree, so the mapping never
 // moves a bit; it enters only the deployment digest.  Raised with every change of a kernel's work
 // mapping (4: one-column-per-lane decode in state order with a separate position update, the
-// overlapped prefill, and the chunk-64 backward under fp32 boundaries).
-constexpr int kMappingVersion = 4;
+// overlapped prefill, and the chunk-64 backward under fp32 boundaries; 5: the chunk-form output
+// kernel with whole column tiles per wave, and the R2 decode step's four launches).
+constexpr int kMappingVersion = 5;
 
 }  // namespace cpr
