@@ -760,8 +760,9 @@ __global__ void __launch_bounds__(256) r2_ring_fill_kernel(PrefillArgs A, RingPa
   if (threadIdx.x == 0) boundary_pos[m.slot] = bpos;
 }
 
-// Workgroups of the list-driven chunk-form kernels in an R2 decode step: 256 (one per CU).
-constexpr int64_t kR2ListGrid = 256;
+// Workgroups of the list-driven chunk-form kernels in an R2 decode step, two per CU: a step's
+// usual few slots at a chunk start give a few hundred state-pass items, one turn each.
+constexpr int64_t kR2ListGrid = 512;
 
 template <int D>
 static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work, hipStream_t stream) {
