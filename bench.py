@@ -566,8 +566,8 @@ def main():
             "us_per_step_max": round(r2_us[-1], 2),
             "resyncs": starts,
             "note": "prompts by gdn_prefill_chunked(R2); each step runs the chunk form over the token ring of "
-                    "the slots at a chunk start (listed on the device; 512 workgroups take them in turn), then the "
-                    "pinned step; ring and workspace "
+                    "the slots at a chunk start (listed on the device; 512 workgroups take them in turn), then their "
+                    "pinned step, on a second stream beside the other slots' step; ring and workspace "
                     f"{(r2pool.r2_ring.numel() + r2pool.r2_workspace.numel()) / 2**20:.0f} MiB"}
         del r2pool, od2
 

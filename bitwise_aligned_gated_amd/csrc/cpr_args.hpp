@@ -66,6 +66,8 @@ struct DecodeArgs {
   int64_t grid_items;         // set per launch: the kernel's work items
   int64_t max_wgs;            // 0: one workgroup per item; else at most this many, taking items in turn
   int32_t skip_advance;       // 1: leave the positions to a later kernel (the R2 ring append)
+  const int32_t* skip_slot;   // nullable [num_slots]: a slot with skip_slot[slot] != 0 is stepped by a later
+                              //   launch (R2: the slots the chunk form resynchronises, on a second stream)
 };
 
 // Gradients of a forward that started every sequence at position 0 (the trainer's case).

@@ -619,13 +619,14 @@ struct R2Work {
   int32_t* gate;
   int64_t* vpos;
   int32_t* list;     // the slots gated in this step, in any order
+  int32_t* lent;     // their batch entries, in the same order
   int32_t* count;    // how many
   float* ws;
 };
 
 int64_t r2_workspace_bytes(int h_v, int d, int num_slots) {
   const int64_t S = num_slots;
-  return pad256((S + 1) * 4) + 2 * pad256(S * 4) + pad256(S * 8) + pad256(S * 4) + pad256(4) +
+  return pad256((S + 1) * 4) + 2 * pad256(S * 4) + pad256(S * 8) + 2 * pad256(S * 4) + pad256(4) +
          S * h_v * chunked_workspace_floats(d) * 4;
 }
 
@@ -642,6 +643,8 @@ static R2Work r2_work(void* work, int num_slots) {
   w.vpos = reinterpret_cast<int64_t*>(p);
   p += pad256(S * 8);
   w.list = reinterpret_cast<int32_t*>(p);
+  p += pad256(S * 4);
+  w.lent = reinterpret_cast<int32_t*>(p);
   p += pad256(S * 4);
   w.count = reinterpret_cast<int32_t*>(p);
   p += pad256(4);
@@ -683,7 +686,10 @@ __global__ void __launch_bounds__(kR2PrepareThreads) r2_prepare_kernel(R2Work W,
     const int64_t at = listed + block_excl_scan_i64(s >= 0 ? 1 : 0, red, &total);
     if (s >= 0) {
       W.gate[s] = 1;
-      if (at < num_slots) W.list[at] = s;                     // a slot listed twice could overflow it
+      if (at < num_slots) {                                   // a slot listed twice could overflow it
+        W.list[at] = s;
+        W.lent[at] = j;
+      }
     }
     listed += total;
   }
@@ -765,7 +771,8 @@ __global__ void __launch_bounds__(256) r2_ring_fill_kernel(PrefillArgs A, RingPa
 constexpr int64_t kR2ListGrid = 512;
 
 template <int D>
-static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work, hipStream_t stream) {
+static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work, hipStream_t stream,
+                                     hipStream_t side, hipEvent_t fork, hipEvent_t join) {
   using M = ChunkCfg<D>;
   const int S = A.num_slots;
   const RingParts R = ring_parts(ring, A.h_k, A.h_v, D, A.chunk, S);
@@ -775,6 +782,13 @@ static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work
   hipLaunchKernelGGL(r2_prepare_kernel, dim3(1), dim3(kR2PrepareThreads), 0, stream, W, A.slot_ids, A.batch, A.pos, S,
                      A.chunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // With a second stream, the listed slots' chain (chunk form, then their step) runs there, beside
+  // the step of every other slot, whose state stream it would otherwise wait for.
+  const bool split = side != nullptr;
+  if (split &&
+      ((e = hipEventRecord(fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess))
+    return e;
+  const hipStream_t cs = split ? side : stream;
   // the chunk form over every gated slot's ring: recorded chunk-start state in, new one into the slot
   PrefillArgs F{};
   F.cu = W.cu;
@@ -798,24 +812,36 @@ static hipError_t launch_decode_r2_t(const DecodeArgs& A, void* ring, void* work
   const int64_t np = static_cast<int64_t>(S) * A.h_v, ns = np * (D / M::NS);
   const unsigned gp = static_cast<unsigned>(np < kR2ListGrid ? np : kR2ListGrid);
   const unsigned gs = static_cast<unsigned>(ns < kR2ListGrid ? ns : kR2ListGrid);
-  hipLaunchKernelGGL((chunk_prep_list_kernel<D>), dim3(gp), dim3(256), 0, stream, F, W.ws, W.list, W.count);
+  hipLaunchKernelGGL((chunk_prep_list_kernel<D>), dim3(gp), dim3(256), 0, cs, F, W.ws, W.list, W.count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_state_list_kernel<D>), dim3(gs), dim3(256), 0, stream, F, W.ws, 1, W.list, W.count);
+  hipLaunchKernelGGL((chunk_state_list_kernel<D>), dim3(gs), dim3(256), 0, cs, F, W.ws, 1, W.list, W.count);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the token from that state (recorded at the chunk start), then the ring and the positions
   DecodeArgs B = A;
   B.events = nullptr;
   B.skip_advance = 1;
-  if ((e = launch_decode(D, D, IO_BF16, B, stream)) != hipSuccess) return e;
+  if (split) {
+    // the listed entries' step after their chunk form; every other slot's step meanwhile
+    const int64_t gl = A.max_wgs > 0 && A.max_wgs < kR2ListGrid ? A.max_wgs : kR2ListGrid;
+    if ((e = launch_decode_list(D, D, IO_BF16, B, W.lent, W.count, static_cast<unsigned>(gl), cs)) != hipSuccess)
+      return e;
+    if ((e = hipEventRecord(join, cs)) != hipSuccess) return e;
+    B.skip_slot = W.gate;
+    if ((e = launch_decode(D, D, IO_BF16, B, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
+  } else {
+    if ((e = launch_decode(D, D, IO_BF16, B, stream)) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((r2_ring_append_kernel<D>), dim3(static_cast<unsigned>(A.batch)), dim3(256), 0, stream, A, R);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record_event(A.events, 1, stream);
 }
 
-hipError_t launch_decode_r2(int d, const DecodeArgs& A, void* ring, void* work, hipStream_t stream) {
-  if (d == 32) return launch_decode_r2_t<32>(A, ring, work, stream);
-  if (d == 64) return launch_decode_r2_t<64>(A, ring, work, stream);
-  if (d == 128) return launch_decode_r2_t<128>(A, ring, work, stream);
+hipError_t launch_decode_r2(int d, const DecodeArgs& A, void* ring, void* work, hipStream_t stream,
+                            hipStream_t side, hipEvent_t fork, hipEvent_t join) {
+  if (d == 32) return launch_decode_r2_t<32>(A, ring, work, stream, side, fork, join);
+  if (d == 64) return launch_decode_r2_t<64>(A, ring, work, stream, side, fork, join);
+  if (d == 128) return launch_decode_r2_t<128>(A, ring, work, stream, side, fork, join);
   return hipErrorInvalidValue;
 }
 

@@ -72,6 +72,7 @@ __device__ __forceinline__ void decode_step_item(const DecodeArgs& A, int64_t vb
   const int col0 = z * Cfg::WG_COLS;
   const int32_t slot = A.slot_ids[e];
   if (slot < 0 || slot >= A.num_slots) return;                  // uniform across the block
+  if (A.skip_slot != nullptr && A.skip_slot[slot] != 0) return; // uniform: a later launch steps it
   // With chunk-start work the position is read here and advanced by decode_advance_kernel after
   // this launch; without it the position is not read, and one workgroup advances it below.
   const bool chunk_work = A.boundary != nullptr || A.round_boundary != 0;
@@ -135,6 +136,24 @@ __global__ void __launch_bounds__((StepCfg<DK, DV>::THREADS)) decode_step_stride
   for (int64_t vb = blockIdx.x; vb < A.grid_items; vb += gridDim.x) {
     if (vb != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
     decode_step_item<DK, DV, IO>(A, vb);
+  }
+}
+
+// The step over listed batch entries only: the workgroups take (listed entry, value head, column
+// group) items in turn.  entries[0 .. *count) are batch indices; the count is known on the device.
+template <int DK, int DV, int IO>
+__global__ void __launch_bounds__((StepCfg<DK, DV>::THREADS)) decode_step_list_kernel(DecodeArgs A,
+                                                                                     const int32_t* entries,
+                                                                                     const int32_t* count) {
+  constexpr int NCG = DV / StepCfg<DK, DV>::WG_COLS;
+  const int64_t per = static_cast<int64_t>(A.h_v) * NCG;
+  const int32_t n = *count < A.batch ? *count : A.batch;
+  const int64_t items = static_cast<int64_t>(n > 0 ? n : 0) * per;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    if (it != blockIdx.x) __syncthreads();                 // the previous item is done with LDS
+    const int32_t en = entries[it / per];
+    if (en < 0 || en >= A.batch) continue;                 // uniform across the block
+    decode_step_item<DK, DV, IO>(A, static_cast<int64_t>(en) * per + it % per);
   }
 }
 
@@ -206,6 +225,22 @@ static hipError_t launch_resync_t(const DecodeArgs& A, hipStream_t stream) {
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream) {
 #define CPR_CASE(D, IOV) \
   if (dk == D && dv == D && io == IOV) return launch_decode_t<D, D, IOV>(A, stream);
+  CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
+  CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
+  CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)
+  CPR_CASE(128, IO_F32) CPR_CASE(128, IO_BF16)
+#undef CPR_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_list(int dk, int dv, int io, const DecodeArgs& A, const int32_t* entries,
+                              const int32_t* count, unsigned grid, hipStream_t stream) {
+#define CPR_CASE(D, IOV)                                                                                         \
+  if (dk == D && dv == D && io == IOV) {                                                                         \
+    hipLaunchKernelGGL((decode_step_list_kernel<D, D, IOV>), dim3(grid), dim3(StepCfg<D, D>::THREADS), 0, stream, \
+                       A, entries, count);                                                                       \
+    return hipGetLastError();                                                                                    \
+  }
   CPR_CASE(16, IO_F32) CPR_CASE(16, IO_BF16)
   CPR_CASE(32, IO_F32) CPR_CASE(32, IO_BF16)
   CPR_CASE(64, IO_F32) CPR_CASE(64, IO_BF16)

@@ -25,6 +25,9 @@ struct gdn_state {
   uint32_t wait_limit;   // polls per bounded wait of the overlapped kernel (0: the default)
   void* r2_ring;         // R2 resynchronisation in decode (gdn_state_attach_r2): token ring and workspace
   void* r2_work;
+  hipStream_t r2_side;   // and the second stream (default priority) and events of its step's fork and join
+  hipEvent_t r2_fork;
+  hipEvent_t r2_join;
 };
 
 namespace {
@@ -264,12 +267,23 @@ int gdn_state_alloc(const gdn_policy* policy, int32_t num_slots, float* state, i
   st->wait_limit = 0;
   st->r2_ring = nullptr;
   st->r2_work = nullptr;
+  st->r2_side = nullptr;
+  st->r2_fork = st->r2_join = nullptr;
   *out = st;
   return ok();
 }
 
+static void release_r2_streams(gdn_state* st) {
+  if (st->r2_join != nullptr) (void)hipEventDestroy(st->r2_join);
+  if (st->r2_fork != nullptr) (void)hipEventDestroy(st->r2_fork);
+  if (st->r2_side != nullptr) (void)hipStreamDestroy(st->r2_side);
+  st->r2_side = nullptr;
+  st->r2_fork = st->r2_join = nullptr;
+}
+
 int gdn_state_free(gdn_state* st) {
   if (st == nullptr) return ok();
+  release_r2_streams(st);
   if (st->owns) {
     (void)hipFree(st->state);
     (void)hipFree(st->pos);
@@ -350,6 +364,7 @@ int gdn_state_attach_r2(gdn_state* st, void* ring, size_t ring_bytes, void* work
   if (st == nullptr) return fail(GDN_EINVAL, "gdn_state_attach_r2: state handle is NULL");
   if (ring == nullptr && workspace == nullptr) {
     st->r2_ring = st->r2_work = nullptr;
+    release_r2_streams(st);
     return ok();
   }
   if (ring == nullptr || workspace == nullptr)
@@ -364,6 +379,17 @@ int gdn_state_attach_r2(gdn_state* st, void* ring, size_t ring_bytes, void* work
                 (long long)rb, workspace_bytes, (long long)wb);
   if ((reinterpret_cast<uintptr_t>(ring) | reinterpret_cast<uintptr_t>(workspace)) % 16 != 0)
     return fail(GDN_EINVAL, "gdn_state_attach_r2: ring and workspace must be 16-byte aligned");
+  if (st->r2_side == nullptr) {
+    // on the current device, which holds the pool; without one (or on failure) the decode step
+    // runs in sequence on the caller's stream, and the error is cleared
+    hipError_t e = hipStreamCreateWithFlags(&st->r2_side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->r2_fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&st->r2_join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      release_r2_streams(st);
+      (void)hipGetLastError();
+    }
+  }
   st->r2_ring = ring;
   st->r2_work = workspace;
   return ok();
@@ -592,7 +618,8 @@ int gdn_decode_step(gdn_state* st, const int32_t* slot_ids, int32_t batch, const
   A.round_boundary = P.state_dtype == GDN_BF16;
   A.events = events;
   const hipError_t e = st->r2_ring != nullptr
-                           ? cpr::launch_decode_r2(P.dk, A, st->r2_ring, st->r2_work, static_cast<hipStream_t>(stream))
+                           ? cpr::launch_decode_r2(P.dk, A, st->r2_ring, st->r2_work, static_cast<hipStream_t>(stream),
+                                                   st->r2_side, st->r2_fork, st->r2_join)
                            : cpr::launch_decode(P.dk, P.dv, P.io_dtype, A, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gdn_decode_step launch");
   return ok();

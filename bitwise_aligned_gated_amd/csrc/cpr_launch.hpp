@@ -24,6 +24,9 @@ hipError_t static_scratch(void** out);
 // Whether every workgroup of the overlapped kernel is resident at once (one per CU).
 bool overlap_fits(int dk, int dv, const PrefillArgs& A);
 hipError_t launch_decode(int dk, int dv, int io, const DecodeArgs& A, hipStream_t stream);
+// The step over the batch entries entries[0 .. *count) only, on `grid` workgroups taking them in turn.
+hipError_t launch_decode_list(int dk, int dv, int io, const DecodeArgs& A, const int32_t* entries,
+                              const int32_t* count, unsigned grid, hipStream_t stream);
 hipError_t launch_resync(int dk, int dv, const DecodeArgs& A, hipStream_t stream);
 hipError_t launch_backward(int dk, int dv, int io, const BackwardArgs& A, hipStream_t stream);
 // Parts of <G, S_0> the adjoint pass stores per chunk start and value head (head dim d).
@@ -58,6 +61,10 @@ int64_t chunked_workspace_floats(int d);
 // ring for slots at a chunk start, then the pinned step, then the ring append).
 int64_t r2_ring_bytes(int h_k, int h_v, int d, int chunk, int num_slots);
 int64_t r2_workspace_bytes(int h_v, int d, int num_slots);
-hipError_t launch_decode_r2(int d, const DecodeArgs& A, void* ring, void* work, hipStream_t stream);
+// The chunk form and the listed slots' step run on the second stream `side` (forked from `stream`
+// and joined back before the ring append by the two events), beside the other slots' step; side
+// NULL: all in sequence on `stream`.
+hipError_t launch_decode_r2(int d, const DecodeArgs& A, void* ring, void* work, hipStream_t stream,
+                            hipStream_t side, hipEvent_t fork, hipEvent_t join);
 
 }  // namespace cpr

@@ -382,7 +382,14 @@ int gdn_state_resync(gdn_state* st, const int32_t* slot_ids, int32_t n, void* st
  *                           [H_v][dv]), a and b (fp32 [H_v]); -1 on bad input.
  *   gdn_r2_workspace_bytes  the chunk form's workspace for one chunk per slot plus small tables.
  *   gdn_state_attach_r2     binds caller-owned device memory (16-byte aligned, at least those
- *                           sizes); both NULL detaches.  Host-only, no device work. */
+ *                           sizes); both NULL detaches.  The first attach also creates, on the
+ *                           current device (the pool's), a second HIP stream at the default
+ *                           priority and two events: gdn_decode_step runs the listed slots'
+ *                           resynchronisation and step on it, forked from and joined back into
+ *                           the caller's stream (graph capture follows the fork), beside the
+ *                           other slots' step.  Where they cannot be created (no device), the
+ *                           step runs in sequence on the caller's stream, with the same bits.
+ *                           Detaching or gdn_state_free releases them.  No device work. */
 int64_t gdn_r2_ring_bytes(const gdn_policy* policy, int32_t num_slots);
 int64_t gdn_r2_workspace_bytes(const gdn_policy* policy, int32_t num_slots);
 int gdn_state_attach_r2(gdn_state* st, void* ring, size_t ring_bytes, void* workspace, size_t workspace_bytes);

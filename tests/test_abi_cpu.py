@@ -320,9 +320,9 @@ def test_r2_sizes_and_attach_errors():
     n = 256 * 64
     ring = 2 * pad(n * 16 * 128 * 2) + pad(n * 32 * 128 * 2) + 2 * pad(n * 32 * 4)
     assert lib.gdn_r2_ring_bytes(ctypes.byref(p.c()), 256) == ring
-    # the one-chunk batch (cu_seqlens, slot ids, gates, positions), the list of gated slots and its
-    # count, then the chunk form's workspace for one row per slot
-    ws = pad(257 * 4) + 2 * pad(256 * 4) + pad(256 * 8) + pad(256 * 4) + pad(4) + 256 * 32 * (3 * 64 * 128 + 2 * 72) * 4
+    # the one-chunk batch (cu_seqlens, slot ids, gates, positions), the list of gated slots, their
+    # batch entries and the count, then the chunk form's workspace for one row per slot
+    ws = pad(257 * 4) + 2 * pad(256 * 4) + pad(256 * 8) + 2 * pad(256 * 4) + pad(4) + 256 * 32 * (3 * 64 * 128 + 2 * 72) * 4
     assert lib.gdn_r2_workspace_bytes(ctypes.byref(p.c()), 256) == ws
     assert lib.gdn_r2_ring_bytes(ctypes.byref(cpr.Policy(16, 32, 128, 128, chunk=100).c()), 4) == -1
     assert lib.gdn_r2_ring_bytes(ctypes.byref(cpr.Policy(16, 32, 16, 16).c()), 4) == -1
