@@ -187,14 +187,16 @@ def _prompt_plus_generated(prompts: gi.GdnInputs, steps, order):
                         prompts.io, cu, *(parts[nm] for nm in ("q", "k", "v", "a", "b")))
 
 
-@pytest.mark.parametrize("dim,chunk", [(32, 16), (128, 64)])
-def test_r2_decode_equals_one_chunked_r2_prefill(dim, chunk):
+@pytest.mark.parametrize("dim,chunk,cap", [(32, 16, 0), (128, 64, 0), (128, 64, 7)])
+def test_r2_decode_equals_one_chunked_r2_prefill(dim, chunk, cap):
     """R2 inside gdn_decode_step: prompts prefilled with gdn_prefill_chunked(R2) into a pool with R2
     attached, then decode steps that cross several chunk starts (slots listed in a different order
     every step): every decode output and the final states equal, bit for bit, one chunked R2
     prefill over prompt and generated tokens; the boundary record holds R2's last chunk-start state.
     The resynchronisation changes values (an R1 decode of the same tokens differs), and the
-    outputs stay within the bf16 tolerance of the oracle."""
+    outputs stay within the bf16 tolerance of the oracle.  With cap > 0 the decode steps run under
+    that workgroup cap (the listed slots' step and the others' step then take their items in
+    turn), with the same bits."""
     cpr = lib()
     lens = [chunk, 1, 100, 2 * chunk, 37, 3 * chunk + 5]
     T = 2 * chunk + 11
@@ -204,7 +206,7 @@ def test_r2_decode_equals_one_chunked_r2_prefill(dim, chunk):
     rng = np.random.default_rng(41)
     order = [rng.permutation(len(lens)).tolist() for _ in range(T)]
     P = policy_of(prompts)
-    say(f"R2 decode dim={dim} C={chunk}: prompts {lens}, {T} steps")
+    say(f"R2 decode dim={dim} C={chunk} cap={cap}: prompts {lens}, {T} steps")
     pool = cpr.StatePool(P, len(lens), boundary=True)
     pool.attach_r2()
     cpr.gdn_prefill_chunked(pool, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b,
@@ -212,6 +214,8 @@ def test_r2_decode_equals_one_chunked_r2_prefill(dim, chunk):
     r1 = cpr.StatePool(P, len(lens), boundary=True)
     cpr.gdn_prefill_chunked(r1, prompts.cu_seqlens, prompts.q, prompts.k, prompts.v, prompts.a, prompts.b,
                             outputs=cpr.GDN_CHUNKED_R2)
+    if cap:
+        pool.set_max_workgroups(cap)
     outs = torch.empty((len(lens), T, P.h_v, P.dv), dtype=torch.bfloat16, device="cuda")
     outs_r1 = torch.empty_like(outs)
     for s, st in enumerate(steps):
