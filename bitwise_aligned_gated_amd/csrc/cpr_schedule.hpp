@@ -10,7 +10,8 @@ constexpr int kLeaf = 8;      // rows per leaf of the pinned dot product
 // moves a bit; it enters only the deployment digest.  Raised with every change of a kernel's work
 // mapping (4: one-column-per-lane decode in state order with a separate position update, the
 // overlapped prefill, and the chunk-64 backward under fp32 boundaries; 5: the chunk-form output
-// kernel with whole column tiles per wave, and the R2 decode step's four launches).
-constexpr int kMappingVersion = 5;
+// kernel with whole column tiles per wave, and the R2 decode step's four launches; 6: the R2 step's
+// listed slots resynchronised and stepped on a second stream, 512 list-driven workgroups).
+constexpr int kMappingVersion = 6;
 
 }  // namespace cpr

@@ -79,10 +79,10 @@ def test_semantic_and_deployment_digests():
         assert cpr.gdn_semantic_digest(other) == cpr.gdn_semantic_digest(p)
     assert cpr.gdn_semantic_digest(cpr.Policy(16, 32, 64, 64)) != cpr.gdn_semantic_digest(p)
     dep = cpr.gdn_deployment_digest(p)
-    # canonical bytes: the tag, chunk (fp32 boundaries) and the kernels' work-mapping version (5)
-    assert dep == hashlib.sha256(b"cpr-gdn-deploy-v1" + struct.pack("<2i", 64, 5)).digest()
+    # canonical bytes: the tag, chunk (fp32 boundaries) and the kernels' work-mapping version (6)
+    assert dep == hashlib.sha256(b"cpr-gdn-deploy-v1" + struct.pack("<2i", 64, 6)).digest()
     assert cpr.gdn_deployment_digest(cpr.Policy(16, 32, 128, 128, chunk=64, boundary="bf16")) == \
-        hashlib.sha256(b"cpr-gdn-deploy-v1" + struct.pack("<2i", 0, 5)).digest()
+        hashlib.sha256(b"cpr-gdn-deploy-v1" + struct.pack("<2i", 0, 6)).digest()
     # fp32 boundaries: chunk is a deployment setting (deployment digest moves, policy digest not)
     p16 = cpr.Policy(16, 32, 128, 128, chunk=16)
     assert cpr.gdn_deployment_digest(p16) != dep and cpr.gdn_policy_digest(p16) == cpr.gdn_policy_digest(p)
